@@ -1,0 +1,66 @@
+"""Token append and copy-on-write of a tail block (bit-exact references).
+
+Test infrastructure only (see the package docstring).
+
+Pools are numpy arrays [NB, B, Hkv, d] (or [L, NB, B, Hkv, d] for the
+multi-layer COW) of any dtype; bf16 pools are passed as their uint16 bit
+patterns so that comparisons are bitwise.  Every function returns a new
+array and leaves its input untouched.
+"""
+
+import numpy as np
+
+
+def append(pool, new, block_tables, positions, B):
+    """Write request s's new token (``new[s]``, [Hkv, d]) at logical position positions[s].
+
+    The token goes to slot pos % B of physical block table[s][pos // B]; no
+    other slot moves ([Slides] "写满一块，再拿下一块").  A negative position
+    means the request writes nothing this step.
+    """
+    out = np.array(pool, copy=True)
+    for s in range(len(positions)):
+        pos = int(positions[s])
+        if pos < 0:
+            continue
+        blk = int(block_tables[s][pos // B])
+        out[blk, pos % B] = new[s]
+    return out
+
+
+def cow_copy(pool, src_blocks, dst_blocks, n_valid):
+    """Copy slots [0, n_valid) of each source block into its destination block.
+
+    The copy-on-write step of [Slides] "先确保分配成功，再改变可见状态"
+    (``copy_valid_kv(tail, new)``): only the valid range is copied; slots at or
+    beyond n_valid of the destination, and every other block, keep their bytes.
+    Pairs are applied in order.
+    """
+    out = np.array(pool, copy=True)
+    for a, b, n in zip(src_blocks, dst_blocks, n_valid):
+        out[int(b), : int(n)] = out[int(a), : int(n)]
+    return out
+
+
+def cow_copy_layers(pools, src_blocks, dst_blocks, n_valid):
+    """The COW copy applied in every layer of a [L, NB, B, Hkv, d] pool.
+
+    All layers share one token -> block numbering, so a copied block must be
+    copied in each layer's storage ([Slides] "128 KiB：每新增一个位置的账单").
+    """
+    return np.stack([cow_copy(p, src_blocks, dst_blocks, n_valid) for p in pools])
+
+
+def gather_padded(pool, block_tables, seq_lens, B, fill):
+    """[S, MB*B, Hkv, d]: token t of request s at [s, t]; positions >= n_s hold ``fill``.
+
+    The contiguous view a block table describes, for checking the device-side
+    address computation bit for bit.
+    """
+    pool = np.asarray(pool)
+    S, MB = np.asarray(block_tables).shape
+    out = np.full((S, MB * B) + pool.shape[2:], fill, dtype=pool.dtype)
+    for s in range(S):
+        for t in range(int(seq_lens[s])):
+            out[s, t] = pool[int(block_tables[s][t // B]), t % B]
+    return out

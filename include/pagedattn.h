@@ -1,0 +1,164 @@
+/*
+ * libpagedattn — paged-attention decode for AMD MI355X (gfx950), C ABI.
+ *
+ * Pages cited (title, then slide / section / equation on that page):
+ *   [Slides]  "PagedAttention：让 KV cache 按需生长"
+ *   [Budgets] "内存预算约束下的语言模型服务：注意力、分页与调度"
+ *   [Serving] "PagedAttention 与在线推理：KV 分页、共享及调度的联合分析"
+ *
+ * Data layout (all row-major, all device memory owned by the caller):
+ *   q             [S, Hq, d]            element type `dtype`
+ *   k_pool/v_pool [NB, B, Hkv, d]       physical block, slot, KV head, dim — K and V
+ *                                       in separate pools ([Slides] "把 token 6 变成
+ *                                       真正的内存地址")
+ *   block_tables  int32 [S, MB]         logical block -> physical block ([Slides]
+ *                                       "顺序留在表里，数据放进空闲块")
+ *   seq_lens      int32 [S]             tokens each request attends to
+ *   out           float32 [S, Hq, d]
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are device pointers unless stated; the library never allocates,
+ *     frees or synchronises inside these calls.  Work is enqueued on `stream`
+ *     (NULL = the default stream) and the call returns.
+ *   - Arguments that live on the host (sizes, the dims struct) are validated
+ *     before anything is enqueued; a failed check returns an error status and
+ *     enqueues nothing.  pa_last_error() then describes the failure
+ *     (thread-local, valid until the next call on that thread).
+ *   - Values that live on the device (lengths, table entries, positions) are
+ *     the caller's contract: tables must be published only after capacity was
+ *     checked ([Slides] "三个空闲块，四个请求同时跨边界").  The kernels still
+ *     never access memory outside the buffers described by `dims`: a request
+ *     whose length exceeds MB*B, or whose table names a block outside [0, NB),
+ *     gets NaN outputs; an append or copy that would leave the pool is skipped.
+ *   - Query head h reads KV head h / (Hq / Hkv) (contiguous GQA groups).
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1, /* null pointer, bad size, Hq % Hkv != 0, ... */
+  PA_ERR_UNSUPPORTED = -2, /* a shape or dtype no kernel here is built for */
+  PA_ERR_WORKSPACE = -3,   /* split-K workspace missing, misaligned or too small */
+  PA_ERR_LAUNCH = -4       /* the HIP runtime refused the launch */
+} pa_status;
+
+typedef enum {
+  PA_F32 = 0, /* IEEE binary32 */
+  PA_BF16 = 1 /* bfloat16 (upper half of a binary32) */
+} pa_dtype;
+
+/* Shape descriptor.  Sizes are element counts. */
+typedef struct {
+  int32_t num_seqs;           /* S  >= 0 (0 makes every call a no-op)          */
+  int32_t num_q_heads;        /* Hq >= 1                                       */
+  int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0                       */
+  int32_t head_dim;           /* d; this build supports 128                    */
+  int32_t max_blocks_per_seq; /* MB >= 1: row stride of block_tables          */
+  int32_t num_blocks;         /* NB >= 1: blocks in each pool                  */
+  pa_dtype dtype;             /* element type of q, pools, new K/V             */
+  int32_t num_splits;         /* split-K parts: 0 = chosen by the library from
+                                 (S, Hkv, MB) alone, >= 1 forces that count     */
+  void* workspace;            /* device scratch for split-K partial states,
+                                 256-byte aligned, caller-owned; may be NULL when
+                                 paged_attn_plan reports 0 bytes                */
+  size_t workspace_bytes;
+} pa_dims;
+
+/* Library version of this header's ABI (PA_ABI_VERSION). */
+int32_t pa_abi_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* pa_status_string(pa_status status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* pa_last_error(void);
+
+/*
+ * Split-K plan for paged_attn_decode at block size B: the number of splits
+ * the decode will use and the workspace it needs (0 when no split is used).
+ * Depends only on host-known sizes, so repeated calls agree.
+ */
+pa_status paged_attn_plan(const pa_dims* dims, int32_t B, int32_t* num_splits,
+                          size_t* workspace_bytes);
+
+/*
+ * One decode step of one layer: for every request s and query head h,
+ *   out[s,h,:] = sum_t softmax_t(scale * <q[s,h,:], K_s[t,g,:]>) * V_s[t,g,:],
+ * t over the seq_lens[s] tokens of request s, g = h / (Hq/Hkv), where token t
+ * lives in slot t % B of physical block block_tables[s][t / B] ([Slides]
+ * "读 token 6，先查表，再找偏移").  Table entries at or past ceil(n/B) are not
+ * read; slots of the last block at or past n are masked and their contents
+ * never enter the result ([Slides] "分页以后，attention 仍然按完整历史归一化",
+ * quiz "逻辑顺序没错，为什么 attention 输出还是错？").  Blocks are combined with
+ * the online-softmax state of [Budgets] eq. (4); long histories are divided
+ * into contiguous block ranges whose (m, l, o) states are merged afterwards,
+ * so the result depends only on logical positions, never on physical ids.
+ * A request with seq_lens[s] == 0 gets out = 0.
+ *
+ * B: block size in tokens (this build: 16).  scale: multiplies q.k (e.g.
+ * 1/sqrt(d)).  Accumulation is float32; out is float32.
+ */
+pa_status paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_tables, const int32_t* seq_lens,
+                            int32_t B, float scale, float* out, hipStream_t stream,
+                            const pa_dims* dims);
+
+/*
+ * Append one token per request ([Slides] "写满一块，再拿下一块"):
+ *   k_pool[block_tables[s][p / B], p % B, :, :] = k_new[s, :, :]   (p = positions[s])
+ * and the same for V.  k_new/v_new are [S, Hkv, d] of `dtype`; positions is
+ * int32 [S] on the device, the logical index the token takes (the request's
+ * length before the write); a negative position skips the request.  The
+ * target block must already be in the table and privately owned — a shared
+ * tail is first copied with kv_cow_copy on the same stream ([Slides]
+ * "先确保分配成功，再改变可见状态").  Bytes are copied exactly.
+ */
+pa_status kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                    const int32_t* block_tables, const int32_t* positions, int32_t B,
+                    hipStream_t stream, const pa_dims* dims);
+
+/*
+ * Copy-on-write of shared tail blocks ([Slides] "只读时共用，要写入时再分开",
+ * "先确保分配成功，再改变可见状态"): for each pair i and each layer l,
+ *   pool_l[dst_blocks[i], 0:n_valid[i], :, :] = pool_l[src_blocks[i], 0:n_valid[i], :, :]
+ * for both K and V.  src_blocks, dst_blocks, n_valid are int32 [num_pairs] on
+ * the device.  Layer l's pool starts layer_stride_elems elements after layer
+ * l-1's (all layers share one block numbering, so a copied block is copied in
+ * every layer); num_layers = 1 ignores the stride.  Slots at or past n_valid
+ * and all other blocks are left untouched.  Destinations must be distinct
+ * and differ from every source.  Enqueue it before the branch's kv_append on
+ * the same stream: stream order makes the copy visible to the write.
+ */
+pa_status kv_cow_copy(void* k_pool, void* v_pool, const int32_t* src_blocks,
+                      const int32_t* dst_blocks, const int32_t* n_valid, int32_t num_pairs,
+                      int32_t B, int32_t num_layers, int64_t layer_stride_elems,
+                      hipStream_t stream, const pa_dims* dims);
+
+/*
+ * Debug helper, not on the decode path: materialise each request's history
+ * contiguously through the same address computation the decode uses.
+ *   k_out[s, t, :, :] = k_pool[block_tables[s][t / B], t % B, :, :]  for t < seq_lens[s]
+ * k_out/v_out are [S, MB*B, Hkv, d] of `dtype`; positions t >= seq_lens[s]
+ * are not written.
+ */
+pa_status paged_kv_gather(const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                          const int32_t* seq_lens, int32_t B, void* k_out, void* v_out,
+                          hipStream_t stream, const pa_dims* dims);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,21 @@
+"""Paged-attention decode for AMD MI355X (gfx950): Python face of libpagedattn.
+
+The compute runs in hand-written HIP kernels behind a C ABI
+(``include/pagedattn.h``); this package only marshals torch tensors into it.
+"""
+
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    PA_BF16,
+    PA_F32,
+    DecodeLaunch,
+    PagedAttnError,
+    declared_functions,
+    kv_append,
+    kv_cow_copy,
+    load,
+    make_dims,
+    paged_attn_decode,
+    paged_attn_plan,
+    paged_kv_gather,
+)

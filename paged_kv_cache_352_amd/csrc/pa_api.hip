@@ -1,0 +1,234 @@
+// C-ABI entry points of libpagedattn: host-side validation, split planning
+// and launches.  Every check on host-resident arguments happens before any
+// work is enqueued; nothing here allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_size(pa_dtype t) { return t == PA_BF16 ? 2 : 4; }
+
+// Shape checks shared by every entry point.
+pa_status check_dims(const pa_dims* d, int32_t B, bool need_attention_shape) {
+  if (!d) return fail(PA_ERR_INVALID_ARG, "dims is NULL");
+  if (d->num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs = %d < 0", d->num_seqs);
+  if (d->num_kv_heads < 1) return fail(PA_ERR_INVALID_ARG, "num_kv_heads = %d < 1", d->num_kv_heads);
+  if (d->head_dim < 1) return fail(PA_ERR_INVALID_ARG, "head_dim = %d < 1", d->head_dim);
+  if (d->max_blocks_per_seq < 1) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq = %d < 1", d->max_blocks_per_seq);
+  if (d->num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "num_blocks = %d < 1", d->num_blocks);
+  if (B < 1) return fail(PA_ERR_INVALID_ARG, "block size B = %d < 1", B);
+  if (d->dtype != PA_F32 && d->dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "dtype %d", (int)d->dtype);
+  if ((int64_t)d->max_blocks_per_seq * B > INT32_MAX)
+    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * B overflows int32");
+  if (need_attention_shape) {
+    if (d->num_q_heads < 1) return fail(PA_ERR_INVALID_ARG, "num_q_heads = %d < 1", d->num_q_heads);
+    if (d->num_q_heads % d->num_kv_heads)
+      return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", d->num_q_heads,
+                  d->num_kv_heads);
+    const int G = d->num_q_heads / d->num_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+      return fail(PA_ERR_UNSUPPORTED, "query heads per KV head = %d (supported: 1, 2, 4, 8)", G);
+    if (d->head_dim != pa::kHeadDim) return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 128)", d->head_dim);
+    if (B != 16) return fail(PA_ERR_UNSUPPORTED, "block size %d (supported: 16)", B);
+    if (d->num_splits < 0) return fail(PA_ERR_INVALID_ARG, "num_splits = %d < 0", d->num_splits);
+  }
+  // slot rows are copied as 16-byte vectors
+  if (((int64_t)d->num_kv_heads * d->head_dim * elem_size(d->dtype)) % 16)
+    return fail(PA_ERR_UNSUPPORTED, "Hkv * d * element size must be a multiple of 16 bytes");
+  return PA_OK;
+}
+
+// Splits depend only on (S, Hkv, MB): enough waves to keep ~8 per CU busy,
+// never fewer than ~8 blocks per split.  Returns (P, blocks per split).
+void plan_splits(const pa_dims* d, int* P_out, int* bps_out) {
+  const int MB = d->max_blocks_per_seq;
+  int P = d->num_splits;
+  if (P == 0) {
+    const int64_t items = (int64_t)d->num_seqs * d->num_kv_heads;
+    const int64_t target = 2048;
+    P = (int)((target + items - 1) / (items > 0 ? items : 1));
+    const int maxP = (MB + 7) / 8;
+    P = P < 1 ? 1 : (P > maxP ? maxP : P);
+    if (P < 1) P = 1;
+  }
+  if (P > MB) P = MB;
+  const int bps = (MB + P - 1) / P;
+  *P_out = (MB + bps - 1) / bps;  // drop splits that could never hold a block
+  *bps_out = bps;
+}
+
+pa_status launched(hipError_t e) {
+  if (e != hipSuccess) return fail(PA_ERR_LAUNCH, "HIP launch failed: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_status_string(pa_status st) {
+  switch (st) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH";
+  }
+  return "PA_UNKNOWN_STATUS";
+}
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+pa_status paged_attn_plan(const pa_dims* dims, int32_t B, int32_t* num_splits, size_t* workspace_bytes) {
+  g_last_error.clear();
+  pa_status st = check_dims(dims, B, true);
+  if (st != PA_OK) return st;
+  if (!num_splits || !workspace_bytes) return fail(PA_ERR_INVALID_ARG, "output pointer is NULL");
+  int P, bps;
+  plan_splits(dims, &P, &bps);
+  *num_splits = P;
+  *workspace_bytes = (P > 1 && dims->num_seqs > 0)
+                         ? pa::decode_workspace_floats(dims->num_seqs, dims->num_q_heads, P) * sizeof(float)
+                         : 0;
+  return PA_OK;
+}
+
+pa_status paged_attn_decode(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                            const int32_t* seq_lens, int32_t B, float scale, float* out, hipStream_t stream,
+                            const pa_dims* dims) {
+  g_last_error.clear();
+  pa_status st = check_dims(dims, B, true);
+  if (st != PA_OK) return st;
+  if (dims->num_seqs == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out)
+    return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16))
+    return fail(PA_ERR_INVALID_ARG, "q, pools and out must be 16-byte aligned");
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+  int P, bps;
+  plan_splits(dims, &P, &bps);
+  const int64_t items = (int64_t)dims->num_kv_heads * dims->num_seqs * P;
+  if (items > INT32_MAX || (int64_t)dims->num_seqs * dims->num_q_heads > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "grid too large");
+
+  pa::DecodeArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.tables = block_tables;
+  a.lens = seq_lens;
+  a.out = out;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.S = dims->num_seqs;
+  a.Hq = dims->num_q_heads;
+  a.Hkv = dims->num_kv_heads;
+  a.MB = dims->max_blocks_per_seq;
+  a.NB = dims->num_blocks;
+  a.P = P;
+  a.bps = bps;
+  if (P > 1) {
+    const size_t need = pa::decode_workspace_floats(a.S, a.Hq, P) * sizeof(float);
+    if (!dims->workspace || dims->workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "split-K needs %zu workspace bytes, got %zu", need,
+                  dims->workspace ? dims->workspace_bytes : (size_t)0);
+    if (!aligned(dims->workspace, 256)) return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    float* ws = static_cast<float*>(dims->workspace);
+    const size_t no = (size_t)a.S * a.Hq * P * pa::kHeadDim;
+    a.ws_o = ws;
+    a.ws_m = ws + no;
+    a.ws_l = ws + no + (size_t)a.S * a.Hq * P;
+  }
+  return launched(pa::launch_decode(a, dims->dtype, B, a.Hq / a.Hkv, stream));
+}
+
+static pa_status kv_common(const pa_dims* dims, int32_t B, void* k_pool, void* v_pool, pa::KvArgs* a) {
+  pa_status st = check_dims(dims, B, false);
+  if (st != PA_OK) return st;
+  if (!k_pool || !v_pool) return fail(PA_ERR_INVALID_ARG, "pool pointer is NULL");
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16)) return fail(PA_ERR_INVALID_ARG, "pools must be 16-byte aligned");
+  const int64_t row = (int64_t)dims->num_kv_heads * dims->head_dim * elem_size(dims->dtype);
+  if (row > INT32_MAX / 2) return fail(PA_ERR_UNSUPPORTED, "slot row too large");
+  a->k_pool = static_cast<uint8_t*>(k_pool);
+  a->v_pool = static_cast<uint8_t*>(v_pool);
+  a->S = dims->num_seqs;
+  a->MB = dims->max_blocks_per_seq;
+  a->NB = dims->num_blocks;
+  a->B = B;
+  a->row_bytes = (int)row;
+  return PA_OK;
+}
+
+pa_status kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new, const int32_t* block_tables,
+                    const int32_t* positions, int32_t B, hipStream_t stream, const pa_dims* dims) {
+  g_last_error.clear();
+  pa::KvArgs a{};
+  if (dims && dims->num_seqs == 0) {
+    pa_status st = check_dims(dims, B, false);
+    return st;
+  }
+  pa_status st = kv_common(dims, B, k_pool, v_pool, &a);
+  if (st != PA_OK) return st;
+  if (!k_new || !v_new || !block_tables || !positions) return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(PA_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
+  if (a.S > 2147483647) return fail(PA_ERR_UNSUPPORTED, "too many requests");
+  return launched(pa::launch_append(a, static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new),
+                                    block_tables, positions, stream));
+}
+
+pa_status kv_cow_copy(void* k_pool, void* v_pool, const int32_t* src_blocks, const int32_t* dst_blocks,
+                      const int32_t* n_valid, int32_t num_pairs, int32_t B, int32_t num_layers,
+                      int64_t layer_stride_elems, hipStream_t stream, const pa_dims* dims) {
+  g_last_error.clear();
+  if (num_pairs < 0) return fail(PA_ERR_INVALID_ARG, "num_pairs = %d < 0", num_pairs);
+  if (num_layers < 1 || num_layers > 65535) return fail(PA_ERR_INVALID_ARG, "num_layers = %d outside [1, 65535]", num_layers);
+  pa::KvArgs a{};
+  pa_status st = kv_common(dims, B, k_pool, v_pool, &a);
+  if (st != PA_OK) return st;
+  if (num_pairs == 0) return PA_OK;
+  if (!src_blocks || !dst_blocks || !n_valid) return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+  const int64_t pool_elems = (int64_t)dims->num_blocks * B * dims->num_kv_heads * dims->head_dim;
+  if (num_layers > 1 && layer_stride_elems < pool_elems)
+    return fail(PA_ERR_INVALID_ARG, "layer_stride_elems %lld smaller than one layer's pool (%lld)",
+                (long long)layer_stride_elems, (long long)pool_elems);
+  const int64_t stride_bytes = num_layers > 1 ? layer_stride_elems * (int64_t)elem_size(dims->dtype) : 0;
+  if (stride_bytes % 16) return fail(PA_ERR_INVALID_ARG, "layer stride must be a multiple of 16 bytes");
+  return launched(pa::launch_cow(a, src_blocks, dst_blocks, n_valid, num_pairs, num_layers, stride_bytes, stream));
+}
+
+pa_status paged_kv_gather(const void* k_pool, const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,
+                          int32_t B, void* k_out, void* v_out, hipStream_t stream, const pa_dims* dims) {
+  g_last_error.clear();
+  pa::KvArgs a{};
+  pa_status st = kv_common(dims, B, const_cast<void*>(k_pool), const_cast<void*>(v_pool), &a);
+  if (st != PA_OK) return st;
+  if (dims->num_seqs == 0) return PA_OK;
+  if (!block_tables || !seq_lens || !k_out || !v_out) return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(k_out, 16) || !aligned(v_out, 16)) return fail(PA_ERR_INVALID_ARG, "outputs must be 16-byte aligned");
+  if (dims->max_blocks_per_seq > 65535) return fail(PA_ERR_UNSUPPORTED, "max_blocks_per_seq > 65535");
+  return launched(pa::launch_gather(a, block_tables, seq_lens, static_cast<uint8_t*>(k_out),
+                                    static_cast<uint8_t*>(v_out), stream));
+}
+
+}  // extern "C"

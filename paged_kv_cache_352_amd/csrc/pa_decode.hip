@@ -1,0 +1,315 @@
+// Paged-attention decode: one query token per request, exact softmax
+// attention over the request's history, read through its block table.
+//
+// [Slides]  = "PagedAttention：让 KV cache 按需生长"
+// [Budgets] = "内存预算约束下的语言模型服务：注意力、分页与调度"
+//
+// What is computed ([Slides] "分页以后，attention 仍然按完整历史归一化"): for
+// each logical block of the request, look up its physical block, load the
+// K/V tile, mask slots at or past the length, score, and fold the block into
+// a running (m, l, o) state with the update of [Budgets] eq. (4).  Long
+// histories are cut into contiguous ranges of logical blocks ("splits"); each
+// range is reduced to its own (m, l, o), and a second kernel merges them
+// ([Slides] quiz "逻辑顺序没错…": mergeable state, not averaged softmaxes).
+//
+// Mapping to CDNA4 (v1, vector ALU):
+//   * one 64-lane wave per work item (request s, KV head g, split p); the G
+//     query heads of the GQA group share every K/V byte the wave loads;
+//   * a K or V tile of one (block, KV head) is B rows of d contiguous
+//     elements, rows Hkv*d apart.  Lane (r, c) loads 16 bytes — dims
+//     [c*E, c*E+E) of row i*RPL + r — so a wave instruction reads RPL whole
+//     rows, each as one contiguous run;
+//   * q.k partial sums are reduced across the LPR lanes of a row with
+//     cross-lane shuffles; the running max is reduced across rows;
+//   * scores are kept in base 2 (scale*log2(e) folded into q) so every
+//     exponential is a single v_exp_f32;
+//   * work items are numbered KV-head-major and handed out XCD by XCD, so
+//     the waves that read one KV head's blocks (a shared prefix, say) sit on
+//     the same L2.
+#include <hip/hip_runtime.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWave = 64;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+struct bf16_t {
+  uint16_t bits;
+};
+
+template <typename T>
+struct Vec16;  // how a 16-byte load unpacks into float32
+
+template <>
+struct Vec16<float> {
+  static constexpr int kElems = 4;
+  __device__ static inline void unpack(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+};
+
+template <>
+struct Vec16<bf16_t> {
+  static constexpr int kElems = 8;
+  // bf16 is the upper half of a binary32, so widening is exact.
+  __device__ static inline void unpack(const uint4& v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ inline float shfl_xor(float v, int mask) { return __shfl_xor(v, mask, kWave); }
+
+// Workgroups are dispatched to the 8 XCDs round-robin; renumber them so that
+// consecutive logical work items share an XCD (and its L2).
+__device__ inline int xcd_remap(int bid, int nwg) {
+  const int x = bid % kNumXcd, k = bid / kNumXcd;
+  const int q = nwg / kNumXcd, rem = nwg % kNumXcd;
+  return x * q + min(x, rem) + k;
+}
+
+template <typename T, int G, int B>
+__global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeArgs a) {
+  constexpr int E = Vec16<T>::kElems;  // elements per 16-byte load
+  constexpr int LPR = kHeadDim / E;    // lanes per row (16 bf16, 32 fp32)
+  constexpr int RPL = kWave / LPR;     // rows per wave load (4 bf16, 2 fp32)
+  constexpr int NL = B / RPL;          // loads per tile
+  static_assert(B % RPL == 0, "block size must be a multiple of the rows one wave load covers");
+
+  const int lane = threadIdx.x;
+  const int c = lane % LPR;
+  const int r = lane / LPR;
+
+  int item = xcd_remap(blockIdx.x, gridDim.x);
+  const int p = item % a.P;
+  item /= a.P;
+  const int s = item % a.S;
+  const int kvh = item / a.S;
+
+  const int n_raw = a.lens[s];
+  bool bad = n_raw < 0 || n_raw > a.MB * B;  // outside what the table can describe
+  const int n = bad ? 0 : n_raw;
+  const int nb = (n + B - 1) / B;
+  const int j0 = p * a.bps;
+  const int j1 = min(nb, j0 + a.bps);
+
+  // q for the G heads of this group, dims [c*E, c*E+E), pre-scaled into base 2.
+  float qf[G][E];
+  {
+    const T* qp = static_cast<const T*>(a.q) + ((int64_t)s * a.Hq + (int64_t)kvh * G) * kHeadDim + c * E;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const uint4 w = *reinterpret_cast<const uint4*>(qp + g * kHeadDim);
+      Vec16<T>::unpack(w, qf[g]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) qf[g][e] *= a.scale_log2;
+    }
+  }
+
+  float m[G], l[G], o[G][E];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = kNegInf;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[g][e] = 0.f;
+  }
+
+  const int64_t row_stride = (int64_t)a.Hkv * kHeadDim;  // elements between slots
+  const int64_t blk_stride = (int64_t)B * row_stride;     // elements between blocks
+  const int64_t lane_off = (int64_t)r * row_stride + (int64_t)kvh * kHeadDim + c * E;
+  const T* kbase = static_cast<const T*>(a.k_pool) + lane_off;
+  const T* vbase = static_cast<const T*>(a.v_pool) + lane_off;
+  const int32_t* trow = a.tables + (int64_t)s * a.MB;
+
+  for (int j = j0; j < j1; ++j) {
+    const int pb = trow[j];
+    if (pb < 0 || pb >= a.NB) {  // a table entry outside the pool: poison, never dereference
+      bad = true;
+      continue;
+    }
+    uint4 kraw[NL], vraw[NL];
+    const T* kb = kbase + (int64_t)pb * blk_stride;
+    const T* vb = vbase + (int64_t)pb * blk_stride;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) kraw[i] = *reinterpret_cast<const uint4*>(kb + i * RPL * row_stride);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) vraw[i] = *reinterpret_cast<const uint4*>(vb + i * RPL * row_stride);
+
+    // Scores of this lane's NL slots for the G heads (base 2).
+    float sc[NL][G];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      float kf[E];
+      Vec16<T>::unpack(kraw[i], kf);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc = fmaf(qf[g][e], kf[e], acc);
+        sc[i][g] = acc;
+      }
+    }
+#pragma unroll
+    for (int mask = 1; mask < LPR; mask <<= 1)
+#pragma unroll
+      for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int g = 0; g < G; ++g) sc[i][g] += shfl_xor(sc[i][g], mask);
+
+    // Mask slots at or past the length ([Slides] quiz "逻辑顺序没错…" step 1).
+    const bool tail = (j + 1) * B > n;
+    bool valid[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      valid[i] = j * B + i * RPL + r < n;
+#pragma unroll
+      for (int g = 0; g < G; ++g) sc[i][g] = valid[i] ? sc[i][g] : kNegInf;
+    }
+
+    // [Budgets] eq. (4): new running max, rescale factor, block weights.
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float bm = sc[0][g];
+#pragma unroll
+      for (int i = 1; i < NL; ++i) bm = fmaxf(bm, sc[i][g]);
+#pragma unroll
+      for (int mask = LPR; mask < kWave; mask <<= 1) bm = fmaxf(bm, shfl_xor(bm, mask));
+      const float mn = fmaxf(m[g], bm);  // finite: slot 0 of block j < nb is valid
+      const float alpha = fast_exp2(m[g] - mn);
+      m[g] = mn;
+      l[g] *= alpha;
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[g][e] *= alpha;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const float pw = valid[i] ? fast_exp2(sc[i][g] - mn) : 0.f;
+        sc[i][g] = pw;
+        l[g] += pw;
+      }
+    }
+
+    // o += p * v over this lane's slots; unwritten slots never enter (0*NaN = NaN).
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      float vf[E];
+      Vec16<T>::unpack(vraw[i], vf);
+      if (tail && !valid[i]) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) vf[e] = 0.f;
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[g][e] = fmaf(sc[i][g], vf[e], o[g][e]);
+    }
+  }
+
+  // Rows hold disjoint slot subsets under the same running max: sum them.
+#pragma unroll
+  for (int mask = LPR; mask < kWave; mask <<= 1) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      l[g] += shfl_xor(l[g], mask);
+#pragma unroll
+      for (int e = 0; e < E; ++e) o[g][e] += shfl_xor(o[g][e], mask);
+    }
+  }
+  if (r != 0) return;
+
+  const float nan = __builtin_nanf("");
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int h = kvh * G + g;
+    if (a.P == 1) {
+      float* dst = a.out + ((int64_t)s * a.Hq + h) * kHeadDim + c * E;
+      const float inv = l[g] > 0.f ? 1.f / l[g] : 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) dst[e] = bad ? nan : o[g][e] * inv;
+    } else {
+      const int64_t slot = ((int64_t)s * a.Hq + h) * a.P + p;
+      float* dst = a.ws_o + slot * kHeadDim + c * E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) dst[e] = o[g][e];
+      if (c == 0) {
+        a.ws_m[slot] = bad ? 0.f : m[g];
+        a.ws_l[slot] = bad ? nan : l[g];
+      }
+    }
+  }
+}
+
+// Merge of the split states of one (request, query head):
+//   M = max_p m_p, L = sum_p 2^(m_p - M) l_p, O = sum_p 2^(m_p - M) o_p, out = O / L.
+// Empty splits carry m = -inf, l = 0 and drop out; all empty gives 0.
+__global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
+  const int sh = blockIdx.x;  // s * Hq + h
+  const int lane = threadIdx.x;
+  const float* ms = a.ws_m + (int64_t)sh * a.P;
+  const float* ls = a.ws_l + (int64_t)sh * a.P;
+  float M = kNegInf;
+  for (int p = 0; p < a.P; ++p) M = fmaxf(M, ms[p]);
+  float* dst = a.out + (int64_t)sh * kHeadDim + lane * 2;
+  if (M == kNegInf) {
+    dst[0] = 0.f;
+    dst[1] = 0.f;
+    return;
+  }
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  const float* os = a.ws_o + (int64_t)sh * a.P * kHeadDim + lane * 2;
+  for (int p = 0; p < a.P; ++p) {
+    const float w = fast_exp2(ms[p] - M);
+    L = fmaf(w, ls[p], L);
+    o0 = fmaf(w, os[p * kHeadDim], o0);
+    o1 = fmaf(w, os[p * kHeadDim + 1], o1);
+  }
+  const float inv = 1.f / L;
+  dst[0] = o0 * inv;
+  dst[1] = o1 * inv;
+}
+
+template <typename T, int G>
+hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  const int items = a.Hkv * a.S * a.P;
+  hipLaunchKernelGGL((decode_split_kernel<T, G, 16>), dim3(items), dim3(kWave), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.P == 1) return e;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.S * a.Hq), dim3(kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_group(const DecodeArgs& a, int G, hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_typed<T, 1>(a, stream);
+    case 2: return launch_typed<T, 2>(a, stream);
+    case 4: return launch_typed<T, 4>(a, stream);
+    case 8: return launch_typed<T, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+size_t decode_workspace_floats(int S, int Hq, int P) {
+  return (size_t)S * Hq * P * (kHeadDim + 2);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int B, int G, hipStream_t stream) {
+  if (B != 16) return hipErrorInvalidValue;
+  return dtype == PA_BF16 ? launch_group<bf16_t>(a, G, stream) : launch_group<float>(a, G, stream);
+}
+
+}  // namespace pa

@@ -1,0 +1,53 @@
+// Internal launch interface shared by the host entry points (pa_api.hip) and
+// the kernel translation units.  Not installed; not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pagedattn.h"
+
+namespace pa {
+
+constexpr int kHeadDim = 128;  // d supported by the decode kernels
+constexpr int kNumXcd = 8;     // MI355X: 8 accelerator dies, each with its own L2
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* tables;
+  const int32_t* lens;
+  float* out;       // final output [S, Hq, d]
+  float* ws_o;      // split partial o [S, Hq, P, d]   (P > 1 only)
+  float* ws_m;      // split partial m [S, Hq, P]      (log2 domain)
+  float* ws_l;      // split partial l [S, Hq, P]
+  float scale_log2; // scale * log2(e): scores are kept in base 2
+  int S, Hq, Hkv, MB, NB;
+  int P;            // number of splits
+  int bps;          // blocks per split
+};
+
+// Workspace floats for P splits: S*Hq*P*(d + 2).
+size_t decode_workspace_floats(int S, int Hq, int P);
+
+hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int B, int G, hipStream_t stream);
+
+struct KvArgs {
+  uint8_t* k_pool;
+  uint8_t* v_pool;
+  int S, MB, NB, B;
+  int row_bytes;  // Hkv * d * element size: one slot of one block
+};
+
+hipError_t launch_append(const KvArgs& a, const uint8_t* k_new, const uint8_t* v_new,
+                         const int32_t* tables, const int32_t* positions, hipStream_t stream);
+
+hipError_t launch_cow(const KvArgs& a, const int32_t* src, const int32_t* dst, const int32_t* n_valid,
+                      int num_pairs, int num_layers, int64_t layer_stride_bytes, hipStream_t stream);
+
+hipError_t launch_gather(const KvArgs& a, const int32_t* tables, const int32_t* lens, uint8_t* k_out,
+                         uint8_t* v_out, hipStream_t stream);
+
+}  // namespace pa

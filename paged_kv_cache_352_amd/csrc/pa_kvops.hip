@@ -1,0 +1,98 @@
+// Data-movement kernels beside the decode: token append, copy-on-write of a
+// tail block's valid slots, and the debug gather.  All three move whole
+// slots, and a slot of one block (all KV heads, all dims) is one contiguous
+// run of Hkv*d elements in the [NB, B, Hkv, d] pool, so each kernel is a
+// 16-byte-vector copy of contiguous runs.  Bytes are copied exactly.
+//
+// [Slides] = "PagedAttention：让 KV cache 按需生长".
+#include <hip/hip_runtime.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ inline void copy16(uint8_t* __restrict__ dst, const uint8_t* __restrict__ src, int64_t bytes) {
+  for (int64_t i = (int64_t)threadIdx.x * 16; i < bytes; i += kThreads * 16)
+    *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(src + i);
+}
+
+// One workgroup per (request, pool).  The token with logical index p goes to
+// slot p % B of block table[p / B]; nothing else moves ([Slides]
+// "写满一块，再拿下一块").  Positions or blocks outside the pool are skipped.
+__global__ __launch_bounds__(kThreads) void append_kernel(KvArgs a, const uint8_t* __restrict__ k_new,
+                                                          const uint8_t* __restrict__ v_new,
+                                                          const int32_t* __restrict__ tables,
+                                                          const int32_t* __restrict__ positions) {
+  const int s = blockIdx.x;
+  const int p = positions[s];
+  if (p < 0 || p >= a.MB * a.B) return;
+  const int blk = tables[(int64_t)s * a.MB + p / a.B];
+  if (blk < 0 || blk >= a.NB) return;
+  uint8_t* pool = blockIdx.y ? a.v_pool : a.k_pool;
+  const uint8_t* src = (blockIdx.y ? v_new : k_new) + (int64_t)s * a.row_bytes;
+  uint8_t* dst = pool + ((int64_t)blk * a.B + p % a.B) * a.row_bytes;
+  copy16(dst, src, a.row_bytes);
+}
+
+// One workgroup per (pair, layer, pool): slots [0, n) of block src -> block dst
+// ([Slides] "先确保分配成功，再改变可见状态", copy_valid_kv).  The valid prefix
+// of a block is one contiguous run of n*row_bytes.
+__global__ __launch_bounds__(kThreads) void cow_kernel(KvArgs a, const int32_t* __restrict__ srcs,
+                                                       const int32_t* __restrict__ dsts,
+                                                       const int32_t* __restrict__ n_valid,
+                                                       int64_t layer_stride_bytes) {
+  const int i = blockIdx.x;
+  const int src = srcs[i], dst = dsts[i], n = n_valid[i];
+  if (src < 0 || src >= a.NB || dst < 0 || dst >= a.NB || n <= 0 || n > a.B || src == dst) return;
+  uint8_t* pool = (blockIdx.z ? a.v_pool : a.k_pool) + (int64_t)blockIdx.y * layer_stride_bytes;
+  const int64_t blk_bytes = (int64_t)a.B * a.row_bytes;
+  copy16(pool + dst * blk_bytes, pool + src * blk_bytes, (int64_t)n * a.row_bytes);
+}
+
+// One workgroup per (request, logical block, pool): the valid slots of that
+// block land at their logical positions in a [S, MB*B, Hkv, d] buffer.
+__global__ __launch_bounds__(kThreads) void gather_kernel(KvArgs a, const int32_t* __restrict__ tables,
+                                                          const int32_t* __restrict__ lens,
+                                                          uint8_t* __restrict__ k_out,
+                                                          uint8_t* __restrict__ v_out) {
+  const int s = blockIdx.x, j = blockIdx.y;
+  int n = lens[s];
+  n = n < 0 ? 0 : (n > a.MB * a.B ? a.MB * a.B : n);
+  if (j * a.B >= n) return;
+  const int blk = tables[(int64_t)s * a.MB + j];
+  if (blk < 0 || blk >= a.NB) return;
+  const int cnt = min(a.B, n - j * a.B);
+  const uint8_t* pool = blockIdx.z ? a.v_pool : a.k_pool;
+  uint8_t* out = blockIdx.z ? v_out : k_out;
+  const int64_t blk_bytes = (int64_t)a.B * a.row_bytes;
+  copy16(out + ((int64_t)s * a.MB * a.B + (int64_t)j * a.B) * a.row_bytes, pool + blk * blk_bytes,
+         (int64_t)cnt * a.row_bytes);
+}
+
+}  // namespace
+
+hipError_t launch_append(const KvArgs& a, const uint8_t* k_new, const uint8_t* v_new, const int32_t* tables,
+                         const int32_t* positions, hipStream_t stream) {
+  hipLaunchKernelGGL(append_kernel, dim3(a.S, 2), dim3(kThreads), 0, stream, a, k_new, v_new, tables,
+                     positions);
+  return hipGetLastError();
+}
+
+hipError_t launch_cow(const KvArgs& a, const int32_t* src, const int32_t* dst, const int32_t* n_valid,
+                      int num_pairs, int num_layers, int64_t layer_stride_bytes, hipStream_t stream) {
+  hipLaunchKernelGGL(cow_kernel, dim3(num_pairs, num_layers, 2), dim3(kThreads), 0, stream, a, src, dst,
+                     n_valid, layer_stride_bytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const KvArgs& a, const int32_t* tables, const int32_t* lens, uint8_t* k_out,
+                         uint8_t* v_out, hipStream_t stream) {
+  hipLaunchKernelGGL(gather_kernel, dim3(a.S, a.MB, 2), dim3(kThreads), 0, stream, a, tables, lens, k_out,
+                     v_out);
+  return hipGetLastError();
+}
+
+}  // namespace pa

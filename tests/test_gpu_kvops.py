@@ -1,0 +1,127 @@
+"""kv_append, kv_cow_copy and paged_kv_gather on the GPU: bit-exact against the oracle.
+
+Whole pools are compared bit for bit, so a stray write anywhere shows up.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_352_amd as pa
+import workloads as W
+from oracle import kvcache as kvc
+from tests.gpu_util import banner, host_bits
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_append_bit_exact(dtype):
+    banner(f"append {dtype}")
+    b = W.custom([0, 1, 5, 16, 17, 31, 32, 33], Hq=8, Hkv=2, dtype=dtype, append=True, device=DEV, seed=1)
+    k0, v0 = host_bits(b.k_pool[0]), host_bits(b.v_pool[0])
+    pa.kv_append(b.k_pool[0], b.v_pool[0], b.k_new[0, 0], b.v_new[0, 0], b.block_tables, b.append_positions[0], b.B)
+    torch.cuda.synchronize()
+    tab, pos = b.block_tables.cpu().numpy(), b.append_positions[0].cpu().numpy()
+    want_k = kvc.append(k0, host_bits(b.k_new[0, 0]), tab, pos, b.B)
+    want_v = kvc.append(v0, host_bits(b.v_new[0, 0]), tab, pos, b.B)
+    assert np.array_equal(host_bits(b.k_pool[0]), want_k)
+    assert np.array_equal(host_bits(b.v_pool[0]), want_v)
+
+
+def test_append_positions_outside_table_are_skipped():
+    banner("append out-of-range positions")
+    b = W.custom([5, 9], Hq=8, Hkv=2, dtype=torch.bfloat16, device=DEV, seed=2)
+    before = host_bits(b.k_pool[0])
+    pos = torch.tensor([-3, b.MB * b.B], dtype=torch.int32, device=DEV)  # skip, and one past the table
+    new = torch.ones((2, 2, 128), dtype=torch.bfloat16, device=DEV)
+    pa.kv_append(b.k_pool[0], b.v_pool[0], new, new, b.block_tables, pos, b.B)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(b.k_pool[0]), before)
+
+
+def test_cow_bit_exact_config4():
+    banner("cow config4")
+    b = W.config4(device=DEV)
+    k0, v0 = host_bits(b.k_pool), host_bits(b.v_pool)
+    pa.kv_cow_copy(b.k_pool, b.v_pool, b.cow_src, b.cow_dst, b.cow_n, b.B)
+    torch.cuda.synchronize()
+    cow = tuple(t.cpu().numpy() for t in (b.cow_src, b.cow_dst, b.cow_n))
+    assert np.array_equal(host_bits(b.k_pool), kvc.cow_copy_layers(k0, *cow))
+    assert np.array_equal(host_bits(b.v_pool), kvc.cow_copy_layers(v0, *cow))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_cow_multi_layer(dtype):
+    banner(f"cow 3 layers {dtype}")
+    b = W.custom([20, 40, 7], Hq=8, Hkv=2, dtype=dtype, L=3, device=DEV, seed=3, spare_blocks=6)
+    tab = b.block_tables.cpu().numpy()
+    spare = [x for x in range(b.NB) if x not in set(tab[:, :].ravel().tolist())]
+    src = torch.tensor([tab[0, 1], tab[1, 2], tab[2, 0]], dtype=torch.int32, device=DEV)
+    dst = torch.tensor(spare[:3], dtype=torch.int32, device=DEV)
+    nv = torch.tensor([4, 16, 7], dtype=torch.int32, device=DEV)
+    k0, v0 = host_bits(b.k_pool), host_bits(b.v_pool)
+    pa.kv_cow_copy(b.k_pool, b.v_pool, src, dst, nv, b.B)
+    torch.cuda.synchronize()
+    args = (src.cpu().numpy(), dst.cpu().numpy(), nv.cpu().numpy())
+    assert np.array_equal(host_bits(b.k_pool), kvc.cow_copy_layers(k0, *args))
+    assert np.array_equal(host_bits(b.v_pool), kvc.cow_copy_layers(v0, *args))
+
+
+def test_cow_then_append_rounds_config4():
+    """COW and every append round enqueued back to back on one stream, then compared."""
+    banner("cow + 64 append rounds config4")
+    b = W.config4(device=DEV)
+    k, v = host_bits(b.k_pool[0]), host_bits(b.v_pool[0])
+    pa.kv_cow_copy(b.k_pool, b.v_pool, b.cow_src, b.cow_dst, b.cow_n, b.B)
+    for r in range(b.rounds):
+        pa.kv_append(b.k_pool[0], b.v_pool[0], b.k_new[r, 0], b.v_new[r, 0], b.block_tables,
+                     b.append_positions[r], b.B)
+    torch.cuda.synchronize()
+    cow = tuple(t.cpu().numpy() for t in (b.cow_src, b.cow_dst, b.cow_n))
+    tab = b.block_tables.cpu().numpy()
+    k, v = kvc.cow_copy(k, *cow), kvc.cow_copy(v, *cow)
+    for r in range(b.rounds):
+        pos = b.append_positions[r].cpu().numpy()
+        k = kvc.append(k, host_bits(b.k_new[r, 0]), tab, pos, b.B)
+        v = kvc.append(v, host_bits(b.v_new[r, 0]), tab, pos, b.B)
+    assert np.array_equal(host_bits(b.k_pool[0]), k)
+    assert np.array_equal(host_bits(b.v_pool[0]), v)
+    # the shared tail block itself never changed (branch 63 wrote only past slot t)
+    t = b.info["t"]
+    tail = b.info["shared_tail"]
+    assert np.array_equal(host_bits(b.k_pool[0, tail, :t]), host_bits(W.config4(device=DEV).k_pool[0, tail, :t]))
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_gather_bit_exact(dtype):
+    banner(f"gather {dtype}")
+    b = W.custom([0, 1, 16, 17, 63, 100], Hq=8, Hkv=2, dtype=dtype, device=DEV, seed=4)
+    ko, vo = pa.paged_kv_gather(b.k_pool[0], b.v_pool[0], b.block_tables, b.seq_lens, b.B)
+    torch.cuda.synchronize()
+    tab, n = b.block_tables.cpu().numpy(), b.seq_lens.cpu().numpy()
+    assert np.array_equal(host_bits(ko), kvc.gather_padded(host_bits(b.k_pool[0]), tab, n, b.B, fill=0))
+    assert np.array_equal(host_bits(vo), kvc.gather_padded(host_bits(b.v_pool[0]), tab, n, b.B, fill=0))
+
+
+def test_append_config3_all_layers():
+    """Full-size append (256 requests, 32 layers): the pool changes exactly at the
+    oracle-predicted slots, which hold the new token."""
+    banner("append config3 32 layers")
+    b = W.config3(device=DEV)
+    tab = b.block_tables.cpu().numpy()
+    pos = b.append_positions[0].cpu().numpy()
+    want_blk = torch.tensor([tab[s, p // 16] for s, p in enumerate(pos)], device=DEV, dtype=torch.long)
+    want_slot = torch.tensor([p % 16 for p in pos], device=DEV, dtype=torch.long)
+    before_k = b.k_pool.view(torch.int16).clone()
+    for layer in range(b.L):
+        pa.kv_append(b.k_pool[layer], b.v_pool[layer], b.k_new[0, layer], b.v_new[0, layer], b.block_tables,
+                     b.append_positions[0], b.B)
+    torch.cuda.synchronize()
+    after_k = b.k_pool.view(torch.int16)
+    assert torch.equal(after_k[:, want_blk, want_slot], b.k_new[0].view(torch.int16))
+    after_k[:, want_blk, want_slot] = before_k[:, want_blk, want_slot]
+    assert torch.equal(after_k, before_k)
+    del before_k
+    assert torch.equal(b.v_pool.view(torch.int16)[:, want_blk, want_slot], b.v_new[0].view(torch.int16))

@@ -26,7 +26,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "paged decode attention KV GB/s (% of MI355X HBM peak) + tokens/s per layer"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_config2_32x4096_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bf16_32x4096_traffic.txt")
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_352_amd", "csrc", "pa_decode.hip")
 
 
@@ -88,6 +88,18 @@ def cpu_baseline(b, min_seconds):
     }
 
 
+def calibrate_copy(torch, dev, n_bytes=1 << 30, reps=5):
+    """A plain elementwise copy of known size: torch.neg over float32, n_bytes in, n_bytes out."""
+    src = torch.ones(n_bytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "float32 neg copy", "bytes_read_per_dispatch": n_bytes,
+                      "bytes_written_per_dispatch": n_bytes, "dispatches": reps}), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -97,6 +109,9 @@ def main():
     ap.add_argument("--rotate", type=int, default=4, help="pool copies cycled across steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB float32 negate-copy kernel (reads 1 GiB, writes 1 GiB) "
+                         "a few times, to scale the HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -115,6 +130,8 @@ def main():
         build()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        return calibrate_copy(torch, dev)
     b = W.config2(device=dev)
     kv_bytes = b.valid_kv_bytes_per_layer()
     pools = [(b.k_pool[0], b.v_pool[0])]

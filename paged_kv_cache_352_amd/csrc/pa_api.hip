@@ -46,8 +46,9 @@ pa_status check_dims(const pa_dims* d, int32_t B, bool need_attention_shape) {
       return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", d->num_q_heads,
                   d->num_kv_heads);
     const int G = d->num_q_heads / d->num_kv_heads;
-    if (G != 1 && G != 2 && G != 4 && G != 8)
-      return fail(PA_ERR_UNSUPPORTED, "query heads per KV head = %d (supported: 1, 2, 4, 8)", G);
+    const bool g_ok = G == 1 || G == 2 || G == 4 || G == 8 || (G == 16 && d->dtype == PA_BF16);
+    if (!g_ok)
+      return fail(PA_ERR_UNSUPPORTED, "query heads per KV head = %d (supported: 1, 2, 4, 8; 16 for bf16)", G);
     if (d->head_dim != pa::kHeadDim) return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 128)", d->head_dim);
     if (B != 16) return fail(PA_ERR_UNSUPPORTED, "block size %d (supported: 16)", B);
     if (d->num_splits < 0) return fail(PA_ERR_INVALID_ARG, "num_splits = %d < 0", d->num_splits);

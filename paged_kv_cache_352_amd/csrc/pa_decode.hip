@@ -12,7 +12,10 @@
 // range is reduced to its own (m, l, o), and a second kernel merges them
 // ([Slides] quiz "逻辑顺序没错…": mergeable state, not averaged softmaxes).
 //
-// Mapping to CDNA4 (v1, vector ALU):
+// This file holds the float32 path (bf16 K/V go to the matrix-core kernel in
+// pa_decode_mfma.hip) and the split merge both paths share.
+//
+// Mapping to CDNA4 (vector ALU):
 //   * one 64-lane wave per work item (request s, KV head g, split p); the G
 //     query heads of the GQA group share every K/V byte the wave loads;
 //   * a K or V tile of one (block, KV head) is B rows of d contiguous
@@ -36,10 +39,6 @@ namespace {
 constexpr int kWave = 64;
 constexpr float kNegInf = -__builtin_huge_valf();
 
-struct bf16_t {
-  uint16_t bits;
-};
-
 template <typename T>
 struct Vec16;  // how a 16-byte load unpacks into float32
 
@@ -51,20 +50,6 @@ struct Vec16<float> {
     f[1] = __uint_as_float(v.y);
     f[2] = __uint_as_float(v.z);
     f[3] = __uint_as_float(v.w);
-  }
-};
-
-template <>
-struct Vec16<bf16_t> {
-  static constexpr int kElems = 8;
-  // bf16 is the upper half of a binary32, so widening is exact.
-  __device__ static inline void unpack(const uint4& v, float* f) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = __uint_as_float(w[i] << 16);
-      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
   }
 };
 
@@ -83,8 +68,8 @@ __device__ inline int xcd_remap(int bid, int nwg) {
 template <typename T, int G, int B>
 __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeArgs a) {
   constexpr int E = Vec16<T>::kElems;  // elements per 16-byte load
-  constexpr int LPR = kHeadDim / E;    // lanes per row (16 bf16, 32 fp32)
-  constexpr int RPL = kWave / LPR;     // rows per wave load (4 bf16, 2 fp32)
+  constexpr int LPR = kHeadDim / E;    // lanes per row (32 for fp32)
+  constexpr int RPL = kWave / LPR;     // rows per wave load (2 for fp32)
   constexpr int NL = B / RPL;          // loads per tile
   static_assert(B % RPL == 0, "block size must be a multiple of the rows one wave load covers");
 
@@ -309,7 +294,14 @@ size_t decode_workspace_floats(int S, int Hq, int P) {
 
 hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int B, int G, hipStream_t stream) {
   if (B != 16) return hipErrorInvalidValue;
-  return dtype == PA_BF16 ? launch_group<bf16_t>(a, G, stream) : launch_group<float>(a, G, stream);
+  if (dtype == PA_BF16) {
+    // bf16: q.k and p.v on the matrix cores; the merge of splits is shared.
+    hipError_t e = launch_decode_mfma(a, G, stream);
+    if (e != hipSuccess || a.P == 1) return e;
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(a.S * a.Hq), dim3(kWave), 0, stream, a);
+    return hipGetLastError();
+  }
+  return launch_group<float>(a, G, stream);
 }
 
 }  // namespace pa

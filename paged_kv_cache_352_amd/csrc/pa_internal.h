@@ -34,6 +34,9 @@ size_t decode_workspace_floats(int S, int Hq, int P);
 
 hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int B, int G, hipStream_t stream);
 
+// bf16 decode on the matrix cores (pa_decode_mfma.hip); G in {1, 2, 4, 8, 16}, B = 16.
+hipError_t launch_decode_mfma(const DecodeArgs& a, int G, hipStream_t stream);
+
 struct KvArgs {
   uint8_t* k_pool;
   uint8_t* v_pool;

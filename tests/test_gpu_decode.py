@@ -98,14 +98,26 @@ def test_edge_lengths(dtype, splits):
     assert_close(got, ref, dtype, "edges")
 
 
-@pytest.mark.parametrize("G,Hkv", [(1, 4), (2, 2), (8, 1)])
-def test_other_group_sizes(G, Hkv):
-    banner(f"group {G} x {Hkv} kv heads")
-    b = W.custom([3, 40, 77], Hq=G * Hkv, Hkv=Hkv, dtype=torch.bfloat16, device=DEV, seed=12)
+@pytest.mark.parametrize("G,Hkv,dtype", [(1, 4, torch.bfloat16), (2, 2, torch.bfloat16), (8, 1, torch.bfloat16),
+                                         (16, 2, torch.bfloat16), (1, 3, torch.float32), (8, 1, torch.float32)])
+def test_other_group_sizes(G, Hkv, dtype):
+    banner(f"group {G} x {Hkv} kv heads {dtype}")
+    b = W.custom([3, 40, 77], Hq=G * Hkv, Hkv=Hkv, dtype=dtype, device=DEV, seed=12)
     ref = HostLayer(b, 0).oracle()
     out = gpu_step(b)[0]
     torch.cuda.synchronize()
-    assert_close(host_f32(out), ref, torch.bfloat16, f"G={G}")
+    assert_close(host_f32(out), ref, dtype, f"G={G}")
+
+
+@pytest.mark.parametrize("splits", [1, 2])
+def test_long_split_walks_several_table_chunks(splits):
+    """A split longer than 64 blocks reads its table slice in several chunks."""
+    banner(f"long split: 2500 / 1100 / 17 tokens, splits={splits}")
+    b = W.custom([2500, 1100, 17], Hq=8, Hkv=2, dtype=torch.bfloat16, device=DEV, seed=14)
+    ref = HostLayer(b, 0).oracle()
+    out = gpu_step(b, num_splits=splits)[0]
+    torch.cuda.synchronize()
+    assert_close(host_f32(out), ref, torch.bfloat16, f"long split P={splits}")
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])

@@ -59,16 +59,24 @@ pa_status check_dims(const pa_dims* d, int32_t B, bool need_attention_shape) {
   return PA_OK;
 }
 
-// Splits depend only on (S, Hkv, MB): enough waves to keep ~8 per CU busy,
-// never fewer than ~8 blocks per split.  Returns (P, blocks per split).
+// Splits depend only on host-known sizes (S, Hkv, MB, dtype), so repeated
+// calls agree.  Returns (P, blocks per split).
+//   bf16 (matrix-core kernel, kMfmaWaves waves per work item): about one
+//     wave per SIMD (1024 on MI355X), each wave keeping at least 4 blocks;
+//   fp32 (vector-ALU kernel, one wave per work item): about 2048 waves, each
+//     split keeping at least 8 blocks.
 void plan_splits(const pa_dims* d, int* P_out, int* bps_out) {
   const int MB = d->max_blocks_per_seq;
   int P = d->num_splits;
   if (P == 0) {
     const int64_t items = (int64_t)d->num_seqs * d->num_kv_heads;
-    const int64_t target = 2048;
-    P = (int)((target + items - 1) / (items > 0 ? items : 1));
-    const int maxP = (MB + 7) / 8;
+    const bool mfma = d->dtype == PA_BF16;
+    const int64_t waves_per_item = mfma ? pa::kMfmaWaves : 1;
+    const int64_t target = mfma ? 1024 : 2048;
+    const int64_t per = items * waves_per_item;
+    P = (int)((target + per - 1) / (per > 0 ? per : 1));
+    const int min_blocks = mfma ? 4 * pa::kMfmaWaves : 8;
+    const int maxP = (MB + min_blocks - 1) / min_blocks;
     P = P < 1 ? 1 : (P > maxP ? maxP : P);
     if (P < 1) P = 1;
   }

@@ -6,13 +6,19 @@
 // Same contract as the vector-ALU kernel in pa_decode.hip ([Slides]
 // "分页以后，attention 仍然按完整历史归一化": look up each logical block,
 // load its K/V tile, mask slots past the length, fold the block into the
-// running (m, l, o) state of [Budgets] eq. (4); splits of a long history are
-// merged afterwards).  What changes is where the arithmetic runs: the two
+// running (m, l, o) state of [Budgets] eq. (4); partial states over disjoint
+// block sets are merged).  What changes is where the arithmetic runs: the two
 // contractions of the GQA group, q.k and p.v, are MFMA instructions, which
 // leaves the vector ALU only the softmax of four scores per lane.
 //
-// One 64-lane wave per (request s, KV head g, split p).  Lane l is (n = l%16,
-// c = l/16).  For one 16-slot block and head dim 128:
+// Work decomposition.  One workgroup of W waves per (request s, KV head g,
+// split p).  Wave w takes logical blocks j0 + w, j0 + w + W, ... of the
+// split's range [j0, j1), keeps its own (m, l, o), and the W states are merged
+// through LDS at the end.  With one split the workgroup writes the final
+// output; with several it writes its merged state and a second kernel merges
+// the splits.
+//
+// One wave and one 16-slot block, head dim 128; lane l is (n = l%16, c = l/16):
 //
 //   q.k  four v_mfma_f32_16x16x32_bf16 with A = the K tile (M = 16 slots,
 //        K = 32 dims) and B = q of the group (N = 16 query heads, zero beyond
@@ -22,12 +28,14 @@
 //        with the scores of head n for slots 4c .. 4c+3.
 //   p.v  that is exactly the A layout (M = 16 heads, K = 16 slots, 4 slots
 //        per lane) of v_mfma_f32_16x16x16_bf16, so the weights feed p.v
-//        without crossing lanes.  The B operand needs V with slots along K;
-//        V arrives slot-major, so each wave transposes its 4 KiB V tile
-//        through LDS (16-bit writes, 64-bit reads).  p is split into a bf16
-//        head and a bf16 remainder (p = hi + lo to about 2^-16 relative) and
-//        both go through the matrix core, so p.v keeps fp32-class accuracy.
-//        The eight accumulators hold o for heads 4c .. 4c+3, dims 16*j + n.
+//        without crossing lanes.  Its B operand needs V with slots along K.
+//        V arrives slot-major; each wave stores its 4 KiB V tile row-major in
+//        LDS (16-byte chunks XOR-swizzled by row) and reads it back with
+//        ds_read_b64_tr_b16, which hands lane (n, c) the dims 16*j + n of
+//        slots 4c .. 4c+3.  p is split into a bf16 head and a bf16 remainder
+//        (p = hi + lo to about 2^-16 relative) and both go through the matrix
+//        core, so p.v keeps fp32-class accuracy.  The eight accumulators hold
+//        o for heads 4c .. 4c+3, dims 16*j + n.
 //
 // Softmax state: lane l keeps m (the running max, base 2) of head n and a
 // partial l over its own four slots of every block; the partials of the four
@@ -48,13 +56,13 @@ constexpr float kNegInf = -__builtin_huge_valf();
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+#define PA_LDS __attribute__((address_space(3)))
 
-// V^T tile in LDS: element (dim d, slot t) at byte
-//   (d / 8) * kGroupBytes + (d % 8) * 32 + 2 * t.
-// Each run of 8 dims is padded by 32 bytes so that the four lane groups of a
-// transposing write land in different banks.
-constexpr int kGroupBytes = 8 * kB * 2 + 32;  // 288
-constexpr int kVtBytes = (128 / 8) * kGroupBytes;  // 4608
+// V tile in LDS: slot t, dims 8k .. 8k+7 (16-byte chunk k) at byte
+//   256 * t + 16 * (k ^ t).
+// The XOR spreads both the row-wise 16-byte writes and the transposing
+// 8-byte reads of one instruction evenly over the banks.
+constexpr int kVtBytes = kB * kHeadDim * 2;  // 4096
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -75,17 +83,33 @@ __device__ inline void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo
   lo = (__float_as_uint(r0) >> 16) | (__float_as_uint(r1) & 0xffff0000u);
 }
 
+// Orders this wave's LDS accesses around it without waiting for anything:
+// one wave's LDS operations execute in issue order, so only the compiler has
+// to be kept from moving them.
+__device__ inline void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 struct Tile {
   uint4 k[4];
   uint4 v[4];
 };
 
-template <int G>
-__global__ __launch_bounds__(kWave) void decode_mfma_kernel(DecodeArgs a) {
-  static_assert(G >= 1 && G <= 16, "the query group must fit the 16 columns of one MFMA tile");
-  __shared__ __attribute__((aligned(16))) uint8_t vt[kVtBytes];
+// One 16-byte load of K/V history.
+__device__ inline uint4 load_kv16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
-  const int lane = threadIdx.x;
+template <int G, int W>
+__global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
+  static_assert(G >= 1 && G <= 16, "the query group must fit the 16 columns of one MFMA tile");
+  __shared__ __attribute__((aligned(16))) uint8_t vt_all[W][kVtBytes];
+  __shared__ float red_m[W][16];
+  __shared__ float red_l[W][16];
+  __shared__ __attribute__((aligned(16))) float red_o[W][G][kHeadDim];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
   const int n16 = lane & 15;
   const int c4 = lane >> 4;
 
@@ -101,16 +125,19 @@ __global__ __launch_bounds__(kWave) void decode_mfma_kernel(DecodeArgs a) {
   const int nb = (n + kB - 1) / kB;
   const int j0 = p * a.bps;
   const int j1 = min(nb, j0 + a.bps);
+  // This wave's blocks: j0 + w + W*t for t in [0, cnt).
+  const int cnt = j1 - j0 - w > 0 ? (j1 - j0 - w + W - 1) / W : 0;
 
   // q of head kvh*G + n16 over the dims this lane contributes, as MFMA B operands.
   bf16x8_t qv[4];
   {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)s * a.Hq + (int64_t)kvh * G) * kHeadDim;
+    const int hq = n16 < G ? n16 : G - 1;  // every lane loads (no divergent loads), then zeros
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (n16 < G) w = *reinterpret_cast<const uint4*>(qp + n16 * kHeadDim + 32 * i + 8 * c4);
-      qv[i] = __builtin_bit_cast(bf16x8_t, w);
+      uint4 v = *reinterpret_cast<const uint4*>(qp + hq * kHeadDim + 32 * i + 8 * c4);
+      if (n16 >= G) v = make_uint4(0, 0, 0, 0);
+      qv[i] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
 
@@ -120,7 +147,7 @@ __global__ __launch_bounds__(kWave) void decode_mfma_kernel(DecodeArgs a) {
   const int64_t lane_off = (int64_t)n16 * row_stride + (int64_t)kvh * kHeadDim + 8 * c4;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pool) + lane_off;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pool) + lane_off;
-  const int32_t* trow = a.tables + (int64_t)s * a.MB;
+  const int32_t* trow = a.tables + (int64_t)s * a.MB + j0 + w;
 
   // Issue the 8 16-byte loads of the K and V tile of physical block pb.
   auto load_tile = [&](int pb, Tile& t) {
@@ -131,9 +158,9 @@ __global__ __launch_bounds__(kWave) void decode_mfma_kernel(DecodeArgs a) {
     const uint16_t* kb = kbase + (int64_t)pb * blk_stride;
     const uint16_t* vb = vbase + (int64_t)pb * blk_stride;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t.k[i] = *reinterpret_cast<const uint4*>(kb + 32 * i);
+    for (int i = 0; i < 4; ++i) t.k[i] = load_kv16(kb + 32 * i);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t.v[i] = *reinterpret_cast<const uint4*>(vb + 32 * i);
+    for (int i = 0; i < 4; ++i) t.v[i] = load_kv16(vb + 32 * i);
   };
 
   float m = kNegInf;  // running max (base 2) of head n16
@@ -142,10 +169,15 @@ __global__ __launch_bounds__(kWave) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) acc[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // LDS addresses: transposing writes (slot n16, dims 32*i + 8*c4 + e) and
-  // B-operand reads (slots 4*c4 .. +3, dim 16*jj + n16).
-  uint8_t* vt_w = vt + 2 * n16;
-  const uint8_t* vt_r = vt + (n16 >> 3) * kGroupBytes + (n16 & 7) * 32 + 8 * c4;
+  // LDS addresses.  Writes: slot n16, chunk 4*i + c4.  Transposing reads for
+  // output dims 16*jj + n16: this lane fetches slot r = 4*c4 + n16/4, dims
+  // 16*jj + 4*(n16%4) .. +3, i.e. half (n16 & 1) of chunk 2*jj + (n16%4)/2.
+  uint8_t* vt = vt_all[w];
+  uint8_t* vt_w = vt + 256 * n16;
+  const int rr = 4 * c4 + (n16 >> 2);
+  const PA_LDS uint8_t* vt_r = (const PA_LDS uint8_t*)vt + 256 * rr + 8 * (n16 & 1);
+  const int bsel = ((n16 & 3) >> 1) ^ (rr & 1);  // low bit of the swizzled chunk
+  const int rhi = rr & 14;                       // the rest of the swizzle
 
   auto process = [&](int j, Tile& cur) {
     // q.k for the 16 slots of block j.
@@ -154,23 +186,16 @@ __global__ __launch_bounds__(kWave) void decode_mfma_kernel(DecodeArgs a) {
     for (int i = 0; i < 4; ++i)
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[i]), qv[i], sc, 0, 0, 0);
 
-    // Transpose V into LDS; slots past the length become zeros so that their
-    // (possibly NaN) contents never meet a zero weight.
+    // V into LDS; slots past the length become zeros so that their (possibly
+    // NaN) contents never meet a zero weight.
     const int valid = n - j * kB;  // >= 1
     if (valid < kB && n16 >= valid) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) cur.v[i] = make_uint4(0, 0, 0, 0);
     }
+    wave_lds_order();  // the previous block's reads of this tile come first
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint8_t* w = vt_w + (4 * i + c4) * kGroupBytes;
-      const uint32_t d[4] = {cur.v[i].x, cur.v[i].y, cur.v[i].z, cur.v[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<uint16_t*>(w + (2 * e) * 32) = (uint16_t)(d[e] & 0xffffu);
-        *reinterpret_cast<uint16_t*>(w + (2 * e + 1) * 32) = (uint16_t)(d[e] >> 16);
-      }
-    }
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(vt_w + 16 * ((4 * i + c4) ^ n16)) = cur.v[i];
 
     // Scores in base 2, masked past the length ([Slides] quiz "逻辑顺序没错…").
     float sv[4];
@@ -206,67 +231,89 @@ __global__ __launch_bounds__(kWave) void decode_mfma_kernel(DecodeArgs a) {
         for (int r = 0; r < 4; ++r) acc[jj][r] *= ar[r];
     }
 
-    __syncthreads();  // the transposed tile is visible to every lane
+    wave_lds_order();  // this block's V tile is in LDS
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
-      const s16x4_t vb = *reinterpret_cast<const s16x4_t*>(vt_r + 2 * jj * kGroupBytes);
+      const int chunk = ((2 * jj) ^ rhi) | bsel;
+      const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(vt_r + 16 * chunk));
       acc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vb, acc[jj], 0, 0, 0);
       acc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vb, acc[jj], 0, 0, 0);
     }
-    __syncthreads();  // reads done before the next block overwrites the tile
   };
 
-  // The split is walked in chunks of up to 64 blocks.  One vector load
-  // brings a chunk's table entries into a register, one per lane; block j's
-  // entry is then read out of lane j - jb.  Within a chunk two tiles are in
-  // flight: block j+1 loads while block j is processed (the load index is
-  // clamped, never conditional, so the wait before each tile covers only that
-  // tile's loads).
-  for (int jb = j0; jb < j1; jb += kWave) {
-    const int je = min(j1, jb + kWave);
-    const int tab = (jb + lane < je) ? trow[jb + lane] : 0;
+  // The wave's blocks are walked in chunks of up to 64.  One vector load
+  // brings a chunk's table entries into a register, one per lane; block t's
+  // entry is then read out of lane t - tb.  Within a chunk two tiles are in
+  // flight: the next block loads while the current one is processed (the load
+  // index is clamped, never conditional, so the wait before each tile covers
+  // only that tile's loads).
+  for (int tb = 0; tb < cnt; tb += kWave) {
+    const int te = min(cnt, tb + kWave);
+    const int tab = trow[(int64_t)min(tb + lane, te - 1) * W];  // lanes past the chunk repeat its last entry
     Tile t0, t1;
     load_tile(__builtin_amdgcn_readlane(tab, 0), t0);
-    for (int j = jb; j < je; j += 2) {
-      load_tile(__builtin_amdgcn_readlane(tab, min(j + 1, je - 1) - jb), t1);
-      process(j, t0);
-      if (j + 1 >= je) break;
-      load_tile(__builtin_amdgcn_readlane(tab, min(j + 2, je - 1) - jb), t0);
-      process(j + 1, t1);
+    for (int t = tb; t < te; t += 2) {
+      load_tile(__builtin_amdgcn_readlane(tab, min(t + 1, te - 1) - tb), t1);
+      __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the current tile's math
+      process(j0 + w + W * t, t0);
+      if (t + 1 >= te) break;
+      load_tile(__builtin_amdgcn_readlane(tab, min(t + 2, te - 1) - tb), t0);
+      __builtin_amdgcn_sched_barrier(0);
+      process(j0 + w + W * (t + 1), t1);
     }
   }
 
-  // Full l of head n16: sum the partials of the four lanes holding that head.
+  // Full l of head n16 in this wave: sum the partials of its four lanes.
   l += __shfl_xor(l, 16, kWave);
   l += __shfl_xor(l, 32, kWave);
 
+  // Merge the W wave states ([Budgets] eq. (4) applied across disjoint block
+  // sets): M = max m_w, L = sum 2^(m_w - M) l_w, O = sum 2^(m_w - M) o_w.
+  if (c4 == 0) {
+    red_m[w][n16] = m;
+    red_l[w][n16] = l;
+  }
+  bad = __syncthreads_or(bad);  // any wave that met an entry outside the pool
+  float mh = kNegInf;  // M of head n16
+#pragma unroll
+  for (int v = 0; v < W; ++v) mh = fmaxf(mh, red_m[v][n16]);
+  // scale of this wave's state for head n16 (0 for a wave that saw no block)
+  const float f = (m == kNegInf) ? 0.f : fast_exp2(m - mh);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int hg = 4 * c4 + r;
+    const float fr = __shfl(f, hg & 15, kWave);
+    if (hg < G) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) red_o[w][hg][16 * jj + n16] = acc[jj][r] * fr;
+    }
+  }
+  __syncthreads();
+
+  // G * 128 outputs, spread over the workgroup's threads.
   const float nan = __builtin_nanf("");
-  if (a.P == 1) {
-    // out = o / l for the heads this lane's accumulators hold.
+  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kWave * W) {
+    const int hg = idx / kHeadDim;
+    const int d = idx % kHeadDim;
+    float M = kNegInf, L = 0.f, O = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int hg = 4 * c4 + r;
-      const float lh = __shfl(l, hg & 15, kWave);
-      if (hg >= G) continue;
-      const float inv = lh > 0.f ? 1.f / lh : 0.f;
-      float* dst = a.out + ((int64_t)s * a.Hq + kvh * G + hg) * kHeadDim + n16;
+    for (int v = 0; v < W; ++v) M = fmaxf(M, red_m[v][hg]);
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) dst[16 * jj] = bad ? nan : acc[jj][r] * inv;
+    for (int v = 0; v < W; ++v) {
+      const float mv = red_m[v][hg];
+      if (mv != kNegInf) L = fmaf(fast_exp2(mv - M), red_l[v][hg], L);
+      O += red_o[v][hg][d];
     }
-  } else {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int hg = 4 * c4 + r;
-      if (hg >= G) continue;
-      const int64_t slot = ((int64_t)s * a.Hq + kvh * G + hg) * a.P + p;
-      float* dst = a.ws_o + slot * kHeadDim + n16;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) dst[16 * jj] = acc[jj][r];
-    }
-    if (c4 == 0 && n16 < G) {
-      const int64_t slot = ((int64_t)s * a.Hq + kvh * G + n16) * a.P + p;
-      a.ws_m[slot] = bad ? 0.f : m;
-      a.ws_l[slot] = bad ? nan : l;
+    const int h = kvh * G + hg;
+    if (a.P == 1) {
+      a.out[((int64_t)s * a.Hq + h) * kHeadDim + d] = bad ? nan : (L > 0.f ? O / L : 0.f);
+    } else {
+      const int64_t slot = ((int64_t)s * a.Hq + h) * a.P + p;
+      a.ws_o[slot * kHeadDim + d] = O;
+      if (d == 0) {
+        a.ws_m[slot] = bad ? 0.f : M;
+        a.ws_l[slot] = bad ? nan : L;
+      }
     }
   }
 }
@@ -274,7 +321,7 @@ __global__ __launch_bounds__(kWave) void decode_mfma_kernel(DecodeArgs a) {
 template <int G>
 hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
   const int items = a.Hkv * a.S * a.P;
-  hipLaunchKernelGGL((decode_mfma_kernel<G>), dim3(items), dim3(kWave), 0, stream, a);
+  hipLaunchKernelGGL((decode_mfma_kernel<G, kMfmaWaves>), dim3(items), dim3(kWave * kMfmaWaves), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@ namespace pa {
 
 constexpr int kHeadDim = 128;  // d supported by the decode kernels
 constexpr int kNumXcd = 8;     // MI355X: 8 accelerator dies, each with its own L2
+constexpr int kMfmaWaves = 4;  // waves per workgroup of the bf16 matrix-core decode
 
 struct DecodeArgs {
   const void* q;

@@ -70,14 +70,17 @@ def test_config4_cow_large_logits(t):
     assert_close(host_f32(out), host.oracle(), torch.bfloat16, "config4")
 
 
-def test_config5_bf16_24_layers():
-    banner("config5 bf16 168x1025 x 24 layers (append + decode, split-K)")
+@pytest.mark.parametrize("splits", [0, 4])
+def test_config5_bf16_24_layers(splits):
+    """168 x 1025 tokens, 24 layers.  Every plan splits the 65 blocks of a request
+    over several waves; splits=4 also splits them over workgroups (merge kernel)."""
+    banner(f"config5 bf16 168x1025 x 24 layers (append + decode), splits={splits}")
     b = W.config5(device=DEV)
     full_layers = (0, 23)
     hosts = {layer: HostLayer(b, layer) for layer in full_layers}
-    P, _ = pa.paged_attn_plan(b.S, b.Hq, b.Hkv, b.D, b.MB, b.NB, b.dtype, b.B)
-    assert P > 1
-    outs = gpu_step(b)
+    P, ws = pa.paged_attn_plan(b.S, b.Hq, b.Hkv, b.D, b.MB, b.NB, b.dtype, b.B, num_splits=splits)
+    assert (P > 1 and ws > 0) if splits else P >= 1
+    outs = gpu_step(b, num_splits=splits)
     torch.cuda.synchronize()
     for layer in full_layers:
         assert_close(host_f32(outs[layer]), hosts[layer].oracle(), torch.bfloat16, f"config5 layer {layer}")

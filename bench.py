@@ -104,6 +104,117 @@ def calibrate_copy(torch, dev, n_bytes=1 << 30, reps=5):
     return 0
 
 
+def graph_time_us(torch, enqueue, launches, replays=5):
+    """Mean GPU time per launch, in microseconds, of ``launches`` calls of
+    ``enqueue()`` captured in one HIP graph and replayed back to back.
+
+    Used for kernels too short to time one by one from Python: the graph
+    keeps the GPU fed, so the time is kernel time plus the graph's own
+    inter-kernel gap."""
+    enqueue()  # load the library and settle shapes outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(launches):
+            enqueue()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(replays):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / (replays * launches)
+    del g
+    return us
+
+
+def rate(nbytes, us):
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us": round(us, 3), "bytes": int(nbytes), "GB_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def side_kernels(torch, pa, W, dev):
+    """kv_append and kv_cow_copy at their workload shapes (one layer).
+
+    kv_append: 256 requests x (K + V) of one token, Hkv 8, d 128, bf16: each
+    launch reads 2 x 256 x 2 KiB of new K/V and writes as much into the pool.
+    kv_cow_copy: the 63 copy-on-write pairs of the prefix-sharing batch, t
+    valid slots each: reads and writes 63 x t x 2 KiB per pool.
+    Both move about a megabyte or less, so their time is launch latency, not
+    bandwidth; the fraction of peak is reported for completeness."""
+    res = {}
+    b = W.config3(device=dev, layers=1)
+    row = b.Hkv * b.D * b.elem_bytes
+    n_app = int((b.append_positions[0] >= 0).sum().item())
+    us = graph_time_us(torch, lambda: pa.kv_append(b.k_pool[0], b.v_pool[0], b.k_new[0, 0], b.v_new[0, 0],
+                                                    b.block_tables, b.append_positions[0], b.B), 64)
+    res["kv_append"] = dict(rate(2 * 2 * n_app * row, us), workload=f"{n_app} requests, Hkv 8, d 128, bf16, one layer")
+    del b
+    b = W.config4(device=dev)
+    t = int(b.info["t"])
+    npairs = int(b.cow_src.numel())
+    us = graph_time_us(torch, lambda: pa.kv_cow_copy(b.k_pool, b.v_pool, b.cow_src, b.cow_dst, b.cow_n, b.B), 64)
+    res["kv_cow_copy"] = dict(rate(2 * 2 * npairs * t * row, us),
+                              workload=f"{npairs} pairs x {t} valid slots, Hkv 8, d 128, bf16, one layer")
+    del b
+    torch.cuda.empty_cache()
+    return res
+
+
+def suite(torch, pa, W, dev):
+    """Decode (and full-step) timings of the other four workloads, one dict each."""
+    out = {}
+
+    def decode_graph(b, layers, reps=1):
+        calls = [pa.DecodeLaunch(b.q[layer], b.k_pool[layer], b.v_pool[layer], b.block_tables, b.seq_lens, b.B,
+                                 b.scale) for layer in layers]
+        def launch_all():
+            for c in calls:
+                c.launch()
+
+        us = graph_time_us(torch, launch_all, reps)
+        return us / len(calls), calls[0].splits
+
+    def full_step_graph(b):
+        def step():
+            if b.cow_src.numel():
+                pa.kv_cow_copy(b.k_pool, b.v_pool, b.cow_src, b.cow_dst, b.cow_n, b.B)
+            for layer in range(b.L):
+                for r in range(b.rounds):
+                    pa.kv_append(b.k_pool[layer], b.v_pool[layer], b.k_new[r, layer], b.v_new[r, layer],
+                                 b.block_tables, b.append_positions[r], b.B)
+                pa.paged_attn_decode(b.q[layer], b.k_pool[layer], b.v_pool[layer], b.block_tables, b.seq_lens,
+                                     b.B, b.scale, out=outs[layer], workspace=ws)
+        _, need = pa.paged_attn_plan(b.S, b.Hq, b.Hkv, b.D, b.MB, b.NB, b.dtype, b.B)
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        outs = [torch.empty((b.S, b.Hq, b.D), dtype=torch.float32, device=dev) for _ in range(b.L)]
+        return graph_time_us(torch, step, 1)
+
+    for name, make, rows in (("fp32 5 requests (37..511 tokens), one layer", W.config1, None),
+                             ("bf16 256 mixed-length requests, 32 layers", W.config3, None),
+                             ("bf16 prefix sharing, 64 branches (COW), one layer", W.config4, None),
+                             ("bf16 168 x 1025 tokens, 24 layers", W.config5, None)):
+        b = make(device=dev)
+        kvb = b.valid_kv_bytes_per_layer()
+        layers = list(range(b.L))
+        us, P = decode_graph(b, layers, reps=1 if b.L > 1 else 50)
+        ent = dict(rate(kvb, us), splits=P, layers=b.L, tokens_per_s_per_layer=round(b.S / (us * 1e-6), 1))
+        if b.L > 1 or b.rounds or b.cow_src.numel():
+            step_us = full_step_graph(b)
+            ent["full_step_us"] = round(step_us, 2)
+            ent["full_step_ops"] = ("kv_cow_copy, " if b.cow_src.numel() else "") + \
+                f"{b.rounds} kv_append round(s) and one decode per layer, {b.L} layer(s)"
+        if name.startswith("bf16 prefix"):
+            ent["note"] = "the shared prefix is cache-resident: logical bytes, no roofline claim"
+        out[name] = ent
+        del b
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +224,11 @@ def main():
     ap.add_argument("--rotate", type=int, default=4, help="pool copies cycled across steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle-seconds", type=float, default=1.0,
+                    help="untimed launches before the warmup steps, so clocks settle")
+    ap.add_argument("--no-side-kernels", action="store_true", help="skip the kv_append / kv_cow_copy timings")
+    ap.add_argument("--suite", metavar="PATH", default=None,
+                    help="also time the other four workloads and write them as JSON to PATH")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB float32 negate-copy kernel (reads 1 GiB, writes 1 GiB) "
                          "a few times, to scale the HBM byte counters")
@@ -148,6 +264,13 @@ def main():
                                        num_splits=args.splits, workspace=first.workspace) for k, v in pools[1:]]
     log(f"workload {b.name}: {kv_bytes / 1e6:.1f} MB valid KV per step, splits={first.splits}")
 
+    # Untimed: let the GPU clocks settle on this load (a fresh box starts
+    # slow), then the W warmup steps.
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_seconds:
+        for i in range(50):
+            calls[i % len(calls)].launch()
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         calls[i % len(calls)].launch()
     torch.cuda.synchronize()
@@ -216,6 +339,16 @@ def main():
             "algorithmic_bytes_per_launch": kv_bytes,
         },
     }
+    del calls, first, pools
+    torch.cuda.empty_cache()
+    if not args.no_side_kernels:
+        res["side_kernels"] = side_kernels(torch, pa, W, dev)
+    if args.suite:
+        st = suite(torch, pa, W, dev)
+        with open(args.suite, "w") as f:
+            json.dump(st, f, indent=1)
+        for k, v in st.items():
+            log(f"suite: {k}: {json.dumps(v)}")
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
     print(json.dumps(res), flush=True)

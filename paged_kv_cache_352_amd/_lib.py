@@ -225,7 +225,9 @@ class DecodeLaunch:
     """A paged_attn_decode call with its arguments marshalled once.
 
     For tight loops (benchmarks, graph capture): ``launch()`` only re-issues the
-    C call.  The tensors must stay alive and keep their shapes.
+    C call.  The tensors must stay alive and keep their shapes.  With
+    ``stream=None`` each launch goes to the stream current at that moment
+    (so a launch inside a graph capture is captured).
     """
 
     def __init__(self, q, k_pool, v_pool, block_tables, seq_lens, B, scale, out=None, num_splits=0,
@@ -240,11 +242,14 @@ class DecodeLaunch:
         self._keep = (q, k_pool, v_pool, block_tables, seq_lens)
         self._dims = make_dims(S, Hq, Hkv, D, MB, NB, q.dtype, num_splits, workspace)
         self._fn = load().paged_attn_decode
-        self._args = (_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), B,
-                      ctypes.c_float(scale), _ptr(self.out), _stream(stream), ctypes.byref(self._dims))
+        self._head = (_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), B,
+                      ctypes.c_float(scale), _ptr(self.out))
+        self._stream = _stream(stream) if stream is not None else None
+        self._dims_ref = ctypes.byref(self._dims)
 
     def launch(self):
-        st = self._fn(*self._args)
-        if st:
-            _check("paged_attn_decode", st)
+        st = self._stream if self._stream is not None else _stream(None)
+        status = self._fn(*self._head, st, self._dims_ref)
+        if status:
+            _check("paged_attn_decode", status)
         return self.out

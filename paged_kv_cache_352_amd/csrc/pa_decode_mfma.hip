@@ -64,6 +64,9 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 // 8-byte reads of one instruction evenly over the banks.
 constexpr int kVtBytes = kB * kHeadDim * 2;  // 4096
 
+// K/V tiles in flight per wave.
+constexpr int kDepth = 2;
+
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline int xcd_remap(int bid, int nwg) {
@@ -243,23 +246,24 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
 
   // The wave's blocks are walked in chunks of up to 64.  One vector load
   // brings a chunk's table entries into a register, one per lane; block t's
-  // entry is then read out of lane t - tb.  Within a chunk two tiles are in
-  // flight: the next block loads while the current one is processed (the load
-  // index is clamped, never conditional, so the wait before each tile covers
-  // only that tile's loads).
+  // entry is then read out of lane t - tb.  Within a chunk kDepth tiles are in
+  // flight: block t + kDepth - 1 is loaded before block t is processed (the
+  // load index is clamped, never conditional, so the wait before each tile
+  // covers only that tile's loads).
   for (int tb = 0; tb < cnt; tb += kWave) {
     const int te = min(cnt, tb + kWave);
     const int tab = trow[(int64_t)min(tb + lane, te - 1) * W];  // lanes past the chunk repeat its last entry
-    Tile t0, t1;
-    load_tile(__builtin_amdgcn_readlane(tab, 0), t0);
-    for (int t = tb; t < te; t += 2) {
-      load_tile(__builtin_amdgcn_readlane(tab, min(t + 1, te - 1) - tb), t1);
-      __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the current tile's math
-      process(j0 + w + W * t, t0);
-      if (t + 1 >= te) break;
-      load_tile(__builtin_amdgcn_readlane(tab, min(t + 2, te - 1) - tb), t0);
-      __builtin_amdgcn_sched_barrier(0);
-      process(j0 + w + W * (t + 1), t1);
+    Tile tq[kDepth];
+#pragma unroll
+    for (int b = 0; b + 1 < kDepth; ++b) load_tile(__builtin_amdgcn_readlane(tab, min(tb + b, te - 1) - tb), tq[b]);
+    for (int t = tb; t < te; t += kDepth) {
+#pragma unroll
+      for (int b = 0; b < kDepth; ++b) {
+        load_tile(__builtin_amdgcn_readlane(tab, min(t + b + kDepth - 1, te - 1) - tb), tq[(b + kDepth - 1) % kDepth]);
+        __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the current tile's math
+        process(j0 + w + W * (t + b), tq[b]);
+        if (t + b + 1 >= te) break;
+      }
     }
   }
 

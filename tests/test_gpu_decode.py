@@ -147,3 +147,27 @@ def test_deterministic_repeat():
     c = gpu_step(b)[0]
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int32), c.view(torch.int32))
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_graph_capture_replays_match_eager(splits):
+    """The library only enqueues on the caller's stream, so a captured launch
+    replays exactly: several replays, with eager work between them, each
+    bit-identical to the eager result."""
+    banner(f"graph capture, splits={splits}")
+    b = W.custom([5, 40, 300, 77], Hq=8, Hkv=2, dtype=torch.bfloat16, device=DEV, seed=21)
+    eager = pa.paged_attn_decode(b.q[0], b.k_pool[0], b.v_pool[0], b.block_tables, b.seq_lens, b.B, b.scale,
+                                 num_splits=splits).clone()
+    launch = pa.DecodeLaunch(b.q[0], b.k_pool[0], b.v_pool[0], b.block_tables, b.seq_lens, b.B, b.scale,
+                             num_splits=splits)
+    launch.launch()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch.launch()
+    for _ in range(4):
+        launch.out.fill_(-1.0)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(launch.out.view(torch.int32), eager.view(torch.int32))

@@ -30,8 +30,13 @@ kvcache     token append and copy-on-write of a block's valid slots.
 online      the (m, l, o) recurrence of [Budgets] eq. (4) and the merge of
             partial states.  Not the oracle: it checks the merge algebra the
             kernel relies on, and is pinned against ``attention``.
+blockmgr    the per-request / per-block bookkeeping and the copy-on-write
+            growth protocol of [Slides], as a plain Python model of the
+            library's block manager.  Pinned by the pages' worked examples
+            (free counts of the shared-tail quiz, the lab's block counts, the
+            24 GiB and 8 GiB pool figures, the 3-blocks / 4-requests case).
 
 No function here is "parity unpinned".
 """
 
-from . import accounting, attention, kvcache, online  # noqa: F401
+from . import accounting, attention, blockmgr, kvcache, online  # noqa: F401

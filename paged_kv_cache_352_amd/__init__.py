@@ -8,8 +8,10 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     PA_BF16,
     PA_F32,
+    BlockManager,
     DecodeLaunch,
     PagedAttnError,
+    PoolExhausted,
     declared_functions,
     kv_append,
     kv_cow_copy,

@@ -13,7 +13,8 @@ import re
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pagedattn.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADERS = [os.path.join(INCLUDE, h) for h in ("pagedattn.h", "pa_blockmgr.h")]
 
 PA_F32, PA_BF16 = 0, 1
 _DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
@@ -21,6 +22,10 @@ _DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
 
 class PagedAttnError(RuntimeError):
     pass
+
+
+class PoolExhausted(PagedAttnError):
+    """The block pool has fewer free blocks than the call needs (nothing changed)."""
 
 
 class PaDims(ctypes.Structure):
@@ -60,6 +65,19 @@ def load():
         "kv_append": (I32, [P, P, P, P, P, P, I32, P, DP]),
         "kv_cow_copy": (I32, [P, P, P, P, P, I32, I32, I32, I64, P, DP]),
         "paged_kv_gather": (I32, [P, P, P, P, I32, P, P, P, DP]),
+        "pa_bm_create": (I32, [I32, I32, I32, P, ctypes.POINTER(ctypes.c_void_p)]),
+        "pa_bm_destroy": (None, [P]),
+        "pa_bm_add_request": (I32, [P, ctypes.POINTER(I32)]),
+        "pa_bm_fork": (I32, [P, I32, ctypes.POINTER(I32)]),
+        "pa_bm_release": (I32, [P, I32]),
+        "pa_bm_reserve": (I32, [P, I32, I32, P, P, P]),
+        "pa_bm_prepare_append": (I32, [P, P, I32, P, P, P, P, ctypes.POINTER(I32)]),
+        "pa_bm_export": (I32, [P, P, I32, P, P, I32]),
+        "pa_bm_num_free": (I32, [P]),
+        "pa_bm_refcount": (I32, [P, I32]),
+        "pa_bm_length": (I32, [P, I32]),
+        "pa_bm_num_blocks": (I32, [P, I32]),
+        "pa_bm_check": (I32, [P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -70,16 +88,24 @@ def load():
 
 
 def declared_functions():
-    """Names of the functions include/pagedattn.h declares."""
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"extern", "sizeof", "if", "defined"})
+    """Names of the functions the headers under include/ declare."""
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"#define[^\n]*", "", text)
+        names |= set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text))
+    return sorted(names - {"extern", "sizeof", "if", "defined"})
+
+
+PA_ERR_NO_SPACE = -5
 
 
 def _check(name, status):
     if status != 0:
         lib = load()
-        raise PagedAttnError(f"{name}: {lib.pa_status_string(status).decode()}: {lib.pa_last_error().decode()}")
+        cls = PoolExhausted if status == PA_ERR_NO_SPACE else PagedAttnError
+        raise cls(f"{name}: {lib.pa_status_string(status).decode()}: {lib.pa_last_error().decode()}")
 
 
 def _ptr(t):
@@ -253,3 +279,100 @@ class DecodeLaunch:
         if status:
             _check("paged_attn_decode", status)
         return self.out
+
+
+def _np_ptr(a):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+class BlockManager:
+    """Host-side block manager of libpagedattn (include/pa_blockmgr.h).
+
+    Tables, lengths, refcounts and the free queue live in the library; this
+    class only marshals.  Arrays returned are numpy int32, ready to copy to
+    the device for kv_cow_copy, kv_append and paged_attn_decode.
+    """
+
+    def __init__(self, num_blocks, block_size, max_blocks_per_seq, free_order=None):
+        import numpy as np
+
+        self._np = np
+        self._lib = load()
+        self.num_blocks, self.block_size, self.max_blocks_per_seq = num_blocks, block_size, max_blocks_per_seq
+        h = ctypes.c_void_p()
+        order = None
+        if free_order is not None:
+            order = np.ascontiguousarray(free_order, dtype=np.int32)
+            if order.shape != (num_blocks,):
+                raise PagedAttnError("free_order must list every block once")
+        _check("pa_bm_create", self._lib.pa_bm_create(num_blocks, block_size, max_blocks_per_seq,
+                                                      _np_ptr(order) if order is not None else None,
+                                                      ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def add_request(self):
+        r = ctypes.c_int32()
+        _check("pa_bm_add_request", self._lib.pa_bm_add_request(self._h, ctypes.byref(r)))
+        return r.value
+
+    def fork(self, parent):
+        r = ctypes.c_int32()
+        _check("pa_bm_fork", self._lib.pa_bm_fork(self._h, parent, ctypes.byref(r)))
+        return r.value
+
+    def release(self, req):
+        _check("pa_bm_release", self._lib.pa_bm_release(self._h, req))
+
+    def reserve(self, req, n_tokens):
+        """Grow by n_tokens; returns (src, dst, n_valid) of the copy-on-write it needs, or None."""
+        cs, cd, cn = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check("pa_bm_reserve", self._lib.pa_bm_reserve(self._h, req, n_tokens, ctypes.byref(cs),
+                                                        ctypes.byref(cd), ctypes.byref(cn)))
+        return (cs.value, cd.value, cn.value) if cn.value > 0 else None
+
+    def prepare_append(self, reqs):
+        """One token for each request: (positions, (cow_src, cow_dst, cow_n))."""
+        np = self._np
+        reqs = np.ascontiguousarray(reqs, dtype=np.int32)
+        n = len(reqs)
+        pos = np.empty(n, np.int32)
+        cs, cd, cn = (np.empty(max(n, 1), np.int32) for _ in range(3))
+        k = ctypes.c_int32()
+        _check("pa_bm_prepare_append", self._lib.pa_bm_prepare_append(
+            self._h, _np_ptr(reqs), n, _np_ptr(pos), _np_ptr(cs), _np_ptr(cd), _np_ptr(cn), ctypes.byref(k)))
+        return pos, (cs[:k.value].copy(), cd[:k.value].copy(), cn[:k.value].copy())
+
+    def export(self, reqs, pad_block=0):
+        """(tables [n, max_blocks_per_seq], lens [n]) for the listed requests."""
+        np = self._np
+        reqs = np.ascontiguousarray(reqs, dtype=np.int32)
+        n = len(reqs)
+        tables = np.empty((n, self.max_blocks_per_seq), np.int32)
+        lens = np.empty(n, np.int32)
+        _check("pa_bm_export", self._lib.pa_bm_export(self._h, _np_ptr(reqs), n, _np_ptr(tables), _np_ptr(lens),
+                                                      pad_block))
+        return tables, lens
+
+    @property
+    def num_free(self):
+        return self._lib.pa_bm_num_free(self._h)
+
+    def refcount(self, block):
+        return self._lib.pa_bm_refcount(self._h, block)
+
+    def length(self, req):
+        return self._lib.pa_bm_length(self._h, req)
+
+    def num_blocks_of(self, req):
+        return self._lib.pa_bm_num_blocks(self._h, req)
+
+    def check(self):
+        _check("pa_bm_check", self._lib.pa_bm_check(self._h))

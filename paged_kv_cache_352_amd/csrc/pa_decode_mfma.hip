@@ -18,30 +18,39 @@
 // output; with several it writes its merged state and a second kernel merges
 // the splits.
 //
-// One wave and one 16-slot block, head dim 128; lane l is (n = l%16, c = l/16):
+// Loads.  One (block, KV head) tile is 16 slot rows of 256 bytes, 2 KiB
+// apart in the [block, slot, KV head, dim] pool ([Slides] "把 token 6 变成真正
+// 的内存地址").  Each 16-byte load instruction of a wave covers 4 whole rows
+// (lane l: row 4*i + l/16, bytes 16*(l%16)), so every row is fetched as full
+// cache lines by one instruction; the next block's K and V are in flight
+// while the current one is processed.  Each wave stages its K and V tiles in
+// its own LDS, 16-byte chunk k of slot t at byte 256*t + 16*(k ^ t), which
+// keeps both the row-wise writes and the operand reads below free of bank
+// conflicts.
+//
+// Math for one wave and one 16-slot block, head dim 128; lane l is
+// (n = l%16, c = l/16):
 //
 //   q.k  four v_mfma_f32_16x16x32_bf16 with A = the K tile (M = 16 slots,
-//        K = 32 dims) and B = q of the group (N = 16 query heads, zero beyond
-//        G).  Lane l loads 16 bytes of K: slot n, dims 32*i + 8*c .. +8, and
-//        holds q of head n over the same dims, so the products pair up
-//        whatever order the hardware sums them in.  The result leaves lane l
-//        with the scores of head n for slots 4c .. 4c+3.
+//        K = 32 dims; lane l reads slot n, dims 32*i + 8*c .. +8 from LDS)
+//        and B = q of the group (N = 16 query heads, zero beyond G; lane l
+//        holds head n over the same dims), so the products pair up whatever
+//        order the hardware sums them in.  The result leaves lane l with the
+//        scores of head n for slots 4c .. 4c+3.
 //   p.v  that is exactly the A layout (M = 16 heads, K = 16 slots, 4 slots
 //        per lane) of v_mfma_f32_16x16x16_bf16, so the weights feed p.v
-//        without crossing lanes.  Its B operand needs V with slots along K.
-//        V arrives slot-major; each wave stores its 4 KiB V tile row-major in
-//        LDS (16-byte chunks XOR-swizzled by row) and reads it back with
-//        ds_read_b64_tr_b16, which hands lane (n, c) the dims 16*j + n of
-//        slots 4c .. 4c+3.  p is split into a bf16 head and a bf16 remainder
-//        (p = hi + lo to about 2^-16 relative) and both go through the matrix
-//        core, so p.v keeps fp32-class accuracy.  The eight accumulators hold
-//        o for heads 4c .. 4c+3, dims 16*j + n.
+//        without crossing lanes.  Its B operand needs V with slots along K:
+//        ds_read_b64_tr_b16 reads the row-major V tile transposed, handing
+//        lane (n, c) the dims 16*j + n of slots 4c .. 4c+3.  p is split into
+//        a bf16 head and a bf16 remainder (p = hi + lo to about 2^-16
+//        relative) and both go through the matrix core, so p.v keeps
+//        fp32-class accuracy.  The eight accumulators hold o for heads
+//        4c .. 4c+3, dims 16*j + n.
 //
 // Softmax state: lane l keeps m (the running max, base 2) of head n and a
 // partial l over its own four slots of every block; the partials of the four
 // lanes of a head are summed once at the end.  The accumulators are rescaled
-// only in blocks where some head's max moved.  The next block's K and V are
-// loaded before the current block is processed.
+// only in blocks where some head's max moved.
 #include <hip/hip_runtime.h>
 
 #include "pa_internal.h"
@@ -56,12 +65,13 @@ constexpr float kNegInf = -__builtin_huge_valf();
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 #define PA_LDS __attribute__((address_space(3)))
 
-// V tile in LDS: slot t, dims 8k .. 8k+7 (16-byte chunk k) at byte
+// K or V tile in LDS: slot t, dims 8k .. 8k+7 (16-byte chunk k) at byte
 //   256 * t + 16 * (k ^ t).
-// The XOR spreads both the row-wise 16-byte writes and the transposing
-// 8-byte reads of one instruction evenly over the banks.
+// The XOR spreads the row-wise 16-byte writes, the 16-byte K operand reads
+// and the transposing 8-byte V reads of one instruction evenly over the banks.
 constexpr int kVtBytes = kB * kHeadDim * 2;  // 4096
 
 // K/V tiles in flight per wave.
@@ -107,6 +117,7 @@ template <int G, int W>
 __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   static_assert(G >= 1 && G <= 16, "the query group must fit the 16 columns of one MFMA tile");
   __shared__ __attribute__((aligned(16))) uint8_t vt_all[W][kVtBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t kt_all[W][kVtBytes];
   __shared__ float red_m[W][16];
   __shared__ float red_l[W][16];
   __shared__ __attribute__((aligned(16))) float red_o[W][G][kHeadDim];
@@ -144,10 +155,10 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
     }
   }
 
-  // Element offset of this lane's 16 bytes inside a block: slot n16, head kvh, dims 8*c4 (+32*i).
+  // Element offset of this lane's 16 bytes inside a block: slot c4 (+4*i), head kvh, dims 8*n16.
   const int64_t row_stride = (int64_t)a.Hkv * kHeadDim;
   const int64_t blk_stride = (int64_t)kB * row_stride;
-  const int64_t lane_off = (int64_t)n16 * row_stride + (int64_t)kvh * kHeadDim + 8 * c4;
+  const int64_t lane_off = (int64_t)c4 * row_stride + (int64_t)kvh * kHeadDim + 8 * n16;
   const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pool) + lane_off;
   const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pool) + lane_off;
   const int32_t* trow = a.tables + (int64_t)s * a.MB + j0 + w;
@@ -161,9 +172,9 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
     const uint16_t* kb = kbase + (int64_t)pb * blk_stride;
     const uint16_t* vb = vbase + (int64_t)pb * blk_stride;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t.k[i] = load_kv16(kb + 32 * i);
+    for (int i = 0; i < 4; ++i) t.k[i] = load_kv16(kb + 4 * i * row_stride);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t.v[i] = load_kv16(vb + 32 * i);
+    for (int i = 0; i < 4; ++i) t.v[i] = load_kv16(vb + 4 * i * row_stride);
   };
 
   float m = kNegInf;  // running max (base 2) of head n16
@@ -172,33 +183,37 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) acc[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // LDS addresses.  Writes: slot n16, chunk 4*i + c4.  Transposing reads for
-  // output dims 16*jj + n16: this lane fetches slot r = 4*c4 + n16/4, dims
-  // 16*jj + 4*(n16%4) .. +3, i.e. half (n16 & 1) of chunk 2*jj + (n16%4)/2.
+  // LDS addresses.  Writes: slot 4*i + c4, chunk n16.  K operand reads: slot
+  // n16, chunk 4*i + c4.  Transposing V reads for output dims 16*jj + n16:
+  // this lane fetches slot r = 4*c4 + n16/4, dims 16*jj + 4*(n16%4) .. +3,
+  // i.e. half (n16 & 1) of chunk 2*jj + (n16%4)/2.
   uint8_t* vt = vt_all[w];
-  uint8_t* vt_w = vt + 256 * n16;
   const int rr = 4 * c4 + (n16 >> 2);
   const PA_LDS uint8_t* vt_r = (const PA_LDS uint8_t*)vt + 256 * rr + 8 * (n16 & 1);
   const int bsel = ((n16 & 3) >> 1) ^ (rr & 1);  // low bit of the swizzled chunk
   const int rhi = rr & 14;                       // the rest of the swizzle
 
+  uint8_t* kt = kt_all[w];
+  const PA_LDS uint8_t* kt_r = (const PA_LDS uint8_t*)kt + 256 * n16;  // K reads: slot n16
+
   auto process = [&](int j, Tile& cur) {
-    // q.k for the 16 slots of block j.
+    const int valid = n - j * kB;  // >= 1
+    wave_lds_order();  // the previous block's reads of these tiles come first
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * i + c4;
+      uint4 vv = cur.v[i];
+      if (r >= valid) vv = make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4*>(kt + 256 * r + 16 * (n16 ^ r)) = cur.k[i];
+      *reinterpret_cast<uint4*>(vt + 256 * r + 16 * (n16 ^ r)) = vv;
+    }
+    wave_lds_order();
     f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, cur.k[i]), qv[i], sc, 0, 0, 0);
-
-    // V into LDS; slots past the length become zeros so that their (possibly
-    // NaN) contents never meet a zero weight.
-    const int valid = n - j * kB;  // >= 1
-    if (valid < kB && n16 >= valid) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) cur.v[i] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const u32x4_t kv = *reinterpret_cast<const PA_LDS u32x4_t*>(kt_r + 16 * ((4 * i + c4) ^ n16));
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qv[i], sc, 0, 0, 0);
     }
-    wave_lds_order();  // the previous block's reads of this tile come first
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(vt_w + 16 * ((4 * i + c4) ^ n16)) = cur.v[i];
 
     // Scores in base 2, masked past the length ([Slides] quiz "逻辑顺序没错…").
     float sv[4];

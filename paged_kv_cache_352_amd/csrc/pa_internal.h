@@ -30,6 +30,9 @@ struct DecodeArgs {
   int bps;          // blocks per split
 };
 
+// Sets the thread's pa_last_error() text (used by the host-only parts).
+void set_last_error(const char* msg);
+
 // Workspace floats for P splits: S*Hq*P*(d + 2).
 size_t decode_workspace_floats(int S, int Hq, int P);
 

@@ -1,0 +1,382 @@
+"""Block manager (include/pa_blockmgr.h) on the CPU: the pages' worked examples,
+the protocol's guarantees, and agreement with the plain-Python model in
+oracle/blockmgr.py on seeded random operation sequences.
+
+Every example test runs against both the C++ manager and the model, so the
+model is pinned by the same printed figures.  Nothing here touches a GPU.
+"""
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_352_amd as pa
+from oracle import accounting as acc
+from oracle import blockmgr as bmo
+
+
+class NoSpace(Exception):
+    pass
+
+
+class Cpp:
+    name = "cpp"
+
+    def __init__(self, num_blocks, block_size, max_blocks, free_order=None):
+        self.m = pa.BlockManager(num_blocks, block_size, max_blocks, free_order)
+        self.MB = max_blocks
+
+    def add_request(self):
+        return self.m.add_request()
+
+    def fork(self, parent):
+        return self.m.fork(parent)
+
+    def release(self, req):
+        self.m.release(req)
+
+    def reserve(self, req, n):
+        try:
+            return self.m.reserve(req, n)
+        except pa.PoolExhausted as e:
+            raise NoSpace(str(e))
+
+    def prepare_append(self, reqs):
+        try:
+            pos, (cs, cd, cn) = self.m.prepare_append(reqs)
+        except pa.PoolExhausted as e:
+            raise NoSpace(str(e))
+        return [int(x) for x in pos], [(int(a), int(b), int(c)) for a, b, c in zip(cs, cd, cn)]
+
+    def num_free(self):
+        return self.m.num_free
+
+    def refcount(self, b):
+        return self.m.refcount(b)
+
+    def length(self, r):
+        return self.m.length(r)
+
+    def blocks_of(self, r):
+        tables, lens = self.m.export([r], pad_block=-1)
+        return [int(b) for b in tables[0] if b >= 0]
+
+    def check(self):
+        self.m.check()
+
+
+class Model:
+    name = "model"
+
+    def __init__(self, num_blocks, block_size, max_blocks, free_order=None):
+        self.m = bmo.BlockManagerModel(num_blocks, block_size, max_blocks, free_order)
+
+    def add_request(self):
+        return self.m.add_request()
+
+    def fork(self, parent):
+        return self.m.fork(parent)
+
+    def release(self, req):
+        self.m.release(req)
+
+    def reserve(self, req, n):
+        try:
+            return self.m.reserve(req, n)
+        except bmo.NoSpace as e:
+            raise NoSpace(str(e))
+
+    def prepare_append(self, reqs):
+        try:
+            return self.m.prepare_append(list(reqs))
+        except bmo.NoSpace as e:
+            raise NoSpace(str(e))
+
+    def num_free(self):
+        return self.m.num_free()
+
+    def refcount(self, b):
+        return self.m.refcount[b]
+
+    def length(self, r):
+        return self.m.lengths[r]
+
+    def blocks_of(self, r):
+        return self.m.blocks_of(r)
+
+    def check(self):
+        held = [0] * len(self.m.refcount)
+        for t in self.m.tables.values():
+            for b in t:
+                held[b] += 1
+        assert held == self.m.refcount
+        assert sorted(self.m.free) == [b for b, c in enumerate(self.m.refcount) if c == 0]
+
+
+@pytest.fixture(params=[Cpp, Model], ids=["cpp", "model"])
+def impl(request):
+    if request.param is Cpp:
+        try:
+            pa.load()
+        except pa.PagedAttnError:
+            from paged_kv_cache_352_amd.build import build
+
+            build()
+    return request.param
+
+
+# ------------------------------------------------------------ worked examples
+
+
+def test_cow_free_count_quiz(impl):
+    """[Slides] quiz "共享尾块之后，谁该释放哪一块？" with slide "一次写入，为什么会先
+    少掉一个空闲块？": B = 4, A and B share a partly filled tail (P2), 5 blocks
+    free.  A's write copies: 4 free, both blocks referenced once.  A finishes:
+    5 free, P2 still 1.  B finishes: 6 free."""
+    m = impl(6, 4, 4)
+    a = m.add_request()
+    assert m.reserve(a, 3) is None  # a, b, c written into one block
+    b = m.fork(a)
+    p2 = m.blocks_of(a)[0]
+    assert m.refcount(p2) == 2 and m.num_free() == 5
+    pos, copies = m.prepare_append([a])
+    assert pos == [3]
+    assert len(copies) == 1
+    src, dst, nvalid = copies[0]
+    assert (src, nvalid) == (p2, 3) and dst != p2
+    assert m.blocks_of(a) == [dst] and m.blocks_of(b) == [p2]
+    assert m.num_free() == 4 and m.refcount(p2) == 1 and m.refcount(dst) == 1
+    m.release(a)
+    assert m.num_free() == 5 and m.refcount(p2) == 1
+    m.release(b)
+    assert m.num_free() == 6
+    m.check()
+
+
+@pytest.mark.parametrize("B,blocks,tail_waste", [(16, 8, 16), (4, 29, 4)])
+def test_lab_block_counts(impl, B, blocks, tail_waste):
+    """[Slides] lab: lengths 17 / 32 / 63 give blocks=8, slots=128, useful=112,
+    tail_waste=16 at B = 16 and blocks=29, tail_waste=4 at B = 4."""
+    m = impl(64, B, 64)
+    reqs = []
+    for n in (17, 32, 63):
+        r = m.add_request()
+        m.reserve(r, n)
+        reqs.append(r)
+    used = sum(len(m.blocks_of(r)) for r in reqs)
+    useful = sum(m.length(r) for r in reqs)
+    assert used == blocks == sum(acc.blocks_for(n, B) for n in (17, 32, 63))
+    assert useful == 112
+    assert used * B - useful == tail_waste
+    assert m.num_free() == 64 - blocks
+    m.check()
+
+
+def test_pool_24gib_holds_47_requests(impl):
+    """[Slides] "24 GiB 的 KV 池，能同时容纳多少请求？": 12,288 blocks at B = 16;
+    47 requests of 257 blocks use 12,079 and leave 209; the 48th needs 257
+    and is refused with nothing changed."""
+    m = impl(12288, 16, 300)
+    n = 4100  # any length with ceil(n / 16) = 257
+    assert acc.blocks_for(n, 16) == 257
+    for _ in range(47):
+        m.reserve(m.add_request(), n)
+    assert m.num_free() == 12288 - 12079 == 209
+    last = m.add_request()
+    with pytest.raises(NoSpace):
+        m.reserve(last, n)
+    assert m.num_free() == 209 and m.length(last) == 0 and m.blocks_of(last) == []
+    assert 257 - m.num_free() == 48  # how many blocks short
+    m.check()
+
+
+def test_pool_8gib_holds_168_requests(impl):
+    """[Slides] quiz "8 GiB 池能容纳多少条 1,025-token 请求？": 10,922 blocks,
+    65 per request, 168 requests, 2 blocks left; the 169th does not fit."""
+    m = impl(10922, 16, 65)
+    for _ in range(168):
+        m.reserve(m.add_request(), 1025)
+    assert m.num_free() == 2
+    with pytest.raises(NoSpace):
+        m.reserve(m.add_request(), 1025)
+    assert m.num_free() == 2
+    m.check()
+
+
+def test_three_free_blocks_four_requests(impl):
+    """[Slides] "三个空闲块，四个请求同时跨边界": four requests each need a new
+    block this step but only three are free: the step is refused before any
+    table changes; running three of them works."""
+    m = impl(7, 4, 4)
+    reqs = [m.add_request() for _ in range(4)]
+    for r in reqs:
+        m.reserve(r, 4)  # full tails
+    assert m.num_free() == 3
+    before = [m.blocks_of(r) for r in reqs]
+    with pytest.raises(NoSpace):
+        m.prepare_append(reqs)
+    assert [m.blocks_of(r) for r in reqs] == before and m.num_free() == 3
+    pos, copies = m.prepare_append(reqs[:3])
+    assert pos == [4, 4, 4] and copies == [] and m.num_free() == 0
+    m.check()
+
+
+def test_occupancy_log_request_50_blocks_short(impl):
+    """[Slides] "占用率只有 70%，为什么请求还是进不来？": 1,000 blocks, 700 in use,
+    a request needing 350 blocks is 50 short and does not get in."""
+    m = impl(1000, 16, 400)
+    for _ in range(7):
+        m.reserve(m.add_request(), 100 * 16)
+    assert m.num_free() == 300
+    r = m.add_request()
+    with pytest.raises(NoSpace):
+        m.reserve(r, 350 * 16)
+    assert 350 - m.num_free() == 50
+    m.check()
+
+
+# ------------------------------------------------------------ protocol guarantees
+
+
+def test_failed_copy_leaves_mapping_intact(impl):
+    """[Slides] "先确保分配成功，再改变可见状态": with no free block the copy of a
+    shared tail cannot be made, and the old mapping stays exactly as it was."""
+    m = impl(1, 4, 4)
+    a = m.add_request()
+    m.reserve(a, 2)
+    b = m.fork(a)
+    assert m.num_free() == 0
+    with pytest.raises(NoSpace):
+        m.prepare_append([b])
+    assert m.blocks_of(a) == m.blocks_of(b) and m.refcount(m.blocks_of(a)[0]) == 2
+    assert m.length(a) == m.length(b) == 2
+    m.check()
+
+
+def test_last_reference_returns_the_block(impl):
+    """A shared block returns to the free queue only with its last reader."""
+    m = impl(4, 4, 4)
+    a = m.add_request()
+    m.reserve(a, 8)  # two full blocks
+    b = m.fork(a)
+    shared = m.blocks_of(a)
+    m.release(a)
+    assert m.num_free() == 2 and all(m.refcount(x) == 1 for x in shared)
+    m.release(b)
+    assert m.num_free() == 4
+    m.check()
+
+
+def test_full_blocks_stay_shared_after_divergence(impl):
+    """Branches that write after sharing get their own tails; full prefix
+    blocks stay shared ([Slides] "只读时共用，要写入时再分开")."""
+    m = impl(16, 4, 8)
+    a = m.add_request()
+    m.reserve(a, 9)  # two full blocks + one token
+    b = m.fork(a)
+    c = m.fork(a)
+    pos, copies = m.prepare_append([a, b, c])
+    assert pos == [9, 9, 9]
+    assert len(copies) == 2  # a and b copy, c is then the tail's only reader
+    ta, tb, tc = m.blocks_of(a), m.blocks_of(b), m.blocks_of(c)
+    assert ta[:2] == tb[:2] == tc[:2]
+    assert len({ta[2], tb[2], tc[2]}) == 3
+    assert all(m.refcount(x) == 3 for x in ta[:2])
+    m.check()
+
+
+def test_leaked_release_exhausts_the_pool(impl):
+    """[Slides] "先确保分配成功…" warns that finishing without releasing
+    (a cancel that skips the release path) slowly leaks the whole pool."""
+    m = impl(10, 4, 4)
+    for _ in range(100):  # released every time: never runs out
+        r = m.add_request()
+        m.reserve(r, 8)
+        m.release(r)
+    assert m.num_free() == 10
+    served = 0
+    with pytest.raises(NoSpace):
+        for _ in range(100):  # never released
+            m.reserve(m.add_request(), 8)
+            served += 1
+    assert served == 5 and m.num_free() == 0
+    m.check()
+
+
+# ------------------------------------------------------------ C++ vs model
+
+
+def _random_ops(seed, steps=400):
+    rng = np.random.default_rng(seed)
+    NB, B, MB = 64, 4, 12
+    order = rng.permutation(NB)
+    c, m = Cpp(NB, B, MB, order), Model(NB, B, MB, order)
+    live = []
+    for _ in range(steps):
+        op = rng.integers(0, 5)
+        if op == 0 or not live:
+            live.append((c.add_request(), m.add_request()))
+            assert live[-1][0] == live[-1][1]
+        elif op == 1:
+            i = live[rng.integers(len(live))][0]
+            live.append((c.fork(i), m.fork(i)))
+        elif op == 2:
+            i = live.pop(rng.integers(len(live)))[0]
+            c.release(i)
+            m.release(i)
+        elif op == 3:
+            i = live[rng.integers(len(live))][0]
+            n = int(rng.integers(0, 7))
+            res = []
+            for x in (c, m):
+                try:
+                    res.append(("ok", x.reserve(i, n)))
+                except NoSpace:
+                    res.append(("nospace", None))
+                except (pa.PagedAttnError, ValueError):
+                    res.append(("invalid", None))
+            assert res[0] == res[1]
+        else:
+            k = int(rng.integers(1, len(live) + 1))
+            pick = [live[j][0] for j in rng.permutation(len(live))[:k]]
+            res = []
+            for x in (c, m):
+                try:
+                    res.append(("ok",) + tuple(x.prepare_append(pick)))
+                except NoSpace:
+                    res.append(("nospace",))
+                except (pa.PagedAttnError, ValueError):
+                    res.append(("invalid",))
+            assert res[0] == res[1]
+        c.check()
+        assert c.num_free() == m.num_free()
+        for i, _ in live:
+            assert c.blocks_of(i) == m.blocks_of(i) and c.length(i) == m.length(i)
+        for blk in range(NB):
+            assert c.refcount(blk) == m.refcount(blk)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_cpp_matches_model_on_random_operations(seed):
+    pa.load()
+    _random_ops(seed)
+
+
+def test_cpp_rejects_bad_arguments():
+    m = pa.BlockManager(8, 4, 2)
+    with pytest.raises(pa.PagedAttnError):
+        m.fork(7)
+    with pytest.raises(pa.PagedAttnError):
+        m.release(3)
+    r = m.add_request()
+    with pytest.raises(pa.PagedAttnError):
+        m.prepare_append([r, r])  # listed twice
+    with pytest.raises(pa.PagedAttnError):
+        m.reserve(r, 9)  # more than 2 blocks of 4
+    with pytest.raises(pa.PagedAttnError):
+        m.reserve(r, -1)
+    with pytest.raises(pa.PagedAttnError):
+        pa.BlockManager(4, 4, 4, free_order=[0, 1, 1, 2])
+    with pytest.raises(pa.PagedAttnError):
+        pa.BlockManager(0, 4, 4)
+    assert m.num_free == 8
+    m.check()

@@ -110,8 +110,20 @@ struct Tile {
   uint4 v[4];
 };
 
-// One 16-byte load of K/V history.
-__device__ inline uint4 load_kv16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+// K/V tiles are read with buffer loads: a descriptor for one physical block
+// (uniform, in SGPRs) plus a 32-bit per-lane byte offset, so the per-lane
+// addresses are four constant registers instead of a 64-bit address per load.
+// The descriptor's size is the block's byte count: the hardware returns zero
+// for any offset past it.
+constexpr int kBufferFlags = 0x00020000;  // word 3 of a raw buffer descriptor on CDNA (32-bit data format)
+
+__device__ inline __amdgpu_buffer_rsrc_t block_rsrc(const char* block, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(block), (short)0, (int)bytes, kBufferFlags);
+}
+
+__device__ inline uint4 load_kv16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
 
 template <int G, int W>
 __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
@@ -155,12 +167,18 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
     }
   }
 
-  // Element offset of this lane's 16 bytes inside a block: slot c4 (+4*i), head kvh, dims 8*n16.
   const int64_t row_stride = (int64_t)a.Hkv * kHeadDim;
   const int64_t blk_stride = (int64_t)kB * row_stride;
-  const int64_t lane_off = (int64_t)c4 * row_stride + (int64_t)kvh * kHeadDim + 8 * n16;
-  const uint16_t* kbase = static_cast<const uint16_t*>(a.k_pool) + lane_off;
-  const uint16_t* vbase = static_cast<const uint16_t*>(a.v_pool) + lane_off;
+  // Byte offsets inside a block (a block is at most a few hundred KiB, so 32
+  // bits suffice); the block's base address is uniform, so each load is an
+  // SGPR base plus one of these four per-lane offsets.
+  uint32_t voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    voff[i] = (uint32_t)(((4 * i + c4) * row_stride + (int64_t)kvh * kHeadDim + 8 * n16) * 2);
+  const char* kpool = static_cast<const char*>(a.k_pool);
+  const char* vpool = static_cast<const char*>(a.v_pool);
+  const uint32_t blk_bytes = (uint32_t)(blk_stride * 2);
   const int32_t* trow = a.tables + (int64_t)s * a.MB + j0 + w;
 
   // Issue the 8 16-byte loads of the K and V tile of physical block pb.
@@ -169,12 +187,12 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
       bad = true;
       pb = 0;
     }
-    const uint16_t* kb = kbase + (int64_t)pb * blk_stride;
-    const uint16_t* vb = vbase + (int64_t)pb * blk_stride;
+    const __amdgpu_buffer_rsrc_t kr = block_rsrc(kpool + (int64_t)pb * blk_bytes, blk_bytes);
+    const __amdgpu_buffer_rsrc_t vr = block_rsrc(vpool + (int64_t)pb * blk_bytes, blk_bytes);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t.k[i] = load_kv16(kb + 4 * i * row_stride);
+    for (int i = 0; i < 4; ++i) t.k[i] = load_kv16(kr, voff[i]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t.v[i] = load_kv16(vb + 4 * i * row_stride);
+    for (int i = 0; i < 4; ++i) t.v[i] = load_kv16(vr, voff[i]);
   };
 
   float m = kNegInf;  // running max (base 2) of head n16

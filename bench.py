@@ -164,6 +164,32 @@ def side_kernels(torch, pa, W, dev):
     return res
 
 
+def swap_time(torch, pa, b, dev, nblocks=250, reps=3):
+    """Swap-out and swap-in of nblocks blocks in every layer through pinned host
+    memory: 250 blocks x 32 layers x 64 KiB = 500 MiB, the amount the pages'
+    recovery-cost example moves (4,000 tokens at 128 KiB per token)."""
+    ids = torch.arange(nblocks, dtype=torch.int32, device=dev)
+    buf = torch.empty((b.L, 2, nblocks, b.B, b.Hkv, b.D), dtype=b.dtype, pin_memory=True)
+    nbytes = buf.numel() * buf.element_size()
+    res = {}
+    for name, fn in (("out", pa.kv_swap_out), ("in", pa.kv_swap_in)):
+        fn(b.k_pool, b.v_pool, ids, buf, b.B)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            fn(b.k_pool, b.v_pool, ids, buf, b.B)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / reps
+        res[f"{name}_ms"] = round(ms, 3)
+        res[f"{name}_GiB_s"] = round(nbytes / (ms * 1e-3) / 2**30, 2)
+    res["bytes"] = nbytes
+    del buf
+    return res
+
+
 def suite(torch, pa, W, dev):
     """Decode (and full-step) timings of the other four workloads, one dict each."""
     out = {}
@@ -193,6 +219,24 @@ def suite(torch, pa, W, dev):
         outs = [torch.empty((b.S, b.Hq, b.D), dtype=torch.float32, device=dev) for _ in range(b.L)]
         return graph_time_us(torch, step, 1)
 
+    # The block-size trade-off on the headline batch: same tokens, B = 8 .. 64,
+    # four pool copies rotated as in the headline measurement.
+    for B in (8, 16, 32, 64):
+        b = W.config2(device=dev, B=B)
+        pools = [(b.k_pool[0], b.v_pool[0])] + [(b.k_pool[0].clone(), b.v_pool[0].clone()) for _ in range(3)]
+        calls = [pa.DecodeLaunch(b.q[0], k, v, b.block_tables, b.seq_lens, b.B, b.scale) for k, v in pools]
+
+        def launch_all():
+            for c in calls:
+                c.launch()
+
+        us = graph_time_us(torch, launch_all, 10) / len(calls)
+        kvb = b.valid_kv_bytes_per_layer()
+        out[f"bf16 32 x 4096 tokens, block size {B}"] = dict(
+            rate(kvb, us), splits=calls[0].splits, layers=1, tokens_per_s_per_layer=round(b.S / (us * 1e-6), 1))
+        del b, pools, calls
+        torch.cuda.empty_cache()
+
     for name, make, rows in (("fp32 5 requests (37..511 tokens), one layer", W.config1, None),
                              ("bf16 256 mixed-length requests, 32 layers", W.config3, None),
                              ("bf16 prefix sharing, 64 branches (COW), one layer", W.config4, None),
@@ -207,6 +251,8 @@ def suite(torch, pa, W, dev):
             ent["full_step_us"] = round(step_us, 2)
             ent["full_step_ops"] = ("kv_cow_copy, " if b.cow_src.numel() else "") + \
                 f"{b.rounds} kv_append round(s) and one decode per layer, {b.L} layer(s)"
+        if name.startswith("bf16 256 mixed"):
+            ent["swap_500MiB"] = swap_time(torch, pa, b, dev)
         if name.startswith("bf16 prefix"):
             ent["note"] = "the shared prefix is cache-resident: logical bytes, no roofline claim"
         out[name] = ent

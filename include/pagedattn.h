@@ -88,7 +88,8 @@ const char* pa_last_error(void);
 /*
  * Split-K plan for paged_attn_decode at block size B: the number of splits
  * the decode will use and the workspace it needs (0 when no split is used).
- * Depends only on host-known sizes, so repeated calls agree.
+ * Depends only on host-known sizes, so repeated calls agree.  A forced
+ * num_splits is capped at ceil(MB * B / max(16, B)).
  */
 pa_status paged_attn_plan(const pa_dims* dims, int32_t B, int32_t* num_splits,
                           size_t* workspace_bytes);
@@ -107,8 +108,9 @@ pa_status paged_attn_plan(const pa_dims* dims, int32_t B, int32_t* num_splits,
  * so the result depends only on logical positions, never on physical ids.
  * A request with seq_lens[s] == 0 gets out = 0.
  *
- * B: block size in tokens (this build: 16).  scale: multiplies q.k (e.g.
- * 1/sqrt(d)).  Accumulation is float32; out is float32.
+ * B: block size in tokens: 4, 8, 16, 32 or 64 (the pages' block-size
+ * trade-off, [Slides] "块越小，省下的是空位，多出来的是管理").  scale:
+ * multiplies q.k (e.g. 1/sqrt(d)).  Accumulation is float32; out is float32.
  */
 pa_status paged_attn_decode(const void* q, const void* k_pool, const void* v_pool,
                             const int32_t* block_tables, const int32_t* seq_lens,
@@ -145,6 +147,28 @@ pa_status kv_cow_copy(void* k_pool, void* v_pool, const int32_t* src_blocks,
                       const int32_t* dst_blocks, const int32_t* n_valid, int32_t num_pairs,
                       int32_t B, int32_t num_layers, int64_t layer_stride_elems,
                       hipStream_t stream, const pa_dims* dims);
+
+/*
+ * Block swap ([Slides] "腾出显存以后，还要付一次恢复成本": a preempted
+ * request's KV can be moved out and back in instead of recomputed).  Whole
+ * blocks — all B slots, all KV heads, K and V, in every layer — move between
+ * the pools and a contiguous buffer laid out
+ *   buf[layer][pool: 0 = K, 1 = V][i][B][Hkv][d]   (dtype of the pools)
+ * for the num_list block ids in `blocks` (int32, device).
+ *   kv_swap_out: buf <- pools;   kv_swap_in: pools <- buf.
+ * buf may be device memory or host memory the device can address (pinned,
+ * e.g. hipHostMalloc); then the kernel reads or writes it across the host
+ * link directly.  buf must be 16-byte aligned and hold
+ * num_layers * 2 * num_list * B * Hkv * d elements.  Layers and strides as in
+ * kv_cow_copy.  Ids outside [0, NB) are skipped.  Bytes are copied exactly;
+ * nothing else in the pools changes.  A swap-in may target other block ids
+ * than the swap-out (the caller's new table then points at them).
+ */
+pa_status kv_swap_out(const void* k_pool, const void* v_pool, const int32_t* blocks, int32_t num_list, void* buf,
+                      int32_t B, int32_t num_layers, int64_t layer_stride_elems, hipStream_t stream,
+                      const pa_dims* dims);
+pa_status kv_swap_in(void* k_pool, void* v_pool, const int32_t* blocks, int32_t num_list, const void* buf, int32_t B,
+                     int32_t num_layers, int64_t layer_stride_elems, hipStream_t stream, const pa_dims* dims);
 
 /*
  * Debug helper, not on the decode path: materialise each request's history

@@ -64,3 +64,24 @@ def gather_padded(pool, block_tables, seq_lens, B, fill):
         for t in range(int(seq_lens[s])):
             out[s, t] = pool[int(block_tables[s][t // B]), t % B]
     return out
+
+
+def swap_out(k_pools, v_pools, blocks):
+    """Whole blocks of every layer into one buffer [L, 2, n, B, Hkv, d] (K then V).
+
+    [Slides] "腾出显存以后，还要付一次恢复成本": moving a preempted request's KV
+    out (and back in, below) instead of recomputing it.  Pools are [L, NB, ...].
+    """
+    k_pools, v_pools = np.asarray(k_pools), np.asarray(v_pools)
+    idx = [int(b) for b in blocks]
+    return np.stack([np.stack([k_pools[l][idx], v_pools[l][idx]]) for l in range(k_pools.shape[0])])
+
+
+def swap_in(k_pools, v_pools, blocks, buf):
+    """The inverse: block blocks[i] of layer l takes buf[l, 0/1, i]; new arrays returned."""
+    k, v = np.array(k_pools, copy=True), np.array(v_pools, copy=True)
+    for l in range(k.shape[0]):
+        for i, b in enumerate(blocks):
+            k[l, int(b)] = buf[l, 0, i]
+            v[l, int(b)] = buf[l, 1, i]
+    return k, v

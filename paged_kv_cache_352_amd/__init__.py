@@ -15,6 +15,8 @@ from ._lib import (  # noqa: F401
     declared_functions,
     kv_append,
     kv_cow_copy,
+    kv_swap_in,
+    kv_swap_out,
     load,
     make_dims,
     paged_attn_decode,

@@ -65,6 +65,8 @@ def load():
         "kv_append": (I32, [P, P, P, P, P, P, I32, P, DP]),
         "kv_cow_copy": (I32, [P, P, P, P, P, I32, I32, I32, I64, P, DP]),
         "paged_kv_gather": (I32, [P, P, P, P, I32, P, P, P, DP]),
+        "kv_swap_out": (I32, [P, P, P, I32, P, I32, I32, I64, P, DP]),
+        "kv_swap_in": (I32, [P, P, P, I32, P, I32, I32, I64, P, DP]),
         "pa_bm_create": (I32, [I32, I32, I32, P, ctypes.POINTER(ctypes.c_void_p)]),
         "pa_bm_destroy": (None, [P]),
         "pa_bm_add_request": (I32, [P, ctypes.POINTER(I32)]),
@@ -223,6 +225,38 @@ def kv_cow_copy(k_pool, v_pool, src_blocks, dst_blocks, n_valid, B, stream=None)
     stride = NB * B * Hkv * D
     _check("kv_cow_copy", lib.kv_cow_copy(_ptr(k_pool), _ptr(v_pool), _ptr(src_blocks), _ptr(dst_blocks),
                                           _ptr(n_valid), n, B, L, stride, _stream(stream), ctypes.byref(d)))
+
+
+def _swap(name, k_pool, v_pool, blocks, buf, B, stream):
+    lib = load()
+    if k_pool.dim() == 4:
+        L, (NB, Bp, Hkv, D) = 1, k_pool.shape
+    else:
+        L, NB, Bp, Hkv, D = k_pool.shape
+    if Bp != B or v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
+        raise PagedAttnError("pool shapes / dtypes disagree")
+    n = blocks.shape[0]
+    if blocks.dtype != torch.int32 or blocks.dim() != 1:
+        raise PagedAttnError("blocks must be int32 [n]")
+    if tuple(buf.shape) != (L, 2, n, B, Hkv, D) or buf.dtype != k_pool.dtype or not buf.is_contiguous():
+        raise PagedAttnError("buf must be a contiguous [L, 2, n, B, Hkv, d] tensor of the pool dtype")
+    if not (buf.is_cuda or buf.is_pinned()):
+        raise PagedAttnError("buf must be device memory or pinned host memory")
+    _need_cuda(k_pool, v_pool, blocks)
+    d = make_dims(0, 1, Hkv, D, 1, NB, k_pool.dtype)
+    fn = getattr(lib, name)
+    _check(name, fn(_ptr(k_pool), _ptr(v_pool), _ptr(blocks), n, _ptr(buf), B, L, NB * B * Hkv * D,
+                    _stream(stream), ctypes.byref(d)))
+
+
+def kv_swap_out(k_pool, v_pool, blocks, buf, B, stream=None):
+    """buf[l, 0/1, i] = K/V of block blocks[i] in layer l; buf may be pinned host memory."""
+    _swap("kv_swap_out", k_pool, v_pool, blocks, buf, B, stream)
+
+
+def kv_swap_in(k_pool, v_pool, blocks, buf, B, stream=None):
+    """K/V of block blocks[i] in layer l = buf[l, 0/1, i]."""
+    _swap("kv_swap_in", k_pool, v_pool, blocks, buf, B, stream)
 
 
 def paged_kv_gather(k_pool, v_pool, block_tables, seq_lens, B, k_out=None, v_out=None, stream=None):

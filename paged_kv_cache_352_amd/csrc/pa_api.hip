@@ -60,7 +60,8 @@ pa_status check_dims(const pa_dims* d, int32_t B, bool need_attention_shape) {
     if (!g_ok)
       return fail(PA_ERR_UNSUPPORTED, "query heads per KV head = %d (supported: 1, 2, 4, 8; 16 for bf16)", G);
     if (d->head_dim != pa::kHeadDim) return fail(PA_ERR_UNSUPPORTED, "head_dim %d (supported: 128)", d->head_dim);
-    if (B != 16) return fail(PA_ERR_UNSUPPORTED, "block size %d (supported: 16)", B);
+    if (B != 4 && B != 8 && B != 16 && B != 32 && B != 64)
+      return fail(PA_ERR_UNSUPPORTED, "block size %d (supported: 4, 8, 16, 32, 64)", B);
     if (d->num_splits < 0) return fail(PA_ERR_INVALID_ARG, "num_splits = %d < 0", d->num_splits);
   }
   // slot rows are copied as 16-byte vectors
@@ -69,33 +70,37 @@ pa_status check_dims(const pa_dims* d, int32_t B, bool need_attention_shape) {
   return PA_OK;
 }
 
-// Splits depend only on host-known sizes (S, Hkv, MB, dtype), so repeated
-// calls agree.  Returns (P, blocks per split).
+// Splits depend only on host-known sizes (S, Hkv, MB, B, dtype), so repeated
+// calls agree.  A split boundary is both a 16-slot tile boundary and a block
+// boundary: split p covers tokens [p*tps, (p+1)*tps) with tps a multiple of
+// max(16, B).  Returns (P, tps).
 //   bf16 (matrix-core kernel, kMfmaWaves waves per work item): about one
-//     wave per SIMD (1024 on MI355X), each wave keeping at least 4 blocks.
+//     wave per SIMD (1024 on MI355X), each wave keeping at least 4 tiles.
 //     Measured on 32 x 4096 tokens: every extra split costs more in partial
 //     states and their merge than the added parallelism returns;
 //   fp32 (vector-ALU kernel, one wave per work item): about 2048 waves, each
-//     split keeping at least 8 blocks.
-void plan_splits(const pa_dims* d, int* P_out, int* bps_out) {
-  const int MB = d->max_blocks_per_seq;
-  int P = d->num_splits;
+//     split keeping at least 8 tiles.
+void plan_splits(const pa_dims* d, int32_t B, int* P_out, int* tps_out) {
+  const int64_t max_tokens = (int64_t)d->max_blocks_per_seq * B;
+  const int64_t unit = B > 16 ? B : 16;
+  const int64_t units = (max_tokens + unit - 1) / unit;
+  int64_t P = d->num_splits;
   if (P == 0) {
     const int64_t items = (int64_t)d->num_seqs * d->num_kv_heads;
     const bool mfma = d->dtype == PA_BF16;
     const int64_t waves_per_item = mfma ? pa::kMfmaWaves : 1;
     const int64_t target = mfma ? 1024 : 2048;
     const int64_t per = items * waves_per_item;
-    P = (int)((target + per - 1) / (per > 0 ? per : 1));
-    const int min_blocks = mfma ? 4 * pa::kMfmaWaves : 8;
-    const int maxP = (MB + min_blocks - 1) / min_blocks;
+    P = (target + per - 1) / (per > 0 ? per : 1);
+    const int64_t min_tokens = mfma ? 64 * pa::kMfmaWaves : 128;
+    const int64_t maxP = (max_tokens + min_tokens - 1) / min_tokens;
     P = P < 1 ? 1 : (P > maxP ? maxP : P);
     if (P < 1) P = 1;
   }
-  if (P > MB) P = MB;
-  const int bps = (MB + P - 1) / P;
-  *P_out = (MB + bps - 1) / bps;  // drop splits that could never hold a block
-  *bps_out = bps;
+  if (P > units) P = units;
+  const int64_t upp = (units + P - 1) / P;  // units per split
+  *P_out = (int)((units + upp - 1) / upp);  // drop splits that could never hold a token
+  *tps_out = (int)(upp * unit);
 }
 
 pa_status launched(hipError_t e) {
@@ -128,8 +133,8 @@ pa_status paged_attn_plan(const pa_dims* dims, int32_t B, int32_t* num_splits, s
   pa_status st = check_dims(dims, B, true);
   if (st != PA_OK) return st;
   if (!num_splits || !workspace_bytes) return fail(PA_ERR_INVALID_ARG, "output pointer is NULL");
-  int P, bps;
-  plan_splits(dims, &P, &bps);
+  int P, tps;
+  plan_splits(dims, B, &P, &tps);
   *num_splits = P;
   *workspace_bytes = (P > 1 && dims->num_seqs > 0)
                          ? pa::decode_workspace_floats(dims->num_seqs, dims->num_q_heads, P) * sizeof(float)
@@ -149,8 +154,8 @@ pa_status paged_attn_decode(const void* q, const void* k_pool, const void* v_poo
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16))
     return fail(PA_ERR_INVALID_ARG, "q, pools and out must be 16-byte aligned");
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
-  int P, bps;
-  plan_splits(dims, &P, &bps);
+  int P, tps;
+  plan_splits(dims, B, &P, &tps);
   const int64_t items = (int64_t)dims->num_kv_heads * dims->num_seqs * P;
   if (items > INT32_MAX || (int64_t)dims->num_seqs * dims->num_q_heads > INT32_MAX)
     return fail(PA_ERR_UNSUPPORTED, "grid too large");
@@ -169,7 +174,7 @@ pa_status paged_attn_decode(const void* q, const void* k_pool, const void* v_poo
   a.MB = dims->max_blocks_per_seq;
   a.NB = dims->num_blocks;
   a.P = P;
-  a.bps = bps;
+  a.tps = tps;
   if (P > 1) {
     const size_t need = pa::decode_workspace_floats(a.S, a.Hq, P) * sizeof(float);
     if (!dims->workspace || dims->workspace_bytes < need)
@@ -237,6 +242,43 @@ pa_status kv_cow_copy(void* k_pool, void* v_pool, const int32_t* src_blocks, con
   const int64_t stride_bytes = num_layers > 1 ? layer_stride_elems * (int64_t)elem_size(dims->dtype) : 0;
   if (stride_bytes % 16) return fail(PA_ERR_INVALID_ARG, "layer stride must be a multiple of 16 bytes");
   return launched(pa::launch_cow(a, src_blocks, dst_blocks, n_valid, num_pairs, num_layers, stride_bytes, stream));
+}
+
+static pa_status kv_swap(void* k_pool, void* v_pool, const int32_t* blocks, int32_t num_list, void* buf,
+                         int32_t B, int32_t num_layers, int64_t layer_stride_elems, bool to_buffer, hipStream_t stream,
+                         const pa_dims* dims) {
+  if (num_list < 0) return fail(PA_ERR_INVALID_ARG, "num_blocks listed = %d < 0", num_list);
+  if (num_list > 2147483647 / 2) return fail(PA_ERR_UNSUPPORTED, "too many blocks listed");
+  if (num_layers < 1 || num_layers > 65535) return fail(PA_ERR_INVALID_ARG, "num_layers = %d outside [1, 65535]", num_layers);
+  pa::KvArgs a{};
+  pa_status st = kv_common(dims, B, k_pool, v_pool, &a);
+  if (st != PA_OK) return st;
+  if (num_list == 0) return PA_OK;
+  if (!blocks || !buf) return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if (!aligned(buf, 16)) return fail(PA_ERR_INVALID_ARG, "the swap buffer must be 16-byte aligned");
+  const int64_t pool_elems = (int64_t)dims->num_blocks * B * dims->num_kv_heads * dims->head_dim;
+  if (num_layers > 1 && layer_stride_elems < pool_elems)
+    return fail(PA_ERR_INVALID_ARG, "layer_stride_elems %lld smaller than one layer's pool (%lld)",
+                (long long)layer_stride_elems, (long long)pool_elems);
+  const int64_t stride_bytes = num_layers > 1 ? layer_stride_elems * (int64_t)elem_size(dims->dtype) : 0;
+  if (stride_bytes % 16) return fail(PA_ERR_INVALID_ARG, "layer stride must be a multiple of 16 bytes");
+  return launched(pa::launch_swap(a, blocks, num_list, static_cast<uint8_t*>(buf), num_layers, stride_bytes,
+                                  to_buffer, stream));
+}
+
+pa_status kv_swap_out(const void* k_pool, const void* v_pool, const int32_t* blocks, int32_t num_list, void* buf,
+                      int32_t B, int32_t num_layers, int64_t layer_stride_elems, hipStream_t stream,
+                      const pa_dims* dims) {
+  g_last_error.clear();
+  return kv_swap(const_cast<void*>(k_pool), const_cast<void*>(v_pool), blocks, num_list, buf, B, num_layers,
+                 layer_stride_elems, true, stream, dims);
+}
+
+pa_status kv_swap_in(void* k_pool, void* v_pool, const int32_t* blocks, int32_t num_list, const void* buf, int32_t B,
+                     int32_t num_layers, int64_t layer_stride_elems, hipStream_t stream, const pa_dims* dims) {
+  g_last_error.clear();
+  return kv_swap(k_pool, v_pool, blocks, num_list, const_cast<void*>(buf), B, num_layers, layer_stride_elems, false,
+                 stream, dims);
 }
 
 pa_status paged_kv_gather(const void* k_pool, const void* v_pool, const int32_t* block_tables, const int32_t* seq_lens,

@@ -70,7 +70,8 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeArgs a) {
   constexpr int E = Vec16<T>::kElems;  // elements per 16-byte load
   constexpr int LPR = kHeadDim / E;    // lanes per row (32 for fp32)
   constexpr int RPL = kWave / LPR;     // rows per wave load (2 for fp32)
-  constexpr int NL = B / RPL;          // loads per tile
+  constexpr int kTile = 16;            // slots processed per step
+  constexpr int NL = kTile / RPL;      // loads per tile (8 for fp32)
   static_assert(B % RPL == 0, "block size must be a multiple of the rows one wave load covers");
 
   const int lane = threadIdx.x;
@@ -84,11 +85,11 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeArgs a) {
   const int kvh = item / a.S;
 
   const int n_raw = a.lens[s];
-  bool bad = n_raw < 0 || n_raw > a.MB * B;  // outside what the table can describe
+  bool bad = n_raw < 0 || (int64_t)n_raw > (int64_t)a.MB * B;  // outside what the table can describe
   const int n = bad ? 0 : n_raw;
-  const int nb = (n + B - 1) / B;
-  const int j0 = p * a.bps;
-  const int j1 = min(nb, j0 + a.bps);
+  const int nt = (n + kTile - 1) / kTile;  // 16-slot tiles of the history
+  const int u0 = p * (a.tps / kTile);
+  const int u1 = min(nt, u0 + a.tps / kTile);
 
   // q for the G heads of this group, dims [c*E, c*E+E), pre-scaled into base 2.
   float qf[G][E];
@@ -114,24 +115,43 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeArgs a) {
 
   const int64_t row_stride = (int64_t)a.Hkv * kHeadDim;  // elements between slots
   const int64_t blk_stride = (int64_t)B * row_stride;     // elements between blocks
-  const int64_t lane_off = (int64_t)r * row_stride + (int64_t)kvh * kHeadDim + c * E;
+  const int64_t lane_off = (int64_t)kvh * kHeadDim + c * E;
   const T* kbase = static_cast<const T*>(a.k_pool) + lane_off;
   const T* vbase = static_cast<const T*>(a.v_pool) + lane_off;
   const int32_t* trow = a.tables + (int64_t)s * a.MB;
 
-  for (int j = j0; j < j1; ++j) {
-    const int pb = trow[j];
-    if (pb < 0 || pb >= a.NB) {  // a table entry outside the pool: poison, never dereference
-      bad = true;
-      continue;
-    }
+  for (int u = u0; u < u1; ++u) {
+    // Row pair i of tile u is slots 16*u + RPL*i + (0 .. RPL-1); B is a
+    // multiple of RPL, so a pair lies in one block.  A pair past the history
+    // reads the history's last block instead (masked below), so no table
+    // entry at or past ceil(n / B) is read.
     uint4 kraw[NL], vraw[NL];
-    const T* kb = kbase + (int64_t)pb * blk_stride;
-    const T* vb = vbase + (int64_t)pb * blk_stride;
+    auto pool_block = [&](int pb) {
+      if (pb < 0 || pb >= a.NB) {  // a table entry outside the pool: poison, never dereference
+        bad = true;
+        pb = 0;
+      }
+      return pb;
+    };
+    if constexpr (B >= kTile) {  // the whole tile lies in one block: one table read
+      const int pb = pool_block(trow[(kTile * u) / B]);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) kraw[i] = *reinterpret_cast<const uint4*>(kb + i * RPL * row_stride);
+      for (int i = 0; i < NL; ++i) {
+        const int64_t off = (int64_t)pb * blk_stride + (int64_t)((kTile * u) % B + RPL * i + r) * row_stride;
+        kraw[i] = *reinterpret_cast<const uint4*>(kbase + off);
+        vraw[i] = *reinterpret_cast<const uint4*>(vbase + off);
+      }
+    } else {
 #pragma unroll
-    for (int i = 0; i < NL; ++i) vraw[i] = *reinterpret_cast<const uint4*>(vb + i * RPL * row_stride);
+      for (int i = 0; i < NL; ++i) {
+        const int tok = kTile * u + RPL * i;
+        const bool live = tok < n;
+        const int pb = pool_block(trow[(live ? tok : n - 1) / B]);
+        const int64_t off = (int64_t)pb * blk_stride + (int64_t)((live ? tok % B : 0) + r) * row_stride;
+        kraw[i] = *reinterpret_cast<const uint4*>(kbase + off);
+        vraw[i] = *reinterpret_cast<const uint4*>(vbase + off);
+      }
+    }
 
     // Scores of this lane's NL slots for the G heads (base 2).
     float sc[NL][G];
@@ -155,11 +175,11 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeArgs a) {
         for (int g = 0; g < G; ++g) sc[i][g] += shfl_xor(sc[i][g], mask);
 
     // Mask slots at or past the length ([Slides] quiz "逻辑顺序没错…" step 1).
-    const bool tail = (j + 1) * B > n;
+    const bool tail = (u + 1) * kTile > n;
     bool valid[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      valid[i] = j * B + i * RPL + r < n;
+      valid[i] = kTile * u + i * RPL + r < n;
 #pragma unroll
       for (int g = 0; g < G; ++g) sc[i][g] = valid[i] ? sc[i][g] : kNegInf;
     }
@@ -172,7 +192,7 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeArgs a) {
       for (int i = 1; i < NL; ++i) bm = fmaxf(bm, sc[i][g]);
 #pragma unroll
       for (int mask = LPR; mask < kWave; mask <<= 1) bm = fmaxf(bm, shfl_xor(bm, mask));
-      const float mn = fmaxf(m[g], bm);  // finite: slot 0 of block j < nb is valid
+      const float mn = fmaxf(m[g], bm);  // finite: slot 0 of tile u < nt is valid
       const float alpha = fast_exp2(m[g] - mn);
       m[g] = mn;
       l[g] *= alpha;
@@ -265,23 +285,31 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
   dst[1] = o1 * inv;
 }
 
-template <typename T, int G>
+template <typename T, int G, int B>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   const int items = a.Hkv * a.S * a.P;
-  hipLaunchKernelGGL((decode_split_kernel<T, G, 16>), dim3(items), dim3(kWave), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.P == 1) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.S * a.Hq), dim3(kWave), 0, stream, a);
+  hipLaunchKernelGGL((decode_split_kernel<T, G, B>), dim3(items), dim3(kWave), 0, stream, a);
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, int B>
 hipError_t launch_group(const DecodeArgs& a, int G, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_typed<T, 1>(a, stream);
-    case 2: return launch_typed<T, 2>(a, stream);
-    case 4: return launch_typed<T, 4>(a, stream);
-    case 8: return launch_typed<T, 8>(a, stream);
+    case 1: return launch_typed<T, 1, B>(a, stream);
+    case 2: return launch_typed<T, 2, B>(a, stream);
+    case 4: return launch_typed<T, 4, B>(a, stream);
+    case 8: return launch_typed<T, 8, B>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_valu(const DecodeArgs& a, int B, int G, hipStream_t stream) {
+  switch (B) {
+    case 4: return launch_group<float, 4>(a, G, stream);
+    case 8: return launch_group<float, 8>(a, G, stream);
+    case 16: return launch_group<float, 16>(a, G, stream);
+    case 32: return launch_group<float, 32>(a, G, stream);
+    case 64: return launch_group<float, 64>(a, G, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -293,15 +321,11 @@ size_t decode_workspace_floats(int S, int Hq, int P) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int B, int G, hipStream_t stream) {
-  if (B != 16) return hipErrorInvalidValue;
-  if (dtype == PA_BF16) {
-    // bf16: q.k and p.v on the matrix cores; the merge of splits is shared.
-    hipError_t e = launch_decode_mfma(a, G, stream);
-    if (e != hipSuccess || a.P == 1) return e;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(a.S * a.Hq), dim3(kWave), 0, stream, a);
-    return hipGetLastError();
-  }
-  return launch_group<float>(a, G, stream);
+  // bf16: q.k and p.v on the matrix cores; fp32: the vector-ALU kernel.
+  hipError_t e = dtype == PA_BF16 ? launch_decode_mfma(a, B, G, stream) : launch_valu(a, B, G, stream);
+  if (e != hipSuccess || a.P == 1) return e;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.S * a.Hq), dim3(kWave), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace pa

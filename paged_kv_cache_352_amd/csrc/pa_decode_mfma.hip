@@ -11,24 +11,28 @@
 // contractions of the GQA group, q.k and p.v, are MFMA instructions, which
 // leaves the vector ALU only the softmax of four scores per lane.
 //
-// Work decomposition.  One workgroup of W waves per (request s, KV head g,
-// split p).  Wave w takes logical blocks j0 + w, j0 + w + W, ... of the
-// split's range [j0, j1), keeps its own (m, l, o), and the W states are merged
-// through LDS at the end.  With one split the workgroup writes the final
-// output; with several it writes its merged state and a second kernel merges
-// the splits.
+// Work decomposition.  The history is cut into 16-slot tiles (the M
+// dimension of the q.k MFMA), whatever the block size B (a power of two from
+// 4 to 64: a tile is part of one block, or spans 16/B blocks).  One workgroup
+// of W waves per (request s, KV head g, split p); wave w takes a contiguous
+// share of the split's tiles, keeps its own (m, l, o), and the W states are
+// merged through LDS at the end.  With one split the workgroup writes the
+// final output; with several it writes its merged state and a second kernel
+// merges the splits.
 //
-// Loads.  One (block, KV head) tile is 16 slot rows of 256 bytes, 2 KiB
-// apart in the [block, slot, KV head, dim] pool ([Slides] "把 token 6 变成真正
-// 的内存地址").  Each 16-byte load instruction of a wave covers 4 whole rows
-// (lane l: row 4*i + l/16, bytes 16*(l%16)), so every row is fetched as full
-// cache lines by one instruction; the next block's K and V are in flight
-// while the current one is processed.  Each wave stages its K and V tiles in
-// its own LDS, 16-byte chunk k of slot t at byte 256*t + 16*(k ^ t), which
-// keeps both the row-wise writes and the operand reads below free of bank
-// conflicts.
+// Loads.  One tile of one KV head is 16 slot rows of 256 bytes, Hkv*256
+// bytes apart in the [block, slot, KV head, dim] pool ([Slides] "把 token 6
+// 变成真正的内存地址").  Each 16-byte load instruction of a wave covers a group
+// of 4 whole rows (lane l: row 4*i + l/16, bytes 16*(l%16)), so every row is
+// fetched as full cache lines by one instruction; B >= 4 keeps each group in
+// one block.  The loads are buffer loads: a descriptor for the block
+// (uniform, in SGPRs) plus constant 32-bit lane offsets.  The next tile's K
+// and V are in flight while the current one is processed.  Each wave stages
+// its K and V tiles in its own LDS, 16-byte chunk k of slot t at byte
+// 256*t + 16*(k ^ t), which keeps both the row-wise writes and the operand
+// reads below free of bank conflicts.
 //
-// Math for one wave and one 16-slot block, head dim 128; lane l is
+// Math for one wave and one 16-slot tile, head dim 128; lane l is
 // (n = l%16, c = l/16):
 //
 //   q.k  four v_mfma_f32_16x16x32_bf16 with A = the K tile (M = 16 slots,
@@ -48,9 +52,9 @@
 //        4c .. 4c+3, dims 16*j + n.
 //
 // Softmax state: lane l keeps m (the running max, base 2) of head n and a
-// partial l over its own four slots of every block; the partials of the four
+// partial l over its own four slots of every tile; the partials of the four
 // lanes of a head are summed once at the end.  The accumulators are rescaled
-// only in blocks where some head's max moved.
+// only in tiles where some head's max moved.
 #include <hip/hip_runtime.h>
 
 #include "pa_internal.h"
@@ -59,7 +63,7 @@ namespace pa {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kB = 16;  // block size this kernel is built for
+constexpr int kTile = 16;  // slots per MFMA tile (the M dimension of q.k)
 constexpr float kNegInf = -__builtin_huge_valf();
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
@@ -72,7 +76,7 @@ typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 //   256 * t + 16 * (k ^ t).
 // The XOR spreads the row-wise 16-byte writes, the 16-byte K operand reads
 // and the transposing 8-byte V reads of one instruction evenly over the banks.
-constexpr int kVtBytes = kB * kHeadDim * 2;  // 4096
+constexpr int kVtBytes = kTile * kHeadDim * 2;  // 4096
 
 // K/V tiles in flight per wave.
 constexpr int kDepth = 2;
@@ -121,13 +125,14 @@ __device__ inline __amdgpu_buffer_rsrc_t block_rsrc(const char* block, uint32_t 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(block), (short)0, (int)bytes, kBufferFlags);
 }
 
-__device__ inline uint4 load_kv16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+__device__ inline uint4 load_kv16(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, soff, 0));
 }
 
-template <int G, int W>
+template <int G, int W, int B>
 __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   static_assert(G >= 1 && G <= 16, "the query group must fit the 16 columns of one MFMA tile");
+  static_assert(B >= 4 && B <= 64 && (B & (B - 1)) == 0, "block size: a power of two from 4 to 64");
   __shared__ __attribute__((aligned(16))) uint8_t vt_all[W][kVtBytes];
   __shared__ __attribute__((aligned(16))) uint8_t kt_all[W][kVtBytes];
   __shared__ float red_m[W][16];
@@ -146,13 +151,16 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   const int kvh = item / a.S;
 
   const int n_raw = a.lens[s];
-  bool bad = n_raw < 0 || n_raw > a.MB * kB;
+  bool bad = n_raw < 0 || (int64_t)n_raw > (int64_t)a.MB * B;
   const int n = bad ? 0 : n_raw;
-  const int nb = (n + kB - 1) / kB;
-  const int j0 = p * a.bps;
-  const int j1 = min(nb, j0 + a.bps);
-  // This wave's blocks: j0 + w + W*t for t in [0, cnt).
-  const int cnt = j1 - j0 - w > 0 ? (j1 - j0 - w + W - 1) / W : 0;
+  const int nb = (n + B - 1) / B;          // blocks holding the history
+  const int nt = (n + kTile - 1) / kTile;  // 16-slot tiles of the history
+  const int u0 = p * (a.tps / kTile);
+  const int u1 = min(nt, u0 + a.tps / kTile);
+  // This wave's tiles: a contiguous share [ua, ub) of the split's tiles.
+  const int share = u1 > u0 ? (u1 - u0 + W - 1) / W : 0;
+  const int ua = min(u1, u0 + w * share);
+  const int ub = min(u1, ua + share);
 
   // q of head kvh*G + n16 over the dims this lane contributes, as MFMA B operands.
   bf16x8_t qv[4];
@@ -167,32 +175,51 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
     }
   }
 
-  const int64_t row_stride = (int64_t)a.Hkv * kHeadDim;
-  const int64_t blk_stride = (int64_t)kB * row_stride;
   // Byte offsets inside a block (a block is at most a few hundred KiB, so 32
-  // bits suffice); the block's base address is uniform, so each load is an
-  // SGPR base plus one of these four per-lane offsets.
-  uint32_t voff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    voff[i] = (uint32_t)(((4 * i + c4) * row_stride + (int64_t)kvh * kHeadDim + 8 * n16) * 2);
+  // bits suffice).  A load is a block descriptor (uniform, in SGPRs) plus the
+  // lane's offset (slot c4 of the row group, KV head kvh, dims 8*n16) plus
+  // the uniform offset of the row group's first slot.
+  const int row_bytes = a.Hkv * kHeadDim * 2;
+  const uint32_t blk_bytes = (uint32_t)B * (uint32_t)row_bytes;
+  const uint32_t voff = (uint32_t)(c4 * row_bytes + (kvh * kHeadDim + 8 * n16) * 2);
   const char* kpool = static_cast<const char*>(a.k_pool);
   const char* vpool = static_cast<const char*>(a.v_pool);
-  const uint32_t blk_bytes = (uint32_t)(blk_stride * 2);
-  const int32_t* trow = a.tables + (int64_t)s * a.MB + j0 + w;
+  const int32_t* trow = a.tables + (int64_t)s * a.MB;
 
-  // Issue the 8 16-byte loads of the K and V tile of physical block pb.
-  auto load_tile = [&](int pb, Tile& t) {
+  // Issue the 8 16-byte loads of the K and V rows of tile u: row group i is
+  // slots 16*u + 4*i .. +3.  `tab` holds table entries eb, eb+1, ... one per
+  // lane.  With B >= 16 the tile lies inside one block; with B < 16 each row
+  // group has its own block, and a group past the history reads the last
+  // block of the history instead (its rows are masked), so no table entry at
+  // or past ceil(n / B) is ever read.
+  auto pool_block = [&](int pb) {
     if (pb < 0 || pb >= a.NB) {  // outside the pool: never dereferenced, result poisoned
       bad = true;
       pb = 0;
     }
-    const __amdgpu_buffer_rsrc_t kr = block_rsrc(kpool + (int64_t)pb * blk_bytes, blk_bytes);
-    const __amdgpu_buffer_rsrc_t vr = block_rsrc(vpool + (int64_t)pb * blk_bytes, blk_bytes);
+    return pb;
+  };
+  auto load_tile = [&](int u, Tile& t, int eb, int tab) {
+    if constexpr (B >= kTile) {
+      const int pb = pool_block(__builtin_amdgcn_readlane(tab, (kTile * u) / B - eb));
+      const __amdgpu_buffer_rsrc_t kr = block_rsrc(kpool + (int64_t)pb * blk_bytes, blk_bytes);
+      const __amdgpu_buffer_rsrc_t vr = block_rsrc(vpool + (int64_t)pb * blk_bytes, blk_bytes);
+      const int row0 = (kTile * u) % B;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t.k[i] = load_kv16(kr, voff[i]);
+      for (int i = 0; i < 4; ++i) t.k[i] = load_kv16(kr, voff, (row0 + 4 * i) * row_bytes);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t.v[i] = load_kv16(vr, voff[i]);
+      for (int i = 0; i < 4; ++i) t.v[i] = load_kv16(vr, voff, (row0 + 4 * i) * row_bytes);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = kTile * u + 4 * i;
+        const bool live = tok < n;
+        const int pb = pool_block(__builtin_amdgcn_readlane(tab, (live ? tok : n - 1) / B - eb));
+        const int soff = live ? (tok % B) * row_bytes : 0;
+        t.k[i] = load_kv16(block_rsrc(kpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
+        t.v[i] = load_kv16(block_rsrc(vpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
+      }
+    }
   };
 
   float m = kNegInf;  // running max (base 2) of head n16
@@ -214,9 +241,9 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   uint8_t* kt = kt_all[w];
   const PA_LDS uint8_t* kt_r = (const PA_LDS uint8_t*)kt + 256 * n16;  // K reads: slot n16
 
-  auto process = [&](int j, Tile& cur) {
-    const int valid = n - j * kB;  // >= 1
-    wave_lds_order();  // the previous block's reads of these tiles come first
+  auto process = [&](int u, Tile& cur) {
+    const int valid = n - u * kTile;  // >= 1
+    wave_lds_order();  // the previous tile's reads of this LDS come first
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * i + c4;
@@ -238,11 +265,11 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) sv[r] = (4 * c4 + r < valid) ? sc[r] * a.scale_log2 : kNegInf;
 
-    // [Budgets] eq. (4): block max over the 16 slots of head n16, new running max.
+    // [Budgets] eq. (4): tile max over the 16 slots of head n16, new running max.
     float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
     bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
-    const float mn = fmaxf(m, bm);  // finite: slot 0 of a block below nb is valid
+    const float mn = fmaxf(m, bm);  // finite: slot 0 of a tile below nt is valid
     const float alpha = fast_exp2(m - mn);
     m = mn;
     float pw[4];
@@ -267,7 +294,7 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
         for (int r = 0; r < 4; ++r) acc[jj][r] *= ar[r];
     }
 
-    wave_lds_order();  // this block's V tile is in LDS
+    wave_lds_order();  // this tile's V is in LDS
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
       const int chunk = ((2 * jj) ^ rhi) | bsel;
@@ -277,24 +304,26 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
     }
   };
 
-  // The wave's blocks are walked in chunks of up to 64.  One vector load
-  // brings a chunk's table entries into a register, one per lane; block t's
-  // entry is then read out of lane t - tb.  Within a chunk kDepth tiles are in
-  // flight: block t + kDepth - 1 is loaded before block t is processed (the
-  // load index is clamped, never conditional, so the wait before each tile
-  // covers only that tile's loads).
-  for (int tb = 0; tb < cnt; tb += kWave) {
-    const int te = min(cnt, tb + kWave);
-    const int tab = trow[(int64_t)min(tb + lane, te - 1) * W];  // lanes past the chunk repeat its last entry
+  // The wave's tiles are walked in chunks whose table entries fit one
+  // register (64 entries, one per lane, read out with readlane): 64 tiles for
+  // B >= 16, 4*B tiles below.  Within a chunk kDepth tiles are in flight:
+  // tile t + kDepth - 1 is loaded before tile t is processed (the load index
+  // is clamped, never conditional, so the wait before each tile covers only
+  // that tile's loads).
+  constexpr int kChunkTiles = B >= kTile ? kWave : 4 * B;
+  for (int tb = ua; tb < ub; tb += kChunkTiles) {
+    const int te = min(ub, tb + kChunkTiles);
+    const int eb = (kTile * tb) / B;
+    const int tab = trow[min(eb + lane, nb - 1)];  // lanes past the history repeat its last entry
     Tile tq[kDepth];
 #pragma unroll
-    for (int b = 0; b + 1 < kDepth; ++b) load_tile(__builtin_amdgcn_readlane(tab, min(tb + b, te - 1) - tb), tq[b]);
+    for (int b = 0; b + 1 < kDepth; ++b) load_tile(min(tb + b, te - 1), tq[b], eb, tab);
     for (int t = tb; t < te; t += kDepth) {
 #pragma unroll
       for (int b = 0; b < kDepth; ++b) {
-        load_tile(__builtin_amdgcn_readlane(tab, min(t + b + kDepth - 1, te - 1) - tb), tq[(b + kDepth - 1) % kDepth]);
+        load_tile(min(t + b + kDepth - 1, te - 1), tq[(b + kDepth - 1) % kDepth], eb, tab);
         __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the current tile's math
-        process(j0 + w + W * (t + b), tq[b]);
+        process(t + b, tq[b]);
         if (t + b + 1 >= te) break;
       }
     }
@@ -355,22 +384,34 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-template <int G>
-hipError_t launch_g(const DecodeArgs& a, hipStream_t stream) {
+template <int G, int B>
+hipError_t launch_gb(const DecodeArgs& a, hipStream_t stream) {
   const int items = a.Hkv * a.S * a.P;
-  hipLaunchKernelGGL((decode_mfma_kernel<G, kMfmaWaves>), dim3(items), dim3(kWave * kMfmaWaves), 0, stream, a);
+  hipLaunchKernelGGL((decode_mfma_kernel<G, kMfmaWaves, B>), dim3(items), dim3(kWave * kMfmaWaves), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int B>
+hipError_t launch_b(const DecodeArgs& a, int G, hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_gb<1, B>(a, stream);
+    case 2: return launch_gb<2, B>(a, stream);
+    case 4: return launch_gb<4, B>(a, stream);
+    case 8: return launch_gb<8, B>(a, stream);
+    case 16: return launch_gb<16, B>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int G, hipStream_t stream) {
-  switch (G) {
-    case 1: return launch_g<1>(a, stream);
-    case 2: return launch_g<2>(a, stream);
-    case 4: return launch_g<4>(a, stream);
-    case 8: return launch_g<8>(a, stream);
-    case 16: return launch_g<16>(a, stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int G, hipStream_t stream) {
+  switch (B) {
+    case 4: return launch_b<4>(a, G, stream);
+    case 8: return launch_b<8>(a, G, stream);
+    case 16: return launch_b<16>(a, G, stream);
+    case 32: return launch_b<32>(a, G, stream);
+    case 64: return launch_b<64>(a, G, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -27,7 +27,7 @@ struct DecodeArgs {
   float scale_log2; // scale * log2(e): scores are kept in base 2
   int S, Hq, Hkv, MB, NB;
   int P;            // number of splits
-  int bps;          // blocks per split
+  int tps;          // tokens per split: split p covers tokens [p*tps, (p+1)*tps), a multiple of max(16, B)
 };
 
 // Sets the thread's pa_last_error() text (used by the host-only parts).
@@ -38,8 +38,9 @@ size_t decode_workspace_floats(int S, int Hq, int P);
 
 hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int B, int G, hipStream_t stream);
 
-// bf16 decode on the matrix cores (pa_decode_mfma.hip); G in {1, 2, 4, 8, 16}, B = 16.
-hipError_t launch_decode_mfma(const DecodeArgs& a, int G, hipStream_t stream);
+// bf16 decode on the matrix cores (pa_decode_mfma.hip); G in {1, 2, 4, 8, 16},
+// B in {4, 8, 16, 32, 64}.
+hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int G, hipStream_t stream);
 
 struct KvArgs {
   uint8_t* k_pool;
@@ -53,6 +54,9 @@ hipError_t launch_append(const KvArgs& a, const uint8_t* k_new, const uint8_t* v
 
 hipError_t launch_cow(const KvArgs& a, const int32_t* src, const int32_t* dst, const int32_t* n_valid,
                       int num_pairs, int num_layers, int64_t layer_stride_bytes, hipStream_t stream);
+
+hipError_t launch_swap(const KvArgs& a, const int32_t* blocks, int nlist, uint8_t* buf, int num_layers,
+                       int64_t layer_stride_bytes, bool to_buffer, hipStream_t stream);
 
 hipError_t launch_gather(const KvArgs& a, const int32_t* tables, const int32_t* lens, uint8_t* k_out,
                          uint8_t* v_out, hipStream_t stream);

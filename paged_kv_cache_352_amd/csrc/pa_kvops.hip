@@ -72,7 +72,34 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(KvArgs a, const int32_
          (int64_t)cnt * a.row_bytes);
 }
 
+// One workgroup per (listed block i, layer, pool): the whole block (all
+// slots, all KV heads) moves between the pool and slot i of a contiguous
+// buffer laid out [layer][pool (K, V)][listed block][slot, head, dim] ([Slides]
+// "腾出显存以后，还要付一次恢复成本": swapping a request's KV out and back in).
+// The buffer may be host memory the device can address; then the copy crosses
+// the host link directly.  Block ids outside the pool are skipped.
+__global__ __launch_bounds__(kThreads) void swap_kernel(KvArgs a, const int32_t* __restrict__ blocks, int nlist,
+                                                        uint8_t* buf, int64_t layer_stride_bytes, int to_buffer) {
+  const int i = blockIdx.x;
+  const int blk = blocks[i];
+  if (blk < 0 || blk >= a.NB) return;
+  const int64_t blk_bytes = (int64_t)a.B * a.row_bytes;
+  uint8_t* pool = (blockIdx.z ? a.v_pool : a.k_pool) + (int64_t)blockIdx.y * layer_stride_bytes + blk * blk_bytes;
+  uint8_t* slot = buf + (((int64_t)blockIdx.y * 2 + blockIdx.z) * nlist + i) * blk_bytes;
+  if (to_buffer)
+    copy16(slot, pool, blk_bytes);
+  else
+    copy16(pool, slot, blk_bytes);
+}
+
 }  // namespace
+
+hipError_t launch_swap(const KvArgs& a, const int32_t* blocks, int nlist, uint8_t* buf, int num_layers,
+                       int64_t layer_stride_bytes, bool to_buffer, hipStream_t stream) {
+  hipLaunchKernelGGL(swap_kernel, dim3(nlist, num_layers, 2), dim3(kThreads), 0, stream, a, blocks, nlist, buf,
+                     layer_stride_bytes, to_buffer ? 1 : 0);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const KvArgs& a, const uint8_t* k_new, const uint8_t* v_new, const int32_t* tables,
                          const int32_t* positions, hipStream_t stream) {

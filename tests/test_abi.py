@@ -90,7 +90,10 @@ def test_plan_rejects_bad_shapes(lib):
     for d, want in cases:
         assert lib.paged_attn_plan(ctypes.byref(d), 16, ctypes.byref(p), ctypes.byref(w)) == want
         assert lib.pa_last_error().decode() != ""
-    assert lib.paged_attn_plan(ctypes.byref(dims()), 8, ctypes.byref(p), ctypes.byref(w)) == UNSUPPORTED
+    for B in (2, 12, 24, 128):  # block sizes are powers of two from 4 to 64
+        assert lib.paged_attn_plan(ctypes.byref(dims()), B, ctypes.byref(p), ctypes.byref(w)) == UNSUPPORTED
+    for B in (4, 8, 16, 32, 64):
+        assert lib.paged_attn_plan(ctypes.byref(dims()), B, ctypes.byref(p), ctypes.byref(w)) == OK
     assert lib.paged_attn_plan(None, 16, ctypes.byref(p), ctypes.byref(w)) == INVALID
 
 
@@ -102,7 +105,7 @@ def test_decode_rejects_before_launch(lib):
     assert decode(lib, dims(), out=None) == INVALID
     assert decode(lib, dims(), q=ctypes.c_void_p(0x7F0000000008)) == INVALID  # not 16-byte aligned
     assert decode(lib, dims(), scale=float("nan")) == INVALID
-    assert decode(lib, dims(), B=32) == UNSUPPORTED
+    assert decode(lib, dims(), B=24) == UNSUPPORTED
     # a split plan with no workspace, then a too-small and a misaligned one
     d = dims(S=1, Hkv=1, Hq=4, MB=64, splits=4)
     assert decode(lib, d) == WORKSPACE
@@ -143,3 +146,15 @@ def test_binding_refuses_host_tensors(lib):
     n = torch.zeros(2, dtype=torch.int32)
     with pytest.raises(_lib.PagedAttnError):
         pa.paged_attn_decode(q, k, k, t, n, 16, 0.1)
+
+
+@no_gpu
+def test_swap_rejects_bad_arguments(lib):
+    d = dims()
+    args = lambda n=2, buf=FAKE, layers=1, stride=0: (FAKE, FAKE, FAKE, n, buf, 16, layers, stride, None, ctypes.byref(d))
+    assert lib.kv_swap_out(*args(n=-1)) == INVALID
+    assert lib.kv_swap_out(*args(buf=None)) == INVALID
+    assert lib.kv_swap_in(*args(buf=ctypes.c_void_p(0x7F0000000008))) == INVALID  # misaligned buffer
+    assert lib.kv_swap_in(*args(layers=0)) == INVALID
+    assert lib.kv_swap_out(*args(layers=2, stride=5)) == INVALID  # stride smaller than one pool
+    assert lib.kv_swap_out(*args(n=0)) == OK  # nothing to do, nothing launched

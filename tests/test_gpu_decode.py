@@ -171,3 +171,52 @@ def test_graph_capture_replays_match_eager(splits):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(launch.out.view(torch.int32), eager.view(torch.int32))
+
+
+@pytest.mark.parametrize("B", [4, 8, 32, 64])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_block_sizes(B, dtype, splits):
+    """Block sizes other than 16 ([Slides] "块越小，省下的是空位，多出来的是管理"):
+    lengths around B and around the 16-slot tile edges, one append round."""
+    banner(f"block size {B} {dtype} splits={splits}")
+    lens = [0, 1, B - 1, B, B + 1, 15, 16, 17, 33, 100, 4 * B + 3, 300]
+    b = W.custom(lens, Hq=8, Hkv=2, B=B, dtype=dtype, append=True, device=DEV, seed=31 + B)
+    ref = HostLayer(b, 0).oracle()
+    out = gpu_step(b, num_splits=splits)[0]
+    torch.cuda.synchronize()
+    got = host_f32(out)
+    assert np.array_equal(got[0], np.zeros_like(got[0]))
+    assert_close(got, ref, dtype, f"B={B}")
+
+
+@pytest.mark.parametrize("B", [4, 8, 32, 64])
+def test_block_sizes_permutation_bitwise(B):
+    banner(f"block size {B}: permuted physical ids, bitwise")
+    b = W.custom([5, 37, 64, 129, 300], Hq=8, Hkv=2, B=B, dtype=torch.bfloat16, device=DEV, seed=41,
+                 spare_blocks=3)
+    base = gpu_step(b, num_splits=2)[0].clone()
+    g = torch.Generator().manual_seed(6)
+    perm = torch.randperm(b.NB, generator=g).to(DEV)
+    k2 = torch.empty_like(b.k_pool)
+    v2 = torch.empty_like(b.v_pool)
+    k2[:, perm] = b.k_pool
+    v2[:, perm] = b.v_pool
+    t2 = perm[b.block_tables.long()].to(torch.int32)
+    out2 = pa.paged_attn_decode(b.q[0], k2[0], v2[0], t2, b.seq_lens, b.B, b.scale, num_splits=2)
+    torch.cuda.synchronize()
+    assert torch.equal(base.view(torch.int32), out2.view(torch.int32))
+
+
+@pytest.mark.parametrize("B", [8, 32, 64])
+def test_block_sizes_32x4096_sampled(B):
+    """The 32 x 4096-token batch at other block sizes (its bench launch plan),
+    sampled requests against the oracle."""
+    banner(f"32 x 4096 at block size {B}")
+    b = W.config2(device=DEV, B=B)
+    rows = [0, 13, 31]
+    ref = HostLayer(b, 0).oracle(rows)
+    out = gpu_step(b)[0]
+    torch.cuda.synchronize()
+    got = host_f32(out)
+    assert_close(np.stack([got[s] for s in rows]), np.stack([ref[s] for s in rows]), torch.bfloat16, f"B={B}")

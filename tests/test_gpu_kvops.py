@@ -125,3 +125,29 @@ def test_append_config3_all_layers():
     assert torch.equal(after_k, before_k)
     del before_k
     assert torch.equal(b.v_pool.view(torch.int16)[:, want_blk, want_slot], b.v_new[0].view(torch.int16))
+
+
+@pytest.mark.parametrize("pinned", [False, True])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_swap_out_and_in_bit_exact(pinned, dtype):
+    """A request's blocks go out to a buffer (device, or pinned host memory the
+    kernel writes across the link) and come back into other block ids."""
+    banner(f"swap {dtype} pinned={pinned}")
+    b = W.custom([20, 40, 7], Hq=8, Hkv=2, dtype=dtype, L=3, device=DEV, seed=5, spare_blocks=6)
+    tab = b.block_tables.cpu().numpy()
+    used = set(tab[:, :].ravel().tolist())
+    out_ids = [int(x) for x in tab[1, :3]]          # request 1's three blocks
+    spare = [x for x in range(b.NB) if x not in used][:3]
+    k0, v0 = host_bits(b.k_pool), host_bits(b.v_pool)
+    shape = (b.L, 2, 3, b.B, b.Hkv, b.D)
+    buf = torch.empty(shape, dtype=dtype, pin_memory=True) if pinned else torch.empty(shape, dtype=dtype, device=DEV)
+    ids = torch.tensor(out_ids, dtype=torch.int32, device=DEV)
+    pa.kv_swap_out(b.k_pool, b.v_pool, ids, buf, b.B)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(buf), kvc.swap_out(k0, v0, out_ids))
+    assert np.array_equal(host_bits(b.k_pool), k0) and np.array_equal(host_bits(b.v_pool), v0)
+    pa.kv_swap_in(b.k_pool, b.v_pool, torch.tensor(spare, dtype=torch.int32, device=DEV), buf, b.B)
+    torch.cuda.synchronize()
+    want_k, want_v = kvc.swap_in(k0, v0, spare, kvc.swap_out(k0, v0, out_ids))
+    assert np.array_equal(host_bits(b.k_pool), want_k)
+    assert np.array_equal(host_bits(b.v_pool), want_v)

@@ -408,3 +408,16 @@ def test_reference_mutant_passes_and_planted_mistakes_are_caught():
     assert _pins_pass(_mutant("none"))
     for kind in ("slot_swap", "off_by_one", "gqa_modulo", "no_scale", "no_max_shift", "transposed_pv"):
         assert not _pins_pass(_mutant(kind)), kind
+
+
+def test_swap_round_trip_and_isolation():
+    """swap_out then swap_in into other ids copies exactly those blocks, in every layer."""
+    rng = np.random.default_rng(9)
+    k = rng.standard_normal((2, 6, 4, 1, 2))
+    v = rng.standard_normal((2, 6, 4, 1, 2))
+    buf = kvc.swap_out(k, v, [4, 1])
+    assert buf.shape == (2, 2, 2, 4, 1, 2)
+    assert np.array_equal(buf[1, 0, 0], k[1, 4]) and np.array_equal(buf[0, 1, 1], v[0, 1])
+    k2, v2 = kvc.swap_in(k, v, [0, 5], buf)
+    assert np.array_equal(k2[:, 0], k[:, 4]) and np.array_equal(v2[:, 5], v[:, 1])
+    assert np.array_equal(k2[:, 1:5], k[:, 1:5]) and np.array_equal(v2[:, 1:5], v[:, 1:5])

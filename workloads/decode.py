@@ -195,13 +195,14 @@ def config1(device="cpu", seed=353):
                      tables_np=tables, spare_ids=spare, rounds_pos=[])
 
 
-def config2(device="cpu", seed=354, S=32, n=4096):
-    """32 requests x 4096 tokens, Hq 32 / Hkv 8, d 128, B 16, bf16; 8192-block pool, all used."""
+def config2(device="cpu", seed=354, S=32, n=4096, B=16):
+    """32 requests x 4096 tokens, Hq 32 / Hkv 8, d 128, B 16 (or another block
+    size), bf16; a pool of exactly the blocks the histories fill (8192 at B 16)."""
     lens = np.full(S, n)
-    NB = S * (-(-n // 16))
+    NB = S * (-(-n // B))
     rng = np.random.Generator(np.random.PCG64(seed))
-    tables, spare = _layout(rng, NB, 16, lens)
-    return _assemble(f"config2_bf16_{S}x{n}", S=S, Hq=32, Hkv=8, D=128, B=16, NB=NB, L=1,
+    tables, spare = _layout(rng, NB, B, lens)
+    return _assemble(f"config2_bf16_{S}x{n}_B{B}", S=S, Hq=32, Hkv=8, D=128, B=B, NB=NB, L=1,
                      dtype=torch.bfloat16, seed=seed, device=device, hist=lens, seq_lens=lens,
                      tables_np=tables, spare_ids=spare, rounds_pos=[])
 

@@ -23,16 +23,21 @@ Modules
 accounting  byte / block / slot accounting ([Serving] M_KV, A_B, W_B, U;
             [Budgets] eq. (1)-(3)).  Pinned to every figure the pages print.
 attention   gather through the block table + dense softmax attention: the
-            definition the paged kernel must reproduce.  Pinned by brute
-            force, by a library routine, by closed forms and invariants.
-kvcache     token append and copy-on-write of a block's valid slots.
-            Pinned by invariants and by hand-checked tiny cases.
+            definition the paged kernel must reproduce, for one new token
+            per request and for T new tokens attending causally (the
+            verification / prompt-chunk form).  Pinned by brute force, by a
+            library routine (with an explicit mask or its causal flag), by
+            closed forms and invariants.
+kvcache     token append (one or T tokens per request) and copy-on-write of
+            a block's valid slots.  Pinned by invariants and by hand-checked
+            tiny cases.
 online      the (m, l, o) recurrence of [Budgets] eq. (4) and the merge of
             partial states.  Not the oracle: it checks the merge algebra the
             kernel relies on, and is pinned against ``attention``.
 blockmgr    the per-request / per-block bookkeeping and the copy-on-write
             growth protocol of [Slides], as a plain Python model of the
-            library's block manager.  Pinned by the pages' worked examples
+            library's block manager, with multi-token growth and rollback.
+            Pinned by the pages' worked examples
             (free counts of the shared-tail quiz, the lab's block counts, the
             24 GiB and 8 GiB pool figures, the 3-blocks / 4-requests case).
 

@@ -104,3 +104,59 @@ def paged_decode_rows(q, k_pool, v_pool, block_tables, seq_lens, B, scale, rows)
         V_s = gather_sequence(v_pool, block_tables[s], n, B)
         res[s] = dense_attention(np.asarray(q)[s], K_s, V_s, scale)
     return res
+
+
+def extend_attention(q_s, K_s, V_s, scale):
+    """T new tokens of one request, each attending causally over the request's history.
+
+    [Serving] §5 places speculative decoding beside paging: a verification
+    step scores several new tokens against one history, and the same holds
+    for a prompt fed in chunks.  Readings of what the pages leave open:
+      * the T new tokens are already in the history (appended first, as for
+        a single decode token), so they are its last T positions;
+      * query i (0-based) sits at logical position n - T + i and attends
+        tokens 0 .. n - T + i: itself and everything before it, nothing after
+        (the causal order of a left-to-right model);
+      * a query whose position would be negative (n < T) attends nothing and
+        gets 0, as a request of length 0 does.
+    q_s [T, Hq, d]; K_s, V_s [n, Hkv, d].  Returns [T, Hq, d] float64; each row
+    is ``dense_attention`` over that query's own prefix of the history.
+    """
+    q_s = np.asarray(q_s)
+    T = q_s.shape[0]
+    n = np.asarray(K_s).shape[0]
+    out = np.zeros(q_s.shape, dtype=np.float64)
+    for i in range(T):
+        pos = n - T + i
+        if pos < 0:
+            continue
+        out[i] = dense_attention(q_s[i], K_s[: pos + 1], V_s[: pos + 1], scale)
+    return out
+
+
+def paged_extend(q, k_pool, v_pool, block_tables, seq_lens, B, scale):
+    """Oracle for T query tokens per request over paged KV: [S, T, Hq, d] float64.
+
+    q is [S, T, Hq, d]; seq_lens counts the whole history including the T
+    new tokens.  Each request's history is gathered through its table, then
+    ``extend_attention`` runs on it.
+    """
+    q = np.asarray(q)
+    out = np.zeros(q.shape, dtype=np.float64)
+    for s in range(q.shape[0]):
+        n = int(seq_lens[s])
+        K_s = gather_sequence(k_pool, block_tables[s], n, B)
+        V_s = gather_sequence(v_pool, block_tables[s], n, B)
+        out[s] = extend_attention(q[s], K_s, V_s, scale)
+    return out
+
+
+def paged_extend_rows(q, k_pool, v_pool, block_tables, seq_lens, B, scale, rows):
+    """``paged_extend`` for selected requests only: {s: [T, Hq, d]}."""
+    res = {}
+    for s in rows:
+        n = int(seq_lens[s])
+        K_s = gather_sequence(k_pool, block_tables[s], n, B)
+        V_s = gather_sequence(v_pool, block_tables[s], n, B)
+        res[s] = extend_attention(np.asarray(q)[s], K_s, V_s, scale)
+    return res

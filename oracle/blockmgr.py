@@ -14,11 +14,18 @@ protocol of [Slides] "PagedAttention：让 KV cache 按需生长":
   * capacity is checked before anything changes ("三个空闲块，四个请求同时
     跨边界"): a call that cannot get all its blocks changes nothing;
   * release ("请求结束，块就能交给下一位"): drop the table; blocks whose
-    refcount reaches 0 go back to the free queue (no prefix cache).
+    refcount reaches 0 go back to the free queue (no prefix cache);
+  * rollback ([Serving] §5: speculative decoding writes KV positions that
+    may be taken back): shorten a request; table entries past the new block
+    count drop one reference each, exactly as in release.
 
 Readings: requests in one decode step are served in the order given, so when
 several share a partly filled tail, the earlier ones copy and the last one
-left writes in place.  Request ids count up from 0.
+left writes in place.  Request ids count up from 0.  Blocks released by a
+release or a rollback join the free queue in table order.  A rollback keeps
+the (now partly valid) tail block as it is: the slots past the new length
+are dead and the next growth writes over them, or copies only the valid
+slots first if the tail is shared.
 """
 
 from collections import deque
@@ -69,6 +76,19 @@ class BlockManagerModel:
                 self.free.append(b)
         del self.lengths[req]
 
+    def truncate(self, req, new_length):
+        """Roll request `req` back to its first new_length tokens."""
+        if not 0 <= new_length <= self.lengths[req]:
+            raise ValueError("new length outside [0, length]")
+        keep = -(-new_length // self.B)
+        table = self.tables[req]
+        for b in table[keep:]:
+            self.refcount[b] -= 1
+            if self.refcount[b] == 0:
+                self.free.append(b)
+        del table[keep:]
+        self.lengths[req] = new_length
+
     # -- growth
     def _blocks_needed(self, length, extra, tail_refcount):
         """Fresh blocks to grow a request of `length` tokens by `extra`."""
@@ -112,6 +132,16 @@ class BlockManagerModel:
 
     def prepare_append(self, reqs):
         """One token per request, in order: (positions, [copies])."""
+        return self.prepare_extend(reqs, 1)
+
+    def prepare_extend(self, reqs, extra):
+        """`extra` tokens per request, in order: (start positions, [copies]).
+
+        All or nothing, like a single token: the blocks of the whole step are
+        counted before any request grows.
+        """
+        if extra < 1:
+            raise ValueError("extra must be >= 1")
         if len(set(reqs)) != len(reqs):
             raise ValueError("a request is listed twice")
         # dry run: who copies, and how many fresh blocks in all
@@ -119,11 +149,11 @@ class BlockManagerModel:
         need = 0
         for r in reqs:
             length = self.lengths[r]
-            if -(-(length + 1) // self.B) > self.MB:
+            if -(-(length + extra) // self.B) > self.MB:
                 raise ValueError("request would exceed its table width")
             tail = self.tables[r][-1] if self.tables[r] else None
             cur = rc.get(tail, self.refcount[tail]) if tail is not None else 0
-            k, copy = self._blocks_needed(length, 1, cur)
+            k, copy = self._blocks_needed(length, extra, cur)
             need += k
             if copy:
                 rc[tail] = cur - 1
@@ -132,7 +162,7 @@ class BlockManagerModel:
         positions, copies = [], []
         for r in reqs:
             positions.append(self.lengths[r])
-            c = self._grow(r, 1)
+            c = self._grow(r, extra)
             if c is not None:
                 copies.append(c)
         return positions, copies

@@ -28,6 +28,25 @@ def append(pool, new, block_tables, positions, B):
     return out
 
 
+def append_tokens(pool, new, block_tables, positions, B):
+    """Write T consecutive tokens per request: ``new[s, i]`` ([Hkv, d]) at position positions[s] + i.
+
+    The multi-token form of ``append`` (a verification step or a prompt chunk
+    adds several tokens at once, [Serving] §5); token i lands in slot
+    (p + i) % B of block table[s][(p + i) // B].  A negative start position
+    skips the request.
+    """
+    out = np.array(pool, copy=True)
+    for s in range(len(positions)):
+        p = int(positions[s])
+        if p < 0:
+            continue
+        for i in range(np.asarray(new).shape[1]):
+            blk = int(block_tables[s][(p + i) // B])
+            out[blk, (p + i) % B] = new[s][i]
+    return out
+
+
 def cow_copy(pool, src_blocks, dst_blocks, n_valid):
     """Copy slots [0, n_valid) of each source block into its destination block.
 

@@ -98,6 +98,29 @@ pa_status pa_bm_prepare_append(pa_block_manager* bm, const int32_t* reqs, int32_
                                int32_t* cow_src, int32_t* cow_dst, int32_t* cow_n, int32_t* num_cow);
 
 /*
+ * pa_bm_prepare_append with n_tokens >= 1 new tokens per request: a
+ * speculative verification step or one chunk of a prompt ([Serving] §5).
+ * positions[i] receives the logical index of request i's first new token,
+ * ready for kv_append_tokens.  All or nothing over the whole step, with the
+ * same copy-on-write order; n_tokens = 1 is pa_bm_prepare_append.
+ */
+pa_status pa_bm_prepare_extend(pa_block_manager* bm, const int32_t* reqs, int32_t n, int32_t n_tokens,
+                               int32_t* positions, int32_t* cow_src, int32_t* cow_dst, int32_t* cow_n,
+                               int32_t* num_cow);
+
+/*
+ * Roll request `req` back to its first new_length tokens (0 <= new_length
+ * <= its length), e.g. to drop the draft tokens a verification step
+ * rejected ([Serving] §5: speculative decoding writes KV positions that may
+ * be taken back).  Table entries past ceil(new_length / B) drop one
+ * reference each and join the free queue at refcount 0, in table order, as
+ * in pa_bm_release.  The tail block stays: its slots at or past the new
+ * length are dead, and the next growth overwrites them (or copies only the
+ * valid slots first if the tail is shared).  Never fails for lack of space.
+ */
+pa_status pa_bm_truncate(pa_block_manager* bm, int32_t req, int32_t new_length);
+
+/*
  * Export, for the n requests in reqs, host arrays ready to copy to the
  * device for the kernels: tables [n, max_blocks_per_seq] (entries past a
  * request's last block hold pad_block) and lens [n].

@@ -74,6 +74,8 @@ def load():
         "pa_bm_release": (I32, [P, I32]),
         "pa_bm_reserve": (I32, [P, I32, I32, P, P, P]),
         "pa_bm_prepare_append": (I32, [P, P, I32, P, P, P, P, ctypes.POINTER(I32)]),
+        "pa_bm_prepare_extend": (I32, [P, P, I32, I32, P, P, P, P, ctypes.POINTER(I32)]),
+        "pa_bm_truncate": (I32, [P, I32, I32]),
         "pa_bm_export": (I32, [P, P, I32, P, P, I32]),
         "pa_bm_num_free": (I32, [P]),
         "pa_bm_refcount": (I32, [P, I32]),
@@ -383,6 +385,23 @@ class BlockManager:
         _check("pa_bm_prepare_append", self._lib.pa_bm_prepare_append(
             self._h, _np_ptr(reqs), n, _np_ptr(pos), _np_ptr(cs), _np_ptr(cd), _np_ptr(cn), ctypes.byref(k)))
         return pos, (cs[:k.value].copy(), cd[:k.value].copy(), cn[:k.value].copy())
+
+    def prepare_extend(self, reqs, n_tokens):
+        """n_tokens for each request: (first positions, (cow_src, cow_dst, cow_n))."""
+        np = self._np
+        reqs = np.ascontiguousarray(reqs, dtype=np.int32)
+        n = len(reqs)
+        pos = np.empty(n, np.int32)
+        cs, cd, cn = (np.empty(max(n, 1), np.int32) for _ in range(3))
+        k = ctypes.c_int32()
+        _check("pa_bm_prepare_extend", self._lib.pa_bm_prepare_extend(
+            self._h, _np_ptr(reqs), n, n_tokens, _np_ptr(pos), _np_ptr(cs), _np_ptr(cd), _np_ptr(cn),
+            ctypes.byref(k)))
+        return pos, (cs[:k.value].copy(), cd[:k.value].copy(), cn[:k.value].copy())
+
+    def truncate(self, req, new_length):
+        """Roll the request back to its first new_length tokens (rejected draft tokens)."""
+        _check("pa_bm_truncate", self._lib.pa_bm_truncate(self._h, req, new_length))
 
     def export(self, reqs, pad_block=0):
         """(tables [n, max_blocks_per_seq], lens [n]) for the listed requests."""

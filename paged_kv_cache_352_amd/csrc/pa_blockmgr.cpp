@@ -201,12 +201,14 @@ pa_status pa_bm_reserve(pa_block_manager* bm, int32_t req, int32_t n_tokens, int
   return PA_OK;
 }
 
-pa_status pa_bm_prepare_append(pa_block_manager* bm, const int32_t* reqs, int32_t n, int32_t* positions,
-                               int32_t* cow_src, int32_t* cow_dst, int32_t* cow_n, int32_t* num_cow) {
+pa_status pa_bm_prepare_extend(pa_block_manager* bm, const int32_t* reqs, int32_t n, int32_t n_tokens,
+                               int32_t* positions, int32_t* cow_src, int32_t* cow_dst, int32_t* cow_n,
+                               int32_t* num_cow) {
   pa::set_last_error("");
   if (!bm || !num_cow) return err(PA_ERR_INVALID_ARG, "NULL argument");
   *num_cow = 0;
   if (n < 0) return err(PA_ERR_INVALID_ARG, "n = %d < 0", n);
+  if (n_tokens < 1) return err(PA_ERR_INVALID_ARG, "n_tokens = %d < 1", n_tokens);
   if (n == 0) return PA_OK;
   if (!reqs || !positions || !cow_src || !cow_dst || !cow_n) return err(PA_ERR_INVALID_ARG, "NULL array");
   try {
@@ -219,7 +221,7 @@ pa_status pa_bm_prepare_append(pa_block_manager* bm, const int32_t* reqs, int32_
       const Request* r = bm->find(reqs[i]);
       if (!r) return err(PA_ERR_INVALID_ARG, "unknown request %d", reqs[i]);
       if (!seen.emplace(reqs[i], i).second) return err(PA_ERR_INVALID_ARG, "request %d listed twice", reqs[i]);
-      if ((int64_t)r->length + 1 > (int64_t)bm->max_blocks * bm->block_size)
+      if ((int64_t)r->length + n_tokens > (int64_t)bm->max_blocks * bm->block_size)
         return err(PA_ERR_INVALID_ARG, "request %d would exceed %d blocks", reqs[i], bm->max_blocks);
       int32_t rc = 0;
       if (!r->table.empty()) {
@@ -228,7 +230,7 @@ pa_status pa_bm_prepare_append(pa_block_manager* bm, const int32_t* reqs, int32_
         rc = it != tail_rc.end() ? it->second : bm->refcount[tail];
       }
       bool cow = false;
-      need += bm->need(*r, 1, rc, &cow);
+      need += bm->need(*r, n_tokens, rc, &cow);
       if (cow) tail_rc[r->table.back()] = rc - 1;
     }
     if (need > (int64_t)bm->free_q.size())
@@ -238,7 +240,7 @@ pa_status pa_bm_prepare_append(pa_block_manager* bm, const int32_t* reqs, int32_
       Request& r = *bm->find(reqs[i]);
       positions[i] = r.length;
       int32_t cs = -1, cd = -1, cn = 0;
-      bm->grow(r, 1, &cs, &cd, &cn);
+      bm->grow(r, n_tokens, &cs, &cd, &cn);
       if (cn > 0) {
         cow_src[*num_cow] = cs;
         cow_dst[*num_cow] = cd;
@@ -250,6 +252,28 @@ pa_status pa_bm_prepare_append(pa_block_manager* bm, const int32_t* reqs, int32_
   } catch (const std::bad_alloc&) {
     return err(PA_ERR_INVALID_ARG, "out of host memory");
   }
+}
+
+pa_status pa_bm_prepare_append(pa_block_manager* bm, const int32_t* reqs, int32_t n, int32_t* positions,
+                               int32_t* cow_src, int32_t* cow_dst, int32_t* cow_n, int32_t* num_cow) {
+  return pa_bm_prepare_extend(bm, reqs, n, 1, positions, cow_src, cow_dst, cow_n, num_cow);
+}
+
+pa_status pa_bm_truncate(pa_block_manager* bm, int32_t req, int32_t new_length) {
+  pa::set_last_error("");
+  if (!bm) return err(PA_ERR_INVALID_ARG, "NULL manager");
+  Request* r = bm->find(req);
+  if (!r) return err(PA_ERR_INVALID_ARG, "unknown request %d", req);
+  if (new_length < 0 || new_length > r->length)
+    return err(PA_ERR_INVALID_ARG, "new length %d outside [0, %d]", new_length, r->length);
+  const size_t keep = (size_t)blocks_for(new_length, bm->block_size);
+  for (size_t j = keep; j < r->table.size(); ++j) {
+    const int32_t b = r->table[j];
+    if (--bm->refcount[b] == 0) bm->free_q.push_back(b);
+  }
+  r->table.resize(keep);
+  r->length = new_length;
+  return PA_OK;
 }
 
 pa_status pa_bm_export(const pa_block_manager* bm, const int32_t* reqs, int32_t n, int32_t* tables, int32_t* lens,

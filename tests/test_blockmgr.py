@@ -47,6 +47,16 @@ class Cpp:
             raise NoSpace(str(e))
         return [int(x) for x in pos], [(int(a), int(b), int(c)) for a, b, c in zip(cs, cd, cn)]
 
+    def prepare_extend(self, reqs, n):
+        try:
+            pos, (cs, cd, cn) = self.m.prepare_extend(reqs, n)
+        except pa.PoolExhausted as e:
+            raise NoSpace(str(e))
+        return [int(x) for x in pos], [(int(a), int(b), int(c)) for a, b, c in zip(cs, cd, cn)]
+
+    def truncate(self, req, n):
+        self.m.truncate(req, n)
+
     def num_free(self):
         return self.m.num_free
 
@@ -90,6 +100,15 @@ class Model:
             return self.m.prepare_append(list(reqs))
         except bmo.NoSpace as e:
             raise NoSpace(str(e))
+
+    def prepare_extend(self, reqs, n):
+        try:
+            return self.m.prepare_extend(list(reqs), n)
+        except bmo.NoSpace as e:
+            raise NoSpace(str(e))
+
+    def truncate(self, req, n):
+        self.m.truncate(req, n)
 
     def num_free(self):
         return self.m.num_free()
@@ -312,7 +331,7 @@ def _random_ops(seed, steps=400):
     c, m = Cpp(NB, B, MB, order), Model(NB, B, MB, order)
     live = []
     for _ in range(steps):
-        op = rng.integers(0, 5)
+        op = rng.integers(0, 7)
         if op == 0 or not live:
             live.append((c.add_request(), m.add_request()))
             assert live[-1][0] == live[-1][1]
@@ -335,13 +354,19 @@ def _random_ops(seed, steps=400):
                 except (pa.PagedAttnError, ValueError):
                     res.append(("invalid", None))
             assert res[0] == res[1]
+        elif op == 5:
+            i = live[rng.integers(len(live))][0]
+            cut = int(rng.integers(0, m.length(i) + 1))
+            c.truncate(i, cut)
+            m.truncate(i, cut)
         else:
             k = int(rng.integers(1, len(live) + 1))
             pick = [live[j][0] for j in rng.permutation(len(live))[:k]]
+            extra = 1 if op == 4 else int(rng.integers(1, 6))
             res = []
             for x in (c, m):
                 try:
-                    res.append(("ok",) + tuple(x.prepare_append(pick)))
+                    res.append(("ok",) + tuple(x.prepare_extend(pick, extra)))
                 except NoSpace:
                     res.append(("nospace",))
                 except (pa.PagedAttnError, ValueError):
@@ -378,5 +403,88 @@ def test_cpp_rejects_bad_arguments():
         pa.BlockManager(4, 4, 4, free_order=[0, 1, 1, 2])
     with pytest.raises(pa.PagedAttnError):
         pa.BlockManager(0, 4, 4)
+    with pytest.raises(pa.PagedAttnError):
+        m.truncate(r, 1)  # longer than the request
+    with pytest.raises(pa.PagedAttnError):
+        m.truncate(r, -1)
+    with pytest.raises(pa.PagedAttnError):
+        m.prepare_extend([r], 0)
     assert m.num_free == 8
+    m.check()
+
+
+# ------------------------------------------------------------ rollback and multi-token growth
+# [Serving] §5: speculative decoding writes draft positions that a rejected
+# verification takes back.  The pages print no numbers for it; these pins are
+# the accounting invariants the growth protocol fixes.
+
+
+def test_rollback_returns_exactly_the_draft_blocks(impl):
+    """Grow by 5 drafts over a block boundary, reject 4: the block only they used returns."""
+    B = 4
+    m = impl(16, B, 8)
+    r = m.add_request()
+    m.reserve(r, 6)  # blocks 0, 1 (6 tokens)
+    before = m.blocks_of(r)
+    pos, copies = m.prepare_extend([r], 5)  # tokens 6..10 -> a third block
+    assert pos == [6] and copies == []
+    assert len(m.blocks_of(r)) == 3 and m.num_free() == 13
+    m.truncate(r, 7)  # one draft accepted
+    assert m.length(r) == 7 and m.blocks_of(r) == before and m.num_free() == 14
+    m.truncate(r, 0)
+    assert m.blocks_of(r) == [] and m.num_free() == 16
+    m.check()
+
+
+def test_rollback_of_a_forked_branch_keeps_shared_blocks(impl):
+    """A branch's rollback drops its own references only; the other sharer keeps every block."""
+    B = 4
+    m = impl(16, B, 8)
+    a = m.add_request()
+    m.reserve(a, 8)  # two full blocks, shared after the fork
+    b = m.fork(a)
+    shared = m.blocks_of(a)
+    pos, copies = m.prepare_extend([b], 3)  # b: tail full, so a fresh block, no copy
+    assert pos == [8] and copies == []
+    m.truncate(b, 2)  # b drops its draft block and the second shared block
+    assert m.blocks_of(a) == shared
+    assert m.refcount(shared[0]) == 2 and m.refcount(shared[1]) == 1
+    assert m.num_free() == 14
+    # b's tail is now partly filled and shared: its next growth copies the 2 valid slots
+    pos, copies = m.prepare_extend([b], 1)
+    assert pos == [2] and len(copies) == 1 and copies[0][0] == shared[0] and copies[0][2] == 2
+    m.check()
+
+
+def test_extend_is_all_or_nothing(impl):
+    """Two requests that each need 2 fresh blocks, with 3 free: nothing changes."""
+    B = 4
+    m = impl(5, B, 8)
+    r1, r2 = m.add_request(), m.add_request()
+    m.reserve(r1, 1)
+    m.reserve(r2, 1)
+    free = m.num_free()
+    assert free == 3
+    with pytest.raises(NoSpace):
+        m.prepare_extend([r1, r2], 8)  # tokens 1..8 -> blocks 2 and 3 of each
+    assert m.num_free() == free and m.length(r1) == 1 and m.length(r2) == 1
+    m.check()
+
+
+def test_extend_then_rollback_round_trip_restores_state(impl):
+    """prepare_extend followed by truncate to the old lengths restores lengths, tables and free count."""
+    rng = np.random.default_rng(4)
+    B = 8
+    m = impl(64, B, 10)
+    reqs = [m.add_request() for _ in range(5)]
+    for r in reqs:
+        m.reserve(r, int(rng.integers(1, 40)))
+    old = {r: (m.length(r), m.blocks_of(r)) for r in reqs}
+    free = m.num_free()
+    pos, copies = m.prepare_extend(reqs, 7)
+    assert copies == [] and pos == [old[r][0] for r in reqs]
+    for r in reqs:
+        m.truncate(r, old[r][0])
+        assert (m.length(r), m.blocks_of(r)) == old[r]
+    assert m.num_free() == free
     m.check()

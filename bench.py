@@ -237,6 +237,40 @@ def suite(torch, pa, W, dev):
         del b, pools, calls
         torch.cuda.empty_cache()
 
+    # Several query tokens per request ([Serving] §5): a speculative-verification
+    # step with T draft tokens over the headline histories (4 rotated pool
+    # copies), and one 512-token prompt chunk.  GB/s counts the history once.
+    for T in (2, 4, 8):
+        b = W.verify_batch(device=dev, T=T)
+        pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
+        pools = [(b.k_pool, b.v_pool)] + [(b.k_pool.clone(), b.v_pool.clone()) for _ in range(3)]
+        calls = [pa.DecodeLaunch(b.q, k, v, b.block_tables, b.seq_lens, b.B, b.scale) for k, v in pools]
+
+        def launch_all():
+            for c in calls:
+                c.launch()
+
+        us = graph_time_us(torch, launch_all, 10) / len(calls)
+        out[f"bf16 verification, 32 x 4096 tokens, T = {T} query tokens"] = dict(
+            rate(b.valid_kv_bytes(), us), splits=calls[0].splits, layers=1,
+            query_tokens_per_s_per_layer=round(b.S * T / (us * 1e-6), 1))
+        del b, pools, calls
+        torch.cuda.empty_cache()
+    b = W.prefill_chunk_batch(device=dev)
+    pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
+    call = pa.DecodeLaunch(b.q, b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B, b.scale)
+    us = graph_time_us(torch, call.launch, 10)
+    lens = b.seq_lens.cpu().tolist()
+    # causal q.k and p.v: 4 * d flops per (query token, head, visible position)
+    flops = sum(4 * b.D * b.Hq * (n - b.T + i + 1) for n in lens for i in range(b.T) if n - b.T + i >= 0)
+    ent = dict(rate(b.valid_kv_bytes(), us), splits=call.splits, layers=1,
+               query_tokens_per_s_per_layer=round(b.S * b.T / (us * 1e-6), 1))
+    ent["TFLOP_s"] = round(flops / (us * 1e-6) / 1e12, 2)
+    ent["frac_bf16_mfma_peak"] = round(flops / (us * 1e-6) / 2.5e15, 4)
+    out[f"bf16 prompt chunk, 8 x 4096 tokens, T = {b.T} query tokens"] = ent
+    del b, call
+    torch.cuda.empty_cache()
+
     for name, make, rows in (("fp32 5 requests (37..511 tokens), one layer", W.config1, None),
                              ("bf16 256 mixed-length requests, 32 layers", W.config3, None),
                              ("bf16 prefix sharing, 64 branches (COW), one layer", W.config4, None),

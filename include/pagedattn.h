@@ -15,6 +15,9 @@
  *                                       "顺序留在表里，数据放进空闲块")
  *   seq_lens      int32 [S]             tokens each request attends to
  *   out           float32 [S, Hq, d]
+ * The several-token entry points (paged_attn_extend, kv_append_tokens) put a
+ * token axis after the request axis: q and out [S, T, Hq, d], new K/V
+ * [S, T, Hkv, d].
  *
  * Conventions shared by every entry point:
  *   - Pointers are device pointers unless stated; the library never allocates,
@@ -44,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 typedef enum {
   PA_OK = 0,
@@ -118,6 +121,35 @@ pa_status paged_attn_decode(const void* q, const void* k_pool, const void* v_poo
                             const pa_dims* dims);
 
 /*
+ * Split-K plan for paged_attn_extend with num_q_tokens (T >= 1) query tokens
+ * per request; T = 1 gives paged_attn_plan's answer.  The workspace holds
+ * partial states for S*T*Hq rows.
+ */
+pa_status paged_attn_extend_plan(const pa_dims* dims, int32_t B, int32_t num_q_tokens, int32_t* num_splits,
+                                 size_t* workspace_bytes);
+
+/*
+ * Attention of T = num_q_tokens new tokens per request over the paged
+ * history: a speculative-verification step or one chunk of a prompt
+ * ([Serving] §5 sets speculative decoding and tiled exact attention beside
+ * paging).  The T tokens are already appended (kv_append_tokens) as the last
+ * T of the seq_lens[s] = n positions; query token i sits at position n-T+i
+ * and attends positions 0 .. n-T+i (itself and everything before it):
+ *   out[s,i,h,:] = sum_{t <= n-T+i} softmax_t(scale * <q[s,i,h,:], K_s[t,g,:]>) * V_s[t,g,:]
+ * with the addressing, masking and online-softmax merging of
+ * paged_attn_decode.  A query whose position n-T+i is negative (n < T)
+ * attends nothing and gets 0.  q and out are [S, T, Hq, d] (q of `dtype`,
+ * out float32).  T = 1 is exactly paged_attn_decode.  Several (token, head)
+ * pairs share each K/V byte read: with bf16, up to 16/G tokens of a
+ * G-head group per pass over the history (8/G with float32); more tokens
+ * are spread over further passes that the same L2 serves.  The workspace is
+ * sized by paged_attn_extend_plan.
+ */
+pa_status paged_attn_extend(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                            const int32_t* seq_lens, int32_t num_q_tokens, int32_t B, float scale, float* out,
+                            hipStream_t stream, const pa_dims* dims);
+
+/*
  * Append one token per request ([Slides] "写满一块，再拿下一块"):
  *   k_pool[block_tables[s][p / B], p % B, :, :] = k_new[s, :, :]   (p = positions[s])
  * and the same for V.  k_new/v_new are [S, Hkv, d] of `dtype`; positions is
@@ -130,6 +162,18 @@ pa_status paged_attn_decode(const void* q, const void* k_pool, const void* v_poo
 pa_status kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                     const int32_t* block_tables, const int32_t* positions, int32_t B,
                     hipStream_t stream, const pa_dims* dims);
+
+/*
+ * kv_append for T = num_tokens consecutive tokens per request (draft tokens
+ * or a prompt chunk, [Serving] §5): k_new/v_new are [S, T, Hkv, d] and
+ * token i of request s goes to logical position positions[s] + i.  A
+ * negative positions[s] skips the request; the blocks of every position
+ * written must already be in the table and private (pa_bm_prepare_extend
+ * reserves them and reports the copies to make first).  T = 1 is kv_append.
+ */
+pa_status kv_append_tokens(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                           const int32_t* block_tables, const int32_t* positions, int32_t num_tokens, int32_t B,
+                           hipStream_t stream, const pa_dims* dims);
 
 /*
  * Copy-on-write of shared tail blocks ([Slides] "只读时共用，要写入时再分开",

@@ -14,12 +14,15 @@ from ._lib import (  # noqa: F401
     PoolExhausted,
     declared_functions,
     kv_append,
+    kv_append_tokens,
     kv_cow_copy,
     kv_swap_in,
     kv_swap_out,
     load,
     make_dims,
     paged_attn_decode,
+    paged_attn_extend,
+    paged_attn_extend_plan,
     paged_attn_plan,
     paged_kv_gather,
 )

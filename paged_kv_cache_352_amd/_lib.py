@@ -62,7 +62,10 @@ def load():
         "pa_last_error": (ctypes.c_char_p, []),
         "paged_attn_plan": (I32, [DP, I32, ctypes.POINTER(I32), ctypes.POINTER(SZ)]),
         "paged_attn_decode": (I32, [P, P, P, P, P, I32, F32, P, P, DP]),
+        "paged_attn_extend_plan": (I32, [DP, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(SZ)]),
+        "paged_attn_extend": (I32, [P, P, P, P, P, I32, I32, F32, P, P, DP]),
         "kv_append": (I32, [P, P, P, P, P, P, I32, P, DP]),
+        "kv_append_tokens": (I32, [P, P, P, P, P, P, I32, I32, P, DP]),
         "kv_cow_copy": (I32, [P, P, P, P, P, I32, I32, I32, I64, P, DP]),
         "paged_kv_gather": (I32, [P, P, P, P, I32, P, P, P, DP]),
         "kv_swap_out": (I32, [P, P, P, I32, P, I32, I32, I64, P, DP]),
@@ -149,10 +152,22 @@ def paged_attn_plan(S, Hq, Hkv, D, MB, NB, dtype, B, num_splits=0):
     return p.value, w.value
 
 
+def paged_attn_extend_plan(S, Hq, Hkv, D, MB, NB, dtype, B, T, num_splits=0):
+    """(splits, workspace bytes) of paged_attn_extend with T query tokens per request."""
+    lib = load()
+    d = make_dims(S, Hq, Hkv, D, MB, NB, dtype, num_splits)
+    p = ctypes.c_int32()
+    w = ctypes.c_size_t()
+    _check("paged_attn_extend_plan",
+           lib.paged_attn_extend_plan(ctypes.byref(d), B, T, ctypes.byref(p), ctypes.byref(w)))
+    return p.value, w.value
+
+
 def _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, B, out):
-    if q.dim() != 3 or k_pool.dim() != 4 or block_tables.dim() != 2 or seq_lens.dim() != 1:
-        raise PagedAttnError("expect q [S,Hq,d], pools [NB,B,Hkv,d], block_tables [S,MB], seq_lens [S]")
-    S, Hq, D = q.shape
+    if q.dim() not in (3, 4) or k_pool.dim() != 4 or block_tables.dim() != 2 or seq_lens.dim() != 1:
+        raise PagedAttnError("expect q [S,Hq,d] (or [S,T,Hq,d]), pools [NB,B,Hkv,d], block_tables [S,MB], "
+                             "seq_lens [S]")
+    S, Hq, D = q.shape[0], q.shape[-2], q.shape[-1]
     NB, Bp, Hkv, Dk = k_pool.shape
     if Bp != B or Dk != D or tuple(v_pool.shape) != tuple(k_pool.shape):
         raise PagedAttnError("pool shapes disagree with q / B")
@@ -162,8 +177,8 @@ def _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, B, out):
         raise PagedAttnError("block_tables and seq_lens need one row per request")
     if q.dtype != k_pool.dtype or v_pool.dtype != k_pool.dtype:
         raise PagedAttnError("q, k_pool and v_pool must share a dtype")
-    if out is not None and (tuple(out.shape) != (S, Hq, D) or out.dtype != torch.float32):
-        raise PagedAttnError("out must be float32 [S, Hq, d]")
+    if out is not None and (tuple(out.shape) != tuple(q.shape) or out.dtype != torch.float32):
+        raise PagedAttnError("out must be float32 and shaped like q")
     return S, Hq, D, NB, Hkv, block_tables.shape[1]
 
 
@@ -171,6 +186,8 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, B, scale, out=N
                       workspace=None, stream=None):
     """out[S, Hq, d] (float32) = one decode step over pools [NB, B, Hkv, d]."""
     lib = load()
+    if q.dim() != 3:
+        raise PagedAttnError("paged_attn_decode takes q [S, Hq, d]")
     S, Hq, D, NB, Hkv, MB = _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, B, out)
     if out is None:
         out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
@@ -185,6 +202,51 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, B, scale, out=N
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), B, ctypes.c_float(scale),
         _ptr(out), _stream(stream), ctypes.byref(d)))
     return out
+
+
+def paged_attn_extend(q, k_pool, v_pool, block_tables, seq_lens, B, scale, out=None, num_splits=0,
+                      workspace=None, stream=None):
+    """out[S, T, Hq, d] (float32): T query tokens per request, the last T of each history, causal."""
+    lib = load()
+    if q.dim() != 4:
+        raise PagedAttnError("paged_attn_extend takes q [S, T, Hq, d]")
+    S, Hq, D, NB, Hkv, MB = _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, B, out)
+    T = q.shape[1]
+    if out is None:
+        out = torch.empty(tuple(q.shape), dtype=torch.float32, device=q.device)
+    _need_cuda(q, k_pool, v_pool, block_tables, seq_lens, out)
+    P, need = paged_attn_extend_plan(S, Hq, Hkv, D, MB, NB, q.dtype, B, T, num_splits)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need_cuda(workspace)
+    d = make_dims(S, Hq, Hkv, D, MB, NB, q.dtype, num_splits, workspace)
+    _check("paged_attn_extend", lib.paged_attn_extend(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), T, B, ctypes.c_float(scale),
+        _ptr(out), _stream(stream), ctypes.byref(d)))
+    return out
+
+
+def kv_append_tokens(k_pool, v_pool, k_new, v_new, block_tables, positions, B, stream=None):
+    """Write k_new/v_new [S, T, Hkv, d]: token i of request s at logical position positions[s] + i."""
+    lib = load()
+    NB, Bp, Hkv, D = k_pool.shape
+    if k_new.dim() != 4:
+        raise PagedAttnError("k_new/v_new must be [S, T, Hkv, d]")
+    S, T = k_new.shape[:2]
+    if Bp != B or tuple(k_new.shape) != (S, T, Hkv, D) or tuple(v_new.shape) != (S, T, Hkv, D):
+        raise PagedAttnError("k_new/v_new must be [S, T, Hkv, d] matching the pools")
+    if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype or v_pool.dtype != k_pool.dtype:
+        raise PagedAttnError("dtype mismatch")
+    if positions.dtype != torch.int32 or block_tables.dtype != torch.int32 or tuple(positions.shape) != (S,):
+        raise PagedAttnError("positions and block_tables must be int32, positions [S]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise PagedAttnError("block_tables must be [S, MB]")
+    _need_cuda(k_pool, v_pool, k_new, v_new, block_tables, positions)
+    d = make_dims(S, 1, Hkv, D, block_tables.shape[1], NB, k_pool.dtype)
+    _check("kv_append_tokens", lib.kv_append_tokens(_ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
+                                                    _ptr(block_tables), _ptr(positions), T, B, _stream(stream),
+                                                    ctypes.byref(d)))
 
 
 def kv_append(k_pool, v_pool, k_new, v_new, block_tables, positions, B, stream=None):
@@ -284,7 +346,8 @@ def paged_kv_gather(k_pool, v_pool, block_tables, seq_lens, B, k_out=None, v_out
 
 
 class DecodeLaunch:
-    """A paged_attn_decode call with its arguments marshalled once.
+    """A paged_attn_decode (q [S, Hq, d]) or paged_attn_extend (q [S, T, Hq, d])
+    call with its arguments marshalled once.
 
     For tight loops (benchmarks, graph capture): ``launch()`` only re-issues the
     C call.  The tensors must stay alive and keep their shapes.  With
@@ -295,17 +358,25 @@ class DecodeLaunch:
     def __init__(self, q, k_pool, v_pool, block_tables, seq_lens, B, scale, out=None, num_splits=0,
                  workspace=None, stream=None):
         S, Hq, D, NB, Hkv, MB = _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, B, out)
-        self.out = out if out is not None else torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
-        self.splits, need = paged_attn_plan(S, Hq, Hkv, D, MB, NB, q.dtype, B, num_splits)
+        self.out = out if out is not None else torch.empty(tuple(q.shape), dtype=torch.float32, device=q.device)
+        extend = q.dim() == 4  # [S, T, Hq, d]: paged_attn_extend
+        if extend:
+            self.splits, need = paged_attn_extend_plan(S, Hq, Hkv, D, MB, NB, q.dtype, B, q.shape[1], num_splits)
+        else:
+            self.splits, need = paged_attn_plan(S, Hq, Hkv, D, MB, NB, q.dtype, B, num_splits)
         if need and workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         self.workspace = workspace
         _need_cuda(q, k_pool, v_pool, block_tables, seq_lens, self.out)
         self._keep = (q, k_pool, v_pool, block_tables, seq_lens)
         self._dims = make_dims(S, Hq, Hkv, D, MB, NB, q.dtype, num_splits, workspace)
-        self._fn = load().paged_attn_decode
-        self._head = (_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), B,
-                      ctypes.c_float(scale), _ptr(self.out))
+        lib = load()
+        self._name = "paged_attn_extend" if extend else "paged_attn_decode"
+        self._fn = getattr(lib, self._name)
+        head = [_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens)]
+        if extend:
+            head.append(q.shape[1])
+        self._head = tuple(head) + (B, ctypes.c_float(scale), _ptr(self.out))
         self._stream = _stream(stream) if stream is not None else None
         self._dims_ref = ctypes.byref(self._dims)
 
@@ -313,7 +384,7 @@ class DecodeLaunch:
         st = self._stream if self._stream is not None else _stream(None)
         status = self._fn(*self._head, st, self._dims_ref)
         if status:
-            _check("paged_attn_decode", status)
+            _check(self._name, status)
         return self.out
 
 

@@ -80,13 +80,21 @@ pa_status check_dims(const pa_dims* d, int32_t B, bool need_attention_shape) {
 //     states and their merge than the added parallelism returns;
 //   fp32 (vector-ALU kernel, one wave per work item): about 2048 waves, each
 //     split keeping at least 8 tiles.
-void plan_splits(const pa_dims* d, int32_t B, int* P_out, int* tps_out) {
+// Several query tokens multiply the work items by the token groups (TG), so
+// fewer splits reach the same wave count.
+int64_t token_groups(const pa_dims* d, int32_t T) {
+  if (T <= 1) return 1;
+  const int per = pa::causal_tokens_per_item(d->dtype, d->num_q_heads / d->num_kv_heads);
+  return ((int64_t)T + per - 1) / per;
+}
+
+void plan_splits(const pa_dims* d, int32_t B, int32_t T, int* P_out, int* tps_out) {
   const int64_t max_tokens = (int64_t)d->max_blocks_per_seq * B;
   const int64_t unit = B > 16 ? B : 16;
   const int64_t units = (max_tokens + unit - 1) / unit;
   int64_t P = d->num_splits;
   if (P == 0) {
-    const int64_t items = (int64_t)d->num_seqs * d->num_kv_heads;
+    const int64_t items = (int64_t)d->num_seqs * d->num_kv_heads * token_groups(d, T);
     const bool mfma = d->dtype == PA_BF16;
     const int64_t waves_per_item = mfma ? pa::kMfmaWaves : 1;
     const int64_t target = mfma ? 1024 : 2048;
@@ -128,26 +136,30 @@ const char* pa_status_string(pa_status st) {
 
 const char* pa_last_error(void) { return g_last_error.c_str(); }
 
-pa_status paged_attn_plan(const pa_dims* dims, int32_t B, int32_t* num_splits, size_t* workspace_bytes) {
-  g_last_error.clear();
+static pa_status plan_common(const pa_dims* dims, int32_t B, int32_t T, int32_t* num_splits,
+                             size_t* workspace_bytes) {
   pa_status st = check_dims(dims, B, true);
   if (st != PA_OK) return st;
+  if (T < 1) return fail(PA_ERR_INVALID_ARG, "num_q_tokens = %d < 1", T);
   if (!num_splits || !workspace_bytes) return fail(PA_ERR_INVALID_ARG, "output pointer is NULL");
   int P, tps;
-  plan_splits(dims, B, &P, &tps);
+  plan_splits(dims, B, T, &P, &tps);
   *num_splits = P;
-  *workspace_bytes = (P > 1 && dims->num_seqs > 0)
-                         ? pa::decode_workspace_floats(dims->num_seqs, dims->num_q_heads, P) * sizeof(float)
-                         : 0;
+  *workspace_bytes =
+      (P > 1 && dims->num_seqs > 0)
+          ? pa::decode_workspace_floats((int64_t)dims->num_seqs * T * dims->num_q_heads, P) * sizeof(float)
+          : 0;
   return PA_OK;
 }
 
-pa_status paged_attn_decode(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
-                            const int32_t* seq_lens, int32_t B, float scale, float* out, hipStream_t stream,
-                            const pa_dims* dims) {
-  g_last_error.clear();
+// Validation, split plan and launch shared by the one-token decode (T = 1)
+// and the several-token causal form.
+static pa_status attend(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                        const int32_t* seq_lens, int32_t T, int32_t B, float scale, float* out, hipStream_t stream,
+                        const pa_dims* dims) {
   pa_status st = check_dims(dims, B, true);
   if (st != PA_OK) return st;
+  if (T < 1) return fail(PA_ERR_INVALID_ARG, "num_q_tokens = %d < 1", T);
   if (dims->num_seqs == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !out)
     return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
@@ -155,10 +167,11 @@ pa_status paged_attn_decode(const void* q, const void* k_pool, const void* v_poo
     return fail(PA_ERR_INVALID_ARG, "q, pools and out must be 16-byte aligned");
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
   int P, tps;
-  plan_splits(dims, B, &P, &tps);
-  const int64_t items = (int64_t)dims->num_kv_heads * dims->num_seqs * P;
-  if (items > INT32_MAX || (int64_t)dims->num_seqs * dims->num_q_heads > INT32_MAX)
-    return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  plan_splits(dims, B, T, &P, &tps);
+  const int64_t TG = token_groups(dims, T);
+  const int64_t items = (int64_t)dims->num_kv_heads * dims->num_seqs * P * TG;
+  const int64_t rows = (int64_t)dims->num_seqs * T * dims->num_q_heads;
+  if (items > INT32_MAX || rows > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "grid too large");
 
   pa::DecodeArgs a{};
   a.q = q;
@@ -175,19 +188,46 @@ pa_status paged_attn_decode(const void* q, const void* k_pool, const void* v_poo
   a.NB = dims->num_blocks;
   a.P = P;
   a.tps = tps;
+  a.T = T;
+  a.TG = (int)TG;
   if (P > 1) {
-    const size_t need = pa::decode_workspace_floats(a.S, a.Hq, P) * sizeof(float);
+    const size_t need = pa::decode_workspace_floats(rows, P) * sizeof(float);
     if (!dims->workspace || dims->workspace_bytes < need)
       return fail(PA_ERR_WORKSPACE, "split-K needs %zu workspace bytes, got %zu", need,
                   dims->workspace ? dims->workspace_bytes : (size_t)0);
     if (!aligned(dims->workspace, 256)) return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     float* ws = static_cast<float*>(dims->workspace);
-    const size_t no = (size_t)a.S * a.Hq * P * pa::kHeadDim;
+    const size_t no = (size_t)rows * P * pa::kHeadDim;
     a.ws_o = ws;
     a.ws_m = ws + no;
-    a.ws_l = ws + no + (size_t)a.S * a.Hq * P;
+    a.ws_l = ws + no + (size_t)rows * P;
   }
   return launched(pa::launch_decode(a, dims->dtype, B, a.Hq / a.Hkv, stream));
+}
+
+pa_status paged_attn_plan(const pa_dims* dims, int32_t B, int32_t* num_splits, size_t* workspace_bytes) {
+  g_last_error.clear();
+  return plan_common(dims, B, 1, num_splits, workspace_bytes);
+}
+
+pa_status paged_attn_extend_plan(const pa_dims* dims, int32_t B, int32_t num_q_tokens, int32_t* num_splits,
+                                 size_t* workspace_bytes) {
+  g_last_error.clear();
+  return plan_common(dims, B, num_q_tokens, num_splits, workspace_bytes);
+}
+
+pa_status paged_attn_decode(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                            const int32_t* seq_lens, int32_t B, float scale, float* out, hipStream_t stream,
+                            const pa_dims* dims) {
+  g_last_error.clear();
+  return attend(q, k_pool, v_pool, block_tables, seq_lens, 1, B, scale, out, stream, dims);
+}
+
+pa_status paged_attn_extend(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                            const int32_t* seq_lens, int32_t num_q_tokens, int32_t B, float scale, float* out,
+                            hipStream_t stream, const pa_dims* dims) {
+  g_last_error.clear();
+  return attend(q, k_pool, v_pool, block_tables, seq_lens, num_q_tokens, B, scale, out, stream, dims);
 }
 
 static pa_status kv_common(const pa_dims* dims, int32_t B, void* k_pool, void* v_pool, pa::KvArgs* a) {
@@ -207,21 +247,32 @@ static pa_status kv_common(const pa_dims* dims, int32_t B, void* k_pool, void* v
   return PA_OK;
 }
 
-pa_status kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new, const int32_t* block_tables,
-                    const int32_t* positions, int32_t B, hipStream_t stream, const pa_dims* dims) {
-  g_last_error.clear();
+static pa_status append_common(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                               const int32_t* block_tables, const int32_t* positions, int32_t T, int32_t B,
+                               hipStream_t stream, const pa_dims* dims) {
+  if (T < 1) return fail(PA_ERR_INVALID_ARG, "num_tokens = %d < 1", T);
   pa::KvArgs a{};
-  if (dims && dims->num_seqs == 0) {
-    pa_status st = check_dims(dims, B, false);
-    return st;
-  }
+  if (dims && dims->num_seqs == 0) return check_dims(dims, B, false);
   pa_status st = kv_common(dims, B, k_pool, v_pool, &a);
   if (st != PA_OK) return st;
   if (!k_new || !v_new || !block_tables || !positions) return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(PA_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
-  if (a.S > 2147483647) return fail(PA_ERR_UNSUPPORTED, "too many requests");
+  if ((int64_t)a.S * T > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "too many tokens");
   return launched(pa::launch_append(a, static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new),
-                                    block_tables, positions, stream));
+                                    block_tables, positions, T, stream));
+}
+
+pa_status kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new, const int32_t* block_tables,
+                    const int32_t* positions, int32_t B, hipStream_t stream, const pa_dims* dims) {
+  g_last_error.clear();
+  return append_common(k_pool, v_pool, k_new, v_new, block_tables, positions, 1, B, stream, dims);
+}
+
+pa_status kv_append_tokens(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                           const int32_t* block_tables, const int32_t* positions, int32_t num_tokens, int32_t B,
+                           hipStream_t stream, const pa_dims* dims) {
+  g_last_error.clear();
+  return append_common(k_pool, v_pool, k_new, v_new, block_tables, positions, num_tokens, B, stream, dims);
 }
 
 pa_status kv_cow_copy(void* k_pool, void* v_pool, const int32_t* src_blocks, const int32_t* dst_blocks,

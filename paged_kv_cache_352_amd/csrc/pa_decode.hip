@@ -29,6 +29,14 @@
 //   * work items are numbered KV-head-major and handed out XCD by XCD, so
 //     the waves that read one KV head's blocks (a shared prefix, say) sit on
 //     the same L2.
+//
+// Several query tokens per request (the causal variant): T new tokens,
+// already the last T positions of the history, token i attending positions
+// 0 .. n-T+i ([Serving] §5: speculative verification and prompt chunks read
+// the same paged history).  A wave then keeps C = 8 (token, head) columns —
+// 8/G tokens of its group — each with its own length limit; a column that
+// has seen no valid position yet keeps the empty state (m = -inf, l = 0,
+// o = 0).  Further tokens go to further work items.
 #include <hip/hip_runtime.h>
 
 #include "pa_internal.h"
@@ -65,8 +73,10 @@ __device__ inline int xcd_remap(int bid, int nwg) {
   return x * q + min(x, rem) + k;
 }
 
-template <typename T, int G, int B>
+template <typename T, int G, bool kCausal, int B>
 __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeArgs a) {
+  constexpr int TC = kCausal ? (G >= 8 ? 1 : 8 / G) : 1;  // query tokens per work item
+  constexpr int C = G * TC;                                // (token, head) columns
   constexpr int E = Vec16<T>::kElems;  // elements per 16-byte load
   constexpr int LPR = kHeadDim / E;    // lanes per row (32 for fp32)
   constexpr int RPL = kWave / LPR;     // rows per wave load (2 for fp32)
@@ -81,32 +91,53 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeArgs a) {
   int item = xcd_remap(blockIdx.x, gridDim.x);
   const int p = item % a.P;
   item /= a.P;
+  int tg = 0;  // which TC query tokens of the request this item takes
+  if constexpr (kCausal) {
+    tg = item % a.TG;
+    item /= a.TG;
+  }
   const int s = item % a.S;
   const int kvh = item / a.S;
 
   const int n_raw = a.lens[s];
   bool bad = n_raw < 0 || (int64_t)n_raw > (int64_t)a.MB * B;  // outside what the table can describe
   const int n = bad ? 0 : n_raw;
-  const int nt = (n + kTile - 1) / kTile;  // 16-slot tiles of the history
+  // Column g is query token tg*TC + g/G, head kvh*G + g%G; it may see the
+  // first lim[g] positions.  The item needs the tiles up to its last token's.
+  int lim[C];
+  int lim_hi = n;
+#pragma unroll
+  for (int g = 0; g < C; ++g) lim[g] = n;
+  if constexpr (kCausal) {
+#pragma unroll
+    for (int g = 0; g < C; ++g) {
+      const int tq = tg * TC + g / G;
+      lim[g] = tq < a.T ? min(n, max(0, n - a.T + 1 + tq)) : n;
+    }
+    lim_hi = min(n, max(0, n - a.T + min(a.T, tg * TC + TC)));
+  }
+  const int nt = (lim_hi + kTile - 1) / kTile;  // 16-slot tiles this item reads
   const int u0 = p * (a.tps / kTile);
   const int u1 = min(nt, u0 + a.tps / kTile);
 
-  // q for the G heads of this group, dims [c*E, c*E+E), pre-scaled into base 2.
-  float qf[G][E];
+  // q of the C columns, dims [c*E, c*E+E), pre-scaled into base 2.
+  float qf[C][E];
   {
-    const T* qp = static_cast<const T*>(a.q) + ((int64_t)s * a.Hq + (int64_t)kvh * G) * kHeadDim + c * E;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const uint4 w = *reinterpret_cast<const uint4*>(qp + g * kHeadDim);
+    for (int g = 0; g < C; ++g) {
+      const int row = kCausal ? min(tg * TC + g / G, a.T - 1) : 0;  // a column past T repeats the last token
+      const T* qp = static_cast<const T*>(a.q) +
+                    (((int64_t)s * a.T + row) * a.Hq + (int64_t)kvh * G + g % G) * kHeadDim + c * E;
+      const uint4 w = *reinterpret_cast<const uint4*>(qp);
       Vec16<T>::unpack(w, qf[g]);
 #pragma unroll
       for (int e = 0; e < E; ++e) qf[g][e] *= a.scale_log2;
     }
   }
 
-  float m[G], l[G], o[G][E];
+  float m[C], l[C], o[C][E];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
+  for (int g = 0; g < C; ++g) {
     m[g] = kNegInf;
     l[g] = 0.f;
 #pragma unroll
@@ -153,14 +184,14 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeArgs a) {
       }
     }
 
-    // Scores of this lane's NL slots for the G heads (base 2).
-    float sc[NL][G];
+    // Scores of this lane's NL slots for the C columns (base 2).
+    float sc[NL][C];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       float kf[E];
       Vec16<T>::unpack(kraw[i], kf);
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
+      for (int g = 0; g < C; ++g) {
         float acc = 0.f;
 #pragma unroll
         for (int e = 0; e < E; ++e) acc = fmaf(qf[g][e], kf[e], acc);
@@ -172,35 +203,45 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < NL; ++i)
 #pragma unroll
-        for (int g = 0; g < G; ++g) sc[i][g] += shfl_xor(sc[i][g], mask);
+        for (int g = 0; g < C; ++g) sc[i][g] += shfl_xor(sc[i][g], mask);
 
-    // Mask slots at or past the length ([Slides] quiz "逻辑顺序没错…" step 1).
+    // Mask slots at or past the length ([Slides] quiz "逻辑顺序没错…" step 1),
+    // and, for several query tokens, past each column's own position.
     const bool tail = (u + 1) * kTile > n;
     bool valid[NL];
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      valid[i] = kTile * u + i * RPL + r < n;
+      const int slot = kTile * u + i * RPL + r;
+      valid[i] = slot < n;
 #pragma unroll
-      for (int g = 0; g < G; ++g) sc[i][g] = valid[i] ? sc[i][g] : kNegInf;
+      for (int g = 0; g < C; ++g) sc[i][g] = slot < lim[g] ? sc[i][g] : kNegInf;
     }
 
     // [Budgets] eq. (4): new running max, rescale factor, block weights.
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int g = 0; g < C; ++g) {
       float bm = sc[0][g];
 #pragma unroll
       for (int i = 1; i < NL; ++i) bm = fmaxf(bm, sc[i][g]);
 #pragma unroll
       for (int mask = LPR; mask < kWave; mask <<= 1) bm = fmaxf(bm, shfl_xor(bm, mask));
-      const float mn = fmaxf(m[g], bm);  // finite: slot 0 of tile u < nt is valid
-      const float alpha = fast_exp2(m[g] - mn);
+      const float mn = fmaxf(m[g], bm);  // decode: finite, slot 0 of tile u < nt is valid
+      float alpha, mref = mn;
+      if constexpr (kCausal) {
+        // a column may have seen nothing yet (mn = -inf): keep its empty state
+        alpha = (m[g] == mn) ? 1.f : fast_exp2(m[g] - mn);
+        mref = (mn == kNegInf) ? 0.f : mn;
+      } else {
+        alpha = fast_exp2(m[g] - mn);
+      }
       m[g] = mn;
       l[g] *= alpha;
 #pragma unroll
       for (int e = 0; e < E; ++e) o[g][e] *= alpha;
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
-        const float pw = valid[i] ? fast_exp2(sc[i][g] - mn) : 0.f;
+        const int slot = kTile * u + i * RPL + r;
+        const float pw = slot < lim[g] ? fast_exp2(sc[i][g] - mref) : 0.f;
         sc[i][g] = pw;
         l[g] += pw;
       }
@@ -216,7 +257,7 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeArgs a) {
         for (int e = 0; e < E; ++e) vf[e] = 0.f;
       }
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+      for (int g = 0; g < C; ++g)
 #pragma unroll
         for (int e = 0; e < E; ++e) o[g][e] = fmaf(sc[i][g], vf[e], o[g][e]);
     }
@@ -226,7 +267,7 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int mask = LPR; mask < kWave; mask <<= 1) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int g = 0; g < C; ++g) {
       l[g] += shfl_xor(l[g], mask);
 #pragma unroll
       for (int e = 0; e < E; ++e) o[g][e] += shfl_xor(o[g][e], mask);
@@ -236,15 +277,17 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeArgs a) {
 
   const float nan = __builtin_nanf("");
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int h = kvh * G + g;
+  for (int g = 0; g < C; ++g) {
+    const int t_out = tg * TC + g / G;
+    if (kCausal && t_out >= a.T) break;
+    const int64_t row = ((int64_t)s * a.T + t_out) * a.Hq + kvh * G + g % G;  // [S, T, Hq] row
     if (a.P == 1) {
-      float* dst = a.out + ((int64_t)s * a.Hq + h) * kHeadDim + c * E;
+      float* dst = a.out + row * kHeadDim + c * E;
       const float inv = l[g] > 0.f ? 1.f / l[g] : 0.f;
 #pragma unroll
       for (int e = 0; e < E; ++e) dst[e] = bad ? nan : o[g][e] * inv;
     } else {
-      const int64_t slot = ((int64_t)s * a.Hq + h) * a.P + p;
+      const int64_t slot = row * a.P + p;
       float* dst = a.ws_o + slot * kHeadDim + c * E;
 #pragma unroll
       for (int e = 0; e < E; ++e) dst[e] = o[g][e];
@@ -260,7 +303,7 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeArgs a) {
 //   M = max_p m_p, L = sum_p 2^(m_p - M) l_p, O = sum_p 2^(m_p - M) o_p, out = O / L.
 // Empty splits carry m = -inf, l = 0 and drop out; all empty gives 0.
 __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
-  const int sh = blockIdx.x;  // s * Hq + h
+  const int sh = blockIdx.x;  // (s * T + t) * Hq + h
   const int lane = threadIdx.x;
   const float* ms = a.ws_m + (int64_t)sh * a.P;
   const float* ls = a.ws_l + (int64_t)sh * a.P;
@@ -285,46 +328,47 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
   dst[1] = o1 * inv;
 }
 
-template <typename T, int G, int B>
+template <typename T, int G, bool kCausal, int B>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-  const int items = a.Hkv * a.S * a.P;
-  hipLaunchKernelGGL((decode_split_kernel<T, G, B>), dim3(items), dim3(kWave), 0, stream, a);
+  const int items = a.Hkv * a.S * a.P * (kCausal ? a.TG : 1);
+  hipLaunchKernelGGL((decode_split_kernel<T, G, kCausal, B>), dim3(items), dim3(kWave), 0, stream, a);
   return hipGetLastError();
 }
 
-template <typename T, int B>
+template <typename T, bool kCausal, int B>
 hipError_t launch_group(const DecodeArgs& a, int G, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_typed<T, 1, B>(a, stream);
-    case 2: return launch_typed<T, 2, B>(a, stream);
-    case 4: return launch_typed<T, 4, B>(a, stream);
-    case 8: return launch_typed<T, 8, B>(a, stream);
+    case 1: return launch_typed<T, 1, kCausal, B>(a, stream);
+    case 2: return launch_typed<T, 2, kCausal, B>(a, stream);
+    case 4: return launch_typed<T, 4, kCausal, B>(a, stream);
+    case 8: return launch_typed<T, 8, kCausal, B>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <bool kCausal>
 hipError_t launch_valu(const DecodeArgs& a, int B, int G, hipStream_t stream) {
   switch (B) {
-    case 4: return launch_group<float, 4>(a, G, stream);
-    case 8: return launch_group<float, 8>(a, G, stream);
-    case 16: return launch_group<float, 16>(a, G, stream);
-    case 32: return launch_group<float, 32>(a, G, stream);
-    case 64: return launch_group<float, 64>(a, G, stream);
+    case 4: return launch_group<float, kCausal, 4>(a, G, stream);
+    case 8: return launch_group<float, kCausal, 8>(a, G, stream);
+    case 16: return launch_group<float, kCausal, 16>(a, G, stream);
+    case 32: return launch_group<float, kCausal, 32>(a, G, stream);
+    case 64: return launch_group<float, kCausal, 64>(a, G, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-size_t decode_workspace_floats(int S, int Hq, int P) {
-  return (size_t)S * Hq * P * (kHeadDim + 2);
-}
+size_t decode_workspace_floats(int64_t rows, int P) { return (size_t)rows * P * (kHeadDim + 2); }
 
 hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int B, int G, hipStream_t stream) {
   // bf16: q.k and p.v on the matrix cores; fp32: the vector-ALU kernel.
-  hipError_t e = dtype == PA_BF16 ? launch_decode_mfma(a, B, G, stream) : launch_valu(a, B, G, stream);
+  const bool causal = a.T > 1;
+  hipError_t e = dtype == PA_BF16 ? launch_decode_mfma(a, B, G, causal, stream)
+                                  : (causal ? launch_valu<true>(a, B, G, stream) : launch_valu<false>(a, B, G, stream));
   if (e != hipSuccess || a.P == 1) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.S * a.Hq), dim3(kWave), 0, stream, a);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.S * a.T * a.Hq), dim3(kWave), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -55,6 +55,18 @@
 // partial l over its own four slots of every tile; the partials of the four
 // lanes of a head are summed once at the end.  The accumulators are rescaled
 // only in tiles where some head's max moved.
+//
+// Several query tokens (the causal variant).  A verification step or a
+// prompt chunk brings T new tokens per request, already appended as the last
+// T positions of the history; token i attends positions 0 .. n-T+i
+// ([Serving] §5 sets speculative decoding beside paging).  The 16 columns of
+// the MFMA tile then hold (token, head) pairs: 16/G tokens of the G-head
+// group per work item, so up to 16/G tokens cost no more K/V traffic than
+// one.  Each column carries its own length limit; a column whose limit lies
+// before a tile sees only -inf there, and its state stays empty (m = -inf,
+// l = 0, o = 0) until a tile reaches it.  More tokens than one item holds
+// are spread over further work items of the same (request, KV head), which
+// the XCD-aware numbering keeps on one L2.
 #include <hip/hip_runtime.h>
 
 #include "pa_internal.h"
@@ -129,15 +141,17 @@ __device__ inline uint4 load_kv16(__amdgpu_buffer_rsrc_t r, uint32_t off, int so
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, soff, 0));
 }
 
-template <int G, int W, int B>
+template <int G, bool kCausal, int W, int B>
 __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   static_assert(G >= 1 && G <= 16, "the query group must fit the 16 columns of one MFMA tile");
   static_assert(B >= 4 && B <= 64 && (B & (B - 1)) == 0, "block size: a power of two from 4 to 64");
+  constexpr int TC = kCausal ? (G >= 16 ? 1 : 16 / G) : 1;  // query tokens per work item
+  constexpr int NC = G * TC;                                  // MFMA columns in use
   __shared__ __attribute__((aligned(16))) uint8_t vt_all[W][kVtBytes];
   __shared__ __attribute__((aligned(16))) uint8_t kt_all[W][kVtBytes];
   __shared__ float red_m[W][16];
   __shared__ float red_l[W][16];
-  __shared__ __attribute__((aligned(16))) float red_o[W][G][kHeadDim];
+  __shared__ __attribute__((aligned(16))) float red_o[W][NC][kHeadDim];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
@@ -147,14 +161,27 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   int item = xcd_remap(blockIdx.x, gridDim.x);
   const int p = item % a.P;
   item /= a.P;
+  int tg = 0;  // which TC query tokens of the request this item takes
+  if constexpr (kCausal) {
+    tg = item % a.TG;
+    item /= a.TG;
+  }
   const int s = item % a.S;
   const int kvh = item / a.S;
 
   const int n_raw = a.lens[s];
   bool bad = n_raw < 0 || (int64_t)n_raw > (int64_t)a.MB * B;
   const int n = bad ? 0 : n_raw;
-  const int nb = (n + B - 1) / B;          // blocks holding the history
-  const int nt = (n + kTile - 1) / kTile;  // 16-slot tiles of the history
+  const int nb = (n + B - 1) / B;  // blocks holding the history
+  // Column n16 is query token tq, head kvh*G + n16%G; it may see the first
+  // lim positions.  The item needs the tiles up to its last token's limit.
+  const int tq = tg * TC + n16 / G;
+  int lim = n, lim_hi = n;
+  if constexpr (kCausal) {
+    lim = tq < a.T ? min(n, max(0, n - a.T + 1 + tq)) : n;
+    lim_hi = min(n, max(0, n - a.T + min(a.T, tg * TC + TC)));
+  }
+  const int nt = (lim_hi + kTile - 1) / kTile;  // 16-slot tiles this item reads
   const int u0 = p * (a.tps / kTile);
   const int u1 = min(nt, u0 + a.tps / kTile);
   // This wave's tiles: a contiguous share [ua, ub) of the split's tiles.
@@ -162,15 +189,19 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   const int ua = min(u1, u0 + w * share);
   const int ub = min(u1, ua + share);
 
-  // q of head kvh*G + n16 over the dims this lane contributes, as MFMA B operands.
+  // q of column n16 over the dims this lane contributes, as MFMA B operands.
   bf16x8_t qv[4];
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) + ((int64_t)s * a.Hq + (int64_t)kvh * G) * kHeadDim;
-    const int hq = n16 < G ? n16 : G - 1;  // every lane loads (no divergent loads), then zeros
+    // every lane loads (no divergent loads), then columns without a query are zeroed
+    const bool live = n16 < NC && tq < a.T;
+    const int row = kCausal ? min(tq, a.T - 1) : 0;
+    const int hq = kCausal ? n16 % G : (n16 < G ? n16 : G - 1);
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         (((int64_t)s * a.T + row) * a.Hq + (int64_t)kvh * G + hq) * kHeadDim;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint4 v = *reinterpret_cast<const uint4*>(qp + hq * kHeadDim + 32 * i + 8 * c4);
-      if (n16 >= G) v = make_uint4(0, 0, 0, 0);
+      uint4 v = *reinterpret_cast<const uint4*>(qp + 32 * i + 8 * c4);
+      if (!live) v = make_uint4(0, 0, 0, 0);
       qv[i] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
@@ -260,21 +291,30 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
       sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qv[i], sc, 0, 0, 0);
     }
 
-    // Scores in base 2, masked past the length ([Slides] quiz "逻辑顺序没错…").
+    // Scores in base 2, masked past the length ([Slides] quiz "逻辑顺序没错…")
+    // or, for several query tokens, past this column's own position.
+    const int vq = kCausal ? lim - u * kTile : valid;
     float sv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = (4 * c4 + r < valid) ? sc[r] * a.scale_log2 : kNegInf;
+    for (int r = 0; r < 4; ++r) sv[r] = (4 * c4 + r < vq) ? sc[r] * a.scale_log2 : kNegInf;
 
     // [Budgets] eq. (4): tile max over the 16 slots of head n16, new running max.
     float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
     bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
     bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
-    const float mn = fmaxf(m, bm);  // finite: slot 0 of a tile below nt is valid
-    const float alpha = fast_exp2(m - mn);
+    const float mn = fmaxf(m, bm);  // decode: finite, slot 0 of a tile below nt is valid
+    float alpha, mref = mn;
+    if constexpr (kCausal) {
+      // a column may have seen nothing yet (mn = -inf): keep its empty state
+      alpha = (m == mn) ? 1.f : fast_exp2(m - mn);
+      mref = (mn == kNegInf) ? 0.f : mn;
+    } else {
+      alpha = fast_exp2(m - mn);
+    }
     m = mn;
     float pw[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pw[r] = fast_exp2(sv[r] - mn);
+    for (int r = 0; r < 4; ++r) pw[r] = fast_exp2(sv[r] - mref);
     l = fmaf(l, alpha, (pw[0] + pw[1]) + (pw[2] + pw[3]));
 
     uint32_t hi0, hi1, lo0, lo1;
@@ -349,18 +389,21 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   for (int r = 0; r < 4; ++r) {
     const int hg = 4 * c4 + r;
     const float fr = __shfl(f, hg & 15, kWave);
-    if (hg < G) {
+    if (hg < NC) {
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) red_o[w][hg][16 * jj + n16] = acc[jj][r] * fr;
     }
   }
   __syncthreads();
 
-  // G * 128 outputs, spread over the workgroup's threads.
+  // NC * 128 outputs (column hg = query token tg*TC + hg/G, head kvh*G + hg%G),
+  // spread over the workgroup's threads.
   const float nan = __builtin_nanf("");
-  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += kWave * W) {
+  for (int idx = threadIdx.x; idx < NC * kHeadDim; idx += kWave * W) {
     const int hg = idx / kHeadDim;
     const int d = idx % kHeadDim;
+    const int t_out = tg * TC + hg / G;
+    if (kCausal && t_out >= a.T) break;  // idx only grows: every later output is past T too
     float M = kNegInf, L = 0.f, O = 0.f;
 #pragma unroll
     for (int v = 0; v < W; ++v) M = fmaxf(M, red_m[v][hg]);
@@ -370,11 +413,11 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
       if (mv != kNegInf) L = fmaf(fast_exp2(mv - M), red_l[v][hg], L);
       O += red_o[v][hg][d];
     }
-    const int h = kvh * G + hg;
+    const int64_t row = ((int64_t)s * a.T + t_out) * a.Hq + kvh * G + hg % G;  // [S, T, Hq] row
     if (a.P == 1) {
-      a.out[((int64_t)s * a.Hq + h) * kHeadDim + d] = bad ? nan : (L > 0.f ? O / L : 0.f);
+      a.out[row * kHeadDim + d] = bad ? nan : (L > 0.f ? O / L : 0.f);
     } else {
-      const int64_t slot = ((int64_t)s * a.Hq + h) * a.P + p;
+      const int64_t slot = row * a.P + p;
       a.ws_o[slot * kHeadDim + d] = O;
       if (d == 0) {
         a.ws_m[slot] = bad ? 0.f : M;
@@ -384,36 +427,42 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-template <int G, int B>
+template <int G, bool kCausal, int B>
 hipError_t launch_gb(const DecodeArgs& a, hipStream_t stream) {
-  const int items = a.Hkv * a.S * a.P;
-  hipLaunchKernelGGL((decode_mfma_kernel<G, kMfmaWaves, B>), dim3(items), dim3(kWave * kMfmaWaves), 0, stream, a);
+  const int items = a.Hkv * a.S * a.P * (kCausal ? a.TG : 1);
+  hipLaunchKernelGGL((decode_mfma_kernel<G, kCausal, kMfmaWaves, B>), dim3(items), dim3(kWave * kMfmaWaves), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
-template <int B>
+template <bool kCausal, int B>
 hipError_t launch_b(const DecodeArgs& a, int G, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_gb<1, B>(a, stream);
-    case 2: return launch_gb<2, B>(a, stream);
-    case 4: return launch_gb<4, B>(a, stream);
-    case 8: return launch_gb<8, B>(a, stream);
-    case 16: return launch_gb<16, B>(a, stream);
+    case 1: return launch_gb<1, kCausal, B>(a, stream);
+    case 2: return launch_gb<2, kCausal, B>(a, stream);
+    case 4: return launch_gb<4, kCausal, B>(a, stream);
+    case 8: return launch_gb<8, kCausal, B>(a, stream);
+    case 16: return launch_gb<16, kCausal, B>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool kCausal>
+hipError_t launch_c(const DecodeArgs& a, int B, int G, hipStream_t stream) {
+  switch (B) {
+    case 4: return launch_b<kCausal, 4>(a, G, stream);
+    case 8: return launch_b<kCausal, 8>(a, G, stream);
+    case 16: return launch_b<kCausal, 16>(a, G, stream);
+    case 32: return launch_b<kCausal, 32>(a, G, stream);
+    case 64: return launch_b<kCausal, 64>(a, G, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int G, hipStream_t stream) {
-  switch (B) {
-    case 4: return launch_b<4>(a, G, stream);
-    case 8: return launch_b<8>(a, G, stream);
-    case 16: return launch_b<16>(a, G, stream);
-    case 32: return launch_b<32>(a, G, stream);
-    case 64: return launch_b<64>(a, G, stream);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int G, bool causal, hipStream_t stream) {
+  return causal ? launch_c<true>(a, B, G, stream) : launch_c<false>(a, B, G, stream);
 }
 
 }  // namespace pa

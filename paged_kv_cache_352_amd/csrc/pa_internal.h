@@ -20,27 +20,37 @@ struct DecodeArgs {
   const void* v_pool;
   const int32_t* tables;
   const int32_t* lens;
-  float* out;       // final output [S, Hq, d]
-  float* ws_o;      // split partial o [S, Hq, P, d]   (P > 1 only)
-  float* ws_m;      // split partial m [S, Hq, P]      (log2 domain)
-  float* ws_l;      // split partial l [S, Hq, P]
+  float* out;       // final output [S, T, Hq, d]
+  float* ws_o;      // split partial o [S, T, Hq, P, d]   (P > 1 only)
+  float* ws_m;      // split partial m [S, T, Hq, P]      (log2 domain)
+  float* ws_l;      // split partial l [S, T, Hq, P]
   float scale_log2; // scale * log2(e): scores are kept in base 2
   int S, Hq, Hkv, MB, NB;
   int P;            // number of splits
   int tps;          // tokens per split: split p covers tokens [p*tps, (p+1)*tps), a multiple of max(16, B)
+  int T;            // query tokens per request (q is [S, T, Hq, d]); the last T of the history, causal
+  int TG;           // work items per (request, KV head, split) along the query tokens: ceil(T / tokens per item)
 };
+
+// Query tokens one work item of the causal (T > 1) kernels covers for group
+// size G: the (token, head) pairs fill the 16 MFMA columns (bf16) or 8
+// accumulator sets of the vector-ALU kernel (fp32).
+constexpr int causal_tokens_per_item(pa_dtype dtype, int G) {
+  return dtype == PA_BF16 ? (G >= 16 ? 1 : 16 / G) : (G >= 8 ? 1 : 8 / G);
+}
 
 // Sets the thread's pa_last_error() text (used by the host-only parts).
 void set_last_error(const char* msg);
 
-// Workspace floats for P splits: S*Hq*P*(d + 2).
-size_t decode_workspace_floats(int S, int Hq, int P);
+// Workspace floats for P splits: S*T*Hq*P*(d + 2).
+size_t decode_workspace_floats(int64_t rows, int P);
 
+// T == 1 runs the decode kernels; T > 1 their causal variants.
 hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int B, int G, hipStream_t stream);
 
-// bf16 decode on the matrix cores (pa_decode_mfma.hip); G in {1, 2, 4, 8, 16},
+// bf16 on the matrix cores (pa_decode_mfma.hip); G in {1, 2, 4, 8, 16},
 // B in {4, 8, 16, 32, 64}.
-hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int G, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int G, bool causal, hipStream_t stream);
 
 struct KvArgs {
   uint8_t* k_pool;
@@ -49,8 +59,9 @@ struct KvArgs {
   int row_bytes;  // Hkv * d * element size: one slot of one block
 };
 
+// T tokens per request: k_new/v_new [S, T, Hkv, d], token i at positions[s] + i.
 hipError_t launch_append(const KvArgs& a, const uint8_t* k_new, const uint8_t* v_new,
-                         const int32_t* tables, const int32_t* positions, hipStream_t stream);
+                         const int32_t* tables, const int32_t* positions, int T, hipStream_t stream);
 
 hipError_t launch_cow(const KvArgs& a, const int32_t* src, const int32_t* dst, const int32_t* n_valid,
                       int num_pairs, int num_layers, int64_t layer_stride_bytes, hipStream_t stream);

@@ -19,20 +19,25 @@ __device__ inline void copy16(uint8_t* __restrict__ dst, const uint8_t* __restri
     *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(src + i);
 }
 
-// One workgroup per (request, pool).  The token with logical index p goes to
-// slot p % B of block table[p / B]; nothing else moves ([Slides]
-// "写满一块，再拿下一块").  Positions or blocks outside the pool are skipped.
+// One workgroup per (request, new token, pool).  Token i of request s takes
+// logical index p = positions[s] + i and goes to slot p % B of block
+// table[p / B]; nothing else moves ([Slides] "写满一块，再拿下一块").  A
+// negative start skips the request; positions or blocks outside the pool are
+// skipped.
 __global__ __launch_bounds__(kThreads) void append_kernel(KvArgs a, const uint8_t* __restrict__ k_new,
                                                           const uint8_t* __restrict__ v_new,
                                                           const int32_t* __restrict__ tables,
-                                                          const int32_t* __restrict__ positions) {
-  const int s = blockIdx.x;
-  const int p = positions[s];
-  if (p < 0 || p >= a.MB * a.B) return;
+                                                          const int32_t* __restrict__ positions, int T) {
+  const int s = blockIdx.x / T;
+  const int i = blockIdx.x % T;
+  const int start = positions[s];
+  if (start < 0) return;
+  const int64_t p = (int64_t)start + i;
+  if (p >= (int64_t)a.MB * a.B) return;
   const int blk = tables[(int64_t)s * a.MB + p / a.B];
   if (blk < 0 || blk >= a.NB) return;
   uint8_t* pool = blockIdx.y ? a.v_pool : a.k_pool;
-  const uint8_t* src = (blockIdx.y ? v_new : k_new) + (int64_t)s * a.row_bytes;
+  const uint8_t* src = (blockIdx.y ? v_new : k_new) + (int64_t)blockIdx.x * a.row_bytes;
   uint8_t* dst = pool + ((int64_t)blk * a.B + p % a.B) * a.row_bytes;
   copy16(dst, src, a.row_bytes);
 }
@@ -102,9 +107,9 @@ hipError_t launch_swap(const KvArgs& a, const int32_t* blocks, int nlist, uint8_
 }
 
 hipError_t launch_append(const KvArgs& a, const uint8_t* k_new, const uint8_t* v_new, const int32_t* tables,
-                         const int32_t* positions, hipStream_t stream) {
-  hipLaunchKernelGGL(append_kernel, dim3(a.S, 2), dim3(kThreads), 0, stream, a, k_new, v_new, tables,
-                     positions);
+                         const int32_t* positions, int T, hipStream_t stream) {
+  hipLaunchKernelGGL(append_kernel, dim3(a.S * T, 2), dim3(kThreads), 0, stream, a, k_new, v_new, tables,
+                     positions, T);
   return hipGetLastError();
 }
 

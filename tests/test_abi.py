@@ -48,10 +48,12 @@ def decode(lib, d, q=FAKE, k=FAKE, v=FAKE, t=FAKE, n=FAKE, B=16, scale=0.1, out=
 
 def test_exports_every_declared_symbol(lib):
     names = pa.declared_functions()
-    assert {"paged_attn_decode", "kv_append", "kv_cow_copy", "paged_kv_gather", "paged_attn_plan"} <= set(names)
+    assert {"paged_attn_decode", "kv_append", "kv_cow_copy", "paged_kv_gather", "paged_attn_plan",
+            "paged_attn_extend", "paged_attn_extend_plan", "kv_append_tokens", "pa_bm_truncate",
+            "pa_bm_prepare_extend"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.pa_abi_version() == 1
+    assert lib.pa_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -158,3 +160,33 @@ def test_swap_rejects_bad_arguments(lib):
     assert lib.kv_swap_in(*args(layers=0)) == INVALID
     assert lib.kv_swap_out(*args(layers=2, stride=5)) == INVALID  # stride smaller than one pool
     assert lib.kv_swap_out(*args(n=0)) == OK  # nothing to do, nothing launched
+
+
+def test_extend_plan_matches_decode_at_one_token_and_scales_workspace(lib):
+    for S, Hq, Hkv, MB, dt in [(32, 32, 8, 256, torch.bfloat16), (5, 8, 2, 32, torch.float32), (7, 16, 1, 9, torch.bfloat16)]:
+        assert pa.paged_attn_extend_plan(S, Hq, Hkv, 128, MB, 10000, dt, 16, 1) == pa.paged_attn_plan(
+            S, Hq, Hkv, 128, MB, 10000, dt, 16)
+        for T in (2, 4, 7, 33):
+            P, ws = pa.paged_attn_extend_plan(S, Hq, Hkv, 128, MB, 10000, dt, 16, T)
+            assert P >= 1 and ws == (S * T * Hq * P * 130 * 4 if P > 1 else 0)
+            # forced splits are honoured as in the one-token plan
+            assert pa.paged_attn_extend_plan(S, Hq, Hkv, 128, MB, 10000, dt, 16, T, num_splits=2)[0] == min(2, MB)
+    p, w = ctypes.c_int32(), ctypes.c_size_t()
+    assert lib.paged_attn_extend_plan(ctypes.byref(dims()), 16, 0, ctypes.byref(p), ctypes.byref(w)) == INVALID
+
+
+@no_gpu
+def test_extend_and_token_append_reject_before_launch(lib):
+    def extend(d, T=4, q=FAKE, out=FAKE, B=16):
+        return lib.paged_attn_extend(q, FAKE, FAKE, FAKE, FAKE, T, B, ctypes.c_float(0.1), out, None,
+                                     ctypes.byref(d))
+    assert extend(dims(), T=0) == INVALID
+    assert extend(dims(), q=None) == INVALID
+    assert extend(dims(Hq=6, Hkv=2)) == UNSUPPORTED
+    assert extend(dims(), B=12) == UNSUPPORTED
+    assert extend(dims(S=1, Hkv=1, Hq=4, MB=64, splits=4)) == WORKSPACE
+    assert extend(dims(S=0), q=None, out=None) == OK
+    d = dims()
+    assert lib.kv_append_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 16, None, ctypes.byref(d)) == INVALID
+    assert lib.kv_append_tokens(FAKE, FAKE, None, FAKE, FAKE, FAKE, 3, 16, None, ctypes.byref(d)) == INVALID
+    assert lib.kv_append_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 0, None, ctypes.byref(d)) == INVALID

@@ -1,0 +1,226 @@
+"""Several query tokens per request on the GPU: kv_append_tokens and paged_attn_extend
+against the float64 oracle (causal attention of the last T tokens over the paged
+history), fp32 within 1e-5 absolute and bf16 within 5e-3 * max|out|; the
+multi-token append bit for bit; bitwise-identical output under a permutation of
+physical ids; and a speculative-decoding loop driven by the block manager
+(grow by T drafts, verify, roll back the rejected ones)."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_352_amd as pa
+import workloads as W
+from oracle import attention as att
+from oracle import kvcache as kvc
+from tests.gpu_util import assert_close, banner, host_bits, host_f32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def gpu_extend(b, num_splits=0):
+    """The step through libpagedattn on one stream: append the T new tokens, then attend."""
+    pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
+    return pa.paged_attn_extend(b.q, b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B, b.scale,
+                                num_splits=num_splits)
+
+
+class HostExtend:
+    """Host copies of a batch's pre-step inputs, and the oracle's answer for them."""
+
+    def __init__(self, b):
+        self.k, self.v = host_f32(b.k_pool), host_f32(b.v_pool)
+        self.q = host_f32(b.q)
+        self.k_new, self.v_new = host_f32(b.k_new), host_f32(b.v_new)
+        self.tables = b.block_tables.cpu().numpy()
+        self.lens = b.seq_lens.cpu().numpy()
+        self.pos = b.positions.cpu().numpy()
+        self.B, self.scale = b.B, b.scale
+
+    def pools_after_step(self):
+        return (kvc.append_tokens(self.k, self.k_new, self.tables, self.pos, self.B),
+                kvc.append_tokens(self.v, self.v_new, self.tables, self.pos, self.B))
+
+    def oracle(self, rows=None):
+        k, v = self.pools_after_step()
+        if rows is None:
+            return att.paged_extend(self.q, k, v, self.tables, self.lens, self.B, self.scale)
+        return att.paged_extend_rows(self.q, k, v, self.tables, self.lens, self.B, self.scale, rows)
+
+
+# lengths around tile (16) and block boundaries, shorter than T, and a few hundred
+RAGGED = [1, 2, 3, 4, 5, 15, 16, 17, 19, 31, 32, 33, 100, 257, 300]
+
+
+def check(b, dtype, what, num_splits=0):
+    host = HostExtend(b)
+    out = gpu_extend(b, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return assert_close(host_f32(out), host.oracle(), dtype, what)
+
+
+@pytest.mark.parametrize("T", [2, 3, 4])
+def test_bf16_one_item_per_group(T):
+    """G = 4: up to 4 tokens share one pass over the history (16 MFMA columns)."""
+    banner(f"extend bf16 G=4 T={T} ragged")
+    b = W.extend_batch(RAGGED, T, Hq=16, Hkv=4, seed=10 + T, device=DEV)
+    check(b, torch.bfloat16, f"bf16 T={T}")
+
+
+@pytest.mark.parametrize("G,T", [(4, 7), (4, 16), (1, 17), (1, 40), (16, 3), (8, 5), (2, 9)])
+def test_bf16_several_items_per_group(G, T):
+    banner(f"extend bf16 G={G} T={T} ragged")
+    b = W.extend_batch(RAGGED, T, Hq=2 * G, Hkv=2, seed=20 + G + T, device=DEV)
+    check(b, torch.bfloat16, f"bf16 G={G} T={T}")
+
+
+@pytest.mark.parametrize("G,T", [(4, 2), (4, 5), (1, 9), (8, 3), (2, 4)])
+def test_fp32(G, T):
+    banner(f"extend fp32 G={G} T={T} ragged")
+    b = W.extend_batch(RAGGED, T, Hq=2 * G, Hkv=2, dtype=torch.float32, seed=30 + G + T, device=DEV)
+    check(b, torch.float32, f"fp32 G={G} T={T}")
+
+
+@pytest.mark.parametrize("dtype,splits", [(torch.bfloat16, 2), (torch.bfloat16, 3), (torch.bfloat16, 7),
+                                          (torch.float32, 2), (torch.float32, 5)])
+def test_forced_splits(dtype, splits):
+    """Split boundaries inside the causal region: later splits of early tokens hold nothing."""
+    banner(f"extend {dtype} splits={splits} T=5")
+    b = W.extend_batch([16, 17, 40, 64, 65, 200, 300], 5, Hq=8, Hkv=2, dtype=dtype, seed=40 + splits,
+                       device=DEV)
+    check(b, dtype, f"splits={splits}", num_splits=splits)
+
+
+@pytest.mark.parametrize("B", [4, 8, 32, 64])
+def test_block_sizes(B):
+    banner(f"extend bf16 B={B} T=4 and fp32 T=3")
+    lens = [1, 3, 4, 5, B - 1, B, B + 1, 2 * B + 3, 150]
+    check(W.extend_batch(lens, 4, Hq=16, Hkv=4, B=B, seed=50 + B, device=DEV), torch.bfloat16, f"bf16 B={B}")
+    check(W.extend_batch(lens, 3, Hq=8, Hkv=2, B=B, dtype=torch.float32, seed=60 + B, device=DEV),
+          torch.float32, f"fp32 B={B}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_one_token_is_the_decode_step_bitwise(dtype):
+    banner(f"extend T=1 vs decode {dtype}")
+    b = W.extend_batch(RAGGED, 1, Hq=8, Hkv=2, dtype=dtype, seed=70, device=DEV)
+    pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
+    ext = pa.paged_attn_extend(b.q, b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B, b.scale)
+    dec = pa.paged_attn_decode(b.q[:, 0].contiguous(), b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B,
+                               b.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(ext[:, 0], dec)
+
+
+@pytest.mark.parametrize("dtype,T", [(torch.bfloat16, 4), (torch.bfloat16, 9), (torch.float32, 3)])
+def test_physical_permutation_is_bitwise_invisible(dtype, T):
+    banner(f"extend permutation {dtype} T={T}")
+    b = W.extend_batch(RAGGED, T, Hq=8, Hkv=2, dtype=dtype, seed=80 + T, device=DEV)
+    out1 = gpu_extend(b).clone()
+    perm = torch.randperm(b.NB, generator=torch.Generator().manual_seed(5)).to(DEV)
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(b.NB, device=DEV)
+    k2 = torch.empty_like(b.k_pool)
+    v2 = torch.empty_like(b.v_pool)
+    k2[inv] = b.k_pool  # block p moves to inv[p]
+    v2[inv] = b.v_pool
+    t2 = inv[b.block_tables.long()].to(torch.int32)
+    out2 = pa.paged_attn_extend(b.q, k2, v2, t2, b.seq_lens, b.B, b.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out1), host_bits(out2))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_append_tokens_bit_exact(dtype):
+    banner(f"kv_append_tokens bit-exact {dtype}")
+    b = W.extend_batch(RAGGED, 6, Hq=8, Hkv=2, dtype=dtype, seed=90, device=DEV)
+    k0, v0 = host_bits(b.k_pool), host_bits(b.v_pool)
+    kn, vn = host_bits(b.k_new), host_bits(b.v_new)
+    tab, pos = b.block_tables.cpu().numpy(), b.positions.cpu().numpy()
+    pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(b.k_pool), kvc.append_tokens(k0, kn, tab, pos, b.B))
+    assert np.array_equal(host_bits(b.v_pool), kvc.append_tokens(v0, vn, tab, pos, b.B))
+
+
+def test_verify_32x4096_T4_sampled():
+    """The verification batch at full size (the launch the benchmark times), sampled requests."""
+    banner("verify bf16 32x4096 T=4 (bench launch configuration), sampled rows")
+    b = W.verify_batch(device=DEV)
+    host = HostExtend(b)
+    out = host_f32(gpu_extend(b))
+    rows = [0, 13, 31]
+    ref = host.oracle(rows)
+    assert_close(np.stack([out[s] for s in rows]), np.stack([ref[s] for s in rows]), torch.bfloat16, "verify")
+    assert np.all(np.isfinite(out))
+
+
+def test_prefill_chunk_512_sampled():
+    """A 512-token prompt chunk over 3584 tokens of history, 8 requests; one sampled request."""
+    banner("prefill chunk bf16 8x4096 T=512, sampled row")
+    b = W.prefill_chunk_batch(device=DEV)
+    host = HostExtend(b)
+    out = host_f32(gpu_extend(b))
+    rows = [5]
+    ref = host.oracle(rows)
+    assert_close(np.stack([out[s] for s in rows]), np.stack([ref[s] for s in rows]), torch.bfloat16, "chunk")
+    assert np.all(np.isfinite(out))
+
+
+def test_speculative_loop_with_rollback():
+    """Branches over a shared 1029-token prefix; each step reserves T = 4 draft
+    positions (copying a shared partial tail first), appends the drafts, verifies
+    them with one paged_attn_extend, then keeps a random number of them and rolls
+    the rest back.  Every step's output is compared with dense attention on the
+    branch's own accepted history plus its drafts, kept on the host."""
+    banner("speculative loop: 4 branches, 10 steps, T=4 drafts, rollback")
+    rng = np.random.default_rng(91)
+    NB, B, MB, Hq, Hkv, D, T = 256, 16, 80, 16, 4, 128, 4
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    bm = pa.BlockManager(NB, B, MB, rng.permutation(NB).astype(np.int32))
+    k_pool = torch.full((NB, B, Hkv, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    v_pool = torch.full_like(k_pool, float("nan"))
+
+    def rand(*shape):
+        return torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(torch.bfloat16)
+
+    parent = bm.add_request()
+    n0 = 1024 + 5
+    bm.reserve(parent, n0)
+    tab, _ = bm.export([parent])
+    k_hist, v_hist = rand(n0, Hkv, D), rand(n0, Hkv, D)
+    t = np.arange(n0)
+    blk = torch.as_tensor(tab[0][t // B], dtype=torch.long, device=DEV)
+    slot = torch.as_tensor(t % B, dtype=torch.long, device=DEV)
+    k_pool[blk, slot] = k_hist.to(DEV)  # prefill placement is test set-up
+    v_pool[blk, slot] = v_hist.to(DEV)
+    branches = [parent] + [bm.fork(parent) for _ in range(3)]
+    hist = {r: (k_hist.clone(), v_hist.clone()) for r in branches}
+    copies = 0
+    for step in range(10):
+        pos, (cs, cd, cn) = bm.prepare_extend(branches, T)
+        copies += len(cs)
+        tables, lens = bm.export(branches)
+        S = len(branches)
+        if len(cs):
+            pa.kv_cow_copy(k_pool, v_pool, *(torch.as_tensor(x, device=DEV) for x in (cs, cd, cn)), B)
+        k_new, v_new, q = rand(S, T, Hkv, D), rand(S, T, Hkv, D), rand(S, T, Hq, D)
+        t_tab = torch.as_tensor(tables, device=DEV)
+        pa.kv_append_tokens(k_pool, v_pool, k_new.to(DEV), v_new.to(DEV), t_tab, torch.as_tensor(pos, device=DEV), B)
+        out = pa.paged_attn_extend(q.to(DEV), k_pool, v_pool, t_tab, torch.as_tensor(lens, device=DEV), B, scale)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        for i, r in enumerate(branches):
+            kh = torch.cat([hist[r][0], k_new[i]])
+            vh = torch.cat([hist[r][1], v_new[i]])
+            assert lens[i] == kh.shape[0] == pos[i] + T
+            ref = att.extend_attention(q[i].float().numpy(), kh.float().numpy(), vh.float().numpy(), scale)
+            err = float(np.max(np.abs(got[i] - ref)))
+            assert np.all(np.isfinite(got[i])) and err <= 5e-3 * float(np.max(np.abs(ref))), (step, i, err)
+            keep = int(rng.integers(0, T + 1))  # drafts accepted this step
+            bm.truncate(r, int(pos[i]) + keep)
+            hist[r] = (kh[: int(pos[i]) + keep], vh[: int(pos[i]) + keep])
+        bm.check()
+    # the first step copies the shared 5-token tail for all but the last branch
+    assert copies >= 3

@@ -16,3 +16,4 @@ from .decode import (  # noqa: F401
     custom,
     make_config,
 )
+from .extend import ExtendBatch, extend_batch, prefill_chunk_batch, verify_batch  # noqa: F401

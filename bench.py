@@ -27,7 +27,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "paged decode attention KV GB/s (% of MI355X HBM peak) + tokens/s per layer"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_bf16_32x4096_traffic.txt")
-KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_352_amd", "csrc", f) for f in ("pa_decode.hip", "pa_decode_mfma.hip")]
+KERNEL_SRCS = [os.path.join(ROOT, "paged_kv_cache_352_amd", "csrc", f)
+               for f in ("pa_decode.hip", "pa_decode_mfma.hip", "pa_mfma_common.h")]
 
 
 def log(*a):
@@ -35,7 +36,7 @@ def log(*a):
 
 
 def kernel_sha():
-    """sha256 over the decode kernel sources, in a fixed order."""
+    """sha256 over the decode kernel sources (kernels, shared device helpers), in a fixed order."""
     h = hashlib.sha256()
     for f in KERNEL_SRCS:
         h.update(open(f, "rb").read())

@@ -365,8 +365,13 @@ size_t decode_workspace_floats(int64_t rows, int P) { return (size_t)rows * P * 
 hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int B, int G, hipStream_t stream) {
   // bf16: q.k and p.v on the matrix cores; fp32: the vector-ALU kernel.
   const bool causal = a.T > 1;
-  hipError_t e = dtype == PA_BF16 ? launch_decode_mfma(a, B, G, causal, stream)
-                                  : (causal ? launch_valu<true>(a, B, G, stream) : launch_valu<false>(a, B, G, stream));
+  hipError_t e;
+  if (use_shared_tile(dtype, G, a.T))
+    e = launch_extend_shared(a, B, G, stream);
+  else if (dtype == PA_BF16)
+    e = launch_decode_mfma(a, B, G, causal, stream);
+  else
+    e = causal ? launch_valu<true>(a, B, G, stream) : launch_valu<false>(a, B, G, stream);
   if (e != hipSuccess || a.P == 1) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(a.S * a.T * a.Hq), dim3(kWave), 0, stream, a);
   return hipGetLastError();

@@ -69,77 +69,20 @@
 // the XCD-aware numbering keeps on one L2.
 #include <hip/hip_runtime.h>
 
-#include "pa_internal.h"
+#include "pa_mfma_common.h"
 
 namespace pa {
 namespace {
 
-constexpr int kWave = 64;
-constexpr int kTile = 16;  // slots per MFMA tile (the M dimension of q.k)
-constexpr float kNegInf = -__builtin_huge_valf();
-
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-#define PA_LDS __attribute__((address_space(3)))
-
-// K or V tile in LDS: slot t, dims 8k .. 8k+7 (16-byte chunk k) at byte
-//   256 * t + 16 * (k ^ t).
-// The XOR spreads the row-wise 16-byte writes, the 16-byte K operand reads
-// and the transposing 8-byte V reads of one instruction evenly over the banks.
-constexpr int kVtBytes = kTile * kHeadDim * 2;  // 4096
+using namespace mfma;
 
 // K/V tiles in flight per wave.
 constexpr int kDepth = 2;
-
-__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ inline int xcd_remap(int bid, int nwg) {
-  const int x = bid % kNumXcd, k = bid / kNumXcd;
-  const int q = nwg / kNumXcd, rem = nwg % kNumXcd;
-  return x * q + min(x, rem) + k;
-}
-
-// bf16 head of an fp32 value by truncation, and the remainder's head:
-// x - hi is exact in fp32 and lo = trunc(x - hi) leaves |x - hi - lo| < 2^-16 |x|.
-__device__ inline void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const uint32_t b0 = __float_as_uint(x0) & 0xffff0000u;
-  const uint32_t b1 = __float_as_uint(x1) & 0xffff0000u;
-  const float r0 = x0 - __uint_as_float(b0);
-  const float r1 = x1 - __uint_as_float(b1);
-  hi = (b0 >> 16) | b1;
-  lo = (__float_as_uint(r0) >> 16) | (__float_as_uint(r1) & 0xffff0000u);
-}
-
-// Orders this wave's LDS accesses around it without waiting for anything:
-// one wave's LDS operations execute in issue order, so only the compiler has
-// to be kept from moving them.
-__device__ inline void wave_lds_order() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 struct Tile {
   uint4 k[4];
   uint4 v[4];
 };
-
-// K/V tiles are read with buffer loads: a descriptor for one physical block
-// (uniform, in SGPRs) plus a 32-bit per-lane byte offset, so the per-lane
-// addresses are four constant registers instead of a 64-bit address per load.
-// The descriptor's size is the block's byte count: the hardware returns zero
-// for any offset past it.
-constexpr int kBufferFlags = 0x00020000;  // word 3 of a raw buffer descriptor on CDNA (32-bit data format)
-
-__device__ inline __amdgpu_buffer_rsrc_t block_rsrc(const char* block, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(block), (short)0, (int)bytes, kBufferFlags);
-}
-
-__device__ inline uint4 load_kv16(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, soff, 0));
-}
 
 template <int G, bool kCausal, int W, int B>
 __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
@@ -259,18 +202,10 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) acc[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // LDS addresses.  Writes: slot 4*i + c4, chunk n16.  K operand reads: slot
-  // n16, chunk 4*i + c4.  Transposing V reads for output dims 16*jj + n16:
-  // this lane fetches slot r = 4*c4 + n16/4, dims 16*jj + 4*(n16%4) .. +3,
-  // i.e. half (n16 & 1) of chunk 2*jj + (n16%4)/2.
+  // Writes: slot 4*i + c4, chunk n16 of this wave's tile; reads as in TileReads.
   uint8_t* vt = vt_all[w];
-  const int rr = 4 * c4 + (n16 >> 2);
-  const PA_LDS uint8_t* vt_r = (const PA_LDS uint8_t*)vt + 256 * rr + 8 * (n16 & 1);
-  const int bsel = ((n16 & 3) >> 1) ^ (rr & 1);  // low bit of the swizzled chunk
-  const int rhi = rr & 14;                       // the rest of the swizzle
-
   uint8_t* kt = kt_all[w];
-  const PA_LDS uint8_t* kt_r = (const PA_LDS uint8_t*)kt + 256 * n16;  // K reads: slot n16
+  const TileReads rd(kt, vt, n16, c4);
 
   auto process = [&](int u, Tile& cur) {
     const int valid = n - u * kTile;  // >= 1
@@ -284,64 +219,9 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
       *reinterpret_cast<uint4*>(vt + 256 * r + 16 * (n16 ^ r)) = vv;
     }
     wave_lds_order();
-    f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4_t kv = *reinterpret_cast<const PA_LDS u32x4_t*>(kt_r + 16 * ((4 * i + c4) ^ n16));
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qv[i], sc, 0, 0, 0);
-    }
-
-    // Scores in base 2, masked past the length ([Slides] quiz "逻辑顺序没错…")
-    // or, for several query tokens, past this column's own position.
-    const int vq = kCausal ? lim - u * kTile : valid;
-    float sv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = (4 * c4 + r < vq) ? sc[r] * a.scale_log2 : kNegInf;
-
-    // [Budgets] eq. (4): tile max over the 16 slots of head n16, new running max.
-    float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
-    bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
-    const float mn = fmaxf(m, bm);  // decode: finite, slot 0 of a tile below nt is valid
-    float alpha, mref = mn;
-    if constexpr (kCausal) {
-      // a column may have seen nothing yet (mn = -inf): keep its empty state
-      alpha = (m == mn) ? 1.f : fast_exp2(m - mn);
-      mref = (mn == kNegInf) ? 0.f : mn;
-    } else {
-      alpha = fast_exp2(m - mn);
-    }
-    m = mn;
-    float pw[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pw[r] = fast_exp2(sv[r] - mref);
-    l = fmaf(l, alpha, (pw[0] + pw[1]) + (pw[2] + pw[3]));
-
-    uint32_t hi0, hi1, lo0, lo1;
-    split_pair(pw[0], pw[1], hi0, lo0);
-    split_pair(pw[2], pw[3], hi1, lo1);
-    const s16x4_t phi = __builtin_bit_cast(s16x4_t, make_uint2(hi0, hi1));
-    const s16x4_t plo = __builtin_bit_cast(s16x4_t, make_uint2(lo0, lo1));
-
-    // Rescale o only where a head's max moved (alpha < 1 somewhere in the wave).
-    if (__any(alpha != 1.f)) {
-      float ar[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * c4 + r, kWave);
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[jj][r] *= ar[r];
-    }
-
-    wave_lds_order();  // this tile's V is in LDS
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int chunk = ((2 * jj) ^ rhi) | bsel;
-      const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(vt_r + 16 * chunk));
-      acc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vb, acc[jj], 0, 0, 0);
-      acc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vb, acc[jj], 0, 0, 0);
-    }
+    // Mask past the length or, for several query tokens, past this column's
+    // own position (then a column may have no valid slot yet).
+    tile_update<kCausal>(rd, qv, acc, m, l, kCausal ? lim - u * kTile : valid, a.scale_log2, n16, c4);
   };
 
   // The wave's tiles are walked in chunks whose table entries fit one

@@ -1,0 +1,243 @@
+// Several query tokens per request on the matrix cores, with each K/V tile
+// shared by the waves of a workgroup.
+//
+// [Slides]  = "PagedAttention：让 KV cache 按需生长"
+// [Budgets] = "内存预算约束下的语言模型服务：注意力、分页与调度"
+// [Serving] = "PagedAttention 与在线推理：KV 分页、共享及调度的联合分析"
+//
+// What is computed is the causal form of paged_attn_extend ([Serving] §5:
+// speculative verification and prompt chunks read the same paged history as
+// a decode step): the T new tokens are the last T positions of the n-token
+// history, token i attends positions 0 .. n-T+i, each block is found through
+// the table, slots past a column's limit are masked, and blocks fold into the
+// (m, l, o) state of [Budgets] eq. (4); splits of the history are merged
+// afterwards as for the decode.
+//
+// When the (token, head) pairs of a request's KV head outnumber the 16
+// columns of one MFMA tile, the one-wave-per-column-set decode layout would
+// stream the history once per 16 columns.  Here a workgroup of 4 waves takes
+// 4 column sets (4 * 16/G tokens of the G-head group) and walks one split of
+// the history tile by tile: every tile's K and V are loaded once, each wave
+// fetching one group of 4 slot rows (16-byte lanes along a row, as in the
+// decode kernel), written to a double-buffered LDS tile in the swizzled
+// layout, and after one workgroup barrier every wave runs the q.k / softmax /
+// p.v step for its own columns on the whole tile.  With two LDS buffers one
+// barrier per tile suffices: a wave overwrites buffer b only after the
+// barrier of the next tile, which no wave passes before it has finished
+// reading b.  Each wave owns its columns, so no state is merged inside the
+// workgroup.
+#include <hip/hip_runtime.h>
+
+#include "pa_mfma_common.h"
+
+namespace pa {
+namespace {
+
+using namespace mfma;
+
+constexpr int kWaves = kSharedTileWaves;  // = row groups of 4 slots per 16-slot tile
+static_assert(kWaves * 4 == kTile, "each wave loads one 4-row group of a tile");
+constexpr int kDepth = 2;  // tiles in flight per workgroup (one 16-byte K and V load per lane each)
+
+template <int G, int B>
+__global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArgs a) {
+  static_assert(G >= 1 && G <= 16, "the query group must fit the 16 columns of one MFMA tile");
+  static_assert(B >= 4 && B <= 64 && (B & (B - 1)) == 0, "block size: a power of two from 4 to 64");
+  constexpr int TC = G >= 16 ? 1 : 16 / G;  // query tokens per wave
+  constexpr int TW = kWaves * TC;           // query tokens per workgroup
+  // [buffer][K, V][tile]
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[2][2][kVtBytes];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int n16 = lane & 15;
+  const int c4 = lane >> 4;
+
+  int item = xcd_remap(blockIdx.x, gridDim.x);
+  const int p = item % a.P;
+  item /= a.P;
+  const int tw = item % a.TG;  // which TW query tokens of the request
+  item /= a.TG;
+  const int s = item % a.S;
+  const int kvh = item / a.S;
+
+  const int n_raw = a.lens[s];
+  bool bad = n_raw < 0 || (int64_t)n_raw > (int64_t)a.MB * B;
+  const int n = bad ? 0 : n_raw;
+  const int nb = (n + B - 1) / B;
+  // Column n16 of wave w is query token tq, head kvh*G + n16%G, and may see
+  // the first lim positions; the workgroup needs the tiles up to its last
+  // token's limit.
+  const int tq = tw * TW + w * TC + n16 / G;
+  const int lim = tq < a.T ? min(n, max(0, n - a.T + 1 + tq)) : n;
+  const int lim_hi = min(n, max(0, n - a.T + min(a.T, tw * TW + TW)));
+  const int nt = (lim_hi + kTile - 1) / kTile;
+  const int u0 = p * (a.tps / kTile);
+  const int u1 = min(nt, u0 + a.tps / kTile);  // the same range for every wave
+
+  bf16x8_t qv[4];
+  {
+    const bool live = tq < a.T;  // columns past T get q = 0 and are never stored
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         (((int64_t)s * a.T + min(tq, a.T - 1)) * a.Hq + (int64_t)kvh * G + n16 % G) * kHeadDim;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 v = *reinterpret_cast<const uint4*>(qp + 32 * i + 8 * c4);
+      if (!live) v = make_uint4(0, 0, 0, 0);
+      qv[i] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  // This wave loads slot rows 4w .. 4w+3 of every tile: lane l takes row
+  // 4w + c4, bytes 16*n16 .. +16 (KV head kvh).
+  const int row_bytes = a.Hkv * kHeadDim * 2;
+  const uint32_t blk_bytes = (uint32_t)B * (uint32_t)row_bytes;
+  const uint32_t voff = (uint32_t)(c4 * row_bytes + (kvh * kHeadDim + 8 * n16) * 2);
+  const char* kpool = static_cast<const char*>(a.k_pool);
+  const char* vpool = static_cast<const char*>(a.v_pool);
+  const int32_t* trow = a.tables + (int64_t)s * a.MB;
+  auto pool_block = [&](int pb) {
+    if (pb < 0 || pb >= a.NB) {  // outside the pool: never dereferenced, result poisoned
+      bad = true;
+      pb = 0;
+    }
+    return pb;
+  };
+  // Rows past the history (only in the last tile, B < 16) read the history's
+  // last block instead and are zeroed or masked; no table entry at or past
+  // ceil(n / B) is read.
+  auto load_rows = [&](int u, uint4& k, uint4& v, int eb, int tab) {
+    if constexpr (B >= kTile) {
+      const int pb = pool_block(__builtin_amdgcn_readlane(tab, (kTile * u) / B - eb));
+      const int soff = ((kTile * u) % B + 4 * w) * row_bytes;
+      k = load_kv16(block_rsrc(kpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
+      v = load_kv16(block_rsrc(vpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
+    } else {
+      const int tok = kTile * u + 4 * w;
+      const bool live = tok < n;
+      const int pb = pool_block(__builtin_amdgcn_readlane(tab, (live ? tok : n - 1) / B - eb));
+      const int soff = live ? (tok % B) * row_bytes : 0;
+      k = load_kv16(block_rsrc(kpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
+      v = load_kv16(block_rsrc(vpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
+    }
+  };
+
+  float m = kNegInf;
+  float l = 0.f;
+  f32x4_t acc[8];
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) acc[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const TileReads rd0(tiles[0][0], tiles[0][1], n16, c4);
+  const int r_own = 4 * w + c4;                     // the slot row this lane writes
+  const int w_off = 256 * r_own + 16 * (n16 ^ r_own);  // its swizzled byte offset in a tile
+
+  // Tile t: write this lane's row of K and V into buffer t & 1, wait for the
+  // other waves' rows, then fold the tile into this wave's columns.
+  auto process = [&](int t, const uint4& k, const uint4& v) {
+    const int buf = t & 1;
+    uint8_t* kt = tiles[buf][0];
+    uint8_t* vt = tiles[buf][1];
+    *reinterpret_cast<uint4*>(kt + w_off) = k;
+    *reinterpret_cast<uint4*>(vt + w_off) = r_own < n - t * kTile ? v : make_uint4(0, 0, 0, 0);
+    __syncthreads();
+    TileReads rd = rd0;
+    rd.k += buf * (2 * kVtBytes);
+    rd.v += buf * (2 * kVtBytes);
+    tile_update<true>(rd, qv, acc, m, l, lim - t * kTile, a.scale_log2, n16, c4);
+  };
+
+  // Table entries are read 64 at a time into one register (one per lane), as
+  // in the decode kernel: chunks of 64 tiles for B >= 16, 4*B tiles below.
+  // Within a chunk tile t + kDepth - 1 is requested before tile t is used.
+  constexpr int kChunkTiles = B >= kTile ? kWave : 4 * B;
+  for (int tb = u0; tb < u1; tb += kChunkTiles) {
+    const int te = min(u1, tb + kChunkTiles);
+    const int eb = (kTile * tb) / B;
+    const int tab = trow[min(eb + lane, nb - 1)];
+    uint4 kq[kDepth], vq[kDepth];
+#pragma unroll
+    for (int b = 0; b + 1 < kDepth; ++b) load_rows(min(tb + b, te - 1), kq[b], vq[b], eb, tab);
+    for (int t = tb; t < te; t += kDepth) {
+#pragma unroll
+      for (int b = 0; b < kDepth; ++b) {
+        constexpr int kNext = kDepth - 1;
+        load_rows(min(t + b + kNext, te - 1), kq[(b + kNext) % kDepth], vq[(b + kNext) % kDepth], eb, tab);
+        __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the current tile's math
+        process(t + b, kq[b], vq[b]);
+        if (t + b + 1 >= te) break;
+      }
+    }
+  }
+
+  // Full l of column n16: sum the partials of its four lanes.
+  l += __shfl_xor(l, 16, kWave);
+  l += __shfl_xor(l, 32, kWave);
+  bad = __syncthreads_or(bad);  // any wave that met an entry outside the pool
+
+  const float nan = __builtin_nanf("");
+  if (a.P == 1) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int col = 4 * c4 + r;
+      const float lc = __shfl(l, col, kWave);
+      const int t_out = tw * TW + w * TC + col / G;
+      if (t_out < a.T) {
+        const float inv = lc > 0.f ? 1.f / lc : 0.f;
+        float* dst = a.out + (((int64_t)s * a.T + t_out) * a.Hq + kvh * G + col % G) * kHeadDim + n16;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) dst[16 * jj] = bad ? nan : acc[jj][r] * inv;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int col = 4 * c4 + r;
+      const int t_out = tw * TW + w * TC + col / G;
+      if (t_out < a.T) {
+        const int64_t slot = (((int64_t)s * a.T + t_out) * a.Hq + kvh * G + col % G) * a.P + p;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) a.ws_o[slot * kHeadDim + 16 * jj + n16] = acc[jj][r];
+      }
+    }
+    if (c4 == 0 && tq < a.T) {  // lane n16 holds column n16's m and l
+      const int64_t slot = (((int64_t)s * a.T + tq) * a.Hq + kvh * G + n16 % G) * a.P + p;
+      a.ws_m[slot] = bad ? 0.f : m;
+      a.ws_l[slot] = bad ? nan : l;
+    }
+  }
+}
+
+template <int G, int B>
+hipError_t launch_gb(const DecodeArgs& a, hipStream_t stream) {
+  const int items = a.Hkv * a.S * a.P * a.TG;
+  hipLaunchKernelGGL((extend_shared_kernel<G, B>), dim3(items), dim3(kWave * kWaves), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int B>
+hipError_t launch_b(const DecodeArgs& a, int G, hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_gb<1, B>(a, stream);
+    case 2: return launch_gb<2, B>(a, stream);
+    case 4: return launch_gb<4, B>(a, stream);
+    case 8: return launch_gb<8, B>(a, stream);
+    case 16: return launch_gb<16, B>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_extend_shared(const DecodeArgs& a, int B, int G, hipStream_t stream) {
+  switch (B) {
+    case 4: return launch_b<4>(a, G, stream);
+    case 8: return launch_b<8>(a, G, stream);
+    case 16: return launch_b<16>(a, G, stream);
+    case 32: return launch_b<32>(a, G, stream);
+    case 64: return launch_b<64>(a, G, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

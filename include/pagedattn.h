@@ -102,8 +102,9 @@ pa_status paged_attn_plan(const pa_dims* dims, int32_t B, int32_t* num_splits,
  *   out[s,h,:] = sum_t softmax_t(scale * <q[s,h,:], K_s[t,g,:]>) * V_s[t,g,:],
  * t over the seq_lens[s] tokens of request s, g = h / (Hq/Hkv), where token t
  * lives in slot t % B of physical block block_tables[s][t / B] ([Slides]
- * "读 token 6，先查表，再找偏移").  Table entries at or past ceil(n/B) are not
- * read; slots of the last block at or past n are masked and their contents
+ * "读 token 6，先查表，再找偏移").  Table entries at or past ceil(n/B) never
+ * address the pools (their values may be anything; the row's MB entries must
+ * be readable); slots of the last block at or past n are masked and their contents
  * never enter the result ([Slides] "分页以后，attention 仍然按完整历史归一化",
  * quiz "逻辑顺序没错，为什么 attention 输出还是错？").  Blocks are combined with
  * the online-softmax state of [Budgets] eq. (4); long histories are divided

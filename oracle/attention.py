@@ -19,7 +19,7 @@ Array conventions (any float dtype in, float64 out):
 Readings of points the pages leave open:
   * GQA mapping: query head h reads KV head h // (Hq / Hkv) (contiguous groups).
   * A request with no tokens attends to nothing: its output is exactly 0.
-  * Table entries at or beyond ceil(n / B) are never read.
+  * Table entries at or beyond ceil(n / B) are never used.
 """
 
 import numpy as np

@@ -176,6 +176,7 @@ static pa_status attend(const void* q, const void* k_pool, const void* v_pool, c
   const int64_t items = (int64_t)dims->num_kv_heads * dims->num_seqs * P * TG;
   const int64_t rows = (int64_t)dims->num_seqs * T * dims->num_q_heads;
   if (items > INT32_MAX || rows > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  if (dims->num_seqs > (1 << 28)) return fail(PA_ERR_UNSUPPORTED, "more than 2^28 requests");  // 32-bit byte offsets
 
   pa::DecodeArgs a{};
   a.q = q;

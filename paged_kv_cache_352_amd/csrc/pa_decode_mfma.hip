@@ -14,9 +14,12 @@
 // Work decomposition.  The history is cut into 16-slot tiles (the M
 // dimension of the q.k MFMA), whatever the block size B (a power of two from
 // 4 to 64: a tile is part of one block, or spans 16/B blocks).  One workgroup
-// of W waves per (request s, KV head g, split p); wave w takes a contiguous
-// share of the split's tiles, keeps its own (m, l, o), and the W states are
-// merged through LDS at the end.  With one split the workgroup writes the
+// of W waves per (request s, KV head g, split p); the split's tiles are dealt
+// to the waves in turn (wave w takes tiles w, w + W, ...), each wave keeps
+// its own (m, l, o), and the W states are merged through LDS at the end.
+// Which tiles a wave takes depends only on the split, not on the length, so
+// its first table entries and first tile are requested before the length
+// has arrived.  With one split the workgroup writes the
 // final output; with several it writes its merged state and a second kernel
 // merges the splits.
 //
@@ -112,25 +115,8 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   const int s = item % a.S;
   const int kvh = item / a.S;
 
-  const int n_raw = a.lens[s];
-  bool bad = n_raw < 0 || (int64_t)n_raw > (int64_t)a.MB * B;
-  const int n = bad ? 0 : n_raw;
-  const int nb = (n + B - 1) / B;  // blocks holding the history
-  // Column n16 is query token tq, head kvh*G + n16%G; it may see the first
-  // lim positions.  The item needs the tiles up to its last token's limit.
+  // Column n16 is query token tq, head kvh*G + n16%G.
   const int tq = tg * TC + n16 / G;
-  int lim = n, lim_hi = n;
-  if constexpr (kCausal) {
-    lim = tq < a.T ? min(n, max(0, n - a.T + 1 + tq)) : n;
-    lim_hi = min(n, max(0, n - a.T + min(a.T, tg * TC + TC)));
-  }
-  const int nt = (lim_hi + kTile - 1) / kTile;  // 16-slot tiles this item reads
-  const int u0 = p * (a.tps / kTile);
-  const int u1 = min(nt, u0 + a.tps / kTile);
-  // This wave's tiles: a contiguous share [ua, ub) of the split's tiles.
-  const int share = u1 > u0 ? (u1 - u0 + W - 1) / W : 0;
-  const int ua = min(u1, u0 + w * share);
-  const int ub = min(u1, ua + share);
 
   // q of column n16 over the dims this lane contributes, as MFMA B operands.
   bf16x8_t qv[4];
@@ -149,6 +135,13 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
     }
   }
 
+  // The length of the request, then (below) its first table entries and
+  // first tile: the length is read with a vector (buffer) load so that it
+  // is in flight together with the entries instead of waiting behind them.
+  const int n_raw = __builtin_amdgcn_readfirstlane(
+      (int)__builtin_amdgcn_raw_buffer_load_b32(block_rsrc(reinterpret_cast<const char*>(a.lens), (uint32_t)a.S * 4u),
+                                                0, s * 4, 0));
+
   // Byte offsets inside a block (a block is at most a few hundred KiB, so 32
   // bits suffice).  A load is a block descriptor (uniform, in SGPRs) plus the
   // lane's offset (slot c4 of the row group, KV head kvh, dims 8*n16) plus
@@ -160,22 +153,38 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   const char* vpool = static_cast<const char*>(a.v_pool);
   const int32_t* trow = a.tables + (int64_t)s * a.MB;
 
-  // Issue the 8 16-byte loads of the K and V rows of tile u: row group i is
-  // slots 16*u + 4*i .. +3.  `tab` holds table entries eb, eb+1, ... one per
-  // lane.  With B >= 16 the tile lies inside one block; with B < 16 each row
-  // group has its own block, and a group past the history reads the last
-  // block of the history instead (its rows are masked), so no table entry at
-  // or past ceil(n / B) is ever read.
-  auto pool_block = [&](int pb) {
+  // The split's tiles are dealt to the waves in turn: the k-th tile of wave
+  // w is u0 + w + W*k.  Table entries are read 64 at a time into one
+  // register: lane j holds entry j % E of the wave's tile kb + j / E, with
+  // E = 16/B entries per tile below B = 16 (one per 4-row group's block
+  // pair or quad) and one above.
+  constexpr int E = B >= kTile ? 1 : kTile / B;
+  constexpr int kChunk = kWave / E;  // wave tiles per register of entries
+  const int u0 = p * (a.tps / kTile);
+  auto wave_tile = [&](int k) { return u0 + w + W * k; };
+  auto lane_entry = [&](int kb) { return (kTile * wave_tile(kb + lane / E)) / B + lane % E; };
+
+  // Issue the 8 16-byte loads of the K and V rows of the wave's k-th tile:
+  // row group i is slots 16*u + 4*i .. +3.  With B >= 16 the tile lies
+  // inside one block; with B < 16 each row group has its own block, and a
+  // group past the history reads the tile's first block instead (its rows
+  // are masked), so no table entry at or past ceil(n / B) addresses the
+  // pool.  A speculative load (issued before the length is known) clamps a
+  // block id outside the pool to block 0 without judging it: it is judged
+  // once the length says whether the tile is part of the history.
+  bool bad = false;
+  auto pool_block = [&](int pb, bool judge) {
     if (pb < 0 || pb >= a.NB) {  // outside the pool: never dereferenced, result poisoned
-      bad = true;
+      bad = bad || judge;
       pb = 0;
     }
     return pb;
   };
-  auto load_tile = [&](int u, Tile& t, int eb, int tab) {
+  int n = 0;
+  auto load_tile = [&](int k, int kb, Tile& t, int tab, bool spec) {
+    const int u = wave_tile(k);
     if constexpr (B >= kTile) {
-      const int pb = pool_block(__builtin_amdgcn_readlane(tab, (kTile * u) / B - eb));
+      const int pb = pool_block(__builtin_amdgcn_readlane(tab, k - kb), !spec);
       const __amdgpu_buffer_rsrc_t kr = block_rsrc(kpool + (int64_t)pb * blk_bytes, blk_bytes);
       const __amdgpu_buffer_rsrc_t vr = block_rsrc(vpool + (int64_t)pb * blk_bytes, blk_bytes);
       const int row0 = (kTile * u) % B;
@@ -187,14 +196,46 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = kTile * u + 4 * i;
-        const bool live = tok < n;
-        const int pb = pool_block(__builtin_amdgcn_readlane(tab, (live ? tok : n - 1) / B - eb));
+        const bool live = spec || tok < n;
+        const int pb = pool_block(__builtin_amdgcn_readlane(tab, (k - kb) * E + (live ? (4 * i) / B : 0)), !spec);
         const int soff = live ? (tok % B) * row_bytes : 0;
         t.k[i] = load_kv16(block_rsrc(kpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
         t.v[i] = load_kv16(block_rsrc(vpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
       }
     }
   };
+
+  // The first register of entries and the wave's first tile depend only on
+  // the split, not on the length: request them before the length arrives,
+  // so a work item waits for two dependent reads (entries, then tile)
+  // instead of three.  Entries read past the history are never used.
+  Tile ring[kDepth];
+  int tab = trow[min(lane_entry(0), a.MB - 1)];
+  load_tile(0, 0, ring[0], tab, true);
+
+  bad = n_raw < 0 || (int64_t)n_raw > (int64_t)a.MB * B;
+  n = bad ? 0 : n_raw;
+  const int nb = (n + B - 1) / B;  // blocks holding the history
+  // Column n16 may see the first lim positions.  The item needs the tiles up
+  // to its last token's limit.
+  int lim = n, lim_hi = n;
+  if constexpr (kCausal) {
+    lim = tq < a.T ? min(n, max(0, n - a.T + 1 + tq)) : n;
+    lim_hi = min(n, max(0, n - a.T + min(a.T, tg * TC + TC)));
+  }
+  const int nt = (lim_hi + kTile - 1) / kTile;  // 16-slot tiles this item reads
+  const int u1 = min(nt, u0 + a.tps / kTile);
+  const int K = u1 > u0 + w ? (u1 - u0 - w + W - 1) / W : 0;  // this wave's tiles
+  if (K > 0) {
+    // judge the entries the speculative first tile used
+    if constexpr (B >= kTile) {
+      pool_block(__builtin_amdgcn_readlane(tab, 0), true);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (kTile * wave_tile(0) + 4 * i < n) pool_block(__builtin_amdgcn_readlane(tab, (4 * i) / B), true);
+    }
+  }
 
   float m = kNegInf;  // running max (base 2) of head n16
   float l = 0.f;      // partial sum over this lane's slots
@@ -224,27 +265,25 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
     tile_update<kCausal>(rd, qv, acc, m, l, kCausal ? lim - u * kTile : valid, a.scale_log2, n16, c4);
   };
 
-  // The wave's tiles are walked in chunks whose table entries fit one
-  // register (64 entries, one per lane, read out with readlane): 64 tiles for
-  // B >= 16, 4*B tiles below.  Within a chunk kDepth tiles are in flight:
-  // tile t + kDepth - 1 is loaded before tile t is processed (the load index
-  // is clamped, never conditional, so the wait before each tile covers only
-  // that tile's loads).
-  constexpr int kChunkTiles = B >= kTile ? kWave : 4 * B;
-  for (int tb = ua; tb < ub; tb += kChunkTiles) {
-    const int te = min(ub, tb + kChunkTiles);
-    const int eb = (kTile * tb) / B;
-    const int tab = trow[min(eb + lane, nb - 1)];  // lanes past the history repeat its last entry
-    Tile tq[kDepth];
+  // The wave's tiles are walked one register of table entries at a time.
+  // Within a register kDepth tiles are in flight: tile k + kDepth - 1 is
+  // loaded before tile k is processed (the load index is clamped, never
+  // conditional, so the wait before each tile covers only that tile's loads).
+  for (int kb = 0; kb < K; kb += kChunk) {
+    const int ke = min(K, kb + kChunk);
+    if (kb > 0) {
+      tab = trow[min(lane_entry(kb), nb - 1)];
+      load_tile(kb, kb, ring[0], tab, false);
+    }
 #pragma unroll
-    for (int b = 0; b + 1 < kDepth; ++b) load_tile(min(tb + b, te - 1), tq[b], eb, tab);
-    for (int t = tb; t < te; t += kDepth) {
+    for (int b = 1; b + 1 < kDepth; ++b) load_tile(min(kb + b, ke - 1), kb, ring[b], tab, false);
+    for (int k = kb; k < ke; k += kDepth) {
 #pragma unroll
       for (int b = 0; b < kDepth; ++b) {
-        load_tile(min(t + b + kDepth - 1, te - 1), tq[(b + kDepth - 1) % kDepth], eb, tab);
+        load_tile(min(k + b + kDepth - 1, ke - 1), kb, ring[(b + kDepth - 1) % kDepth], tab, false);
         __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the current tile's math
-        process(t + b, tq[b]);
-        if (t + b + 1 >= te) break;
+        process(wave_tile(k + b), ring[b]);
+        if (k + b + 1 >= ke) break;
       }
     }
   }

@@ -87,12 +87,15 @@ struct Tile {
   uint4 v[4];
 };
 
-template <int G, bool kCausal, int W, int B>
+// NS: 16-column sets per wave (2 only with several query tokens: each K and
+// V operand a wave reads from LDS then feeds both sets).
+template <int G, bool kCausal, int NS, int W, int B>
 __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   static_assert(G >= 1 && G <= 16, "the query group must fit the 16 columns of one MFMA tile");
   static_assert(B >= 4 && B <= 64 && (B & (B - 1)) == 0, "block size: a power of two from 4 to 64");
-  constexpr int TC = kCausal ? (G >= 16 ? 1 : 16 / G) : 1;  // query tokens per work item
-  constexpr int NC = G * TC;                                  // MFMA columns in use
+  static_assert(NS == 1 || (NS == 2 && kCausal), "two column sets only for several query tokens");
+  constexpr int TC = kCausal ? (G >= 16 ? 1 : 16 / G) : 1;  // query tokens per column set
+  constexpr int NC = G * TC;                                  // MFMA columns in use per set
   __shared__ __attribute__((aligned(16))) uint8_t vt_all[W][kVtBytes];
   __shared__ __attribute__((aligned(16))) uint8_t kt_all[W][kVtBytes];
   __shared__ float red_m[W][16];
@@ -107,7 +110,7 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   int item = xcd_remap(blockIdx.x, gridDim.x);
   const int p = item % a.P;
   item /= a.P;
-  int tg = 0;  // which TC query tokens of the request this item takes
+  int tg = 0;  // which NS*TC query tokens of the request this item takes
   if constexpr (kCausal) {
     tg = item % a.TG;
     item /= a.TG;
@@ -115,15 +118,18 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   const int s = item % a.S;
   const int kvh = item / a.S;
 
-  // Column n16 is query token tq, head kvh*G + n16%G.
-  const int tq = tg * TC + n16 / G;
+  // Column n16 of set j is query token tq[j], head kvh*G + n16%G.
+  int tq[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) tq[j] = (tg * NS + j) * TC + n16 / G;
 
-  // q of column n16 over the dims this lane contributes, as MFMA B operands.
-  bf16x8_t qv[4];
-  {
+  // q of each column over the dims this lane contributes, as MFMA B operands.
+  bf16x8_t qv[NS][4];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
     // every lane loads (no divergent loads), then columns without a query are zeroed
-    const bool live = n16 < NC && tq < a.T;
-    const int row = kCausal ? min(tq, a.T - 1) : 0;
+    const bool live = n16 < NC && tq[j] < a.T;
+    const int row = kCausal ? min(tq[j], a.T - 1) : 0;
     const int hq = kCausal ? n16 % G : (n16 < G ? n16 : G - 1);
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
                          (((int64_t)s * a.T + row) * a.Hq + (int64_t)kvh * G + hq) * kHeadDim;
@@ -131,7 +137,7 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
     for (int i = 0; i < 4; ++i) {
       uint4 v = *reinterpret_cast<const uint4*>(qp + 32 * i + 8 * c4);
       if (!live) v = make_uint4(0, 0, 0, 0);
-      qv[i] = __builtin_bit_cast(bf16x8_t, v);
+      qv[j][i] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
 
@@ -216,12 +222,16 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   bad = n_raw < 0 || (int64_t)n_raw > (int64_t)a.MB * B;
   n = bad ? 0 : n_raw;
   const int nb = (n + B - 1) / B;  // blocks holding the history
-  // Column n16 may see the first lim positions.  The item needs the tiles up
-  // to its last token's limit.
-  int lim = n, lim_hi = n;
+  // Column n16 of set j may see the first lim[j] positions.  The item needs
+  // the tiles up to its last token's limit.
+  int lim[NS];
+  int lim_hi = n;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) lim[j] = n;
   if constexpr (kCausal) {
-    lim = tq < a.T ? min(n, max(0, n - a.T + 1 + tq)) : n;
-    lim_hi = min(n, max(0, n - a.T + min(a.T, tg * TC + TC)));
+#pragma unroll
+    for (int j = 0; j < NS; ++j) lim[j] = tq[j] < a.T ? min(n, max(0, n - a.T + 1 + tq[j])) : n;
+    lim_hi = min(n, max(0, n - a.T + min(a.T, (tg + 1) * NS * TC)));
   }
   const int nt = (lim_hi + kTile - 1) / kTile;  // 16-slot tiles this item reads
   const int u1 = min(nt, u0 + a.tps / kTile);
@@ -237,11 +247,16 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
     }
   }
 
-  float m = kNegInf;  // running max (base 2) of head n16
-  float l = 0.f;      // partial sum over this lane's slots
-  f32x4_t acc[8];     // o: heads 4*c4 + r, dims 16*jj + n16
+  float m[NS];         // running max (base 2) of column n16
+  float l[NS];         // partial sum over this lane's slots
+  f32x4_t acc[NS][8];  // o: columns 4*c4 + r, dims 16*jj + n16
 #pragma unroll
-  for (int jj = 0; jj < 8; ++jj) acc[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NS; ++j) {
+    m[j] = kNegInf;
+    l[j] = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) acc[j][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   // Writes: slot 4*i + c4, chunk n16 of this wave's tile; reads as in TileReads.
   uint8_t* vt = vt_all[w];
@@ -262,7 +277,14 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
     wave_lds_order();
     // Mask past the length or, for several query tokens, past this column's
     // own position (then a column may have no valid slot yet).
-    tile_update<kCausal>(rd, qv, acc, m, l, kCausal ? lim - u * kTile : valid, a.scale_log2, n16, c4);
+    if constexpr (NS == 1) {
+      tile_update<kCausal>(rd, qv[0], acc[0], m[0], l[0], kCausal ? lim[0] - u * kTile : valid, a.scale_log2, n16, c4);
+    } else {
+      int vq[NS];
+#pragma unroll
+      for (int j = 0; j < NS; ++j) vq[j] = lim[j] - u * kTile;
+      tile_update_sets<NS, true>(rd, qv, acc, m, l, vq, a.scale_log2, n16, c4);
+    }
   };
 
   // The wave's tiles are walked one register of table entries at a time.
@@ -288,59 +310,68 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
     }
   }
 
-  // Full l of head n16 in this wave: sum the partials of its four lanes.
-  l += __shfl_xor(l, 16, kWave);
-  l += __shfl_xor(l, 32, kWave);
-
   // Merge the W wave states ([Budgets] eq. (4) applied across disjoint block
-  // sets): M = max m_w, L = sum 2^(m_w - M) l_w, O = sum 2^(m_w - M) o_w.
-  if (c4 == 0) {
-    red_m[w][n16] = m;
-    red_l[w][n16] = l;
-  }
-  bad = __syncthreads_or(bad);  // any wave that met an entry outside the pool
-  float mh = kNegInf;  // M of head n16
-#pragma unroll
-  for (int v = 0; v < W; ++v) mh = fmaxf(mh, red_m[v][n16]);
-  // scale of this wave's state for head n16 (0 for a wave that saw no block)
-  const float f = (m == kNegInf) ? 0.f : fast_exp2(m - mh);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int hg = 4 * c4 + r;
-    const float fr = __shfl(f, hg & 15, kWave);
-    if (hg < NC) {
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) red_o[w][hg][16 * jj + n16] = acc[jj][r] * fr;
-    }
-  }
-  __syncthreads();
-
-  // NC * 128 outputs (column hg = query token tg*TC + hg/G, head kvh*G + hg%G),
-  // spread over the workgroup's threads.
+  // sets): M = max m_w, L = sum 2^(m_w - M) l_w, O = sum 2^(m_w - M) o_w;
+  // one column set after the other through the same LDS.
   const float nan = __builtin_nanf("");
-  for (int idx = threadIdx.x; idx < NC * kHeadDim; idx += kWave * W) {
-    const int hg = idx / kHeadDim;
-    const int d = idx % kHeadDim;
-    const int t_out = tg * TC + hg / G;
-    if (kCausal && t_out >= a.T) break;  // idx only grows: every later output is past T too
-    float M = kNegInf, L = 0.f, O = 0.f;
 #pragma unroll
-    for (int v = 0; v < W; ++v) M = fmaxf(M, red_m[v][hg]);
-#pragma unroll
-    for (int v = 0; v < W; ++v) {
-      const float mv = red_m[v][hg];
-      if (mv != kNegInf) L = fmaf(fast_exp2(mv - M), red_l[v][hg], L);
-      O += red_o[v][hg][d];
+  for (int j = 0; j < NS; ++j) {
+    // Full l of column n16 in this wave: sum the partials of its four lanes.
+    float lj = l[j];
+    lj += __shfl_xor(lj, 16, kWave);
+    lj += __shfl_xor(lj, 32, kWave);
+    if (j > 0) __syncthreads();  // the previous set's outputs have been read
+    if (c4 == 0) {
+      red_m[w][n16] = m[j];
+      red_l[w][n16] = lj;
     }
-    const int64_t row = ((int64_t)s * a.T + t_out) * a.Hq + kvh * G + hg % G;  // [S, T, Hq] row
-    if (a.P == 1) {
-      a.out[row * kHeadDim + d] = bad ? nan : (L > 0.f ? O / L : 0.f);
+    if (j == 0) {
+      bad = __syncthreads_or(bad);  // any wave that met an entry outside the pool
     } else {
-      const int64_t slot = row * a.P + p;
-      a.ws_o[slot * kHeadDim + d] = O;
-      if (d == 0) {
-        a.ws_m[slot] = bad ? 0.f : M;
-        a.ws_l[slot] = bad ? nan : L;
+      __syncthreads();
+    }
+    float mh = kNegInf;  // M of column n16
+#pragma unroll
+    for (int v = 0; v < W; ++v) mh = fmaxf(mh, red_m[v][n16]);
+    // scale of this wave's state for column n16 (0 for a wave that saw no block)
+    const float f = (m[j] == kNegInf) ? 0.f : fast_exp2(m[j] - mh);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int hg = 4 * c4 + r;
+      const float fr = __shfl(f, hg & 15, kWave);
+      if (hg < NC) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) red_o[w][hg][16 * jj + n16] = acc[j][jj][r] * fr;
+      }
+    }
+    __syncthreads();
+
+    // NC * 128 outputs (column hg = query token (tg*NS + j)*TC + hg/G, head
+    // kvh*G + hg%G), spread over the workgroup's threads.
+    for (int idx = threadIdx.x; idx < NC * kHeadDim; idx += kWave * W) {
+      const int hg = idx / kHeadDim;
+      const int d = idx % kHeadDim;
+      const int t_out = (tg * NS + j) * TC + hg / G;
+      if (kCausal && t_out >= a.T) break;  // idx only grows: every later output is past T too
+      float M = kNegInf, L = 0.f, O = 0.f;
+#pragma unroll
+      for (int v = 0; v < W; ++v) M = fmaxf(M, red_m[v][hg]);
+#pragma unroll
+      for (int v = 0; v < W; ++v) {
+        const float mv = red_m[v][hg];
+        if (mv != kNegInf) L = fmaf(fast_exp2(mv - M), red_l[v][hg], L);
+        O += red_o[v][hg][d];
+      }
+      const int64_t row = ((int64_t)s * a.T + t_out) * a.Hq + kvh * G + hg % G;  // [S, T, Hq] row
+      if (a.P == 1) {
+        a.out[row * kHeadDim + d] = bad ? nan : (L > 0.f ? O / L : 0.f);
+      } else {
+        const int64_t slot = row * a.P + p;
+        a.ws_o[slot * kHeadDim + d] = O;
+        if (d == 0) {
+          a.ws_m[slot] = bad ? 0.f : M;
+          a.ws_l[slot] = bad ? nan : L;
+        }
       }
     }
   }
@@ -349,7 +380,14 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
 template <int G, bool kCausal, int B>
 hipError_t launch_gb(const DecodeArgs& a, hipStream_t stream) {
   const int items = a.Hkv * a.S * a.P * (kCausal ? a.TG : 1);
-  hipLaunchKernelGGL((decode_mfma_kernel<G, kCausal, kMfmaWaves, B>), dim3(items), dim3(kWave * kMfmaWaves), 0,
+  if constexpr (kCausal) {
+    if (decode_column_sets(PA_BF16, G, a.T) == 2) {
+      hipLaunchKernelGGL((decode_mfma_kernel<G, true, 2, kMfmaWaves, B>), dim3(items), dim3(kWave * kMfmaWaves), 0,
+                         stream, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((decode_mfma_kernel<G, kCausal, 1, kMfmaWaves, B>), dim3(items), dim3(kWave * kMfmaWaves), 0,
                      stream, a);
   return hipGetLastError();
 }

@@ -16,7 +16,8 @@
 // When the (token, head) pairs of a request's KV head outnumber the 16
 // columns of one MFMA tile, the one-wave-per-column-set decode layout would
 // stream the history once per 16 columns.  Here a workgroup of 4 waves takes
-// 4 column sets (4 * 16/G tokens of the G-head group) and walks one split of
+// 4 or 8 column sets, one or two per wave (each K and V operand a wave reads
+// from LDS feeds all of its sets), and walks one split of
 // the history tile by tile: every tile's K and V are loaded once, each wave
 // fetching one group of 4 slot rows (16-byte lanes along a row, as in the
 // decode kernel), written to a double-buffered LDS tile in the swizzled
@@ -39,12 +40,15 @@ constexpr int kWaves = kSharedTileWaves;  // = row groups of 4 slots per 16-slot
 static_assert(kWaves * 4 == kTile, "each wave loads one 4-row group of a tile");
 constexpr int kDepth = 2;  // tiles in flight per workgroup (one 16-byte K and V load per lane each)
 
-template <int G, int B>
+// kSets: 16-column sets per wave (1 or 2); each K and V operand read from
+// LDS feeds all of them.
+template <int G, int kSets, int B>
 __global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArgs a) {
   static_assert(G >= 1 && G <= 16, "the query group must fit the 16 columns of one MFMA tile");
   static_assert(B >= 4 && B <= 64 && (B & (B - 1)) == 0, "block size: a power of two from 4 to 64");
-  constexpr int TC = G >= 16 ? 1 : 16 / G;  // query tokens per wave
-  constexpr int TW = kWaves * TC;           // query tokens per workgroup
+  constexpr int TC = G >= 16 ? 1 : 16 / G;  // query tokens per 16-column set
+  constexpr int TS = kSets * TC;            // query tokens per wave
+  constexpr int TW = kWaves * TS;           // query tokens per workgroup
   // [buffer][K, V][tile]
   __shared__ __attribute__((aligned(16))) uint8_t tiles[2][2][kVtBytes];
 
@@ -65,26 +69,31 @@ __global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArg
   bool bad = n_raw < 0 || (int64_t)n_raw > (int64_t)a.MB * B;
   const int n = bad ? 0 : n_raw;
   const int nb = (n + B - 1) / B;
-  // Column n16 of wave w is query token tq, head kvh*G + n16%G, and may see
-  // the first lim positions; the workgroup needs the tiles up to its last
-  // token's limit.
-  const int tq = tw * TW + w * TC + n16 / G;
-  const int lim = tq < a.T ? min(n, max(0, n - a.T + 1 + tq)) : n;
+  // Column n16 of set j of wave w is query token tq[j], head kvh*G + n16%G,
+  // and may see the first lim[j] positions; the workgroup needs the tiles up
+  // to its last token's limit.
+  int tq[kSets], lim[kSets];
+#pragma unroll
+  for (int j = 0; j < kSets; ++j) {
+    tq[j] = tw * TW + w * TS + j * TC + n16 / G;
+    lim[j] = tq[j] < a.T ? min(n, max(0, n - a.T + 1 + tq[j])) : n;
+  }
   const int lim_hi = min(n, max(0, n - a.T + min(a.T, tw * TW + TW)));
   const int nt = (lim_hi + kTile - 1) / kTile;
   const int u0 = p * (a.tps / kTile);
   const int u1 = min(nt, u0 + a.tps / kTile);  // the same range for every wave
 
-  bf16x8_t qv[4];
-  {
-    const bool live = tq < a.T;  // columns past T get q = 0 and are never stored
+  bf16x8_t qv[kSets][4];
+#pragma unroll
+  for (int j = 0; j < kSets; ++j) {
+    const bool live = tq[j] < a.T;  // columns past T get q = 0 and are never stored
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         (((int64_t)s * a.T + min(tq, a.T - 1)) * a.Hq + (int64_t)kvh * G + n16 % G) * kHeadDim;
+                         (((int64_t)s * a.T + min(tq[j], a.T - 1)) * a.Hq + (int64_t)kvh * G + n16 % G) * kHeadDim;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint4 v = *reinterpret_cast<const uint4*>(qp + 32 * i + 8 * c4);
       if (!live) v = make_uint4(0, 0, 0, 0);
-      qv[i] = __builtin_bit_cast(bf16x8_t, v);
+      qv[j][i] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
 
@@ -122,11 +131,15 @@ __global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArg
     }
   };
 
-  float m = kNegInf;
-  float l = 0.f;
-  f32x4_t acc[8];
+  float m[kSets], l[kSets];
+  f32x4_t acc[kSets][8];
 #pragma unroll
-  for (int jj = 0; jj < 8; ++jj) acc[jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kSets; ++j) {
+    m[j] = kNegInf;
+    l[j] = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) acc[j][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
 
   const TileReads rd0(tiles[0][0], tiles[0][1], n16, c4);
   const int r_own = 4 * w + c4;                     // the slot row this lane writes
@@ -144,7 +157,10 @@ __global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArg
     TileReads rd = rd0;
     rd.k += buf * (2 * kVtBytes);
     rd.v += buf * (2 * kVtBytes);
-    tile_update<true>(rd, qv, acc, m, l, lim - t * kTile, a.scale_log2, n16, c4);
+    int vq[kSets];
+#pragma unroll
+    for (int j = 0; j < kSets; ++j) vq[j] = lim[j] - t * kTile;
+    tile_update_sets<kSets, true>(rd, qv, acc, m, l, vq, a.scale_log2, n16, c4);
   };
 
   // Table entries are read 64 at a time into one register (one per lane), as
@@ -170,40 +186,46 @@ __global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArg
     }
   }
 
-  // Full l of column n16: sum the partials of its four lanes.
-  l += __shfl_xor(l, 16, kWave);
-  l += __shfl_xor(l, 32, kWave);
+  // Full l of column n16 of each set: sum the partials of its four lanes.
+#pragma unroll
+  for (int j = 0; j < kSets; ++j) {
+    l[j] += __shfl_xor(l[j], 16, kWave);
+    l[j] += __shfl_xor(l[j], 32, kWave);
+  }
   bad = __syncthreads_or(bad);  // any wave that met an entry outside the pool
 
   const float nan = __builtin_nanf("");
-  if (a.P == 1) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int col = 4 * c4 + r;
-      const float lc = __shfl(l, col, kWave);
-      const int t_out = tw * TW + w * TC + col / G;
-      if (t_out < a.T) {
-        const float inv = lc > 0.f ? 1.f / lc : 0.f;
-        float* dst = a.out + (((int64_t)s * a.T + t_out) * a.Hq + kvh * G + col % G) * kHeadDim + n16;
+  for (int j = 0; j < kSets; ++j) {
+    if (a.P == 1) {
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) dst[16 * jj] = bad ? nan : acc[jj][r] * inv;
+      for (int r = 0; r < 4; ++r) {
+        const int col = 4 * c4 + r;
+        const float lc = __shfl(l[j], col, kWave);
+        const int t_out = tw * TW + w * TS + j * TC + col / G;
+        if (t_out < a.T) {
+          const float inv = lc > 0.f ? 1.f / lc : 0.f;
+          float* dst = a.out + (((int64_t)s * a.T + t_out) * a.Hq + kvh * G + col % G) * kHeadDim + n16;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) dst[16 * jj] = bad ? nan : acc[j][jj][r] * inv;
+        }
       }
-    }
-  } else {
+    } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int col = 4 * c4 + r;
-      const int t_out = tw * TW + w * TC + col / G;
-      if (t_out < a.T) {
-        const int64_t slot = (((int64_t)s * a.T + t_out) * a.Hq + kvh * G + col % G) * a.P + p;
+      for (int r = 0; r < 4; ++r) {
+        const int col = 4 * c4 + r;
+        const int t_out = tw * TW + w * TS + j * TC + col / G;
+        if (t_out < a.T) {
+          const int64_t slot = (((int64_t)s * a.T + t_out) * a.Hq + kvh * G + col % G) * a.P + p;
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) a.ws_o[slot * kHeadDim + 16 * jj + n16] = acc[jj][r];
+          for (int jj = 0; jj < 8; ++jj) a.ws_o[slot * kHeadDim + 16 * jj + n16] = acc[j][jj][r];
+        }
       }
-    }
-    if (c4 == 0 && tq < a.T) {  // lane n16 holds column n16's m and l
-      const int64_t slot = (((int64_t)s * a.T + tq) * a.Hq + kvh * G + n16 % G) * a.P + p;
-      a.ws_m[slot] = bad ? 0.f : m;
-      a.ws_l[slot] = bad ? nan : l;
+      if (c4 == 0 && tq[j] < a.T) {  // lane n16 holds column n16's m and l
+        const int64_t slot = (((int64_t)s * a.T + tq[j]) * a.Hq + kvh * G + n16 % G) * a.P + p;
+        a.ws_m[slot] = bad ? 0.f : m[j];
+        a.ws_l[slot] = bad ? nan : l[j];
+      }
     }
   }
 }
@@ -211,7 +233,10 @@ __global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArg
 template <int G, int B>
 hipError_t launch_gb(const DecodeArgs& a, hipStream_t stream) {
   const int items = a.Hkv * a.S * a.P * a.TG;
-  hipLaunchKernelGGL((extend_shared_kernel<G, B>), dim3(items), dim3(kWave * kWaves), 0, stream, a);
+  if (shared_tile_sets(PA_BF16, G, a.T) == 2)
+    hipLaunchKernelGGL((extend_shared_kernel<G, 2, B>), dim3(items), dim3(kWave * kWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL((extend_shared_kernel<G, 1, B>), dim3(items), dim3(kWave * kWaves), 0, stream, a);
   return hipGetLastError();
 }
 

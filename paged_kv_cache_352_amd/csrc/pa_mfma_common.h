@@ -107,26 +107,30 @@ struct TileReads {
 // kMayBeEmpty a column may have no valid slot yet (m stays -inf and its
 // state empty); without it the caller guarantees slot 0 of the tile is valid
 // for every column.
+// The softmax part of the step: from the raw q.k scores sc of lane (n16, c4)
+// (column n16, slots 4*c4 .. +3), mask, update m and l, rescale acc when a
+// column's max moved, and return p as bf16 head / remainder A operands.
 template <bool kMayBeEmpty>
-__device__ __attribute__((always_inline)) inline void tile_update(const TileReads& rd, const bf16x8_t (&qv)[4],
-                                                                  f32x4_t (&acc)[8], float& m, float& l, int vq,
-                                                                  float scale_log2, int n16, int c4) {
-  f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const u32x4_t kv = *reinterpret_cast<const PA_LDS u32x4_t*>(rd.k + 16 * ((4 * i + c4) ^ n16));
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qv[i], sc, 0, 0, 0);
-  }
-
+__device__ __attribute__((always_inline)) inline void softmax_step(const f32x4_t& sc, f32x4_t (&acc)[8], float& m,
+                                                                   float& l, int vq, float scale_log2, int c4,
+                                                                   s16x4_t& phi, s16x4_t& plo) {
   // Scores in base 2, masked past the column's limit ([Slides] quiz "逻辑顺序没错…").
   float sv[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) sv[r] = (4 * c4 + r < vq) ? sc[r] * scale_log2 : kNegInf;
 
-  // Tile max over the 16 slots of column n16, new running max.
+  // Tile max over the 16 slots of column n16, new running max.  The four
+  // lanes of a column sit 16 lanes apart: v_permlane16_swap / 32_swap
+  // exchange rows of 16 / 32 lanes in the vector ALU, so the max of each
+  // returned pair is the max over the lane and its partner (lane ^ 16, then
+  // lane ^ 32) without a round trip through the LDS crossbar.
   float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-  bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
-  bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+  {
+    const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+    bm = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+    const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+    bm = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+  }
   const float mn = fmaxf(m, bm);
   float alpha, mref = mn;
   if constexpr (kMayBeEmpty) {
@@ -145,8 +149,8 @@ __device__ __attribute__((always_inline)) inline void tile_update(const TileRead
   uint32_t hi0, hi1, lo0, lo1;
   split_pair(pw[0], pw[1], hi0, lo0);
   split_pair(pw[2], pw[3], hi1, lo1);
-  const s16x4_t phi = __builtin_bit_cast(s16x4_t, make_uint2(hi0, hi1));
-  const s16x4_t plo = __builtin_bit_cast(s16x4_t, make_uint2(lo0, lo1));
+  phi = __builtin_bit_cast(s16x4_t, make_uint2(hi0, hi1));
+  plo = __builtin_bit_cast(s16x4_t, make_uint2(lo0, lo1));
 
   // Rescale o only where a column's max moved (alpha < 1 somewhere in the wave).
   if (__any(alpha != 1.f)) {
@@ -158,6 +162,20 @@ __device__ __attribute__((always_inline)) inline void tile_update(const TileRead
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[jj][r] *= ar[r];
   }
+}
+
+template <bool kMayBeEmpty>
+__device__ __attribute__((always_inline)) inline void tile_update(const TileReads& rd, const bf16x8_t (&qv)[4],
+                                                                  f32x4_t (&acc)[8], float& m, float& l, int vq,
+                                                                  float scale_log2, int n16, int c4) {
+  f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4_t kv = *reinterpret_cast<const PA_LDS u32x4_t*>(rd.k + 16 * ((4 * i + c4) ^ n16));
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qv[i], sc, 0, 0, 0);
+  }
+  s16x4_t phi, plo;
+  softmax_step<kMayBeEmpty>(sc, acc, m, l, vq, scale_log2, c4, phi, plo);
 
   wave_lds_order();  // this tile's V is in LDS
 #pragma unroll
@@ -166,6 +184,42 @@ __device__ __attribute__((always_inline)) inline void tile_update(const TileRead
     const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(rd.v + 16 * chunk));
     acc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vb, acc[jj], 0, 0, 0);
     acc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vb, acc[jj], 0, 0, 0);
+  }
+}
+
+// The same step for NS sets of 16 columns at once (NS query-token groups of
+// one wave): each K and V operand is read from LDS once and feeds NS sets of
+// MFMAs, and the NS dependency chains interleave.
+template <int NS, bool kMayBeEmpty>
+__device__ __attribute__((always_inline)) inline void tile_update_sets(const TileReads& rd,
+                                                                       const bf16x8_t (&qv)[NS][4],
+                                                                       f32x4_t (&acc)[NS][8], float (&m)[NS],
+                                                                       float (&l)[NS], const int (&vq)[NS],
+                                                                       float scale_log2, int n16, int c4) {
+  f32x4_t sc[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) sc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4_t kv = *reinterpret_cast<const PA_LDS u32x4_t*>(rd.k + 16 * ((4 * i + c4) ^ n16));
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+      sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qv[j][i], sc[j], 0, 0, 0);
+  }
+  s16x4_t phi[NS], plo[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) softmax_step<kMayBeEmpty>(sc[j], acc[j], m[j], l[j], vq[j], scale_log2, c4, phi[j], plo[j]);
+
+  wave_lds_order();  // this tile's V is in LDS
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const int chunk = ((2 * jj) ^ rd.rhi) | rd.bsel;
+    const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(rd.v + 16 * chunk));
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      acc[j][jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi[j], vb, acc[j][jj], 0, 0, 0);
+      acc[j][jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo[j], vb, acc[j][jj], 0, 0, 0);
+    }
   }
 }
 

@@ -8,7 +8,7 @@ import torch
 
 import paged_kv_cache_352_amd as pa
 import workloads as W
-from tests.gpu_util import HostLayer, assert_close, banner, gpu_step, host_f32
+from tests.gpu_util import HostLayer, assert_close, banner, gpu_step, host_bits, host_f32
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -114,9 +114,10 @@ def test_other_group_sizes(G, Hkv, dtype):
 
 @pytest.mark.parametrize("splits", [1, 2])
 def test_long_split_walks_several_table_chunks(splits):
-    """A split longer than 64 blocks reads its table slice in several chunks."""
-    banner(f"long split: 2500 / 1100 / 17 tokens, splits={splits}")
-    b = W.custom([2500, 1100, 17], Hq=8, Hkv=2, dtype=torch.bfloat16, device=DEV, seed=14)
+    """A wave with more than 64 tiles (a split over 4 x 64 blocks) reads its table
+    entries in several registers."""
+    banner(f"long split: 5000 / 1100 / 17 tokens, splits={splits}")
+    b = W.custom([5000, 1100, 17], Hq=8, Hkv=2, dtype=torch.bfloat16, device=DEV, seed=14)
     ref = HostLayer(b, 0).oracle()
     out = gpu_step(b, num_splits=splits)[0]
     torch.cuda.synchronize()
@@ -220,3 +221,26 @@ def test_block_sizes_32x4096_sampled(B):
     torch.cuda.synchronize()
     got = host_f32(out)
     assert_close(np.stack([got[s] for s in rows]), np.stack([ref[s] for s in rows]), torch.bfloat16, f"B={B}")
+
+
+@pytest.mark.parametrize("B,dtype", [(16, torch.bfloat16), (4, torch.bfloat16), (64, torch.bfloat16),
+                                     (8, torch.float32), (16, torch.float32)])
+def test_table_entries_past_the_history_may_hold_anything(B, dtype):
+    """Entries at or past ceil(n/B) never address the pools: filling them with ids
+    outside the pool (negative, past NB, INT32 extremes) changes no output bit and
+    poisons nothing, although the kernel reads its first entries before the length."""
+    banner(f"garbage table padding B={B} {dtype}")
+    lens = [0, 1, 5, B, B + 1, 33, 70, 300]
+    b = W.custom(lens, Hq=8, Hkv=2, B=B, dtype=dtype, device=DEV, seed=15, spare_blocks=3)
+    ref = HostLayer(b, 0).oracle()
+    base = gpu_step(b)[0].clone()
+    tab = b.block_tables.cpu().numpy()
+    garbage = np.array([-7, b.NB, b.NB + 12345, 2**31 - 1, -2**31], dtype=np.int64)
+    for s_, n in enumerate(lens):
+        need = -(-n // B)
+        tab[s_, need:] = garbage[(np.arange(tab.shape[1] - need) + s_) % len(garbage)]
+    t2 = torch.as_tensor(tab.astype(np.int32), device=DEV)
+    out = pa.paged_attn_decode(b.q[0], b.k_pool[0], b.v_pool[0], t2, b.seq_lens, B, b.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out), host_bits(base))
+    assert_close(host_f32(out), ref, dtype, f"garbage padding B={B}")

@@ -60,16 +60,20 @@ def check(b, dtype, what, num_splits=0):
     return assert_close(host_f32(out), host.oracle(), dtype, what)
 
 
-@pytest.mark.parametrize("T", [2, 3, 4])
+@pytest.mark.parametrize("T", [2, 3, 4, 5, 8])
 def test_bf16_one_item_per_group(T):
-    """G = 4: up to 4 tokens share one pass over the history (16 MFMA columns)."""
+    """G = 4: up to 8 tokens share one pass over the history (one or two sets of
+    16 MFMA columns per wave)."""
     banner(f"extend bf16 G=4 T={T} ragged")
     b = W.extend_batch(RAGGED, T, Hq=16, Hkv=4, seed=10 + T, device=DEV)
     check(b, torch.bfloat16, f"bf16 T={T}")
 
 
-@pytest.mark.parametrize("G,T", [(4, 7), (4, 16), (1, 17), (1, 40), (16, 3), (8, 5), (2, 9)])
+@pytest.mark.parametrize("G,T", [(4, 7), (4, 16), (1, 17), (1, 40), (16, 3), (8, 5), (2, 9),
+                                 (4, 40), (16, 9), (2, 70), (8, 33)])
 def test_bf16_several_items_per_group(G, T):
+    """Separate items per column set up to two sets; the shared-tile kernel above,
+    with one 16-column set per wave, or two once every wave can fill two."""
     banner(f"extend bf16 G={G} T={T} ragged")
     b = W.extend_batch(RAGGED, T, Hq=2 * G, Hkv=2, seed=20 + G + T, device=DEV)
     check(b, torch.bfloat16, f"bf16 G={G} T={T}")
@@ -82,14 +86,15 @@ def test_fp32(G, T):
     check(b, torch.float32, f"fp32 G={G} T={T}")
 
 
-@pytest.mark.parametrize("dtype,splits", [(torch.bfloat16, 2), (torch.bfloat16, 3), (torch.bfloat16, 7),
-                                          (torch.float32, 2), (torch.float32, 5)])
-def test_forced_splits(dtype, splits):
+@pytest.mark.parametrize("dtype,splits,T", [(torch.bfloat16, 2, 5), (torch.bfloat16, 3, 5), (torch.bfloat16, 7, 5),
+                                            (torch.float32, 2, 5), (torch.float32, 5, 5), (torch.bfloat16, 3, 12),
+                                            (torch.bfloat16, 4, 40)])
+def test_forced_splits(dtype, splits, T):
     """Split boundaries inside the causal region: later splits of early tokens hold nothing."""
-    banner(f"extend {dtype} splits={splits} T=5")
-    b = W.extend_batch([16, 17, 40, 64, 65, 200, 300], 5, Hq=8, Hkv=2, dtype=dtype, seed=40 + splits,
+    banner(f"extend {dtype} splits={splits} T={T}")
+    b = W.extend_batch([16, 17, 40, 64, 65, 200, 300], T, Hq=8, Hkv=2, dtype=dtype, seed=40 + splits + T,
                        device=DEV)
-    check(b, dtype, f"splits={splits}", num_splits=splits)
+    check(b, dtype, f"splits={splits} T={T}", num_splits=splits)
 
 
 @pytest.mark.parametrize("B", [4, 8, 32, 64])
@@ -113,7 +118,8 @@ def test_one_token_is_the_decode_step_bitwise(dtype):
     assert torch.equal(ext[:, 0], dec)
 
 
-@pytest.mark.parametrize("dtype,T", [(torch.bfloat16, 4), (torch.bfloat16, 9), (torch.float32, 3)])
+@pytest.mark.parametrize("dtype,T", [(torch.bfloat16, 4), (torch.bfloat16, 6), (torch.bfloat16, 9),
+                                     (torch.bfloat16, 40), (torch.float32, 3)])
 def test_physical_permutation_is_bitwise_invisible(dtype, T):
     banner(f"extend permutation {dtype} T={T}")
     b = W.extend_batch(RAGGED, T, Hq=8, Hkv=2, dtype=dtype, seed=80 + T, device=DEV)

@@ -141,10 +141,12 @@ pa_status paged_attn_extend_plan(const pa_dims* dims, int32_t B, int32_t num_q_t
  * paged_attn_decode.  A query whose position n-T+i is negative (n < T)
  * attends nothing and gets 0.  q and out are [S, T, Hq, d] (q of `dtype`,
  * out float32).  T = 1 is exactly paged_attn_decode.  Several (token, head)
- * pairs share each K/V byte read: with bf16, up to 16/G tokens of a
- * G-head group per pass over the history (8/G with float32); more tokens
- * are spread over further passes that the same L2 serves.  The workspace is
- * sized by paged_attn_extend_plan.
+ * pairs share each K/V byte read: with bf16, up to 32/G tokens of a G-head
+ * group in one pass over the history (two sets of 16 matrix-core columns);
+ * more tokens go to workgroups whose waves take different tokens and share
+ * each K/V tile through LDS (16 or 32 tokens of a 4-head group per
+ * workgroup), each workgroup streaming the history once.  With float32, 8/G
+ * tokens per pass.  The workspace is sized by paged_attn_extend_plan.
  */
 pa_status paged_attn_extend(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
                             const int32_t* seq_lens, int32_t num_q_tokens, int32_t B, float scale, float* out,

@@ -21,11 +21,12 @@
 // the history tile by tile: every tile's K and V are loaded once, each wave
 // fetching one group of 4 slot rows (16-byte lanes along a row, as in the
 // decode kernel), written to a double-buffered LDS tile in the swizzled
-// layout, and after one workgroup barrier every wave runs the q.k / softmax /
-// p.v step for its own columns on the whole tile.  With two LDS buffers one
-// barrier per tile suffices: a wave overwrites buffer b only after the
-// barrier of the next tile, which no wave passes before it has finished
-// reading b.  Each wave owns its columns, so no state is merged inside the
+// layout.  Tiles go two at a time: after one workgroup barrier every wave
+// runs the q.k / softmax / p.v step for its own columns on both tiles, p.v
+// on the 32-deep MFMA (twice the work per issue of the 16-deep one).  With
+// two LDS buffers one barrier per pair suffices: a wave overwrites buffer b
+// only after the barrier of the next pair, which no wave passes before it
+// has finished reading b.  Each wave owns its columns, so no state is merged inside the
 // workgroup.
 #include <hip/hip_runtime.h>
 
@@ -49,8 +50,8 @@ __global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArg
   constexpr int TC = G >= 16 ? 1 : 16 / G;  // query tokens per 16-column set
   constexpr int TS = kSets * TC;            // query tokens per wave
   constexpr int TW = kWaves * TS;           // query tokens per workgroup
-  // [buffer][K, V][tile]
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[2][2][kVtBytes];
+  // [buffer][tile a, tile b][K, V][tile bytes]
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[2][2][2][kVtBytes];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
@@ -141,47 +142,66 @@ __global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArg
     for (int jj = 0; jj < 8; ++jj) acc[j][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  const TileReads rd0(tiles[0][0], tiles[0][1], n16, c4);
-  const int r_own = 4 * w + c4;                     // the slot row this lane writes
+  const TileReads rd0(tiles[0][0][0], tiles[0][0][1], n16, c4);
+  const int r_own = 4 * w + c4;                        // the slot row this lane writes
   const int w_off = 256 * r_own + 16 * (n16 ^ r_own);  // its swizzled byte offset in a tile
 
-  // Tile t: write this lane's row of K and V into buffer t & 1, wait for the
-  // other waves' rows, then fold the tile into this wave's columns.
-  auto process = [&](int t, const uint4& k, const uint4& v) {
-    const int buf = t & 1;
-    uint8_t* kt = tiles[buf][0];
-    uint8_t* vt = tiles[buf][1];
-    *reinterpret_cast<uint4*>(kt + w_off) = k;
-    *reinterpret_cast<uint4*>(vt + w_off) = r_own < n - t * kTile ? v : make_uint4(0, 0, 0, 0);
+  // This lane's rows of two consecutive tiles.
+  struct Rows {
+    uint4 ka, va, kb, vb;
+  };
+  auto load_pair = [&](int t, Rows& r, int eb, int tab, int te) {
+    load_rows(t, r.ka, r.va, eb, tab);
+    load_rows(min(t + 1, te - 1), r.kb, r.vb, eb, tab);  // past the range: a copy of tile t, masked below
+  };
+
+  // Tiles t and t+1: write this lane's rows into buffer (t/2) & 1, wait for
+  // the other waves' rows, then fold both tiles into this wave's columns.
+  auto process = [&](int t, const Rows& r, int te) {
+    const int buf = (t >> 1) & 1;
+    const int tb_loaded = min(t + 1, te - 1);
+    uint8_t* base = &tiles[buf][0][0][0];
+    *reinterpret_cast<uint4*>(base + w_off) = r.ka;
+    *reinterpret_cast<uint4*>(base + kVtBytes + w_off) = r_own < n - t * kTile ? r.va : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(base + 2 * kVtBytes + w_off) = r.kb;
+    *reinterpret_cast<uint4*>(base + 3 * kVtBytes + w_off) =
+        r_own < n - tb_loaded * kTile ? r.vb : make_uint4(0, 0, 0, 0);
     __syncthreads();
-    TileReads rd = rd0;
-    rd.k += buf * (2 * kVtBytes);
-    rd.v += buf * (2 * kVtBytes);
-    int vq[kSets];
+    TileReads ra = rd0, rb = rd0;
+    ra.k += buf * (4 * kVtBytes);
+    ra.v += buf * (4 * kVtBytes);
+    rb.k += buf * (4 * kVtBytes) + 2 * kVtBytes;
+    rb.v += buf * (4 * kVtBytes) + 2 * kVtBytes;
+    int vqa[kSets], vqb[kSets];
 #pragma unroll
-    for (int j = 0; j < kSets; ++j) vq[j] = lim[j] - t * kTile;
-    tile_update_sets<kSets, true>(rd, qv, acc, m, l, vq, a.scale_log2, n16, c4);
+    for (int j = 0; j < kSets; ++j) {
+      vqa[j] = lim[j] - t * kTile;
+      vqb[j] = t + 1 < te ? lim[j] - (t + 1) * kTile : 0;  // no tile b past the range
+    }
+    pair_update_sets<kSets, true>(ra, rb, qv, acc, m, l, vqa, vqb, a.scale_log2, n16, c4);
   };
 
   // Table entries are read 64 at a time into one register (one per lane), as
-  // in the decode kernel: chunks of 64 tiles for B >= 16, 4*B tiles below.
-  // Within a chunk tile t + kDepth - 1 is requested before tile t is used.
+  // in the decode kernel: chunks of 64 tiles for B >= 16, 4*B tiles below
+  // (an even count, so a pair never straddles two chunks).  Within a chunk
+  // the next pair is requested before the current one is used.
   constexpr int kChunkTiles = B >= kTile ? kWave : 4 * B;
+  static_assert(kChunkTiles % 2 == 0, "pairs of tiles stay inside one chunk");
   for (int tb = u0; tb < u1; tb += kChunkTiles) {
     const int te = min(u1, tb + kChunkTiles);
     const int eb = (kTile * tb) / B;
     const int tab = trow[min(eb + lane, nb - 1)];
-    uint4 kq[kDepth], vq[kDepth];
+    Rows ring[kDepth];
 #pragma unroll
-    for (int b = 0; b + 1 < kDepth; ++b) load_rows(min(tb + b, te - 1), kq[b], vq[b], eb, tab);
-    for (int t = tb; t < te; t += kDepth) {
+    for (int b = 0; b + 1 < kDepth; ++b) load_pair(min(tb + 2 * b, te - 1), ring[b], eb, tab, te);
+    for (int t = tb; t < te; t += 2 * kDepth) {
 #pragma unroll
       for (int b = 0; b < kDepth; ++b) {
         constexpr int kNext = kDepth - 1;
-        load_rows(min(t + b + kNext, te - 1), kq[(b + kNext) % kDepth], vq[(b + kNext) % kDepth], eb, tab);
-        __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the current tile's math
-        process(t + b, kq[b], vq[b]);
-        if (t + b + 1 >= te) break;
+        load_pair(min(t + 2 * (b + kNext), te - 1), ring[(b + kNext) % kDepth], eb, tab, te);
+        __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the current pair's math
+        process(t + 2 * b, ring[b], te);
+        if (t + 2 * b + 2 >= te) break;
       }
     }
   }

@@ -107,24 +107,21 @@ struct TileReads {
 // kMayBeEmpty a column may have no valid slot yet (m stays -inf and its
 // state empty); without it the caller guarantees slot 0 of the tile is valid
 // for every column.
-// The softmax part of the step: from the raw q.k scores sc of lane (n16, c4)
-// (column n16, slots 4*c4 .. +3), mask, update m and l, rescale acc when a
-// column's max moved, and return p as bf16 head / remainder A operands.
-template <bool kMayBeEmpty>
-__device__ __attribute__((always_inline)) inline void softmax_step(const f32x4_t& sc, f32x4_t (&acc)[8], float& m,
-                                                                   float& l, int vq, float scale_log2, int c4,
-                                                                   s16x4_t& phi, s16x4_t& plo) {
-  // Scores in base 2, masked past the column's limit ([Slides] quiz "逻辑顺序没错…").
-  float sv[4];
+// The core of the online-softmax step for one lane: sv holds the lane's R
+// scores of column n16 (base 2, already masked to -inf past the column's
+// limit); update the running max m (over the four lanes of the column,
+// which sit 16 lanes apart), the partial sum l, rescale acc when some
+// column's max moved, and leave the weights p = 2^(s - m) in pw.
+template <int R, bool kMayBeEmpty>
+__device__ __attribute__((always_inline)) inline void softmax_core(const float (&sv)[R], f32x4_t (&acc)[8],
+                                                                   float& m, float& l, int c4, float (&pw)[R]) {
+  // Tile max over the column's slots, new running max.  v_permlane16_swap /
+  // 32_swap exchange rows of 16 / 32 lanes in the vector ALU, so the max of
+  // each returned pair is the max over the lane and its partner (lane ^ 16,
+  // then lane ^ 32) without a round trip through the LDS crossbar.
+  float bm = sv[0];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) sv[r] = (4 * c4 + r < vq) ? sc[r] * scale_log2 : kNegInf;
-
-  // Tile max over the 16 slots of column n16, new running max.  The four
-  // lanes of a column sit 16 lanes apart: v_permlane16_swap / 32_swap
-  // exchange rows of 16 / 32 lanes in the vector ALU, so the max of each
-  // returned pair is the max over the lane and its partner (lane ^ 16, then
-  // lane ^ 32) without a round trip through the LDS crossbar.
-  float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  for (int r = 1; r < R; ++r) bm = fmaxf(bm, sv[r]);
   {
     const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
     bm = fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
@@ -141,16 +138,12 @@ __device__ __attribute__((always_inline)) inline void softmax_step(const f32x4_t
     alpha = fast_exp2(m - mn);
   }
   m = mn;
-  float pw[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) pw[r] = fast_exp2(sv[r] - mref);
-  l = fmaf(l, alpha, (pw[0] + pw[1]) + (pw[2] + pw[3]));
-
-  uint32_t hi0, hi1, lo0, lo1;
-  split_pair(pw[0], pw[1], hi0, lo0);
-  split_pair(pw[2], pw[3], hi1, lo1);
-  phi = __builtin_bit_cast(s16x4_t, make_uint2(hi0, hi1));
-  plo = __builtin_bit_cast(s16x4_t, make_uint2(lo0, lo1));
+  for (int r = 0; r < R; ++r) pw[r] = fast_exp2(sv[r] - mref);
+  float sum = (pw[0] + pw[1]) + (pw[2] + pw[3]);
+#pragma unroll
+  for (int r = 4; r < R; r += 4) sum += (pw[r] + pw[r + 1]) + (pw[r + 2] + pw[r + 3]);
+  l = fmaf(l, alpha, sum);
 
   // Rescale o only where a column's max moved (alpha < 1 somewhere in the wave).
   if (__any(alpha != 1.f)) {
@@ -162,6 +155,26 @@ __device__ __attribute__((always_inline)) inline void softmax_step(const f32x4_t
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[jj][r] *= ar[r];
   }
+}
+
+// The softmax part of the one-tile step: from the raw q.k scores sc of lane
+// (n16, c4) (column n16, slots 4*c4 .. +3), mask, update the state and
+// return p as bf16 head / remainder A operands of the 16-slot p.v.
+template <bool kMayBeEmpty>
+__device__ __attribute__((always_inline)) inline void softmax_step(const f32x4_t& sc, f32x4_t (&acc)[8], float& m,
+                                                                   float& l, int vq, float scale_log2, int c4,
+                                                                   s16x4_t& phi, s16x4_t& plo) {
+  // Scores in base 2, masked past the column's limit ([Slides] quiz "逻辑顺序没错…").
+  float sv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) sv[r] = (4 * c4 + r < vq) ? sc[r] * scale_log2 : kNegInf;
+  float pw[4];
+  softmax_core<4, kMayBeEmpty>(sv, acc, m, l, c4, pw);
+  uint32_t hi0, hi1, lo0, lo1;
+  split_pair(pw[0], pw[1], hi0, lo0);
+  split_pair(pw[2], pw[3], hi1, lo1);
+  phi = __builtin_bit_cast(s16x4_t, make_uint2(hi0, hi1));
+  plo = __builtin_bit_cast(s16x4_t, make_uint2(lo0, lo1));
 }
 
 template <bool kMayBeEmpty>
@@ -219,6 +232,73 @@ __device__ __attribute__((always_inline)) inline void tile_update_sets(const Til
     for (int j = 0; j < NS; ++j) {
       acc[j][jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi[j], vb, acc[j][jj], 0, 0, 0);
       acc[j][jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo[j], vb, acc[j][jj], 0, 0, 0);
+    }
+  }
+}
+
+// The step for two consecutive tiles a and b (32 slots) and NS sets of 16
+// columns.  q.k runs per tile as above; the softmax takes the lane's 8
+// scores (slots 4*c4 .. +3 of a, then of b); and p.v runs on
+// v_mfma_f32_16x16x32_bf16, which does twice the work of the 16-slot
+// instruction per issue: its K index 8*c4 + i stands for slot 4*c4 + i of
+// tile a (i < 4) or of tile b (i >= 4), so the A operand is the lane's 8
+// weights in that order and the B operand is the two transposing V reads
+// (tile a, then tile b) of the same lane side by side.
+template <int NS, bool kMayBeEmpty>
+__device__ __attribute__((always_inline)) inline void pair_update_sets(const TileReads& ra, const TileReads& rb,
+                                                                       const bf16x8_t (&qv)[NS][4],
+                                                                       f32x4_t (&acc)[NS][8], float (&m)[NS],
+                                                                       float (&l)[NS], const int (&vqa)[NS],
+                                                                       const int (&vqb)[NS], float scale_log2,
+                                                                       int n16, int c4) {
+  f32x4_t sa[NS], sb[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    sa[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    sb[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4_t ka = *reinterpret_cast<const PA_LDS u32x4_t*>(ra.k + 16 * ((4 * i + c4) ^ n16));
+    const u32x4_t kb = *reinterpret_cast<const PA_LDS u32x4_t*>(rb.k + 16 * ((4 * i + c4) ^ n16));
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      sa[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qv[j][i], sa[j], 0, 0, 0);
+      sb[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb), qv[j][i], sb[j], 0, 0, 0);
+    }
+  }
+  bf16x8_t phi[NS], plo[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    float sv[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sv[r] = (4 * c4 + r < vqa[j]) ? sa[j][r] * scale_log2 : kNegInf;
+      sv[4 + r] = (4 * c4 + r < vqb[j]) ? sb[j][r] * scale_log2 : kNegInf;
+    }
+    float pw[8];
+    softmax_core<8, kMayBeEmpty>(sv, acc[j], m[j], l[j], c4, pw);
+    uint32_t h[4], lo[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) split_pair(pw[2 * q], pw[2 * q + 1], h[q], lo[q]);
+    phi[j] = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
+    plo[j] = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+  }
+
+  wave_lds_order();  // both tiles' V are in LDS
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const int ca = ((2 * jj) ^ ra.rhi) | ra.bsel;
+    const int cb = ((2 * jj) ^ rb.rhi) | rb.bsel;
+    const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(ra.v + 16 * ca));
+    const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(rb.v + 16 * cb));
+    const bf16x8_t v8 = __builtin_bit_cast(
+        bf16x8_t, make_uint4(__builtin_bit_cast(uint2, va).x, __builtin_bit_cast(uint2, va).y,
+                             __builtin_bit_cast(uint2, vb).x, __builtin_bit_cast(uint2, vb).y));
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      acc[j][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[j], v8, acc[j][jj], 0, 0, 0);
+      acc[j][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[j], v8, acc[j][jj], 0, 0, 0);
     }
   }
 }

@@ -64,12 +64,12 @@
 // T positions of the history; token i attends positions 0 .. n-T+i
 // ([Serving] §5 sets speculative decoding beside paging).  The 16 columns of
 // the MFMA tile then hold (token, head) pairs: 16/G tokens of the G-head
-// group per work item, so up to 16/G tokens cost no more K/V traffic than
-// one.  Each column carries its own length limit; a column whose limit lies
-// before a tile sees only -inf there, and its state stays empty (m = -inf,
-// l = 0, o = 0) until a tile reaches it.  More tokens than one item holds
-// are spread over further work items of the same (request, KV head), which
-// the XCD-aware numbering keeps on one L2.
+// group per column set, and a wave keeps one or two sets (NS), so up to
+// 32/G tokens cost one pass over the history; each K and V operand read from
+// LDS feeds both sets.  Each column carries its own length limit; a column
+// whose limit lies before a tile sees only -inf there, and its state stays
+// empty (m = -inf, l = 0, o = 0) until a tile reaches it.  Still more tokens
+// go to the shared-tile kernel (pa_extend_mfma.hip).
 #include <hip/hip_runtime.h>
 
 #include "pa_mfma_common.h"

@@ -14,19 +14,19 @@
 // afterwards as for the decode.
 //
 // When the (token, head) pairs of a request's KV head outnumber the 16
-// columns of one MFMA tile, the one-wave-per-column-set decode layout would
-// stream the history once per 16 columns.  Here a workgroup of 4 waves takes
-// 4 or 8 column sets, one or two per wave (each K and V operand a wave reads
-// from LDS feeds all of its sets), and walks one split of
-// the history tile by tile: every tile's K and V are loaded once, each wave
-// fetching one group of 4 slot rows (16-byte lanes along a row, as in the
-// decode kernel), written to a double-buffered LDS tile in the swizzled
-// layout.  Tiles go two at a time: after one workgroup barrier every wave
-// runs the q.k / softmax / p.v step for its own columns on both tiles, p.v
-// on the 32-deep MFMA (twice the work per issue of the 16-deep one).  With
-// two LDS buffers one barrier per pair suffices: a wave overwrites buffer b
-// only after the barrier of the next pair, which no wave passes before it
-// has finished reading b.  Each wave owns its columns, so no state is merged inside the
+// columns of two column sets of one wave, the decode layout would stream
+// the history once per 32 columns.  Here a workgroup of 4 waves takes 4 or 8
+// column sets, one or two per wave (each K and V operand a wave reads from
+// LDS feeds all of its sets), and walks one split of the history tile by
+// tile: every tile's K and V are loaded once, each wave fetching one group
+// of 4 slot rows (16-byte lanes along a row, as in the decode kernel), and
+// written to a double-buffered LDS tile in the swizzled layout.  Tiles go
+// two at a time: after one workgroup barrier every wave runs the q.k /
+// softmax / p.v step for its own columns on both tiles, p.v on the 32-deep
+// MFMA (twice the work per issue of the 16-deep one).  With two LDS buffers
+// one barrier per pair suffices: a wave overwrites buffer b only after the
+// barrier of the next pair, which no wave passes before it has finished
+// reading b.  Each wave owns its columns, so no state is merged inside the
 // workgroup.
 #include <hip/hip_runtime.h>
 
@@ -39,7 +39,7 @@ using namespace mfma;
 
 constexpr int kWaves = kSharedTileWaves;  // = row groups of 4 slots per 16-slot tile
 static_assert(kWaves * 4 == kTile, "each wave loads one 4-row group of a tile");
-constexpr int kDepth = 2;  // tiles in flight per workgroup (one 16-byte K and V load per lane each)
+constexpr int kDepth = 2;  // tile pairs in flight per wave (this lane's K and V rows of two tiles each)
 
 // kSets: 16-column sets per wave (1 or 2); each K and V operand read from
 // LDS feeds all of them.

@@ -387,6 +387,11 @@ def main():
 
     gbs = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (mean_launch_ms * 1e-3) / 1e9
+    # Everything a launch must touch besides the valid K/V: q, out, the table
+    # rows and lengths, and the split workspace (written once, read once).
+    ws_bytes = 2 * first.workspace.numel() if first.workspace is not None else 0
+    other_bytes = (b.S * b.Hq * b.D * b.elem_bytes + b.S * b.Hq * b.D * 4 + b.S * b.MB * 4 + b.S * 4 + ws_bytes)
+    traffic = measured_traffic()
     res = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -409,13 +414,16 @@ def main():
         },
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "tokens_per_s_per_layer": round(b.S / (ms_step * 1e-3), 1),
+        "total_GB_s": round((kv_bytes + other_bytes) / (ms_step * 1e-3) / 1e9, 2),
+        "total_bytes_per_step": kv_bytes + other_bytes,
+        "dram_GB_s": round(traffic / (mean_launch_ms * 1e-3) / 1e9, 2) if traffic else None,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(),
+            "traffic": traffic,
             "kernel": "one paged_attn_decode launch (decode kernel, plus the split merge when it splits)",
             "algorithmic_bytes_per_launch": kv_bytes,
         },

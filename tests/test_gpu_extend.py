@@ -137,6 +137,30 @@ def test_physical_permutation_is_bitwise_invisible(dtype, T):
     assert np.array_equal(host_bits(out1), host_bits(out2))
 
 
+@pytest.mark.parametrize("T,splits", [(4, 0), (8, 3), (40, 0), (40, 2)])
+def test_graph_capture_replays_match_eager(T, splits):
+    """A captured paged_attn_extend replays bit-identically, several times, with
+    eager work between the replays (decode-kernel and shared-tile variants, with
+    and without the split merge)."""
+    banner(f"extend graph capture T={T} splits={splits}")
+    b = W.extend_batch([9, 40, 300, 77, 130], T, Hq=8, Hkv=2, seed=95 + T, device=DEV)
+    pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
+    eager = pa.paged_attn_extend(b.q, b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B, b.scale,
+                                 num_splits=splits).clone()
+    launch = pa.DecodeLaunch(b.q, b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B, b.scale, num_splits=splits)
+    launch.launch()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch.launch()
+    for _ in range(4):
+        launch.out.fill_(-1.0)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(launch.out.view(torch.int32), eager.view(torch.int32))
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_append_tokens_bit_exact(dtype):
     banner(f"kv_append_tokens bit-exact {dtype}")

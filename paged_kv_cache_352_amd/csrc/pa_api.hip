@@ -70,8 +70,8 @@ pa_status check_dims(const pa_dims* d, int32_t B, bool need_attention_shape) {
   return PA_OK;
 }
 
-// Splits depend only on host-known sizes (S, Hkv, MB, B, dtype), so repeated
-// calls agree.  A split boundary is both a 16-slot tile boundary and a block
+// Splits depend only on host-known sizes (S, Hq, Hkv, MB, B, dtype and the
+// query-token count T), so repeated calls agree.  A split boundary is both a 16-slot tile boundary and a block
 // boundary: split p covers tokens [p*tps, (p+1)*tps) with tps a multiple of
 // max(16, B).  Returns (P, tps).
 //   bf16 (matrix-core kernel, kMfmaWaves waves per work item): about one
@@ -82,7 +82,7 @@ pa_status check_dims(const pa_dims* d, int32_t B, bool need_attention_shape) {
 //     split keeping at least 8 tiles.
 // Several query tokens multiply the work items by the token groups (TG), so
 // fewer splits reach the same wave count.  The shared-tile kernel (bf16, more
-// tokens than two waves' columns) streams each tile once per workgroup of
+// tokens than two 16-column sets hold) streams each tile once per workgroup of
 // kSharedTileWaves waves, all of which walk every tile of the split: about
 // two workgroups per CU (2048 waves), each split keeping at least 16 tiles
 // (more splits measured slower for 32 x 4096 tokens).
@@ -107,7 +107,6 @@ void plan_splits(const pa_dims* d, int32_t B, int32_t T, int* P_out, int* tps_ou
     const int64_t min_tokens = shared ? 256 : (mfma ? 64 * pa::kMfmaWaves : 128);
     const int64_t maxP = (max_tokens + min_tokens - 1) / min_tokens;
     P = P < 1 ? 1 : (P > maxP ? maxP : P);
-    if (P < 1) P = 1;
   }
   if (P > units) P = units;
   const int64_t upp = (units + P - 1) / P;  // units per split

@@ -244,3 +244,27 @@ def test_table_entries_past_the_history_may_hold_anything(B, dtype):
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(out), host_bits(base))
     assert_close(host_f32(out), ref, dtype, f"garbage padding B={B}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_bad_lengths_and_out_of_pool_entries_poison_only_their_request(dtype):
+    """Device-resident values are the caller's contract, but a length past MB*B, a
+    negative length, or a table entry outside [0, NB) below ceil(n/B) yields NaN for
+    that request only, without any access outside the buffers; the other requests
+    still match the oracle."""
+    banner(f"bad lengths / out-of-pool entries {dtype}")
+    lens = [40, 70, 33, 20, 100]
+    b = W.custom(lens, Hq=8, Hkv=2, dtype=dtype, device=DEV, seed=16, spare_blocks=2)
+    ref = HostLayer(b, 0).oracle()
+    tab = b.block_tables.clone()
+    tab[1, 2] = b.NB + 5          # inside the history of request 1 (70 tokens = 5 blocks)
+    ln = b.seq_lens.clone()
+    ln[2] = b.MB * b.B + 1        # longer than the table can describe
+    ln[3] = -3
+    out = pa.paged_attn_decode(b.q[0], b.k_pool[0], b.v_pool[0], tab, ln, b.B, b.scale)
+    torch.cuda.synchronize()
+    got = host_f32(out)
+    for s_ in (1, 2, 3):
+        assert np.all(np.isnan(got[s_])), s_
+    for s_ in (0, 4):
+        assert_close(got[s_], ref[s_], dtype, f"request {s_}")

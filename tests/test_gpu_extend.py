@@ -254,3 +254,28 @@ def test_speculative_loop_with_rollback():
         bm.check()
     # the first step copies the shared 5-token tail for all but the last branch
     assert copies >= 3
+
+
+@pytest.mark.parametrize("T", [4, 40])
+def test_bad_lengths_and_out_of_pool_entries_poison_only_their_request(T):
+    """As for the decode: NaN for the request with a bad length or an out-of-pool
+    entry inside its history, the oracle's answer for the others (decode-kernel and
+    shared-tile variants)."""
+    banner(f"extend bad inputs T={T}")
+    lens = [60, 90, 50, 45, 120]
+    b = W.extend_batch(lens, T, Hq=8, Hkv=2, seed=97 + T, device=DEV)
+    host = HostExtend(b)
+    pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
+    ref = host.oracle()
+    tab = b.block_tables.clone()
+    tab[1, 1] = -9
+    ln = b.seq_lens.clone()
+    ln[2] = b.MB * b.B + 16
+    ln[3] = -1
+    out = pa.paged_attn_extend(b.q, b.k_pool, b.v_pool, tab, ln, b.B, b.scale)
+    torch.cuda.synchronize()
+    got = host_f32(out)
+    for s_ in (1, 2, 3):
+        assert np.all(np.isnan(got[s_])), s_
+    for s_ in (0, 4):
+        assert_close(got[s_], ref[s_], torch.bfloat16, f"request {s_}")

@@ -205,11 +205,16 @@ def suite(torch, pa, W, dev):
         us = graph_time_us(torch, launch_all, reps)
         return us / len(calls), calls[0].splits
 
-    def full_step_graph(b):
+    def full_step_graph(b, fused=False):
         def step():
             if b.cow_src.numel():
                 pa.kv_cow_copy(b.k_pool, b.v_pool, b.cow_src, b.cow_dst, b.cow_n, b.B)
             for layer in range(b.L):
+                if fused:  # the step's one append round inside the decode launch
+                    pa.paged_attn_decode_append(b.q[layer], b.k_pool[layer], b.v_pool[layer], b.k_new[0, layer],
+                                                b.v_new[0, layer], b.block_tables, b.append_positions[0],
+                                                b.seq_lens, b.B, b.scale, out=outs[layer], workspace=ws)
+                    continue
                 for r in range(b.rounds):
                     pa.kv_append(b.k_pool[layer], b.v_pool[layer], b.k_new[r, layer], b.v_new[r, layer],
                                  b.block_tables, b.append_positions[r], b.B)
@@ -286,6 +291,9 @@ def suite(torch, pa, W, dev):
             ent["full_step_us"] = round(step_us, 2)
             ent["full_step_ops"] = ("kv_cow_copy, " if b.cow_src.numel() else "") + \
                 f"{b.rounds} kv_append round(s) and one decode per layer, {b.L} layer(s)"
+            if b.rounds == 1 and not b.cow_src.numel():
+                ent["full_step_fused_us"] = round(full_step_graph(b, fused=True), 2)
+                ent["full_step_fused_ops"] = f"one paged_attn_decode_append per layer, {b.L} layer(s)"
         if name.startswith("bf16 256 mixed"):
             ent["swap_500MiB"] = swap_time(torch, pa, b, dev)
         if name.startswith("bf16 prefix"):

@@ -122,6 +122,26 @@ pa_status paged_attn_decode(const void* q, const void* k_pool, const void* v_poo
                             const pa_dims* dims);
 
 /*
+ * One decode step with the step's token appended in the same call:
+ * kv_append(k_pool, v_pool, k_new, v_new, block_tables, positions, B) then
+ * paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, B, scale,
+ * out), with the same results bit for bit (the append order of [Slides]
+ * "写满一块，再拿下一块" and the attention of paged_attn_decode).  k_new / v_new
+ * are [S, Hkv, d] of `dtype`, positions int32 [S] (negative: no append for
+ * that request), all device memory; seq_lens counts the appended token.
+ * With bf16 one kernel does both: the work item that attends position
+ * positions[s] of KV head g writes that head's row into the pool and uses
+ * the new K/V for the position directly, so one launch replaces two.  With
+ * float32 the two kernels run one after the other on `stream`.  The target
+ * block must be in the table and privately owned (copy-on-write first, as
+ * for kv_append).  Workspace and splits as for paged_attn_decode.
+ */
+pa_status paged_attn_decode_append(const void* q, const void* k_pool, const void* v_pool, const void* k_new,
+                                   const void* v_new, const int32_t* block_tables, const int32_t* positions,
+                                   const int32_t* seq_lens, int32_t B, float scale, float* out, hipStream_t stream,
+                                   const pa_dims* dims);
+
+/*
  * Split-K plan for paged_attn_extend with num_q_tokens (T >= 1) query tokens
  * per request; T = 1 gives paged_attn_plan's answer.  The workspace holds
  * partial states for S*T*Hq rows.

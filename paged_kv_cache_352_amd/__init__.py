@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     load,
     make_dims,
     paged_attn_decode,
+    paged_attn_decode_append,
     paged_attn_extend,
     paged_attn_extend_plan,
     paged_attn_plan,

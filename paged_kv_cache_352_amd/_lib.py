@@ -62,6 +62,7 @@ def load():
         "pa_last_error": (ctypes.c_char_p, []),
         "paged_attn_plan": (I32, [DP, I32, ctypes.POINTER(I32), ctypes.POINTER(SZ)]),
         "paged_attn_decode": (I32, [P, P, P, P, P, I32, F32, P, P, DP]),
+        "paged_attn_decode_append": (I32, [P, P, P, P, P, P, P, P, I32, F32, P, P, DP]),
         "paged_attn_extend_plan": (I32, [DP, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(SZ)]),
         "paged_attn_extend": (I32, [P, P, P, P, P, I32, I32, F32, P, P, DP]),
         "kv_append": (I32, [P, P, P, P, P, P, I32, P, DP]),
@@ -201,6 +202,34 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, B, scale, out=N
     _check("paged_attn_decode", lib.paged_attn_decode(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), B, ctypes.c_float(scale),
         _ptr(out), _stream(stream), ctypes.byref(d)))
+    return out
+
+
+def paged_attn_decode_append(q, k_pool, v_pool, k_new, v_new, block_tables, positions, seq_lens, B, scale, out=None,
+                             num_splits=0, workspace=None, stream=None):
+    """kv_append(k_new, v_new at positions) then paged_attn_decode, in one call (one kernel for bf16)."""
+    lib = load()
+    if q.dim() != 3:
+        raise PagedAttnError("paged_attn_decode_append takes q [S, Hq, d]")
+    S, Hq, D, NB, Hkv, MB = _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, B, out)
+    if tuple(k_new.shape) != (S, Hkv, D) or tuple(v_new.shape) != (S, Hkv, D):
+        raise PagedAttnError("k_new/v_new must be [S, Hkv, d]")
+    if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype:
+        raise PagedAttnError("k_new/v_new must have the pool dtype")
+    if positions.dtype != torch.int32 or tuple(positions.shape) != (S,):
+        raise PagedAttnError("positions must be int32 [S]")
+    if out is None:
+        out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
+    _need_cuda(q, k_pool, v_pool, k_new, v_new, block_tables, positions, seq_lens, out)
+    P, need = paged_attn_plan(S, Hq, Hkv, D, MB, NB, q.dtype, B, num_splits)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _need_cuda(workspace)
+    d = make_dims(S, Hq, Hkv, D, MB, NB, q.dtype, num_splits, workspace)
+    _check("paged_attn_decode_append", lib.paged_attn_decode_append(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), _ptr(block_tables), _ptr(positions),
+        _ptr(seq_lens), B, ctypes.c_float(scale), _ptr(out), _stream(stream), ctypes.byref(d)))
     return out
 
 

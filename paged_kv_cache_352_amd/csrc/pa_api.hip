@@ -157,9 +157,14 @@ static pa_status plan_common(const pa_dims* dims, int32_t B, int32_t T, int32_t*
 
 // Validation, split plan and launch shared by the one-token decode (T = 1)
 // and the several-token causal form.
+static pa_status kv_common(const pa_dims* dims, int32_t B, void* k_pool, void* v_pool, pa::KvArgs* a);
+
+// k_new / v_new / positions non-NULL: append the step's token first (fused
+// into the bf16 decode kernel; fp32 runs the append kernel, then the decode).
 static pa_status attend(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
                         const int32_t* seq_lens, int32_t T, int32_t B, float scale, float* out, hipStream_t stream,
-                        const pa_dims* dims) {
+                        const pa_dims* dims, const void* k_new = nullptr, const void* v_new = nullptr,
+                        const int32_t* positions = nullptr) {
   pa_status st = check_dims(dims, B, true);
   if (st != PA_OK) return st;
   if (T < 1) return fail(PA_ERR_INVALID_ARG, "num_q_tokens = %d < 1", T);
@@ -194,6 +199,14 @@ static pa_status attend(const void* q, const void* k_pool, const void* v_pool, c
   a.tps = tps;
   a.T = T;
   a.TG = (int)TG;
+  if (k_new) {
+    if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(PA_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
+    if (dims->dtype == PA_BF16) {
+      a.k_new = k_new;
+      a.v_new = v_new;
+      a.positions = positions;
+    }
+  }
   if (P > 1) {
     const size_t need = pa::decode_workspace_floats(rows, P) * sizeof(float);
     if (!dims->workspace || dims->workspace_bytes < need)
@@ -205,6 +218,14 @@ static pa_status attend(const void* q, const void* k_pool, const void* v_pool, c
     a.ws_o = ws;
     a.ws_m = ws + no;
     a.ws_l = ws + no + (size_t)rows * P;
+  }
+  if (k_new && dims->dtype != PA_BF16) {
+    pa::KvArgs ka{};
+    st = kv_common(dims, B, const_cast<void*>(k_pool), const_cast<void*>(v_pool), &ka);
+    if (st != PA_OK) return st;
+    st = launched(pa::launch_append(ka, static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new),
+                                    block_tables, positions, 1, stream));
+    if (st != PA_OK) return st;
   }
   return launched(pa::launch_decode(a, dims->dtype, B, a.Hq / a.Hkv, stream));
 }
@@ -225,6 +246,16 @@ pa_status paged_attn_decode(const void* q, const void* k_pool, const void* v_poo
                             const pa_dims* dims) {
   g_last_error.clear();
   return attend(q, k_pool, v_pool, block_tables, seq_lens, 1, B, scale, out, stream, dims);
+}
+
+pa_status paged_attn_decode_append(const void* q, const void* k_pool, const void* v_pool, const void* k_new,
+                                   const void* v_new, const int32_t* block_tables, const int32_t* positions,
+                                   const int32_t* seq_lens, int32_t B, float scale, float* out, hipStream_t stream,
+                                   const pa_dims* dims) {
+  g_last_error.clear();
+  if (dims && dims->num_seqs > 0 && (!k_new || !v_new || !positions))
+    return fail(PA_ERR_INVALID_ARG, "k_new, v_new and positions are required");
+  return attend(q, k_pool, v_pool, block_tables, seq_lens, 1, B, scale, out, stream, dims, k_new, v_new, positions);
 }
 
 pa_status paged_attn_extend(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,

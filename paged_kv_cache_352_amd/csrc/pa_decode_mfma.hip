@@ -88,12 +88,14 @@ struct Tile {
 };
 
 // NS: 16-column sets per wave (2 only with several query tokens: each K and
-// V operand a wave reads from LDS then feeds both sets).
-template <int G, bool kCausal, int NS, int W, int B>
+// V operand a wave reads from LDS then feeds both sets).  kAppend: the step's
+// new token is appended in the same launch (one query token only).
+template <int G, bool kCausal, int NS, int W, int B, bool kAppend = false>
 __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   static_assert(G >= 1 && G <= 16, "the query group must fit the 16 columns of one MFMA tile");
   static_assert(B >= 4 && B <= 64 && (B & (B - 1)) == 0, "block size: a power of two from 4 to 64");
   static_assert(NS == 1 || (NS == 2 && kCausal), "two column sets only for several query tokens");
+  static_assert(!(kAppend && kCausal), "the fused append is for one query token");
   constexpr int TC = kCausal ? (G >= 16 ? 1 : 16 / G) : 1;  // query tokens per column set
   constexpr int NC = G * TC;                                  // MFMA columns in use per set
   __shared__ __attribute__((aligned(16))) uint8_t vt_all[W][kVtBytes];
@@ -147,6 +149,22 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   const int n_raw = __builtin_amdgcn_readfirstlane(
       (int)__builtin_amdgcn_raw_buffer_load_b32(block_rsrc(reinterpret_cast<const char*>(a.lens), (uint32_t)a.S * 4u),
                                                 0, s * 4, 0));
+
+  // Fused append ([Slides] "写满一块，再拿下一块"): the new token of request s
+  // goes to logical position pos.  This lane keeps 16 bytes of its K and V
+  // (dims 8*n16 .. +8 of KV head kvh), which replace the pool's row for pos
+  // wherever a tile holds it, so this step never reads the slot it writes;
+  // the work item whose split holds pos writes the row into the pool for
+  // the steps that follow.  The result is bit for bit that of kv_append
+  // followed by the decode.
+  int pos = -1;
+  uint4 k_in = make_uint4(0, 0, 0, 0), v_in = make_uint4(0, 0, 0, 0);
+  if constexpr (kAppend) {
+    pos = a.positions[s];
+    const int64_t src = ((int64_t)s * a.Hkv + kvh) * kHeadDim + 8 * n16;
+    k_in = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.k_new) + src);
+    v_in = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v_new) + src);
+  }
 
   // Byte offsets inside a block (a block is at most a few hundred KiB, so 32
   // bits suffice).  A load is a block descriptor (uniform, in SGPRs) plus the
@@ -247,6 +265,21 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
     }
   }
 
+  if constexpr (kAppend) {
+    // The work item whose split holds pos writes the new row (16 lanes of
+    // wave 0, 16 bytes each of K and V); a position or block outside the
+    // table or the pool is skipped, as kv_append skips it.
+    const bool mine = a.P == 1 || pos / a.tps == p;
+    if (mine && w == 0 && c4 == 0 && pos >= 0 && (int64_t)pos < (int64_t)a.MB * B) {
+      const int blk = trow[pos / B];
+      if (blk >= 0 && blk < a.NB) {
+        const int64_t dst = (((int64_t)blk * B + pos % B) * a.Hkv + kvh) * kHeadDim + 8 * n16;
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(const_cast<void*>(a.k_pool)) + dst) = k_in;
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(const_cast<void*>(a.v_pool)) + dst) = v_in;
+      }
+    }
+  }
+
   float m[NS];         // running max (base 2) of column n16
   float l[NS];         // partial sum over this lane's slots
   f32x4_t acc[NS][8];  // o: columns 4*c4 + r, dims 16*jj + n16
@@ -269,9 +302,16 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * i + c4;
+      uint4 kk = cur.k[i];
       uint4 vv = cur.v[i];
+      if constexpr (kAppend) {
+        if (u * kTile + r == pos) {  // the token this step appends
+          kk = k_in;
+          vv = v_in;
+        }
+      }
       if (r >= valid) vv = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(kt + 256 * r + 16 * (n16 ^ r)) = cur.k[i];
+      *reinterpret_cast<uint4*>(kt + 256 * r + 16 * (n16 ^ r)) = kk;
       *reinterpret_cast<uint4*>(vt + 256 * r + 16 * (n16 ^ r)) = vv;
     }
     wave_lds_order();
@@ -380,6 +420,13 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
 template <int G, bool kCausal, int B>
 hipError_t launch_gb(const DecodeArgs& a, hipStream_t stream) {
   const int items = a.Hkv * a.S * a.P * (kCausal ? a.TG : 1);
+  if constexpr (!kCausal) {
+    if (a.k_new) {
+      hipLaunchKernelGGL((decode_mfma_kernel<G, false, 1, kMfmaWaves, B, true>), dim3(items),
+                         dim3(kWave * kMfmaWaves), 0, stream, a);
+      return hipGetLastError();
+    }
+  }
   if constexpr (kCausal) {
     if (decode_column_sets(PA_BF16, G, a.T) == 2) {
       hipLaunchKernelGGL((decode_mfma_kernel<G, true, 2, kMfmaWaves, B>), dim3(items), dim3(kWave * kMfmaWaves), 0,

@@ -28,6 +28,9 @@ struct DecodeArgs {
   int S, Hq, Hkv, MB, NB;
   int P;            // number of splits
   int tps;          // tokens per split: split p covers tokens [p*tps, (p+1)*tps), a multiple of max(16, B)
+  const void* k_new;          // fused append (bf16 decode only): new K/V [S, Hkv, d] written at
+  const void* v_new;          //   positions[s] and used for that position in this step; NULL
+  const int32_t* positions;   //   otherwise
   int T;            // query tokens per request (q is [S, T, Hq, d]); the last T of the history, causal
   int TG;           // work items per (request, KV head, split) along the query tokens: ceil(T / tokens per item)
 };

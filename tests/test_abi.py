@@ -50,6 +50,7 @@ def test_exports_every_declared_symbol(lib):
     names = pa.declared_functions()
     assert {"paged_attn_decode", "kv_append", "kv_cow_copy", "paged_kv_gather", "paged_attn_plan",
             "paged_attn_extend", "paged_attn_extend_plan", "kv_append_tokens", "pa_bm_truncate",
+            "paged_attn_decode_append",
             "pa_bm_prepare_extend"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
@@ -190,3 +191,17 @@ def test_extend_and_token_append_reject_before_launch(lib):
     assert lib.kv_append_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 16, None, ctypes.byref(d)) == INVALID
     assert lib.kv_append_tokens(FAKE, FAKE, None, FAKE, FAKE, FAKE, 3, 16, None, ctypes.byref(d)) == INVALID
     assert lib.kv_append_tokens(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 0, None, ctypes.byref(d)) == INVALID
+
+
+@no_gpu
+def test_decode_append_rejects_before_launch(lib):
+    d = dims()
+    f = lambda kn=FAKE, vn=FAKE, pos=FAKE, B=16: lib.paged_attn_decode_append(
+        FAKE, FAKE, FAKE, kn, vn, FAKE, pos, FAKE, B, ctypes.c_float(0.1), FAKE, None, ctypes.byref(d))
+    assert f(kn=None) == INVALID
+    assert f(pos=None) == INVALID
+    assert f(vn=ctypes.c_void_p(0x7F0000000008)) == INVALID  # misaligned
+    assert f(B=12) == UNSUPPORTED
+    e = dims(S=0)
+    assert lib.paged_attn_decode_append(None, None, None, None, None, None, None, None, 16, ctypes.c_float(0.1),
+                                        None, None, ctypes.byref(e)) == OK

@@ -10,7 +10,7 @@ import torch
 import paged_kv_cache_352_amd as pa
 import workloads as W
 from oracle import kvcache as kvc
-from tests.gpu_util import banner, host_bits
+from tests.gpu_util import HostLayer, assert_close, banner, host_bits, host_f32
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -151,3 +151,57 @@ def test_swap_out_and_in_bit_exact(pinned, dtype):
     want_k, want_v = kvc.swap_in(k0, v0, spare, kvc.swap_out(k0, v0, out_ids))
     assert np.array_equal(host_bits(b.k_pool), want_k)
     assert np.array_equal(host_bits(b.v_pool), want_v)
+
+
+def _fused_vs_two_step(b, layer, splits):
+    """Run kv_append + paged_attn_decode on copies of the pools and the fused call
+    on the originals; return (two-step out, fused out, pools of each)."""
+    k2, v2 = b.k_pool[layer].clone(), b.v_pool[layer].clone()
+    pa.kv_append(k2, v2, b.k_new[0, layer], b.v_new[0, layer], b.block_tables, b.append_positions[0], b.B)
+    ref = pa.paged_attn_decode(b.q[layer], k2, v2, b.block_tables, b.seq_lens, b.B, b.scale, num_splits=splits)
+    k1, v1 = b.k_pool[layer], b.v_pool[layer]
+    got = pa.paged_attn_decode_append(b.q[layer], k1, v1, b.k_new[0, layer], b.v_new[0, layer], b.block_tables,
+                                      b.append_positions[0], b.seq_lens, b.B, b.scale, num_splits=splits)
+    torch.cuda.synchronize()
+    return ref, got, (k2, v2), (k1, v1)
+
+
+@pytest.mark.parametrize("make,splits", [("config3", 0), ("config3", 3), ("config5", 0), ("config5", 4)])
+def test_decode_append_fused_equals_two_step(make, splits):
+    """One fused launch gives the same output and the same pools, bit for bit, as
+    kv_append followed by paged_attn_decode (mixed lengths including histories
+    0, 1, 16 and 17; a token going into a fresh block)."""
+    banner(f"fused append+decode vs two-step: {make} splits={splits}")
+    b = getattr(W, make)(device=DEV, layers=1)
+    ref, got, (k2, v2), (k1, v1) = _fused_vs_two_step(b, 0, splits)
+    assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
+    assert np.array_equal(host_bits(k1), host_bits(k2)) and np.array_equal(host_bits(v1), host_bits(v2))
+
+
+@pytest.mark.parametrize("B,dtype", [(4, torch.bfloat16), (64, torch.bfloat16), (16, torch.float32),
+                                     (8, torch.float32)])
+def test_decode_append_fused_block_sizes_and_fp32(B, dtype):
+    banner(f"fused append+decode B={B} {dtype}")
+    lens = [1, 2, B, B + 1, 2 * B + 3, 150, 300]
+    b = W.custom(lens, Hq=8, Hkv=2, B=B, dtype=dtype, append=True, device=DEV, seed=31)
+    ref, got, (k2, v2), (k1, v1) = _fused_vs_two_step(b, 0, 0)
+    assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
+    assert np.array_equal(host_bits(k1), host_bits(k2)) and np.array_equal(host_bits(v1), host_bits(v2))
+    # and against the oracle
+    host = HostLayer(b, 0)
+    assert_close(host_f32(got), host.oracle(), dtype, f"fused B={B}")
+
+
+def test_decode_append_skips_negative_positions():
+    """A negative position writes nothing (the pool keeps its bytes), as kv_append."""
+    banner("fused append+decode skips")
+    b = W.custom([20, 33, 17, 50], Hq=8, Hkv=2, dtype=torch.bfloat16, append=True, device=DEV, seed=32)
+    pos = b.append_positions[0].clone()
+    pos[1] = -1
+    tab = b.block_tables
+    ref_k = b.k_pool[0].clone()
+    k1, v1 = b.k_pool[0], b.v_pool[0]
+    pa.paged_attn_decode_append(b.q[0], k1, v1, b.k_new[0, 0], b.v_new[0, 0], tab, pos, b.seq_lens, b.B, b.scale)
+    torch.cuda.synchronize()
+    want = kvc.append(host_bits(ref_k), host_bits(b.k_new[0, 0]), tab.cpu().numpy(), pos.cpu().numpy(), b.B)
+    assert np.array_equal(host_bits(k1), want)

@@ -21,8 +21,10 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def test_manager_cow_append_decode_matches_dense_histories():
-    banner("block manager: 8 branches over a shared 2053-token prefix, 24 steps")
+@pytest.mark.parametrize("fused", [False, True])
+def test_manager_cow_append_decode_matches_dense_histories(fused):
+    """With fused=True each step's append runs inside paged_attn_decode_append."""
+    banner(f"block manager: 8 branches over a shared 2053-token prefix, 24 steps, fused={fused}")
     rng = np.random.default_rng(77)
     NB, B, MB, Hq, Hkv, D = 512, 16, 160, 32, 8, 128
     scale = float(np.float32(1.0 / np.sqrt(D)))
@@ -65,8 +67,13 @@ def test_manager_cow_append_decode_matches_dense_histories():
             pa.kv_cow_copy(k_pool, v_pool, *(torch.as_tensor(x, device=DEV) for x in (cs, cd, cn)), B)
         k_new, v_new, q = rand(S, Hkv, D), rand(S, Hkv, D), rand(S, Hq, D)
         t_tab = torch.as_tensor(tables, device=DEV)
-        pa.kv_append(k_pool, v_pool, k_new.to(DEV), v_new.to(DEV), t_tab, torch.as_tensor(pos, device=DEV), B)
-        out = pa.paged_attn_decode(q.to(DEV), k_pool, v_pool, t_tab, torch.as_tensor(lens, device=DEV), B, scale)
+        t_pos, t_lens = torch.as_tensor(pos, device=DEV), torch.as_tensor(lens, device=DEV)
+        if fused:
+            out = pa.paged_attn_decode_append(q.to(DEV), k_pool, v_pool, k_new.to(DEV), v_new.to(DEV), t_tab, t_pos,
+                                              t_lens, B, scale)
+        else:
+            pa.kv_append(k_pool, v_pool, k_new.to(DEV), v_new.to(DEV), t_tab, t_pos, B)
+            out = pa.paged_attn_decode(q.to(DEV), k_pool, v_pool, t_tab, t_lens, B, scale)
         torch.cuda.synchronize()
         got = out.cpu().numpy()
         for i, r in enumerate(branches):

@@ -102,7 +102,9 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t kt_all[W][kVtBytes];
   __shared__ float red_m[W][16];
   __shared__ float red_l[W][16];
-  __shared__ __attribute__((aligned(16))) float red_o[W][NC][kHeadDim];
+  // o per wave and column; rows padded by 4 floats so that the four lane groups of a
+  // store land in different banks
+  __shared__ __attribute__((aligned(16))) float red_o[W][NC][kHeadDim + 4];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
@@ -352,7 +354,9 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
 
   // Merge the W wave states ([Budgets] eq. (4) applied across disjoint block
   // sets): M = max m_w, L = sum 2^(m_w - M) l_w, O = sum 2^(m_w - M) o_w;
-  // one column set after the other through the same LDS.
+  // one column set after the other through the same LDS.  Each wave leaves
+  // its m, l and unscaled o there; one barrier later every thread finishes
+  // two adjacent outputs of one column.
   const float nan = __builtin_nanf("");
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
@@ -365,49 +369,49 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
       red_m[w][n16] = m[j];
       red_l[w][n16] = lj;
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int hg = 4 * c4 + r;
+      if (hg < NC) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) red_o[w][hg][16 * jj + n16] = acc[j][jj][r];
+      }
+    }
     if (j == 0) {
       bad = __syncthreads_or(bad);  // any wave that met an entry outside the pool
     } else {
       __syncthreads();
     }
-    float mh = kNegInf;  // M of column n16
-#pragma unroll
-    for (int v = 0; v < W; ++v) mh = fmaxf(mh, red_m[v][n16]);
-    // scale of this wave's state for column n16 (0 for a wave that saw no block)
-    const float f = (m[j] == kNegInf) ? 0.f : fast_exp2(m[j] - mh);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int hg = 4 * c4 + r;
-      const float fr = __shfl(f, hg & 15, kWave);
-      if (hg < NC) {
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) red_o[w][hg][16 * jj + n16] = acc[j][jj][r] * fr;
-      }
-    }
-    __syncthreads();
 
     // NC * 128 outputs (column hg = query token (tg*NS + j)*TC + hg/G, head
-    // kvh*G + hg%G), spread over the workgroup's threads.
-    for (int idx = threadIdx.x; idx < NC * kHeadDim; idx += kWave * W) {
-      const int hg = idx / kHeadDim;
-      const int d = idx % kHeadDim;
+    // kvh*G + hg%G), two adjacent dims per thread.
+    for (int idx = threadIdx.x; idx < NC * (kHeadDim / 2); idx += kWave * W) {
+      const int hg = idx / (kHeadDim / 2);
+      const int d = 2 * (idx % (kHeadDim / 2));
       const int t_out = (tg * NS + j) * TC + hg / G;
       if (kCausal && t_out >= a.T) break;  // idx only grows: every later output is past T too
-      float M = kNegInf, L = 0.f, O = 0.f;
+      float M = kNegInf;
 #pragma unroll
       for (int v = 0; v < W; ++v) M = fmaxf(M, red_m[v][hg]);
+      float L = 0.f, O0 = 0.f, O1 = 0.f;
 #pragma unroll
       for (int v = 0; v < W; ++v) {
         const float mv = red_m[v][hg];
-        if (mv != kNegInf) L = fmaf(fast_exp2(mv - M), red_l[v][hg], L);
-        O += red_o[v][hg][d];
+        // scale of wave v's state (0 for a wave that saw no valid slot)
+        const float f = mv == kNegInf ? 0.f : fast_exp2(mv - M);
+        if (mv != kNegInf) L = fmaf(f, red_l[v][hg], L);
+        const float2 o = *reinterpret_cast<const float2*>(&red_o[v][hg][d]);
+        O0 = fmaf(o.x, f, O0);
+        O1 = fmaf(o.y, f, O1);
       }
       const int64_t row = ((int64_t)s * a.T + t_out) * a.Hq + kvh * G + hg % G;  // [S, T, Hq] row
       if (a.P == 1) {
-        a.out[row * kHeadDim + d] = bad ? nan : (L > 0.f ? O / L : 0.f);
+        const float2 r = bad ? make_float2(nan, nan)
+                             : (L > 0.f ? make_float2(O0 / L, O1 / L) : make_float2(0.f, 0.f));
+        *reinterpret_cast<float2*>(a.out + row * kHeadDim + d) = r;
       } else {
         const int64_t slot = row * a.P + p;
-        a.ws_o[slot * kHeadDim + d] = O;
+        *reinterpret_cast<float2*>(a.ws_o + slot * kHeadDim + d) = make_float2(O0, O1);
         if (d == 0) {
           a.ws_m[slot] = bad ? 0.f : M;
           a.ws_l[slot] = bad ? nan : L;

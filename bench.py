@@ -277,6 +277,37 @@ def suite(torch, pa, W, dev):
     del b, call
     torch.cuda.empty_cache()
 
+    # The attention part of recomputing a swapped-out request's KV instead of
+    # swapping it back ([Slides] recovery-cost example: 4,000 tokens, 32
+    # layers): the whole prompt again in 512-token chunks, chunk c attending
+    # the request's pages up to its own last token.  The projections that
+    # produce K and V are not part of this library, so this is a lower bound
+    # on recomputation; one layer is timed and the 32 layers are 32 times it.
+    n_re, chunk, layers_re = 4000, 512, 32
+    b = W.extend_batch([n_re], n_re, seed=360, device=dev, name="reprefill_bf16_1x4000")
+    pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
+    calls = []
+    for c0 in range(0, n_re, chunk):
+        t_c = min(chunk, n_re - c0)
+        lens_c = torch.tensor([c0 + t_c], dtype=torch.int32, device=dev)
+        calls.append(pa.DecodeLaunch(b.q[:, c0:c0 + t_c].contiguous(), b.k_pool, b.v_pool, b.block_tables, lens_c,
+                                     b.B, b.scale))
+
+    def reprefill():
+        for c in calls:
+            c.launch()
+
+    us = graph_time_us(torch, reprefill, 5)
+    flops = 4 * b.D * b.Hq * n_re * (n_re + 1) // 2  # position t of the prompt sees t + 1 positions
+    out[f"bf16 re-prefill attention, one {n_re}-token request in {chunk}-token chunks"] = dict(
+        us_per_layer=round(us, 2), chunks=len(calls), TFLOP_s=round(flops / (us * 1e-6) / 1e12, 2),
+        frac_bf16_mfma_peak=round(flops / (us * 1e-6) / 2.5e15, 4),
+        ms_for_32_layers=round(us * layers_re / 1e3, 3),
+        note="attention only (K/V projections are outside this library): a lower bound on recomputing "
+             "the KV that swap_500MiB moves")
+    del b, calls
+    torch.cuda.empty_cache()
+
     for name, make, rows in (("fp32 5 requests (37..511 tokens), one layer", W.config1, None),
                              ("bf16 256 mixed-length requests, 32 layers", W.config3, None),
                              ("bf16 prefix sharing, 64 branches (COW), one layer", W.config4, None),

@@ -198,6 +198,27 @@ def test_prefill_chunk_512_sampled():
     assert np.all(np.isfinite(out))
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_chunked_prefill_matches_one_pass(dtype):
+    """A whole prompt in chunks, as when a swapped-out request's KV is recomputed:
+    chunk c attends the request's pages up to its own last token, and the chunks
+    together equal one causal pass over the prompt.  Chunks of 256, 256, 83 and 5
+    tokens take the shared-tile kernel and then the decode kernel's causal form."""
+    banner(f"extend {dtype} chunked prefill 600 = 256 + 256 + 83 + 5")
+    n, bounds = 600, [0, 256, 512, 595, 600]
+    b = W.extend_batch([n], n, Hq=8, Hkv=2, dtype=dtype, seed=61, device=DEV)  # every token new
+    host = HostExtend(b)
+    ref = host.oracle()  # [1, n, Hq, d]: causal over the whole prompt
+    pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
+    outs = []
+    for c0, c1 in zip(bounds[:-1], bounds[1:]):
+        lens_c = torch.tensor([c1], dtype=torch.int32, device=DEV)
+        outs.append(pa.paged_attn_extend(b.q[:, c0:c1].contiguous(), b.k_pool, b.v_pool, b.block_tables, lens_c,
+                                         b.B, b.scale))
+    torch.cuda.synchronize()
+    assert_close(host_f32(torch.cat(outs, dim=1)), ref, dtype, "chunked prefill")
+
+
 def test_speculative_loop_with_rollback():
     """Branches over a shared 1029-token prefix; each step reserves T = 4 draft
     positions (copying a shared partial tail first), appends the drafts, verifies

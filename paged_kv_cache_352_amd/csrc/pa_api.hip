@@ -79,7 +79,10 @@ pa_status check_dims(const pa_dims* d, int32_t B, bool need_attention_shape) {
 //     Measured on 32 x 4096 tokens: every extra split costs more in partial
 //     states and their merge than the added parallelism returns;
 //   fp32 (vector-ALU kernel, one wave per work item): about 2048 waves, each
-//     split keeping at least 8 tiles.
+//     split keeping at least 2 tiles.  A wave walks its blocks one dependent
+//     read after another, so few requests want many short splits: 5 requests
+//     of at most 511 tokens took 24.8 us with 4 splits, 16.8 us with 8 and
+//     14.1 us with 16 (merge included).
 // Several query tokens multiply the work items by the token groups (TG), so
 // fewer splits reach the same wave count.  The shared-tile kernel (bf16, more
 // tokens than two 16-column sets hold) streams each tile once per workgroup of
@@ -104,7 +107,7 @@ void plan_splits(const pa_dims* d, int32_t B, int32_t T, int* P_out, int* tps_ou
     const int64_t target = (mfma && !shared) ? 1024 : 2048;
     const int64_t per = items * waves_per_item;
     P = (target + per - 1) / (per > 0 ? per : 1);
-    const int64_t min_tokens = shared ? 256 : (mfma ? 64 * pa::kMfmaWaves : 128);
+    const int64_t min_tokens = shared ? 256 : (mfma ? 64 * pa::kMfmaWaves : 32);
     const int64_t maxP = (max_tokens + min_tokens - 1) / min_tokens;
     P = P < 1 ? 1 : (P > maxP ? maxP : P);
   }

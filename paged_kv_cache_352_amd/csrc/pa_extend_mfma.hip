@@ -54,7 +54,9 @@ __global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArg
   __shared__ __attribute__((aligned(16))) uint8_t tiles[2][2][2][kVtBytes];
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
+  // The wave index, in a scalar register: the compiler cannot see that it is
+  // uniform, and block offsets and table lanes derived from it must be scalar.
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int n16 = lane & 15;
   const int c4 = lane >> 4;
 

@@ -180,7 +180,12 @@ __global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArg
       vqa[j] = lim[j] - t * kTile;
       vqb[j] = t + 1 < te ? lim[j] - (t + 1) * kTile : 0;  // no tile b past the range
     }
-    pair_update_sets<kSets, true>(ra, rb, qv, acc, m, l, vqa, vqb, a.scale_log2, n16, c4);
+    // Below the diagonal (both tiles inside every column's limit, as for all
+    // but the last pairs of a chunk) nothing is masked and no column is empty.
+    bool full = true;
+#pragma unroll
+    for (int j = 0; j < kSets; ++j) full = full && vqb[j] >= kTile;
+    pair_update_sets<kSets, true>(ra, rb, qv, acc, m, l, vqa, vqb, a.scale_log2, n16, c4, !__all(full));
   };
 
   // Table entries are read 64 at a time into one register (one per lane), as

@@ -98,27 +98,34 @@ struct TileReads {
 //        (N = 16 columns); lane (n16, c4) gets column n16's scores for slots
 //        4*c4 .. 4*c4+3;
 //   mask slots at or past vq (the column's limit minus the tile's first
-//        slot), new running max m, weights p = 2^(s - m), partial l over the
-//        lane's four slots;
+//        slot), the column's reference m (below), weights p = 2^(s - m),
+//        partial l over the lane's four slots;
 //   p.v  p split into a bf16 head and remainder (both through the matrix
 //        core), B = V read transposed with ds_read_b64_tr_b16; acc[jj][r]
 //        holds o of column 4*c4 + r, dims 16*jj + n16.
-// The accumulators are rescaled only when some column's max moved.  With
-// kMayBeEmpty a column may have no valid slot yet (m stays -inf and its
-// state empty); without it the caller guarantees slot 0 of the tile is valid
-// for every column.
+// The running max m is a reference, not always the exact max: it moves only
+// when a tile's max exceeds it by more than kLazyMax (base 2), and then to
+// that tile's max.  Weights are taken against it, so they stay below
+// 2^kLazyMax, and l and o carry the same reference, so o / l and the merge
+// of states (which rescales by 2^(m_w - M) whatever m_w is) are unchanged;
+// the accumulators are rescaled only in the rare tiles where a reference
+// moves.  With kMayBeEmpty a column may have no valid slot yet (m stays -inf
+// and its state empty); without it the caller guarantees slot 0 of the tile
+// is valid for every column.
 // The core of the online-softmax step for one lane: sv holds the lane's R
 // scores of column n16 (base 2, already masked to -inf past the column's
-// limit); update the running max m (over the four lanes of the column,
-// which sit 16 lanes apart), the partial sum l, rescale acc when some
-// column's max moved, and leave the weights p = 2^(s - m) in pw.
+// limit); update the reference m (over the four lanes of the column, which
+// sit 16 lanes apart), the partial sum l, rescale acc when some column's
+// reference moved, and leave the weights p = 2^(s - m) in pw.
+constexpr float kLazyMax = 8.f;
+
 template <int R, bool kMayBeEmpty>
 __device__ __attribute__((always_inline)) inline void softmax_core(const float (&sv)[R], f32x4_t (&acc)[8],
                                                                    float& m, float& l, int c4, float (&pw)[R]) {
-  // Tile max over the column's slots, new running max.  v_permlane16_swap /
-  // 32_swap exchange rows of 16 / 32 lanes in the vector ALU, so the max of
-  // each returned pair is the max over the lane and its partner (lane ^ 16,
-  // then lane ^ 32) without a round trip through the LDS crossbar.
+  // Tile max over the column's slots.  v_permlane16_swap / 32_swap exchange
+  // rows of 16 / 32 lanes in the vector ALU, so the max of each returned
+  // pair is the max over the lane and its partner (lane ^ 16, then lane ^ 32)
+  // without a round trip through the LDS crossbar.
   float bm = sv[0];
 #pragma unroll
   for (int r = 1; r < R; ++r) bm = fmaxf(bm, sv[r]);
@@ -128,16 +135,13 @@ __device__ __attribute__((always_inline)) inline void softmax_core(const float (
     const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
     bm = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
   }
-  const float mn = fmaxf(m, bm);
-  float alpha, mref = mn;
-  if constexpr (kMayBeEmpty) {
-    // a column that has seen nothing yet (mn = -inf) keeps its empty state
-    alpha = (m == mn) ? 1.f : fast_exp2(m - mn);
-    mref = (mn == kNegInf) ? 0.f : mn;
-  } else {
-    alpha = fast_exp2(m - mn);
-  }
-  m = mn;
+  // A column that has seen nothing (m = -inf) moves to its first finite tile
+  // max; one whose tile is all -inf (kMayBeEmpty) keeps its empty state.
+  const bool move = bm > m + kLazyMax;
+  const float alpha = move ? fast_exp2(m - bm) : 1.f;
+  if (move) m = bm;
+  float mref = m;
+  if constexpr (kMayBeEmpty) mref = (m == kNegInf) ? 0.f : m;
 #pragma unroll
   for (int r = 0; r < R; ++r) pw[r] = fast_exp2(sv[r] - mref);
   float sum = (pw[0] + pw[1]) + (pw[2] + pw[3]);
@@ -145,8 +149,8 @@ __device__ __attribute__((always_inline)) inline void softmax_core(const float (
   for (int r = 4; r < R; r += 4) sum += (pw[r] + pw[r + 1]) + (pw[r + 2] + pw[r + 3]);
   l = fmaf(l, alpha, sum);
 
-  // Rescale o only where a column's max moved (alpha < 1 somewhere in the wave).
-  if (__any(alpha != 1.f)) {
+  // Rescale o only where a column's reference moved.
+  if (__any(move)) {
     float ar[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * c4 + r, kWave);
@@ -243,14 +247,16 @@ __device__ __attribute__((always_inline)) inline void tile_update_sets(const Til
 // instruction per issue: its K index 8*c4 + i stands for slot 4*c4 + i of
 // tile a (i < 4) or of tile b (i >= 4), so the A operand is the lane's 8
 // weights in that order and the B operand is the two transposing V reads
-// (tile a, then tile b) of the same lane side by side.
+// (tile a, then tile b) of the same lane side by side.  mask = false (the
+// same in every lane): the caller has checked that both tiles lie wholly
+// inside every column's limit, so no slot is masked.
 template <int NS, bool kMayBeEmpty>
 __device__ __attribute__((always_inline)) inline void pair_update_sets(const TileReads& ra, const TileReads& rb,
                                                                        const bf16x8_t (&qv)[NS][4],
                                                                        f32x4_t (&acc)[NS][8], float (&m)[NS],
                                                                        float (&l)[NS], const int (&vqa)[NS],
                                                                        const int (&vqb)[NS], float scale_log2,
-                                                                       int n16, int c4) {
+                                                                       int n16, int c4, bool mask = true) {
   f32x4_t sa[NS], sb[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
@@ -273,8 +279,12 @@ __device__ __attribute__((always_inline)) inline void pair_update_sets(const Til
     float sv[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sv[r] = (4 * c4 + r < vqa[j]) ? sa[j][r] * scale_log2 : kNegInf;
-      sv[4 + r] = (4 * c4 + r < vqb[j]) ? sb[j][r] * scale_log2 : kNegInf;
+      sv[r] = sa[j][r] * scale_log2;
+      sv[4 + r] = sb[j][r] * scale_log2;
+      if (mask) {
+        sv[r] = (4 * c4 + r < vqa[j]) ? sv[r] : kNegInf;
+        sv[4 + r] = (4 * c4 + r < vqb[j]) ? sv[4 + r] : kNegInf;
+      }
     }
     float pw[8];
     softmax_core<8, kMayBeEmpty>(sv, acc[j], m[j], l[j], c4, pw);

@@ -268,3 +268,40 @@ def test_bad_lengths_and_out_of_pool_entries_poison_only_their_request(dtype):
         assert np.all(np.isnan(got[s_])), s_
     for s_ in (0, 4):
         assert_close(got[s_], ref[s_], dtype, f"request {s_}")
+
+
+def _ramp_keys(b, q, k_pool, lens, step):
+    """Make head g*G of every KV head g see the logit step * (t // 64) - 40 at
+    position t (K rows parallel to that head's q, q [S, Hq, d]), so the max
+    climbs along the history in stairs of `step`.  Returns {(s, g): rows [n, d]}
+    as written."""
+    G = b.Hq // b.Hkv
+    q = q.float()
+    tables = b.block_tables.cpu().numpy()
+    out = {}
+    for s in range(b.S):
+        n = int(lens[s])
+        t = torch.arange(n, device=k_pool.device)
+        blk = torch.as_tensor(tables[s, (t // b.B).cpu().numpy()], device=k_pool.device)
+        for g in range(b.Hkv):
+            qh = q[s, g * G]
+            logit = step * (t // 64).float() - 40.0
+            rows = ((logit / (b.scale * qh.dot(qh)))[:, None] * qh[None, :]).to(k_pool.dtype)
+            k_pool[blk, t % b.B, g] = rows
+            out[(s, g)] = rows
+    return out
+
+
+@pytest.mark.parametrize("step", [5.0, 10.0])
+def test_rising_logits(step):
+    """Logits climbing along the history in stairs of 5 or 10 (7.2 and 14.4 in base 2, below
+    and above the 8 by which a tile's max must exceed the matrix-core kernels' reference
+    before it moves), up to about 190: the reference moves many times or never after the
+    first tiles, and the last stair dominates the output."""
+    banner(f"decode bf16 rising logits, stairs of {step}")
+    b = W.custom([100, 600, 1500], Hq=8, Hkv=2, dtype=torch.bfloat16, seed=70, device=DEV)
+    _ramp_keys(b, b.q[0], b.k_pool[0], b.seq_lens.cpu().numpy(), step)
+    host = HostLayer(b, 0)
+    out = gpu_step(b)[0]
+    torch.cuda.synchronize()
+    assert_close(host_f32(out), host.oracle(), torch.bfloat16, f"rising logits step {step}")

@@ -219,6 +219,26 @@ def test_chunked_prefill_matches_one_pass(dtype):
     assert_close(host_f32(torch.cat(outs, dim=1)), ref, dtype, "chunked prefill")
 
 
+@pytest.mark.parametrize("T", [5, 40])
+def test_rising_logits(T):
+    """Logits climbing along the history in stairs of 10 (14.4 in base 2, beyond the
+    reference-move threshold of the matrix-core kernels), for the decode kernel's causal
+    form (T = 5) and the shared-tile kernel (T = 40)."""
+    from tests.test_gpu_decode import _ramp_keys
+
+    banner(f"extend bf16 rising logits T={T}")
+    b = W.extend_batch([100, 600, 1500], T, Hq=8, Hkv=2, seed=71 + T, device=DEV)
+    pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
+    lens = b.seq_lens.cpu().numpy()
+    rows = _ramp_keys(b, b.q[:, -1], b.k_pool, lens, 10.0)  # aimed at the last query token's heads
+    for (s, g), r in rows.items():  # the new tokens' K as now in the pool, for the host's re-append
+        b.k_new[s, :, g] = r[int(lens[s]) - T:]
+    host = HostExtend(b)
+    out = pa.paged_attn_extend(b.q, b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B, b.scale)
+    torch.cuda.synchronize()
+    assert_close(host_f32(out), host.oracle(), torch.bfloat16, f"rising logits T={T}")
+
+
 def test_speculative_loop_with_rollback():
     """Branches over a shared 1029-token prefix; each step reserves T = 4 draft
     positions (copying a shared partial tail first), appends the drafts, verifies

@@ -246,7 +246,7 @@ def suite(torch, pa, W, dev):
     # Several query tokens per request ([Serving] §5): a speculative-verification
     # step with T draft tokens over the headline histories (4 rotated pool
     # copies), and one 512-token prompt chunk.  GB/s counts the history once.
-    for T in (2, 4, 8, 16):
+    for T in (2, 4, 8, 16, 24):
         b = W.verify_batch(device=dev, T=T)
         pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
         pools = [(b.k_pool, b.v_pool)] + [(b.k_pool.clone(), b.v_pool.clone()) for _ in range(3)]

@@ -55,11 +55,14 @@ constexpr bool use_shared_tile(pa_dtype dtype, int G, int T) {
 }
 
 // 16-column sets per wave of the shared-tile kernel: two (each K and V
-// operand read from LDS feeds both) once the tokens fill two sets in every
-// wave, else one.  Measured: 639 vs 675 us for a 512-token chunk of 4-head
-// groups, but 184 vs 143 us for 16 tokens, where half the waves would idle.
+// operand read from LDS feeds both) once one set per wave would take more
+// than one workgroup per (request, KV head) and so more than one pass over
+// the history, else one.  Measured on 32 x 4096 tokens of 4-head groups:
+// 639 vs 675 us for a 512-token chunk; 148-155 vs 169-171 us for 17-28
+// tokens (some waves idle, one pass instead of two); but 184 vs 143 us for
+// 16 tokens, which one set per wave covers in one pass.
 constexpr int shared_tile_sets(pa_dtype dtype, int G, int T) {
-  return T >= 2 * kSharedTileWaves * tokens_per_wave(dtype, G) ? 2 : 1;
+  return T > kSharedTileWaves * tokens_per_wave(dtype, G) ? 2 : 1;
 }
 
 // 16-column sets per wave of the bf16 decode kernel: two when the query

@@ -70,10 +70,11 @@ def test_bf16_one_item_per_group(T):
 
 
 @pytest.mark.parametrize("G,T", [(4, 7), (4, 16), (1, 17), (1, 40), (16, 3), (8, 5), (2, 9),
-                                 (4, 40), (16, 9), (2, 70), (8, 33)])
+                                 (4, 40), (16, 9), (2, 70), (8, 33), (4, 17), (4, 24), (2, 36), (1, 65)])
 def test_bf16_several_items_per_group(G, T):
     """Separate items per column set up to two sets; the shared-tile kernel above,
-    with one 16-column set per wave, or two once every wave can fill two."""
+    with one 16-column set per wave, or two once one set per wave would need a
+    second workgroup (then some waves may hold no live column)."""
     banner(f"extend bf16 G={G} T={T} ragged")
     b = W.extend_batch(RAGGED, T, Hq=2 * G, Hkv=2, seed=20 + G + T, device=DEV)
     check(b, torch.bfloat16, f"bf16 G={G} T={T}")

@@ -262,19 +262,24 @@ def suite(torch, pa, W, dev):
             query_tokens_per_s_per_layer=round(b.S * T / (us * 1e-6), 1))
         del b, pools, calls
         torch.cuda.empty_cache()
+    # The prompt chunk with each softmax weight as a bf16 head plus remainder
+    # (the default), and rounded once to bf16 (PA_FLAG_BF16_WEIGHTS).
     b = W.prefill_chunk_batch(device=dev)
     pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
-    call = pa.DecodeLaunch(b.q, b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B, b.scale)
-    us = graph_time_us(torch, call.launch, 10)
     lens = b.seq_lens.cpu().tolist()
     # causal q.k and p.v: 4 * d flops per (query token, head, visible position)
     flops = sum(4 * b.D * b.Hq * (n - b.T + i + 1) for n in lens for i in range(b.T) if n - b.T + i >= 0)
-    ent = dict(rate(b.valid_kv_bytes(), us), splits=call.splits, layers=1,
-               query_tokens_per_s_per_layer=round(b.S * b.T / (us * 1e-6), 1))
-    ent["TFLOP_s"] = round(flops / (us * 1e-6) / 1e12, 2)
-    ent["frac_bf16_mfma_peak"] = round(flops / (us * 1e-6) / 2.5e15, 4)
-    out[f"bf16 prompt chunk, 8 x 4096 tokens, T = {b.T} query tokens"] = ent
-    del b, call
+    for bf16_weights, tag in ((False, ""), (True, ", bf16 weights")):
+        call = pa.DecodeLaunch(b.q, b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B, b.scale,
+                               bf16_weights=bf16_weights)
+        us = graph_time_us(torch, call.launch, 10)
+        ent = dict(rate(b.valid_kv_bytes(), us), splits=call.splits, layers=1,
+                   query_tokens_per_s_per_layer=round(b.S * b.T / (us * 1e-6), 1))
+        ent["TFLOP_s"] = round(flops / (us * 1e-6) / 1e12, 2)
+        ent["frac_bf16_mfma_peak"] = round(flops / (us * 1e-6) / 2.5e15, 4)
+        out[f"bf16 prompt chunk, 8 x 4096 tokens, T = {b.T} query tokens{tag}"] = ent
+        del call
+    del b
     torch.cuda.empty_cache()
 
     # The attention part of recomputing a swapped-out request's KV instead of
@@ -286,26 +291,28 @@ def suite(torch, pa, W, dev):
     n_re, chunk, layers_re = 4000, 512, 32
     b = W.extend_batch([n_re], n_re, seed=360, device=dev, name="reprefill_bf16_1x4000")
     pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
-    calls = []
-    for c0 in range(0, n_re, chunk):
-        t_c = min(chunk, n_re - c0)
-        lens_c = torch.tensor([c0 + t_c], dtype=torch.int32, device=dev)
-        calls.append(pa.DecodeLaunch(b.q[:, c0:c0 + t_c].contiguous(), b.k_pool, b.v_pool, b.block_tables, lens_c,
-                                     b.B, b.scale))
+    for bf16_weights, tag in ((False, ""), (True, ", bf16 weights")):
+        calls = []
+        for c0 in range(0, n_re, chunk):
+            t_c = min(chunk, n_re - c0)
+            lens_c = torch.tensor([c0 + t_c], dtype=torch.int32, device=dev)
+            calls.append(pa.DecodeLaunch(b.q[:, c0:c0 + t_c].contiguous(), b.k_pool, b.v_pool, b.block_tables,
+                                         lens_c, b.B, b.scale, bf16_weights=bf16_weights))
 
-    def reprefill():
-        for c in calls:
-            c.launch()
+        def reprefill():
+            for c in calls:
+                c.launch()
 
-    us = graph_time_us(torch, reprefill, 5)
-    flops = 4 * b.D * b.Hq * n_re * (n_re + 1) // 2  # position t of the prompt sees t + 1 positions
-    out[f"bf16 re-prefill attention, one {n_re}-token request in {chunk}-token chunks"] = dict(
-        us_per_layer=round(us, 2), chunks=len(calls), TFLOP_s=round(flops / (us * 1e-6) / 1e12, 2),
-        frac_bf16_mfma_peak=round(flops / (us * 1e-6) / 2.5e15, 4),
-        ms_for_32_layers=round(us * layers_re / 1e3, 3),
-        note="attention only (K/V projections are outside this library): a lower bound on recomputing "
-             "the KV that swap_500MiB moves")
-    del b, calls
+        us = graph_time_us(torch, reprefill, 5)
+        flops = 4 * b.D * b.Hq * n_re * (n_re + 1) // 2  # position t of the prompt sees t + 1 positions
+        out[f"bf16 re-prefill attention, one {n_re}-token request in {chunk}-token chunks{tag}"] = dict(
+            us_per_layer=round(us, 2), chunks=len(calls), TFLOP_s=round(flops / (us * 1e-6) / 1e12, 2),
+            frac_bf16_mfma_peak=round(flops / (us * 1e-6) / 2.5e15, 4),
+            ms_for_32_layers=round(us * layers_re / 1e3, 3),
+            note="attention only (K/V projections are outside this library): a lower bound on recomputing "
+                 "the KV that swap_500MiB moves")
+        del calls
+    del b
     torch.cuda.empty_cache()
 
     for name, make, rows in (("fp32 5 requests (37..511 tokens), one layer", W.config1, None),

@@ -48,6 +48,7 @@ pa_status check_dims(const pa_dims* d, int32_t B, bool need_attention_shape) {
   if (d->num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "num_blocks = %d < 1", d->num_blocks);
   if (B < 1) return fail(PA_ERR_INVALID_ARG, "block size B = %d < 1", B);
   if (d->dtype != PA_F32 && d->dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "dtype %d", (int)d->dtype);
+  if (d->flags & ~PA_FLAG_BF16_WEIGHTS) return fail(PA_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)d->flags);
   if ((int64_t)d->max_blocks_per_seq * B > INT32_MAX)
     return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq * B overflows int32");
   if (need_attention_shape) {
@@ -202,6 +203,7 @@ static pa_status attend(const void* q, const void* k_pool, const void* v_pool, c
   a.tps = tps;
   a.T = T;
   a.TG = (int)TG;
+  a.bf16_weights = (dims->flags & PA_FLAG_BF16_WEIGHTS) != 0;
   if (k_new) {
     if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(PA_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
     if (dims->dtype == PA_BF16) {

@@ -28,6 +28,13 @@
 // barrier of the next pair, which no wave passes before it has finished
 // reading b.  Each wave owns its columns, so no state is merged inside the
 // workgroup.
+//
+// The weights p enter p.v in one of two forms.  By default each is a bf16
+// head plus a bf16 remainder, both rounded to nearest, through two MFMAs
+// (weights within 2^-18 of p), and l is summed in fp32 by the vector ALU.
+// With PA_FLAG_BF16_WEIGHTS each is rounded once to bf16 and l is summed by
+// one more MFMA from the same rounded weights, so o / l stays a weighted
+// mean of V: a third less matrix-core work per pair, weights within 2^-9.
 #include <hip/hip_runtime.h>
 
 #include "pa_mfma_common.h"
@@ -42,8 +49,10 @@ static_assert(kWaves * 4 == kTile, "each wave loads one 4-row group of a tile");
 constexpr int kDepth = 2;  // tile pairs in flight per wave (this lane's K and V rows of two tiles each)
 
 // kSets: 16-column sets per wave (1 or 2); each K and V operand read from
-// LDS feeds all of them.
-template <int G, int kSets, int B>
+// LDS feeds all of them.  kOneRounding: p rounded once to bf16 and l summed
+// on the matrix core from the rounded weights (PA_FLAG_BF16_WEIGHTS), else p
+// as a bf16 head plus remainder and l summed in fp32 by the vector ALU.
+template <int G, int kSets, int B, bool kOneRounding>
 __global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArgs a) {
   static_assert(G >= 1 && G <= 16, "the query group must fit the 16 columns of one MFMA tile");
   static_assert(B >= 4 && B <= 64 && (B & (B - 1)) == 0, "block size: a power of two from 4 to 64");
@@ -134,12 +143,15 @@ __global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArg
     }
   };
 
-  float m[kSets], l[kSets];
+  float m[kSets];
+  float l[kSets];       // two roundings: partial l of column n16 over this lane's slots
+  f32x4_t lacc[kSets];  // one rounding: l of column 4*c4 + r, in the accumulator layout of o
   f32x4_t acc[kSets][8];
 #pragma unroll
   for (int j = 0; j < kSets; ++j) {
     m[j] = kNegInf;
     l[j] = 0.f;
+    lacc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) acc[j][jj] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
@@ -185,7 +197,10 @@ __global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArg
     bool full = true;
 #pragma unroll
     for (int j = 0; j < kSets; ++j) full = full && vqb[j] >= kTile;
-    pair_update_sets<kSets, true>(ra, rb, qv, acc, m, l, vqa, vqb, a.scale_log2, n16, c4, !__all(full));
+    if constexpr (kOneRounding)
+      pair_update_sets_rn<kSets, true>(ra, rb, qv, acc, lacc, m, vqa, vqb, a.scale_log2, n16, c4, !__all(full));
+    else
+      pair_update_sets<kSets, true>(ra, rb, qv, acc, m, l, vqa, vqb, a.scale_log2, n16, c4, !__all(full));
   };
 
   // Table entries are read 64 at a time into one register (one per lane), as
@@ -213,11 +228,16 @@ __global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArg
     }
   }
 
-  // Full l of column n16 of each set: sum the partials of its four lanes.
+  // The full l of every column in the layout of o: lane (n16, c4) gets the
+  // l of columns 4*c4 .. 4*c4+3.
+  if constexpr (!kOneRounding) {
 #pragma unroll
-  for (int j = 0; j < kSets; ++j) {
-    l[j] += __shfl_xor(l[j], 16, kWave);
-    l[j] += __shfl_xor(l[j], 32, kWave);
+    for (int j = 0; j < kSets; ++j) {
+      l[j] += __shfl_xor(l[j], 16, kWave);  // the four lanes of column n16
+      l[j] += __shfl_xor(l[j], 32, kWave);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lacc[j][r] = __shfl(l[j], 4 * c4 + r, kWave);
+    }
   }
   bad = __syncthreads_or(bad);  // any wave that met an entry outside the pool
 
@@ -228,7 +248,7 @@ __global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArg
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int col = 4 * c4 + r;
-        const float lc = __shfl(l[j], col, kWave);
+        const float lc = lacc[j][r];
         const int t_out = tw * TW + w * TS + j * TC + col / G;
         if (t_out < a.T) {
           const float inv = lc > 0.f ? 1.f / lc : 0.f;
@@ -248,22 +268,36 @@ __global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArg
           for (int jj = 0; jj < 8; ++jj) a.ws_o[slot * kHeadDim + 16 * jj + n16] = acc[j][jj][r];
         }
       }
-      if (c4 == 0 && tq[j] < a.T) {  // lane n16 holds column n16's m and l
+      // Lane n16 holds column n16's m; its l sits in element n16 % 4 of the
+      // lanes with c4 = n16 / 4.
+      float lr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lr[r] = __shfl(lacc[j][r], 16 * (n16 >> 2), kWave);
+      const float lj = (n16 & 3) == 0 ? lr[0] : (n16 & 3) == 1 ? lr[1] : (n16 & 3) == 2 ? lr[2] : lr[3];
+      if (c4 == 0 && tq[j] < a.T) {
         const int64_t slot = (((int64_t)s * a.T + tq[j]) * a.Hq + kvh * G + n16 % G) * a.P + p;
         a.ws_m[slot] = bad ? 0.f : m[j];
-        a.ws_l[slot] = bad ? nan : l[j];
+        a.ws_l[slot] = bad ? nan : lj;
       }
     }
   }
 }
 
-template <int G, int B>
-hipError_t launch_gb(const DecodeArgs& a, hipStream_t stream) {
+template <int G, int B, bool kOneRounding>
+void launch_gbr(const DecodeArgs& a, hipStream_t stream) {
   const int items = a.Hkv * a.S * a.P * a.TG;
   if (shared_tile_sets(PA_BF16, G, a.T) == 2)
-    hipLaunchKernelGGL((extend_shared_kernel<G, 2, B>), dim3(items), dim3(kWave * kWaves), 0, stream, a);
+    hipLaunchKernelGGL((extend_shared_kernel<G, 2, B, kOneRounding>), dim3(items), dim3(kWave * kWaves), 0, stream, a);
   else
-    hipLaunchKernelGGL((extend_shared_kernel<G, 1, B>), dim3(items), dim3(kWave * kWaves), 0, stream, a);
+    hipLaunchKernelGGL((extend_shared_kernel<G, 1, B, kOneRounding>), dim3(items), dim3(kWave * kWaves), 0, stream, a);
+}
+
+template <int G, int B>
+hipError_t launch_gb(const DecodeArgs& a, hipStream_t stream) {
+  if (a.bf16_weights)
+    launch_gbr<G, B, true>(a, stream);
+  else
+    launch_gbr<G, B, false>(a, stream);
   return hipGetLastError();
 }
 

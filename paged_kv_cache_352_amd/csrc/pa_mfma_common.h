@@ -119,9 +119,10 @@ struct TileReads {
 // reference moved, and leave the weights p = 2^(s - m) in pw.
 constexpr float kLazyMax = 8.f;
 
-template <int R, bool kMayBeEmpty>
+template <int R, bool kMayBeEmpty, bool kSumL = true>
 __device__ __attribute__((always_inline)) inline void softmax_core(const float (&sv)[R], f32x4_t (&acc)[8],
-                                                                   float& m, float& l, int c4, float (&pw)[R]) {
+                                                                   float& m, float& l, int c4, float (&pw)[R],
+                                                                   f32x4_t* lacc = nullptr) {
   // Tile max over the column's slots.  v_permlane16_swap / 32_swap exchange
   // rows of 16 / 32 lanes in the vector ALU, so the max of each returned
   // pair is the max over the lane and its partner (lane ^ 16, then lane ^ 32)
@@ -144,10 +145,12 @@ __device__ __attribute__((always_inline)) inline void softmax_core(const float (
   if constexpr (kMayBeEmpty) mref = (m == kNegInf) ? 0.f : m;
 #pragma unroll
   for (int r = 0; r < R; ++r) pw[r] = fast_exp2(sv[r] - mref);
-  float sum = (pw[0] + pw[1]) + (pw[2] + pw[3]);
+  if constexpr (kSumL) {
+    float sum = (pw[0] + pw[1]) + (pw[2] + pw[3]);
 #pragma unroll
-  for (int r = 4; r < R; r += 4) sum += (pw[r] + pw[r + 1]) + (pw[r + 2] + pw[r + 3]);
-  l = fmaf(l, alpha, sum);
+    for (int r = 4; r < R; r += 4) sum += (pw[r] + pw[r + 1]) + (pw[r + 2] + pw[r + 3]);
+    l = fmaf(l, alpha, sum);
+  }
 
   // Rescale o only where a column's reference moved.
   if (__any(move)) {
@@ -158,6 +161,10 @@ __device__ __attribute__((always_inline)) inline void softmax_core(const float (
     for (int jj = 0; jj < 8; ++jj)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[jj][r] *= ar[r];
+    if (lacc) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) (*lacc)[r] *= ar[r];
+    }
   }
 }
 
@@ -240,6 +247,23 @@ __device__ __attribute__((always_inline)) inline void tile_update_sets(const Til
   }
 }
 
+// Two fp32 values rounded to bf16 (to nearest, ties to even; one
+// v_cvt_pk_bf16_f32), packed low then high.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ inline uint32_t pack_bf16_rn(float x0, float x1) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){x0, x1}, bf16x2_t));
+}
+
+// Head and remainder of two weights: hi = bf16(x) rounded to nearest, and
+// lo = bf16(x - hi) rounded to nearest (x - hi is exact in fp32), so
+// |x - hi - lo| <= 2^-9 |x - hi| <= 2^-18 |x|.
+__device__ inline void split_pair_rn(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16_rn(x0, x1);
+  lo = pack_bf16_rn(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xffff0000u));
+}
+
 // The step for two consecutive tiles a and b (32 slots) and NS sets of 16
 // columns.  q.k runs per tile as above; the softmax takes the lane's 8
 // scores (slots 4*c4 .. +3 of a, then of b); and p.v runs on
@@ -249,7 +273,9 @@ __device__ __attribute__((always_inline)) inline void tile_update_sets(const Til
 // weights in that order and the B operand is the two transposing V reads
 // (tile a, then tile b) of the same lane side by side.  mask = false (the
 // same in every lane): the caller has checked that both tiles lie wholly
-// inside every column's limit, so no slot is masked.
+// inside every column's limit, so no slot is masked.  p is split into a head
+// and a remainder rounded to nearest (split_pair_rn), which keeps the weights
+// within 2^-18 of p instead of the 2^-16 of the truncating split.
 template <int NS, bool kMayBeEmpty>
 __device__ __attribute__((always_inline)) inline void pair_update_sets(const TileReads& ra, const TileReads& rb,
                                                                        const bf16x8_t (&qv)[NS][4],
@@ -290,7 +316,7 @@ __device__ __attribute__((always_inline)) inline void pair_update_sets(const Til
     softmax_core<8, kMayBeEmpty>(sv, acc[j], m[j], l[j], c4, pw);
     uint32_t h[4], lo[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) split_pair(pw[2 * q], pw[2 * q + 1], h[q], lo[q]);
+    for (int q = 0; q < 4; ++q) split_pair_rn(pw[2 * q], pw[2 * q + 1], h[q], lo[q]);
     phi[j] = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
     plo[j] = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
   }
@@ -310,6 +336,77 @@ __device__ __attribute__((always_inline)) inline void pair_update_sets(const Til
       acc[j][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[j], v8, acc[j][jj], 0, 0, 0);
       acc[j][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[j], v8, acc[j][jj], 0, 0, 0);
     }
+  }
+}
+
+// The pair step with p rounded once to bf16 (to nearest) and the softmax
+// denominator summed by the matrix core from the same rounded weights:
+// lacc[j][r] = the sum over slots of p~ of column 4*c4 + r, one extra
+// 16x16x32 MFMA per pair against a B operand of ones, in the accumulator
+// layout of o.  o / l is then an exact weighted mean of V with weights
+// p~ / sum p~, each p~ within 2^-9 of p relative, and rounding to nearest
+// leaves no common sign to the errors, so they partly cancel over the
+// history.  q.k, the mask and the reference max are as in pair_update_sets;
+// p.v and l take 9 MFMAs per set instead of 16, with no split of p.
+
+template <int NS, bool kMayBeEmpty>
+__device__ __attribute__((always_inline)) inline void pair_update_sets_rn(const TileReads& ra, const TileReads& rb,
+                                                                          const bf16x8_t (&qv)[NS][4],
+                                                                          f32x4_t (&acc)[NS][8], f32x4_t (&lacc)[NS],
+                                                                          float (&m)[NS], const int (&vqa)[NS],
+                                                                          const int (&vqb)[NS], float scale_log2,
+                                                                          int n16, int c4, bool mask = true) {
+  f32x4_t sa[NS], sb[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    sa[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    sb[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4_t ka = *reinterpret_cast<const PA_LDS u32x4_t*>(ra.k + 16 * ((4 * i + c4) ^ n16));
+    const u32x4_t kb = *reinterpret_cast<const PA_LDS u32x4_t*>(rb.k + 16 * ((4 * i + c4) ^ n16));
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      sa[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qv[j][i], sa[j], 0, 0, 0);
+      sb[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb), qv[j][i], sb[j], 0, 0, 0);
+    }
+  }
+  bf16x8_t pr[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    float sv[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sv[r] = sa[j][r] * scale_log2;
+      sv[4 + r] = sb[j][r] * scale_log2;
+      if (mask) {
+        sv[r] = (4 * c4 + r < vqa[j]) ? sv[r] : kNegInf;
+        sv[4 + r] = (4 * c4 + r < vqb[j]) ? sv[4 + r] : kNegInf;
+      }
+    }
+    float pw[8];
+    float unused = 0.f;
+    softmax_core<8, kMayBeEmpty, false>(sv, acc[j], m[j], unused, c4, pw, &lacc[j]);
+    pr[j] = __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16_rn(pw[0], pw[1]), pack_bf16_rn(pw[2], pw[3]),
+                                                    pack_bf16_rn(pw[4], pw[5]), pack_bf16_rn(pw[6], pw[7])));
+  }
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+#pragma unroll
+  for (int j = 0; j < NS; ++j) lacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pr[j], ones, lacc[j], 0, 0, 0);
+
+  wave_lds_order();  // both tiles' V are in LDS
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const int ca = ((2 * jj) ^ ra.rhi) | ra.bsel;
+    const int cb = ((2 * jj) ^ rb.rhi) | rb.bsel;
+    const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(ra.v + 16 * ca));
+    const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(rb.v + 16 * cb));
+    const bf16x8_t v8 = __builtin_bit_cast(
+        bf16x8_t, make_uint4(__builtin_bit_cast(uint2, va).x, __builtin_bit_cast(uint2, va).y,
+                             __builtin_bit_cast(uint2, vb).x, __builtin_bit_cast(uint2, vb).y));
+#pragma unroll
+    for (int j = 0; j < NS; ++j) acc[j][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pr[j], v8, acc[j][jj], 0, 0, 0);
   }
 }
 

@@ -54,7 +54,7 @@ def test_exports_every_declared_symbol(lib):
             "pa_bm_prepare_extend"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.pa_abi_version() == 2
+    assert lib.pa_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -117,6 +117,25 @@ def test_decode_rejects_before_launch(lib):
     d = dims(S=1, Hkv=1, Hq=4, MB=64, splits=4, ws=0x7F0000100010, ws_bytes=1 << 20)
     assert decode(lib, d) == WORKSPACE
     assert "workspace" in lib.pa_last_error().decode()
+
+
+@no_gpu
+def test_unknown_flags_are_rejected_before_launch(lib):
+    """pa_dims.flags carries PA_FLAG_BF16_WEIGHTS (1) only; any other bit is refused
+    by every attention entry point before anything is enqueued."""
+    assert lib.pa_abi_version() == _lib.ABI_VERSION == 3
+    for bad in (2, 4, 1 << 30, -1):
+        d = dims()
+        d.flags = bad
+        assert decode(lib, d) == INVALID
+        assert "flags" in lib.pa_last_error().decode()
+        assert lib.paged_attn_extend(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 16, ctypes.c_float(0.1), FAKE, None,
+                                     ctypes.byref(d)) == INVALID
+    # the defined bit passes the flag check (and then fails on the NULL q, as without it)
+    d = dims()
+    d.flags = _lib.FLAG_BF16_WEIGHTS
+    assert decode(lib, d, q=None) == INVALID
+    assert "NULL" in lib.pa_last_error().decode()
 
 
 def test_empty_batch_is_a_noop(lib):

@@ -19,11 +19,11 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def gpu_extend(b, num_splits=0):
+def gpu_extend(b, num_splits=0, bf16_weights=False):
     """The step through libpagedattn on one stream: append the T new tokens, then attend."""
     pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
     return pa.paged_attn_extend(b.q, b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B, b.scale,
-                                num_splits=num_splits)
+                                num_splits=num_splits, bf16_weights=bf16_weights)
 
 
 class HostExtend:
@@ -53,9 +53,9 @@ class HostExtend:
 RAGGED = [1, 2, 3, 4, 5, 15, 16, 17, 19, 31, 32, 33, 100, 257, 300]
 
 
-def check(b, dtype, what, num_splits=0):
+def check(b, dtype, what, num_splits=0, bf16_weights=False):
     host = HostExtend(b)
-    out = gpu_extend(b, num_splits=num_splits)
+    out = gpu_extend(b, num_splits=num_splits, bf16_weights=bf16_weights)
     torch.cuda.synchronize()
     return assert_close(host_f32(out), host.oracle(), dtype, what)
 
@@ -78,6 +78,45 @@ def test_bf16_several_items_per_group(G, T):
     banner(f"extend bf16 G={G} T={T} ragged")
     b = W.extend_batch(RAGGED, T, Hq=2 * G, Hkv=2, seed=20 + G + T, device=DEV)
     check(b, torch.bfloat16, f"bf16 G={G} T={T}")
+
+
+# PA_FLAG_BF16_WEIGHTS on the shared-tile path: group sizes, one and two
+# column sets, forced splits (l leaves through the split workspace), block sizes.
+@pytest.mark.parametrize("G,T,splits,B", [(4, 17, 0, 16), (4, 40, 0, 16), (1, 40, 0, 16), (2, 70, 0, 16),
+                                          (8, 33, 0, 16), (16, 9, 0, 16), (4, 24, 0, 16), (4, 40, 4, 16),
+                                          (2, 36, 3, 16), (4, 40, 0, 4), (4, 40, 0, 64)])
+def test_bf16_weights_flag(G, T, splits, B):
+    """Weights rounded once to bf16, l summed from the rounded weights: within the
+    bf16 tolerance of the oracle, and not the default form's result."""
+    banner(f"extend bf16 weights G={G} T={T} splits={splits} B={B}")
+    lens = RAGGED + [2 * B + 1, 4 * B - 1]
+    b = W.extend_batch(lens, T, Hq=2 * G, Hkv=2, B=B, seed=200 + G + T + B, device=DEV)
+    host = HostExtend(b)
+    pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
+    fast = pa.paged_attn_extend(b.q, b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B, b.scale,
+                                num_splits=splits, bf16_weights=True)
+    exact = pa.paged_attn_extend(b.q, b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B, b.scale,
+                                 num_splits=splits)
+    torch.cuda.synchronize()
+    ref = host.oracle()
+    err_fast = assert_close(host_f32(fast), ref, torch.bfloat16, "bf16 weights")
+    err_exact = assert_close(host_f32(exact), ref, torch.bfloat16, "head + remainder")
+    print(f"  max abs err: bf16 weights {err_fast:.3e}, head + remainder {err_exact:.3e}", flush=True)
+    assert not torch.equal(fast, exact)
+
+
+@pytest.mark.parametrize("dtype,G,T", [(torch.bfloat16, 4, 1), (torch.bfloat16, 4, 5), (torch.bfloat16, 4, 8),
+                                       (torch.bfloat16, 1, 16), (torch.float32, 4, 20)])
+def test_bf16_weights_flag_ignored_off_the_shared_tile_path(dtype, G, T):
+    """Decode-kernel forms (up to two column sets) and float32 keep the head and
+    remainder: bitwise the same output with and without the flag."""
+    banner(f"extend flag ignored {dtype} G={G} T={T}")
+    b = W.extend_batch(RAGGED, T, Hq=2 * G, Hkv=2, dtype=dtype, seed=230 + G + T, device=DEV)
+    pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
+    a = pa.paged_attn_extend(b.q, b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B, b.scale, bf16_weights=True)
+    c = pa.paged_attn_extend(b.q, b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B, b.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(a), host_bits(c))
 
 
 @pytest.mark.parametrize("G,T", [(4, 2), (4, 5), (1, 9), (8, 3), (2, 4)])
@@ -187,12 +226,13 @@ def test_verify_32x4096_T4_sampled():
     assert np.all(np.isfinite(out))
 
 
-def test_prefill_chunk_512_sampled():
+@pytest.mark.parametrize("bf16_weights", [False, True])
+def test_prefill_chunk_512_sampled(bf16_weights):
     """A 512-token prompt chunk over 3584 tokens of history, 8 requests; one sampled request."""
-    banner("prefill chunk bf16 8x4096 T=512, sampled row")
+    banner(f"prefill chunk bf16 8x4096 T=512 bf16_weights={bf16_weights}, sampled row")
     b = W.prefill_chunk_batch(device=DEV)
     host = HostExtend(b)
-    out = host_f32(gpu_extend(b))
+    out = host_f32(gpu_extend(b, bf16_weights=bf16_weights))
     rows = [5]
     ref = host.oracle(rows)
     assert_close(np.stack([out[s] for s in rows]), np.stack([ref[s] for s in rows]), torch.bfloat16, "chunk")
@@ -220,8 +260,8 @@ def test_chunked_prefill_matches_one_pass(dtype):
     assert_close(host_f32(torch.cat(outs, dim=1)), ref, dtype, "chunked prefill")
 
 
-@pytest.mark.parametrize("T", [5, 40])
-def test_rising_logits(T):
+@pytest.mark.parametrize("T,bf16_weights", [(5, False), (40, False), (40, True)])
+def test_rising_logits(T, bf16_weights):
     """Logits climbing along the history in stairs of 10 (14.4 in base 2, beyond the
     reference-move threshold of the matrix-core kernels), for the decode kernel's causal
     form (T = 5) and the shared-tile kernel (T = 40)."""
@@ -235,7 +275,8 @@ def test_rising_logits(T):
     for (s, g), r in rows.items():  # the new tokens' K as now in the pool, for the host's re-append
         b.k_new[s, :, g] = r[int(lens[s]) - T:]
     host = HostExtend(b)
-    out = pa.paged_attn_extend(b.q, b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B, b.scale)
+    out = pa.paged_attn_extend(b.q, b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B, b.scale,
+                               bf16_weights=bf16_weights)
     torch.cuda.synchronize()
     assert_close(host_f32(out), host.oracle(), torch.bfloat16, f"rising logits T={T}")
 

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   const int n16 = lane & 15;
   const int c4 = lane >> 4;
 
-  int item = xcd_remap(blockIdx.x, gridDim.x);
+  int item = a.plain_order ? (int)blockIdx.x : xcd_remap(blockIdx.x, gridDim.x);
   const int p = item % a.P;
   item /= a.P;
   int tg = 0;  // which NS*TC query tokens of the request this item takes
@@ -423,9 +423,23 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
+// Workgroups of this kernel resident at once on MI355X: 256 CUs, two each
+// (172-181 VGPRs per wave).
+constexpr int kResidentItems = 2 * 256;
+
 template <int G, bool kCausal, int B>
-hipError_t launch_gb(const DecodeArgs& a, hipStream_t stream) {
-  const int items = a.Hkv * a.S * a.P * (kCausal ? a.TG : 1);
+hipError_t launch_gb(const DecodeArgs& args, hipStream_t stream) {
+  const int items = args.Hkv * args.S * args.P * (kCausal ? args.TG : 1);
+  // Which items an XCD runs.  Grouped (xcd_remap), each XCD takes a
+  // contiguous range, which is one KV head of every request; in launch order
+  // the XCDs take items in turn, so every XCD sees every KV head, one head
+  // after the other over the launch.  Measured on one box: grouped is faster
+  // while the items fit in one or two rounds of resident workgroups (32 x
+  // 4096: 96.0 vs 101.3 us; 64 x 2048: 97.4 vs 103.0; 128 x 1024: 99.1 vs
+  // 100.9), launch order once there are more (256 requests of 1-513 tokens:
+  // 58.7 vs 61.0 us; 512 x 256: 104.3 vs 108.0).
+  DecodeArgs a = args;
+  a.plain_order = items > 2 * kResidentItems;
   if constexpr (!kCausal) {
     if (a.k_new) {
       hipLaunchKernelGGL((decode_mfma_kernel<G, false, 1, kMfmaWaves, B, true>), dim3(items),

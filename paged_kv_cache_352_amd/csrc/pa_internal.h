@@ -34,6 +34,7 @@ struct DecodeArgs {
   int T;            // query tokens per request (q is [S, T, Hq, d]); the last T of the history, causal
   int TG;           // work items per (request, KV head, split) along the query tokens: ceil(T / tokens per item)
   bool bf16_weights;  // PA_FLAG_BF16_WEIGHTS: the shared-tile kernel rounds p once to bf16
+  bool plain_order;   // bf16 decode: work items in launch order, not grouped by XCD (set at launch)
 };
 
 constexpr int kSharedTileWaves = 4;  // waves of the shared-tile several-token kernel

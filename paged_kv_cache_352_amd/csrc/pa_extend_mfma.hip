@@ -53,7 +53,7 @@ constexpr int kDepth = 2;  // tile pairs in flight per wave (this lane's K and V
 // on the matrix core from the rounded weights (PA_FLAG_BF16_WEIGHTS), else p
 // as a bf16 head plus remainder and l summed in fp32 by the vector ALU.
 template <int G, int kSets, int B, bool kOneRounding>
-__global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(DecodeArgs a) {
   static_assert(G >= 1 && G <= 16, "the query group must fit the 16 columns of one MFMA tile");
   static_assert(B >= 4 && B <= 64 && (B & (B - 1)) == 0, "block size: a power of two from 4 to 64");
   constexpr int TC = G >= 16 ? 1 : 16 / G;  // query tokens per 16-column set
@@ -95,6 +95,12 @@ __global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArg
   const int u0 = p * (a.tps / kTile);
   const int u1 = min(nt, u0 + a.tps / kTile);  // the same range for every wave
 
+  // q enters the matrix core as given; with a negative scale it enters
+  // negated (exact in bf16) and the magnitude of the scale is used, so the
+  // scores are scaled by c >= 0 and keep their order: (-q).k * |c| = q.k * c.
+  const bool neg_scale = a.scale_log2 < 0.f;
+  const float c_log2 = neg_scale ? -a.scale_log2 : a.scale_log2;
+  const uint32_t qsign = neg_scale ? 0x80008000u : 0u;
   bf16x8_t qv[kSets][4];
 #pragma unroll
   for (int j = 0; j < kSets; ++j) {
@@ -104,6 +110,7 @@ __global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArg
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint4 v = *reinterpret_cast<const uint4*>(qp + 32 * i + 8 * c4);
+      v = make_uint4(v.x ^ qsign, v.y ^ qsign, v.z ^ qsign, v.w ^ qsign);
       if (!live) v = make_uint4(0, 0, 0, 0);
       qv[j][i] = __builtin_bit_cast(bf16x8_t, v);
     }
@@ -193,14 +200,16 @@ __global__ __launch_bounds__(kWave * kWaves) void extend_shared_kernel(DecodeArg
       vqb[j] = t + 1 < te ? lim[j] - (t + 1) * kTile : 0;  // no tile b past the range
     }
     // Below the diagonal (both tiles inside every column's limit, as for all
-    // but the last pairs of a chunk) nothing is masked and no column is empty.
+    // but the last pairs of a chunk) nothing is masked and no column is
+    // empty: the step without masks takes the scores unscaled.
     bool full = true;
 #pragma unroll
     for (int j = 0; j < kSets; ++j) full = full && vqb[j] >= kTile;
+    const bool mask = !__all(full);
     if constexpr (kOneRounding)
-      pair_update_sets_rn<kSets, true>(ra, rb, qv, acc, lacc, m, vqa, vqb, a.scale_log2, n16, c4, !__all(full));
+      pair_update_sets_rn<kSets, true>(ra, rb, qv, acc, lacc, m, vqa, vqb, c_log2, n16, c4, mask);
     else
-      pair_update_sets<kSets, true>(ra, rb, qv, acc, m, l, vqa, vqb, a.scale_log2, n16, c4, !__all(full));
+      pair_update_sets<kSets, true>(ra, rb, qv, acc, m, l, vqa, vqb, c_log2, n16, c4, mask);
   };
 
   // Table entries are read 64 at a time into one register (one per lane), as

@@ -119,10 +119,14 @@ struct TileReads {
 // reference moved, and leave the weights p = 2^(s - m) in pw.
 constexpr float kLazyMax = 8.f;
 
-template <int R, bool kMayBeEmpty, bool kSumL = true>
+// With kRaw, sv holds unscaled, unmasked scores and c >= 0 the base-2
+// scale: the tile max is taken on them and scaled once (c * max s = max c*s
+// for c >= 0, rounding included), and each weight is 2^(fma(s, c, -m)), so
+// no score is multiplied or masked on its own.
+template <int R, bool kMayBeEmpty, bool kSumL = true, bool kRaw = false>
 __device__ __attribute__((always_inline)) inline void softmax_core(const float (&sv)[R], f32x4_t (&acc)[8],
                                                                    float& m, float& l, int c4, float (&pw)[R],
-                                                                   f32x4_t* lacc = nullptr) {
+                                                                   f32x4_t* lacc = nullptr, float c = 1.f) {
   // Tile max over the column's slots.  v_permlane16_swap / 32_swap exchange
   // rows of 16 / 32 lanes in the vector ALU, so the max of each returned
   // pair is the max over the lane and its partner (lane ^ 16, then lane ^ 32)
@@ -136,6 +140,7 @@ __device__ __attribute__((always_inline)) inline void softmax_core(const float (
     const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
     bm = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
   }
+  if constexpr (kRaw) bm *= c;
   // A column that has seen nothing (m = -inf) moves to its first finite tile
   // max; one whose tile is all -inf (kMayBeEmpty) keeps its empty state.
   const bool move = bm > m + kLazyMax;
@@ -144,7 +149,7 @@ __device__ __attribute__((always_inline)) inline void softmax_core(const float (
   float mref = m;
   if constexpr (kMayBeEmpty) mref = (m == kNegInf) ? 0.f : m;
 #pragma unroll
-  for (int r = 0; r < R; ++r) pw[r] = fast_exp2(sv[r] - mref);
+  for (int r = 0; r < R; ++r) pw[r] = kRaw ? fast_exp2(fmaf(sv[r], c, -mref)) : fast_exp2(sv[r] - mref);
   if constexpr (kSumL) {
     float sum = (pw[0] + pw[1]) + (pw[2] + pw[3]);
 #pragma unroll
@@ -271,18 +276,22 @@ __device__ inline void split_pair_rn(float x0, float x1, uint32_t& hi, uint32_t&
 // instruction per issue: its K index 8*c4 + i stands for slot 4*c4 + i of
 // tile a (i < 4) or of tile b (i >= 4), so the A operand is the lane's 8
 // weights in that order and the B operand is the two transposing V reads
-// (tile a, then tile b) of the same lane side by side.  mask = false (the
-// same in every lane): the caller has checked that both tiles lie wholly
-// inside every column's limit, so no slot is masked.  p is split into a head
-// and a remainder rounded to nearest (split_pair_rn), which keeps the weights
-// within 2^-18 of p instead of the 2^-16 of the truncating split.
+// (tile a, then tile b) of the same lane side by side.  p is split into a
+// head and a remainder rounded to nearest (split_pair_rn), which keeps the
+// weights within 2^-18 of p instead of the 2^-16 of the truncating split.
+// mask = false (the same in every lane): the caller has checked that both
+// tiles lie wholly inside every column's limit; then no slot is masked, no
+// column is empty, and the scores go to softmax_core unscaled
+// (scale_log2 >= 0 required), which saves a multiply, a compare and a
+// select per score.  Only the softmax differs between the two forms; the
+// matrix-core steps around it are shared.
 template <int NS, bool kMayBeEmpty>
 __device__ __attribute__((always_inline)) inline void pair_update_sets(const TileReads& ra, const TileReads& rb,
                                                                        const bf16x8_t (&qv)[NS][4],
                                                                        f32x4_t (&acc)[NS][8], float (&m)[NS],
                                                                        float (&l)[NS], const int (&vqa)[NS],
                                                                        const int (&vqb)[NS], float scale_log2,
-                                                                       int n16, int c4, bool mask = true) {
+                                                                       int n16, int c4, bool mask) {
   f32x4_t sa[NS], sb[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
@@ -300,25 +309,37 @@ __device__ __attribute__((always_inline)) inline void pair_update_sets(const Til
     }
   }
   bf16x8_t phi[NS], plo[NS];
-#pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    float sv[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sv[r] = sa[j][r] * scale_log2;
-      sv[4 + r] = sb[j][r] * scale_log2;
-      if (mask) {
-        sv[r] = (4 * c4 + r < vqa[j]) ? sv[r] : kNegInf;
-        sv[4 + r] = (4 * c4 + r < vqb[j]) ? sv[4 + r] : kNegInf;
-      }
-    }
-    float pw[8];
-    softmax_core<8, kMayBeEmpty>(sv, acc[j], m[j], l[j], c4, pw);
+  auto weights = [&](int j, const float (&pw)[8]) {
     uint32_t h[4], lo[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) split_pair_rn(pw[2 * q], pw[2 * q + 1], h[q], lo[q]);
     phi[j] = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
     plo[j] = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+  };
+  if (mask) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      float sv[8], pw[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sv[r] = (4 * c4 + r < vqa[j]) ? sa[j][r] * scale_log2 : kNegInf;
+        sv[4 + r] = (4 * c4 + r < vqb[j]) ? sb[j][r] * scale_log2 : kNegInf;
+      }
+      softmax_core<8, kMayBeEmpty>(sv, acc[j], m[j], l[j], c4, pw);
+      weights(j, pw);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      float sv[8], pw[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sv[r] = sa[j][r];
+        sv[4 + r] = sb[j][r];
+      }
+      softmax_core<8, false, true, true>(sv, acc[j], m[j], l[j], c4, pw, nullptr, scale_log2);
+      weights(j, pw);
+    }
   }
 
   wave_lds_order();  // both tiles' V are in LDS
@@ -355,7 +376,7 @@ __device__ __attribute__((always_inline)) inline void pair_update_sets_rn(const 
                                                                           f32x4_t (&acc)[NS][8], f32x4_t (&lacc)[NS],
                                                                           float (&m)[NS], const int (&vqa)[NS],
                                                                           const int (&vqb)[NS], float scale_log2,
-                                                                          int n16, int c4, bool mask = true) {
+                                                                          int n16, int c4, bool mask) {
   f32x4_t sa[NS], sb[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
@@ -372,6 +393,8 @@ __device__ __attribute__((always_inline)) inline void pair_update_sets_rn(const 
       sb[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb), qv[j][i], sb[j], 0, 0, 0);
     }
   }
+  // One softmax form here (the mask applied by selects where needed): two
+  // forms, as in pair_update_sets, took this kernel past 256 registers.
   bf16x8_t pr[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {

@@ -105,6 +105,17 @@ def test_bf16_weights_flag(G, T, splits, B):
     assert not torch.equal(fast, exact)
 
 
+@pytest.mark.parametrize("T,bf16_weights", [(4, False), (40, False), (40, True), (300, False)])
+def test_negative_scale(T, bf16_weights):
+    """A negative scale (legal, if unusual) reverses the order of the logits: the
+    decode-kernel form (T = 4) and the shared-tile kernel, which feeds q negated and
+    the scale's magnitude to its unmasked steps, both match the oracle."""
+    banner(f"extend bf16 negative scale T={T} bf16_weights={bf16_weights}")
+    b = W.extend_batch([T + 1, T + 60, T + 700], T, Hq=8, Hkv=2, seed=250 + T, device=DEV)
+    b.scale = -abs(b.scale) * 3.0
+    check(b, torch.bfloat16, f"negative scale T={T}", bf16_weights=bf16_weights)
+
+
 @pytest.mark.parametrize("dtype,G,T", [(torch.bfloat16, 4, 1), (torch.bfloat16, 4, 5), (torch.bfloat16, 4, 8),
                                        (torch.bfloat16, 1, 16), (torch.float32, 4, 20)])
 def test_bf16_weights_flag_ignored_off_the_shared_tile_path(dtype, G, T):

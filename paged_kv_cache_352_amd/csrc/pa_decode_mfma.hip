@@ -29,7 +29,8 @@
 // of 4 whole rows (lane l: row 4*i + l/16, bytes 16*(l%16)), so every row is
 // fetched as full cache lines by one instruction; B >= 4 keeps each group in
 // one block.  The loads are buffer loads: a descriptor for the block
-// (uniform, in SGPRs) plus constant 32-bit lane offsets.  The next tile's K
+// (uniform, in SGPRs) plus constant 32-bit lane offsets, with the
+// non-temporal hint, since every K/V byte is read once.  The next tile's K
 // and V are in flight while the current one is processed.  Each wave stages
 // its K and V tiles in its own LDS, 16-byte chunk k of slot t at byte
 // 256*t + 16*(k ^ t), which keeps both the row-wise writes and the operand
@@ -217,9 +218,9 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
       const __amdgpu_buffer_rsrc_t vr = block_rsrc(vpool + (int64_t)pb * blk_bytes, blk_bytes);
       const int row0 = (kTile * u) % B;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) t.k[i] = load_kv16(kr, voff, (row0 + 4 * i) * row_bytes);
+      for (int i = 0; i < 4; ++i) t.k[i] = load_kv16<true>(kr, voff, (row0 + 4 * i) * row_bytes);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) t.v[i] = load_kv16(vr, voff, (row0 + 4 * i) * row_bytes);
+      for (int i = 0; i < 4; ++i) t.v[i] = load_kv16<true>(vr, voff, (row0 + 4 * i) * row_bytes);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -227,8 +228,8 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
         const bool live = spec || tok < n;
         const int pb = pool_block(__builtin_amdgcn_readlane(tab, (k - kb) * E + (live ? (4 * i) / B : 0)), !spec);
         const int soff = live ? (tok % B) * row_bytes : 0;
-        t.k[i] = load_kv16(block_rsrc(kpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
-        t.v[i] = load_kv16(block_rsrc(vpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
+        t.k[i] = load_kv16<true>(block_rsrc(kpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
+        t.v[i] = load_kv16<true>(block_rsrc(vpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
       }
     }
   };

@@ -133,20 +133,25 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(Decode
   };
   // Rows past the history (only in the last tile, B < 16) read the history's
   // last block instead and are zeroed or masked; no table entry at or past
-  // ceil(n / B) is read.
+  // ceil(n / B) is read.  With one column set per wave a workgroup covers all
+  // query tokens of its (request, KV head), so each K/V byte is read once and
+  // the loads carry the non-temporal hint; with two, several workgroups may
+  // read the same history, and it is left to the caches (measured on the
+  // 512-token chunk: 414 vs 440 us without and with the hint).
+  constexpr bool kStream = kSets == 1;
   auto load_rows = [&](int u, uint4& k, uint4& v, int eb, int tab) {
     if constexpr (B >= kTile) {
       const int pb = pool_block(__builtin_amdgcn_readlane(tab, (kTile * u) / B - eb));
       const int soff = ((kTile * u) % B + 4 * w) * row_bytes;
-      k = load_kv16(block_rsrc(kpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
-      v = load_kv16(block_rsrc(vpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
+      k = load_kv16<kStream>(block_rsrc(kpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
+      v = load_kv16<kStream>(block_rsrc(vpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
     } else {
       const int tok = kTile * u + 4 * w;
       const bool live = tok < n;
       const int pb = pool_block(__builtin_amdgcn_readlane(tab, (live ? tok : n - 1) / B - eb));
       const int soff = live ? (tok % B) * row_bytes : 0;
-      k = load_kv16(block_rsrc(kpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
-      v = load_kv16(block_rsrc(vpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
+      k = load_kv16<kStream>(block_rsrc(kpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
+      v = load_kv16<kStream>(block_rsrc(vpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
     }
   };
 

@@ -152,9 +152,10 @@ static pa_status plan_common(const pa_dims* dims, int32_t B, int32_t T, int32_t*
   int P, tps;
   plan_splits(dims, B, T, &P, &tps);
   *num_splits = P;
+  const int Pm = pa::merged_splits(dims->dtype, P);
   *workspace_bytes =
-      (P > 1 && dims->num_seqs > 0)
-          ? pa::decode_workspace_floats((int64_t)dims->num_seqs * T * dims->num_q_heads, P) * sizeof(float)
+      (Pm > 1 && dims->num_seqs > 0)
+          ? pa::decode_workspace_floats((int64_t)dims->num_seqs * T * dims->num_q_heads, Pm) * sizeof(float)
           : 0;
   return PA_OK;
 }
@@ -199,7 +200,10 @@ static pa_status attend(const void* q, const void* k_pool, const void* v_pool, c
   a.Hkv = dims->num_kv_heads;
   a.MB = dims->max_blocks_per_seq;
   a.NB = dims->num_blocks;
-  a.P = P;
+  // float32 runs its splits as the waves of workgroups (valu_waves) and
+  // keeps P for the groups that reach the merge.
+  a.W = dims->dtype == PA_F32 ? pa::valu_waves(P) : 1;
+  a.P = pa::merged_splits(dims->dtype, P);
   a.tps = tps;
   a.T = T;
   a.TG = (int)TG;
@@ -212,17 +216,17 @@ static pa_status attend(const void* q, const void* k_pool, const void* v_pool, c
       a.positions = positions;
     }
   }
-  if (P > 1) {
-    const size_t need = pa::decode_workspace_floats(rows, P) * sizeof(float);
+  if (a.P > 1) {
+    const size_t need = pa::decode_workspace_floats(rows, a.P) * sizeof(float);
     if (!dims->workspace || dims->workspace_bytes < need)
       return fail(PA_ERR_WORKSPACE, "split-K needs %zu workspace bytes, got %zu", need,
                   dims->workspace ? dims->workspace_bytes : (size_t)0);
     if (!aligned(dims->workspace, 256)) return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     float* ws = static_cast<float*>(dims->workspace);
-    const size_t no = (size_t)rows * P * pa::kHeadDim;
+    const size_t no = (size_t)rows * a.P * pa::kHeadDim;
     a.ws_o = ws;
     a.ws_m = ws + no;
-    a.ws_l = ws + no + (size_t)rows * P;
+    a.ws_l = ws + no + (size_t)rows * a.P;
   }
   if (k_new && dims->dtype != PA_BF16) {
     pa::KvArgs ka{};

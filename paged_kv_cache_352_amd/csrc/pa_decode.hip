@@ -9,15 +9,21 @@
 // K/V tile, mask slots at or past the length, score, and fold the block into
 // a running (m, l, o) state with the update of [Budgets] eq. (4).  Long
 // histories are cut into contiguous ranges of logical blocks ("splits"); each
-// range is reduced to its own (m, l, o), and a second kernel merges them
-// ([Slides] quiz "逻辑顺序没错…": mergeable state, not averaged softmaxes).
+// range is reduced to its own (m, l, o), and the states are merged
+// ([Slides] quiz "逻辑顺序没错…": mergeable state, not averaged softmaxes):
+// by the waves of one workgroup through LDS for groups of up to 4 splits
+// (float32), and by a second kernel across groups and for the matrix-core
+// kernels' splits.
 //
 // This file holds the float32 path (bf16 K/V go to the matrix-core kernel in
 // pa_decode_mfma.hip) and the split merge both paths share.
 //
 // Mapping to CDNA4 (vector ALU):
 //   * one 64-lane wave per work item (request s, KV head g, split p); the G
-//     query heads of the GQA group share every K/V byte the wave loads;
+//     query heads of the GQA group share every K/V byte the wave loads; the
+//     waves of up to 4 consecutive splits form one workgroup and merge their
+//     states in LDS, so a request cut into at most 4 splits needs no second
+//     kernel and more splits leave a quarter as many partial states;
 //   * a K or V tile of one (block, KV head) is B rows of d contiguous
 //     elements, rows Hkv*d apart.  Lane (r, c) loads 16 bytes — dims
 //     [c*E, c*E+E) of row i*RPL + r — so a wave instruction reads RPL whole
@@ -73,8 +79,10 @@ __device__ inline int xcd_remap(int bid, int nwg) {
   return x * q + min(x, rem) + k;
 }
 
-template <typename T, int G, bool kCausal, int B>
-__global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeArgs a) {
+// W waves per workgroup, one split each; their W states are merged through
+// LDS at the end.
+template <typename T, int G, bool kCausal, int B, int W>
+__global__ __launch_bounds__(kWave * W) void decode_split_kernel(DecodeArgs a) {
   constexpr int TC = kCausal ? (G >= 8 ? 1 : 8 / G) : 1;  // query tokens per work item
   constexpr int C = G * TC;                                // (token, head) columns
   constexpr int E = Vec16<T>::kElems;  // elements per 16-byte load
@@ -84,12 +92,16 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeArgs a) {
   constexpr int NL = kTile / RPL;      // loads per tile (8 for fp32)
   static_assert(B % RPL == 0, "block size must be a multiple of the rows one wave load covers");
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x % kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int c = lane % LPR;
   const int r = lane / LPR;
 
+  // The workgroup takes group pg of W consecutive splits (a.P groups per
+  // request, KV head and token group); its wave w runs split pg*W + w.
   int item = xcd_remap(blockIdx.x, gridDim.x);
-  const int p = item % a.P;
+  const int pg = item % a.P;
+  const int p = pg * W + w;
   item /= a.P;
   int tg = 0;  // which TC query tokens of the request this item takes
   if constexpr (kCausal) {
@@ -273,27 +285,54 @@ __global__ __launch_bounds__(kWave) void decode_split_kernel(DecodeArgs a) {
       for (int e = 0; e < E; ++e) o[g][e] += shfl_xor(o[g][e], mask);
     }
   }
-  if (r != 0) return;
+
+  // Merge the W split states ([Budgets] eq. (4) across disjoint block sets,
+  // in split order): M = max m_w, L = sum 2^(m_w - M) l_w,
+  // O = sum 2^(m_w - M) o_w.  A wave whose split holds no tile keeps m = -inf
+  // and drops out; with one group of splits the result is the output, else
+  // the group's partial state for the merge kernel.
+  __shared__ float red_m[W][C];
+  __shared__ float red_l[W][C];
+  __shared__ float red_o[W][C][kHeadDim];
+  if (r == 0) {
+#pragma unroll
+    for (int g = 0; g < C; ++g) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) red_o[w][g][c * E + e] = o[g][e];
+      if (c == 0) {
+        red_m[w][g] = m[g];
+        red_l[w][g] = l[g];
+      }
+    }
+  }
+  bad = __syncthreads_or(bad);  // any wave that met an entry outside the pool
 
   const float nan = __builtin_nanf("");
-#pragma unroll
-  for (int g = 0; g < C; ++g) {
+  for (int idx = threadIdx.x; idx < C * kHeadDim; idx += kWave * W) {
+    const int g = idx / kHeadDim;
+    const int d = idx % kHeadDim;
     const int t_out = tg * TC + g / G;
-    if (kCausal && t_out >= a.T) break;
+    if (kCausal && t_out >= a.T) break;  // idx only grows: every later column is past T too
+    float M = kNegInf;
+#pragma unroll
+    for (int v = 0; v < W; ++v) M = fmaxf(M, red_m[v][g]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int v = 0; v < W; ++v) {
+      const float mv = red_m[v][g];
+      const float f = mv == kNegInf ? 0.f : fast_exp2(mv - M);
+      L = fmaf(f, red_l[v][g], L);
+      O = fmaf(f, red_o[v][g][d], O);
+    }
     const int64_t row = ((int64_t)s * a.T + t_out) * a.Hq + kvh * G + g % G;  // [S, T, Hq] row
     if (a.P == 1) {
-      float* dst = a.out + row * kHeadDim + c * E;
-      const float inv = l[g] > 0.f ? 1.f / l[g] : 0.f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) dst[e] = bad ? nan : o[g][e] * inv;
+      a.out[row * kHeadDim + d] = bad ? nan : (L > 0.f ? O / L : 0.f);
     } else {
-      const int64_t slot = row * a.P + p;
-      float* dst = a.ws_o + slot * kHeadDim + c * E;
-#pragma unroll
-      for (int e = 0; e < E; ++e) dst[e] = o[g][e];
-      if (c == 0) {
-        a.ws_m[slot] = bad ? 0.f : m[g];
-        a.ws_l[slot] = bad ? nan : l[g];
+      const int64_t slot = row * a.P + pg;
+      a.ws_o[slot * kHeadDim + d] = O;
+      if (d == 0) {
+        a.ws_m[slot] = bad ? 0.f : M;
+        a.ws_l[slot] = bad ? nan : L;
       }
     }
   }
@@ -331,7 +370,12 @@ __global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
 template <typename T, int G, bool kCausal, int B>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   const int items = a.Hkv * a.S * a.P * (kCausal ? a.TG : 1);
-  hipLaunchKernelGGL((decode_split_kernel<T, G, kCausal, B>), dim3(items), dim3(kWave), 0, stream, a);
+  switch (a.W) {
+    case 1: hipLaunchKernelGGL((decode_split_kernel<T, G, kCausal, B, 1>), dim3(items), dim3(kWave), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((decode_split_kernel<T, G, kCausal, B, 2>), dim3(items), dim3(kWave * 2), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_split_kernel<T, G, kCausal, B, 4>), dim3(items), dim3(kWave * 4), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

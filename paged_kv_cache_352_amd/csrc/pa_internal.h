@@ -35,7 +35,29 @@ struct DecodeArgs {
   int TG;           // work items per (request, KV head, split) along the query tokens: ceil(T / tokens per item)
   bool bf16_weights;  // PA_FLAG_BF16_WEIGHTS: the shared-tile kernel rounds p once to bf16
   bool plain_order;   // bf16 decode: work items in launch order, not grouped by XCD (set at launch)
+  int W;              // float32: splits per workgroup, one wave each, merged in LDS (P counts the groups)
 };
+
+// float32 decode: the P splits of one (request, KV head, token group) run in
+// groups of up to kMaxValuWaves (the smallest power of two >= P), one wave
+// each, as the waves of one workgroup, and each group merges its states in
+// LDS; with more than one group the groups' partial states go to the merge
+// kernel.  Measured on 5 requests of 37-511 tokens (16 splits): 13.6 us with
+// one wave per workgroup, 12.1 us with groups of 4, 22 us with one group of
+// 16 (a CU's four SIMDs then run a whole request's vector-ALU work).
+constexpr int kMaxValuWaves = 4;
+
+constexpr int valu_waves(int P) {
+  int w = 1;
+  while (w < P && w < kMaxValuWaves) w *= 2;
+  return w;
+}
+
+// Partial states per output row that reach the split workspace and the
+// merge kernel: P for bf16, the groups of valu_waves(P) splits for float32.
+constexpr int merged_splits(pa_dtype dtype, int P) {
+  return dtype == PA_F32 ? (P + valu_waves(P) - 1) / valu_waves(P) : P;
+}
 
 constexpr int kSharedTileWaves = 4;  // waves of the shared-tile several-token kernel
 

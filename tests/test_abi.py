@@ -72,6 +72,10 @@ def test_plan_is_deterministic_and_covers_table(lib):
         P, ws = a
         assert 1 <= P <= MB
         assert ws == (S * Hq * P * 130 * 4 if P > 1 else 0)
+    # float32: up to 4 splits need no workspace (merged in LDS); 16 splits leave 4 groups, 6 splits 2
+    assert pa.paged_attn_plan(5, 8, 2, 128, 32, 64, torch.float32, 16, num_splits=4) == (4, 0)
+    assert pa.paged_attn_plan(5, 8, 2, 128, 32, 64, torch.float32, 16, num_splits=16) == (16, 5 * 8 * 4 * 130 * 4)
+    assert pa.paged_attn_plan(5, 8, 2, 128, 96, 64, torch.float32, 16, num_splits=6) == (6, 5 * 8 * 2 * 130 * 4)
     # forced split counts are honoured (clamped to the table width)
     assert pa.paged_attn_plan(5, 8, 2, 128, 32, 64, torch.float32, 16, num_splits=3)[0] == 3
     assert pa.paged_attn_plan(5, 8, 2, 128, 32, 64, torch.float32, 16, num_splits=1)[0] == 1
@@ -182,13 +186,27 @@ def test_swap_rejects_bad_arguments(lib):
     assert lib.kv_swap_out(*args(n=0)) == OK  # nothing to do, nothing launched
 
 
+def merged_splits(P, dt):
+    """Partial states per output row that reach the split workspace: float32 runs
+    groups of up to 4 splits (the next power of two) as the waves of one
+    workgroup and merges each group in LDS, so only the groups' states are written."""
+    if dt != torch.float32:
+        return P
+    w = 1
+    while w < P and w < 4:
+        w *= 2
+    return -(-P // w)
+
+
 def test_extend_plan_matches_decode_at_one_token_and_scales_workspace(lib):
-    for S, Hq, Hkv, MB, dt in [(32, 32, 8, 256, torch.bfloat16), (5, 8, 2, 32, torch.float32), (7, 16, 1, 9, torch.bfloat16)]:
+    for S, Hq, Hkv, MB, dt in [(32, 32, 8, 256, torch.bfloat16), (5, 8, 2, 32, torch.float32), (7, 16, 1, 9, torch.bfloat16),
+                               (2, 8, 2, 4096, torch.float32)]:
         assert pa.paged_attn_extend_plan(S, Hq, Hkv, 128, MB, 10000, dt, 16, 1) == pa.paged_attn_plan(
             S, Hq, Hkv, 128, MB, 10000, dt, 16)
         for T in (2, 4, 7, 33):
             P, ws = pa.paged_attn_extend_plan(S, Hq, Hkv, 128, MB, 10000, dt, 16, T)
-            assert P >= 1 and ws == (S * T * Hq * P * 130 * 4 if P > 1 else 0)
+            Pm = merged_splits(P, dt)
+            assert P >= 1 and ws == (S * T * Hq * Pm * 130 * 4 if Pm > 1 else 0)
             # forced splits are honoured as in the one-token plan
             assert pa.paged_attn_extend_plan(S, Hq, Hkv, 128, MB, 10000, dt, 16, T, num_splits=2)[0] == min(2, MB)
     p, w = ctypes.c_int32(), ctypes.c_size_t()

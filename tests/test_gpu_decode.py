@@ -112,16 +112,20 @@ def test_other_group_sizes(G, Hkv, dtype):
     assert_close(host_f32(out), ref, dtype, f"G={G}")
 
 
-@pytest.mark.parametrize("splits", [1, 2])
-def test_long_split_walks_several_table_chunks(splits):
+@pytest.mark.parametrize("splits,dtype", [(1, torch.bfloat16), (2, torch.bfloat16), (1, torch.float32),
+                                          (7, torch.float32), (16, torch.float32), (48, torch.float32),
+                                          (0, torch.float32)])
+def test_long_split_walks_several_table_chunks(splits, dtype):
     """A wave with more than 64 tiles (a split over 4 x 64 blocks) reads its table
-    entries in several registers."""
-    banner(f"long split: 5000 / 1100 / 17 tokens, splits={splits}")
-    b = W.custom([5000, 1100, 17], Hq=8, Hkv=2, dtype=torch.bfloat16, device=DEV, seed=14)
+    entries in several registers.  float32: groups of up to 4 splits are the
+    waves of one workgroup and merge in LDS; 7, 16 and 48 splits leave 2, 4 and 12
+    groups for the merge kernel."""
+    banner(f"long split: 5000 / 1100 / 17 tokens, splits={splits} {dtype}")
+    b = W.custom([5000, 1100, 17], Hq=8, Hkv=2, dtype=dtype, device=DEV, seed=14)
     ref = HostLayer(b, 0).oracle()
     out = gpu_step(b, num_splits=splits)[0]
     torch.cuda.synchronize()
-    assert_close(host_f32(out), ref, torch.bfloat16, f"long split P={splits}")
+    assert_close(host_f32(out), ref, dtype, f"long split P={splits}")
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])

@@ -53,6 +53,21 @@ namespace {
 constexpr int kWave = 64;
 constexpr float kNegInf = -__builtin_huge_valf();
 
+// A 16-byte K/V load; kStream marks it non-temporal (each byte is read once
+// per decode step: one query token, one work item per split of the history).
+// The several-token form leaves it to the caches, since its token groups
+// read the same history.
+typedef unsigned int u32x4_native __attribute__((ext_vector_type(4)));
+
+template <bool kStream>
+__device__ inline uint4 load_row16(const void* p) {
+  if constexpr (kStream) {
+    const u32x4_native v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_native*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
+  return *reinterpret_cast<const uint4*>(p);
+}
+
 template <typename T>
 struct Vec16;  // how a 16-byte load unpacks into float32
 
@@ -181,8 +196,8 @@ __global__ __launch_bounds__(kWave * W) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const int64_t off = (int64_t)pb * blk_stride + (int64_t)((kTile * u) % B + RPL * i + r) * row_stride;
-        kraw[i] = *reinterpret_cast<const uint4*>(kbase + off);
-        vraw[i] = *reinterpret_cast<const uint4*>(vbase + off);
+        kraw[i] = load_row16<!kCausal>(kbase + off);
+        vraw[i] = load_row16<!kCausal>(vbase + off);
       }
     } else {
 #pragma unroll
@@ -191,8 +206,8 @@ __global__ __launch_bounds__(kWave * W) void decode_split_kernel(DecodeArgs a) {
         const bool live = tok < n;
         const int pb = pool_block(trow[(live ? tok : n - 1) / B]);
         const int64_t off = (int64_t)pb * blk_stride + (int64_t)((live ? tok % B : 0) + r) * row_stride;
-        kraw[i] = *reinterpret_cast<const uint4*>(kbase + off);
-        vraw[i] = *reinterpret_cast<const uint4*>(vbase + off);
+        kraw[i] = load_row16<!kCausal>(kbase + off);
+        vraw[i] = load_row16<!kCausal>(vbase + off);
       }
     }
 

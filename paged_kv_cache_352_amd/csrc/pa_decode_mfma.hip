@@ -434,13 +434,15 @@ hipError_t launch_gb(const DecodeArgs& args, hipStream_t stream) {
   // Which items an XCD runs.  Grouped (xcd_remap), each XCD takes a
   // contiguous range, which is one KV head of every request; in launch order
   // the XCDs take items in turn, so every XCD sees every KV head, one head
-  // after the other over the launch.  Measured on one box: grouped is faster
-  // while the items fit in one or two rounds of resident workgroups (32 x
-  // 4096: 96.0 vs 101.3 us; 64 x 2048: 97.4 vs 103.0; 128 x 1024: 99.1 vs
-  // 100.9), launch order once there are more (256 requests of 1-513 tokens:
-  // 58.7 vs 61.0 us; 512 x 256: 104.3 vs 108.0).
+  // after the other over the launch.  Measured on one box (non-temporal
+  // loads): grouped is faster while the items fit in one round of resident
+  // workgroups (32 x 4096: 82.6-86.7 vs 91.4 us; 64 x 2048: 88.5 vs 93.4 us),
+  // launch order once they take more (168 x 1025 tokens: 62.5 vs 64.2 us per
+  // layer; 256 requests of 1-513 tokens: 54.2 vs 56.7 us; 128 requests of
+  // 1-4096 tokens: 210.9 vs 211.6 us; 128 x 1024 tokens, exactly two rounds:
+  // 92.0 vs 91.8 us).
   DecodeArgs a = args;
-  a.plain_order = items > 2 * kResidentItems;
+  a.plain_order = items > kResidentItems;
   if constexpr (!kCausal) {
     if (a.k_new) {
       hipLaunchKernelGGL((decode_mfma_kernel<G, false, 1, kMfmaWaves, B, true>), dim3(items),

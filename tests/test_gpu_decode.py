@@ -101,6 +101,21 @@ def test_edge_lengths(dtype, splits):
     assert_close(got, ref, dtype, "edges")
 
 
+@pytest.mark.parametrize("dtype,splits", [(torch.bfloat16, 0), (torch.bfloat16, 3), (torch.float32, 0),
+                                          (torch.float32, 6)])
+def test_negative_and_zero_scale(dtype, splits):
+    """A negative scale reverses the order of the logits and a zero scale makes every
+    weight equal (the mean of the valid V rows); both match the oracle."""
+    for scale in (-0.3, 0.0):
+        banner(f"decode {dtype} scale={scale} splits={splits}")
+        b = W.custom([1, 16, 17, 300, 1000], Hq=8, Hkv=2, dtype=dtype, device=DEV, seed=15)
+        b.scale = scale
+        ref = HostLayer(b, 0).oracle()
+        out = gpu_step(b, num_splits=splits)[0]
+        torch.cuda.synchronize()
+        assert_close(host_f32(out), ref, dtype, f"scale={scale}")
+
+
 @pytest.mark.parametrize("G,Hkv,dtype", [(1, 4, torch.bfloat16), (2, 2, torch.bfloat16), (8, 1, torch.bfloat16),
                                          (16, 2, torch.bfloat16), (1, 3, torch.float32), (8, 1, torch.float32)])
 def test_other_group_sizes(G, Hkv, dtype):

@@ -107,13 +107,15 @@ def test_bf16_weights_flag(G, T, splits, B):
 
 @pytest.mark.parametrize("T,bf16_weights", [(4, False), (40, False), (40, True), (300, False)])
 def test_negative_scale(T, bf16_weights):
-    """A negative scale (legal, if unusual) reverses the order of the logits: the
-    decode-kernel form (T = 4) and the shared-tile kernel, which feeds q negated and
-    the scale's magnitude to its unmasked steps, both match the oracle."""
-    banner(f"extend bf16 negative scale T={T} bf16_weights={bf16_weights}")
-    b = W.extend_batch([T + 1, T + 60, T + 700], T, Hq=8, Hkv=2, seed=250 + T, device=DEV)
-    b.scale = -abs(b.scale) * 3.0
-    check(b, torch.bfloat16, f"negative scale T={T}", bf16_weights=bf16_weights)
+    """A negative scale (legal, if unusual) reverses the order of the logits, and a
+    zero scale weighs every visible position the same: the decode-kernel form (T = 4)
+    and the shared-tile kernel, which feeds q negated and the scale's magnitude to its
+    unmasked steps, both match the oracle."""
+    for factor in (-3.0, 0.0):  # a zero scale: every visible position weighs the same
+        banner(f"extend bf16 scale x {factor} T={T} bf16_weights={bf16_weights}")
+        b = W.extend_batch([T + 1, T + 60, T + 700], T, Hq=8, Hkv=2, seed=250 + T, device=DEV)
+        b.scale = abs(b.scale) * factor
+        check(b, torch.bfloat16, f"scale x {factor} T={T}", bf16_weights=bf16_weights)
 
 
 @pytest.mark.parametrize("dtype,G,T", [(torch.bfloat16, 4, 1), (torch.bfloat16, 4, 5), (torch.bfloat16, 4, 8),

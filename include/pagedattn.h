@@ -111,9 +111,12 @@ const char* pa_last_error(void);
 
 /*
  * Split-K plan for paged_attn_decode at block size B: the number of splits
- * the decode will use and the workspace it needs (0 when no split is used).
- * Depends only on host-known sizes, so repeated calls agree.  A forced
- * num_splits is capped at ceil(MB * B / max(16, B)).
+ * the decode will use and the workspace it needs.  The workspace holds the
+ * partial states that reach the merge: one per split with bf16; with float32
+ * the splits run in groups of up to 4 that merge inside one workgroup, so it
+ * holds one per group, and none for up to 4 splits.  0 bytes when nothing
+ * reaches the merge.  Depends only on host-known sizes, so repeated calls
+ * agree.  A forced num_splits is capped at ceil(MB * B / max(16, B)).
  */
 pa_status paged_attn_plan(const pa_dims* dims, int32_t B, int32_t* num_splits,
                           size_t* workspace_bytes);

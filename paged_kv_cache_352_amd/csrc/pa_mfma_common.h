@@ -128,10 +128,10 @@ struct TileReads {
 // reference moved, and leave the weights p = 2^(s - m) in pw.
 constexpr float kLazyMax = 8.f;
 
-// With kRaw, sv holds unscaled, unmasked scores and c >= 0 the base-2
-// scale: the tile max is taken on them and scaled once (c * max s = max c*s
-// for c >= 0, rounding included), and each weight is 2^(fma(s, c, -m)), so
-// no score is multiplied or masked on its own.
+// With kRaw, sv holds unscaled scores and c >= 0 the base-2 scale (c > 0
+// where a masked score is -inf): the tile max is taken on them and scaled
+// once (c * max s = max c*s for c >= 0, rounding included), and each weight
+// is 2^(fma(s, c, -m)), so no score is multiplied on its own.
 template <int R, bool kMayBeEmpty, bool kSumL = true, bool kRaw = false>
 __device__ __attribute__((always_inline)) inline void softmax_core(const float (&sv)[R], f32x4_t (&acc)[8],
                                                                    float& m, float& l, int c4, float (&pw)[R],
@@ -403,15 +403,19 @@ __device__ __attribute__((always_inline)) inline void pair_update_sets_rn(const 
     }
   }
   // One softmax form here (the mask applied by selects where needed): two
-  // forms, as in pair_update_sets, took this kernel past 256 registers.
+  // forms, as in pair_update_sets, took this kernel past 256 registers.  The
+  // scores go in unscaled (softmax_core's kRaw), with the scale kept at least
+  // FLT_MIN so that a masked -inf stays -inf (a zero scale then still gives
+  // equal weights: the scaled scores round to 0).
+  const float c = fmaxf(scale_log2, __FLT_MIN__);
   bf16x8_t pr[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     float sv[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sv[r] = sa[j][r] * scale_log2;
-      sv[4 + r] = sb[j][r] * scale_log2;
+      sv[r] = sa[j][r];
+      sv[4 + r] = sb[j][r];
       if (mask) {
         sv[r] = (4 * c4 + r < vqa[j]) ? sv[r] : kNegInf;
         sv[4 + r] = (4 * c4 + r < vqb[j]) ? sv[4 + r] : kNegInf;
@@ -419,7 +423,7 @@ __device__ __attribute__((always_inline)) inline void pair_update_sets_rn(const 
     }
     float pw[8];
     float unused = 0.f;
-    softmax_core<8, kMayBeEmpty, false>(sv, acc[j], m[j], unused, c4, pw, &lacc[j]);
+    softmax_core<8, kMayBeEmpty, false, true>(sv, acc[j], m[j], unused, c4, pw, &lacc[j], c);
     pr[j] = __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16_rn(pw[0], pw[1]), pack_bf16_rn(pw[2], pw[3]),
                                                     pack_bf16_rn(pw[4], pw[5]), pack_bf16_rn(pw[6], pw[7])));
   }

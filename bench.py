@@ -362,8 +362,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path has no "
-              "multi-GPU mode in this build.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); libpagedattn has no "
+              "multi-GPU mode.", file=sys.stderr)
         return 2
 
     import torch

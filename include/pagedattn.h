@@ -86,7 +86,7 @@ typedef struct {
   int32_t num_seqs;           /* S  >= 0 (0 makes every call a no-op)          */
   int32_t num_q_heads;        /* Hq >= 1                                       */
   int32_t num_kv_heads;       /* Hkv >= 1, Hq % Hkv == 0                       */
-  int32_t head_dim;           /* d; this build supports 128                    */
+  int32_t head_dim;           /* d; the kernels support 128                    */
   int32_t max_blocks_per_seq; /* MB >= 1: row stride of block_tables          */
   int32_t num_blocks;         /* NB >= 1: blocks in each pool                  */
   pa_dtype dtype;             /* element type of q, pools, new K/V             */

@@ -32,9 +32,9 @@
 // (uniform, in SGPRs) plus constant 32-bit lane offsets, with the
 // non-temporal hint, since every K/V byte is read once.  The next tile's K
 // and V are in flight while the current one is processed.  Each wave stages
-// its K and V tiles in its own LDS, 16-byte chunk k of slot t at byte
-// 256*t + 16*(k ^ t), which keeps both the row-wise writes and the operand
-// reads below free of bank conflicts.
+// its K and V tiles in its own LDS in the swizzled layouts of
+// pa_mfma_common.h (k_pos, v_pos), which keep the row-wise writes and the
+// operand reads below free of bank conflicts.
 //
 // Math for one wave and one 16-slot tile, head dim 128; lane l is
 // (n = l%16, c = l/16):
@@ -316,8 +316,8 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
         }
       }
       if (r >= valid) vv = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(kt + 256 * r + 16 * (n16 ^ r)) = kk;
-      *reinterpret_cast<uint4*>(vt + 256 * r + 16 * (n16 ^ r)) = vv;
+      *reinterpret_cast<uint4*>(kt + 256 * r + 16 * k_pos(n16, r)) = kk;
+      *reinterpret_cast<uint4*>(vt + 256 * r + 16 * v_pos(n16, r)) = vv;
     }
     wave_lds_order();
     // Mask past the length or, for several query tokens, past this column's

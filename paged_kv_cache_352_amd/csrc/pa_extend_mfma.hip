@@ -170,7 +170,8 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(Decode
 
   const TileReads rd0(tiles[0][0][0], tiles[0][0][1], n16, c4);
   const int r_own = 4 * w + c4;                        // the slot row this lane writes
-  const int w_off = 256 * r_own + 16 * (n16 ^ r_own);  // its swizzled byte offset in a tile
+  const int wk_off = 256 * r_own + 16 * k_pos(n16, r_own);  // its swizzled byte offsets in a K
+  const int wv_off = 256 * r_own + 16 * v_pos(n16, r_own);  // and in a V tile
 
   // This lane's rows of two consecutive tiles.
   struct Rows {
@@ -187,10 +188,10 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(Decode
     const int buf = (t >> 1) & 1;
     const int tb_loaded = min(t + 1, te - 1);
     uint8_t* base = &tiles[buf][0][0][0];
-    *reinterpret_cast<uint4*>(base + w_off) = r.ka;
-    *reinterpret_cast<uint4*>(base + kVtBytes + w_off) = r_own < n - t * kTile ? r.va : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(base + 2 * kVtBytes + w_off) = r.kb;
-    *reinterpret_cast<uint4*>(base + 3 * kVtBytes + w_off) =
+    *reinterpret_cast<uint4*>(base + wk_off) = r.ka;
+    *reinterpret_cast<uint4*>(base + kVtBytes + wv_off) = r_own < n - t * kTile ? r.va : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(base + 2 * kVtBytes + wk_off) = r.kb;
+    *reinterpret_cast<uint4*>(base + 3 * kVtBytes + wv_off) =
         r_own < n - tb_loaded * kTile ? r.vb : make_uint4(0, 0, 0, 0);
     __syncthreads();
     TileReads ra = rd0, rb = rd0;

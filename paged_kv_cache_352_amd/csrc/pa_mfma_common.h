@@ -25,11 +25,19 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 #define PA_LDS __attribute__((address_space(3)))
 
-// K or V tile in LDS: slot t, dims 8k .. 8k+7 (16-byte chunk k) at byte
-//   256 * t + 16 * (k ^ t).
-// The XOR spreads the row-wise 16-byte writes, the 16-byte K operand reads
-// and the transposing 8-byte V reads of one instruction evenly over the banks.
+// K tile in LDS: slot t, dims 8k .. 8k+7 (16-byte chunk k) at byte
+//   256 * t + 16 * k_pos(k, t),  k_pos = k ^ t;
+// V tile: the 32-byte pair of chunks k/2 is swizzled instead,
+//   256 * t + 16 * v_pos(k, t),  v_pos = ((k/2 ^ (t % 8)) * 2) | (k % 2).
+// A 16-byte row-wise write covers a whole row per 16 lanes, so any order of
+// the chunks in a row suits it.  The K operand reads (16 lanes: 16 slots, one
+// chunk each) need the chunk to move with the slot; the transposing V reads
+// (32 lanes: 8 slots, 32 bytes each) need the pair to move with the slot, so
+// that the 8 slots of one half-wave fall on 8 different 32-byte bank groups.
 constexpr int kVtBytes = kTile * kHeadDim * 2;  // 4096
+
+__device__ inline int k_pos(int k, int t) { return k ^ t; }
+__device__ inline int v_pos(int k, int t) { return (((k >> 1) ^ (t & 7)) << 1) | (k & 1); }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -86,19 +94,21 @@ __device__ inline uint4 load_kv16(__amdgpu_buffer_rsrc_t r, uint32_t off, int so
 // LDS read addresses of one lane for a swizzled 16-slot K/V tile at kt / vt.
 // K operand reads: slot n16, chunk 4*i + c4.  Transposing V reads for output
 // dims 16*jj + n16: this lane fetches slot r = 4*c4 + n16/4, dims
-// 16*jj + 4*(n16%4) .. +3, i.e. half (n16 & 1) of chunk 2*jj + (n16%4)/2.
+// 16*jj + 4*(n16%4) .. +3, i.e. half (n16 & 1) of chunk 2*jj + (n16%4)/2,
+// which sits at v_pos = ((jj ^ (r % 8)) * 2) | (n16%4)/2.
 struct TileReads {
   const PA_LDS uint8_t* k;  // + 16 * chunk
-  const PA_LDS uint8_t* v;  // + 16 * chunk
-  int rhi, bsel;            // the swizzle of the V chunk: ((2*jj) ^ rhi) | bsel
+  const PA_LDS uint8_t* v;  // + 16 * vchunk(jj)
+  int rx, bsel;             // r % 8 and (n16 % 4) / 2
 
   __device__ inline TileReads(const uint8_t* kt, const uint8_t* vt, int n16, int c4) {
     const int rr = 4 * c4 + (n16 >> 2);
     k = (const PA_LDS uint8_t*)kt + 256 * n16;
     v = (const PA_LDS uint8_t*)vt + 256 * rr + 8 * (n16 & 1);
-    bsel = ((n16 & 3) >> 1) ^ (rr & 1);
-    rhi = rr & 14;
+    bsel = (n16 & 3) >> 1;
+    rx = rr & 7;
   }
+  __device__ inline int vchunk(int jj) const { return ((jj ^ rx) << 1) | bsel; }
 };
 
 // Fold one 16-slot tile, already in LDS, into one wave's state for its 16
@@ -209,7 +219,7 @@ __device__ __attribute__((always_inline)) inline void tile_update(const TileRead
   f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const u32x4_t kv = *reinterpret_cast<const PA_LDS u32x4_t*>(rd.k + 16 * ((4 * i + c4) ^ n16));
+    const u32x4_t kv = *reinterpret_cast<const PA_LDS u32x4_t*>(rd.k + 16 * k_pos(4 * i + c4, n16));
     sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qv[i], sc, 0, 0, 0);
   }
   s16x4_t phi, plo;
@@ -218,7 +228,7 @@ __device__ __attribute__((always_inline)) inline void tile_update(const TileRead
   wave_lds_order();  // this tile's V is in LDS
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
-    const int chunk = ((2 * jj) ^ rd.rhi) | rd.bsel;
+    const int chunk = rd.vchunk(jj);
     const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(rd.v + 16 * chunk));
     acc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(phi, vb, acc[jj], 0, 0, 0);
     acc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(plo, vb, acc[jj], 0, 0, 0);
@@ -239,7 +249,7 @@ __device__ __attribute__((always_inline)) inline void tile_update_sets(const Til
   for (int j = 0; j < NS; ++j) sc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const u32x4_t kv = *reinterpret_cast<const PA_LDS u32x4_t*>(rd.k + 16 * ((4 * i + c4) ^ n16));
+    const u32x4_t kv = *reinterpret_cast<const PA_LDS u32x4_t*>(rd.k + 16 * k_pos(4 * i + c4, n16));
 #pragma unroll
     for (int j = 0; j < NS; ++j)
       sc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qv[j][i], sc[j], 0, 0, 0);
@@ -251,7 +261,7 @@ __device__ __attribute__((always_inline)) inline void tile_update_sets(const Til
   wave_lds_order();  // this tile's V is in LDS
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
-    const int chunk = ((2 * jj) ^ rd.rhi) | rd.bsel;
+    const int chunk = rd.vchunk(jj);
     const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(rd.v + 16 * chunk));
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
@@ -309,8 +319,8 @@ __device__ __attribute__((always_inline)) inline void pair_update_sets(const Til
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const u32x4_t ka = *reinterpret_cast<const PA_LDS u32x4_t*>(ra.k + 16 * ((4 * i + c4) ^ n16));
-    const u32x4_t kb = *reinterpret_cast<const PA_LDS u32x4_t*>(rb.k + 16 * ((4 * i + c4) ^ n16));
+    const u32x4_t ka = *reinterpret_cast<const PA_LDS u32x4_t*>(ra.k + 16 * k_pos(4 * i + c4, n16));
+    const u32x4_t kb = *reinterpret_cast<const PA_LDS u32x4_t*>(rb.k + 16 * k_pos(4 * i + c4, n16));
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       sa[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qv[j][i], sa[j], 0, 0, 0);
@@ -354,8 +364,8 @@ __device__ __attribute__((always_inline)) inline void pair_update_sets(const Til
   wave_lds_order();  // both tiles' V are in LDS
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
-    const int ca = ((2 * jj) ^ ra.rhi) | ra.bsel;
-    const int cb = ((2 * jj) ^ rb.rhi) | rb.bsel;
+    const int ca = ra.vchunk(jj);
+    const int cb = rb.vchunk(jj);
     const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(ra.v + 16 * ca));
     const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(rb.v + 16 * cb));
     const bf16x8_t v8 = __builtin_bit_cast(
@@ -394,8 +404,8 @@ __device__ __attribute__((always_inline)) inline void pair_update_sets_rn(const 
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const u32x4_t ka = *reinterpret_cast<const PA_LDS u32x4_t*>(ra.k + 16 * ((4 * i + c4) ^ n16));
-    const u32x4_t kb = *reinterpret_cast<const PA_LDS u32x4_t*>(rb.k + 16 * ((4 * i + c4) ^ n16));
+    const u32x4_t ka = *reinterpret_cast<const PA_LDS u32x4_t*>(ra.k + 16 * k_pos(4 * i + c4, n16));
+    const u32x4_t kb = *reinterpret_cast<const PA_LDS u32x4_t*>(rb.k + 16 * k_pos(4 * i + c4, n16));
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       sa[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qv[j][i], sa[j], 0, 0, 0);
@@ -434,8 +444,8 @@ __device__ __attribute__((always_inline)) inline void pair_update_sets_rn(const 
   wave_lds_order();  // both tiles' V are in LDS
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
-    const int ca = ((2 * jj) ^ ra.rhi) | ra.bsel;
-    const int cb = ((2 * jj) ^ rb.rhi) | rb.bsel;
+    const int ca = ra.vchunk(jj);
+    const int cb = rb.vchunk(jj);
     const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(ra.v + 16 * ca));
     const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(rb.v + 16 * cb));
     const bf16x8_t v8 = __builtin_bit_cast(

@@ -80,7 +80,9 @@ __device__ inline __amdgpu_buffer_rsrc_t block_rsrc(const char* block, uint32_t 
 
 // kStream: the load carries the non-temporal hint (cache-policy bit nt on
 // gfx950), for data that one work item reads once and no other reads again
-// soon: the decode kernel's K/V rows.  Same box, against plain loads:
+// soon: the decode kernel's K/V rows, and the shared-tile kernel's when one
+// workgroup covers all query tokens of a history.  Same box, against plain
+// loads, decode:
 // 32 x 4096 tokens 96.0 -> 86.7 us, 256 mixed-length requests 59.3-60.0 ->
 // 54.6 us per layer, 168 x 1025 tokens 70.8 -> 64.7 us per layer.
 constexpr int kCachePolicyNT = 2;

@@ -52,7 +52,7 @@ constexpr int kDepth = 2;  // tile pairs in flight per wave (this lane's K and V
 // LDS feeds all of them.  kOneRounding: p rounded once to bf16 and l summed
 // on the matrix core from the rounded weights (PA_FLAG_BF16_WEIGHTS), else p
 // as a bf16 head plus remainder and l summed in fp32 by the vector ALU.
-template <int G, int kSets, int B, bool kOneRounding>
+template <int G, int kSets, int B, bool kOneRounding, bool kStream>
 __global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(DecodeArgs a) {
   static_assert(G >= 1 && G <= 16, "the query group must fit the 16 columns of one MFMA tile");
   static_assert(B >= 4 && B <= 64 && (B & (B - 1)) == 0, "block size: a power of two from 4 to 64");
@@ -133,12 +133,11 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(Decode
   };
   // Rows past the history (only in the last tile, B < 16) read the history's
   // last block instead and are zeroed or masked; no table entry at or past
-  // ceil(n / B) is read.  With one column set per wave a workgroup covers all
-  // query tokens of its (request, KV head), so each K/V byte is read once and
-  // the loads carry the non-temporal hint; with two, several workgroups may
-  // read the same history, and it is left to the caches (measured on the
-  // 512-token chunk: 414 vs 440 us without and with the hint).
-  constexpr bool kStream = kSets == 1;
+  // ceil(n / B) is read.  kStream: one workgroup covers all query tokens of
+  // its (request, KV head) (a.TG == 1), so each K/V byte is read once and the
+  // loads carry the non-temporal hint; otherwise several workgroups read the
+  // same history, and it is left to the caches (measured on the 512-token
+  // chunk: 414 vs 440 us without and with the hint).
   auto load_rows = [&](int u, uint4& k, uint4& v, int eb, int tab) {
     if constexpr (B >= kTile) {
       const int pb = pool_block(__builtin_amdgcn_readlane(tab, (kTile * u) / B - eb));
@@ -301,10 +300,16 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(Decode
 template <int G, int B, bool kOneRounding>
 void launch_gbr(const DecodeArgs& a, hipStream_t stream) {
   const int items = a.Hkv * a.S * a.P * a.TG;
-  if (shared_tile_sets(PA_BF16, G, a.T) == 2)
-    hipLaunchKernelGGL((extend_shared_kernel<G, 2, B, kOneRounding>), dim3(items), dim3(kWave * kWaves), 0, stream, a);
+  // One column set per wave is chosen only while one workgroup holds all T tokens (a.TG == 1).
+  if (shared_tile_sets(PA_BF16, G, a.T) == 1)
+    hipLaunchKernelGGL((extend_shared_kernel<G, 1, B, kOneRounding, true>), dim3(items), dim3(kWave * kWaves), 0,
+                       stream, a);
+  else if (a.TG == 1)
+    hipLaunchKernelGGL((extend_shared_kernel<G, 2, B, kOneRounding, true>), dim3(items), dim3(kWave * kWaves), 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL((extend_shared_kernel<G, 1, B, kOneRounding>), dim3(items), dim3(kWave * kWaves), 0, stream, a);
+    hipLaunchKernelGGL((extend_shared_kernel<G, 2, B, kOneRounding, false>), dim3(items), dim3(kWave * kWaves), 0,
+                       stream, a);
 }
 
 template <int G, int B>

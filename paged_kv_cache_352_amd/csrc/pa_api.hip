@@ -111,8 +111,10 @@ void plan_splits(const pa_dims* d, int32_t B, int32_t T, int* P_out, int* tps_ou
     // Shortest split worth a work item: 256 tokens for the shared-tile kernel,
     // 64 per wave for the matrix-core decode, one 16-slot tile for the float32
     // kernel (5 requests of 37-511 tokens: 32 splits 10.3 us, 16 splits 12.1 us).
+    // No automatic split is shorter: 3 x 300 bf16 tokens run as one split in
+    // 6.8 us, as two of 160 tokens plus the merge in 7.7 us.
     const int64_t min_tokens = shared ? 256 : (mfma ? 64 * pa::kMfmaWaves : 16);
-    const int64_t maxP = (max_tokens + min_tokens - 1) / min_tokens;
+    const int64_t maxP = max_tokens / min_tokens > 1 ? max_tokens / min_tokens : 1;
     P = P < 1 ? 1 : (P > maxP ? maxP : P);
   }
   if (P > units) P = units;

@@ -82,6 +82,17 @@ def test_plan_is_deterministic_and_covers_table(lib):
     assert pa.paged_attn_plan(5, 8, 2, 128, 4, 64, torch.float32, 16, num_splits=9)[0] == 4
 
 
+def test_automatic_bf16_splits_are_never_shorter_than_256_tokens(lib):
+    # bf16 decode: a table of 19 blocks (304 tokens) stays one split, 32 blocks take two of 256
+    assert pa.paged_attn_plan(3, 16, 2, 128, 19, 64, torch.bfloat16, 16)[0] == 1
+    assert pa.paged_attn_plan(3, 16, 2, 128, 32, 64, torch.bfloat16, 16)[0] == 2
+    assert pa.paged_attn_plan(3, 16, 2, 128, 15, 64, torch.bfloat16, 16)[0] == 1
+    for MB in (1, 17, 19, 33, 47, 64, 250):
+        P, _ = pa.paged_attn_plan(1, 32, 8, 128, MB, 10000, torch.bfloat16, 16)
+        tokens = MB * 16
+        assert P == 1 or -(-tokens // P) >= 256, (MB, P)
+
+
 def test_plan_rejects_bad_shapes(lib):
     p, w = ctypes.c_int32(), ctypes.c_size_t()
     cases = [

@@ -116,7 +116,10 @@ const char* pa_last_error(void);
  * the splits run in groups of up to 4 that merge inside one workgroup, so it
  * holds one per group, and none for up to 4 splits.  0 bytes when nothing
  * reaches the merge.  Depends only on host-known sizes, so repeated calls
- * agree.  A forced num_splits is capped at ceil(MB * B / max(16, B)).
+ * agree.  With dims->num_splits = 0 the plan takes enough splits to occupy
+ * the GPU's compute units, but none shorter than 256 table slots with bf16
+ * (16 with float32), and at least one.  A forced num_splits is capped at
+ * ceil(MB * B / max(16, B)).
  */
 pa_status paged_attn_plan(const pa_dims* dims, int32_t B, int32_t* num_splits,
                           size_t* workspace_bytes);

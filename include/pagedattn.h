@@ -119,9 +119,8 @@ const char* pa_last_error(void);
  * agree.  With dims->num_splits = 0 the plan takes enough splits to occupy
  * the GPU's compute units, but no more than the table holds whole runs of
  * 256 slots with bf16 (16 with float32), and at least one; the table is cut
- * into equal runs of whole 16-slot tiles, the last run taking the rest.  A
- * forced num_splits is capped at
- * ceil(MB * B / max(16, B)).
+ * into equal runs of whole max(16, B)-slot units, the last run taking the
+ * rest.  A forced num_splits is capped at ceil(MB * B / max(16, B)).
  */
 pa_status paged_attn_plan(const pa_dims* dims, int32_t B, int32_t* num_splits,
                           size_t* workspace_bytes);

@@ -39,7 +39,8 @@ def kernel_sha():
     """sha256 over the decode kernel sources (kernels, shared device helpers), in a fixed order."""
     h = hashlib.sha256()
     for f in KERNEL_SRCS:
-        h.update(open(f, "rb").read())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
 
 
@@ -49,7 +50,9 @@ def measured_traffic():
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    with open(TRAFFIC_FILE) as fh:
+        lines = fh.read().splitlines()
+    for line in lines:
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()

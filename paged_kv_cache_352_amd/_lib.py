@@ -107,7 +107,8 @@ def declared_functions():
     """Names of the functions the headers under include/ declare."""
     names = set()
     for h in HEADERS:
-        text = open(h).read()
+        with open(h) as f:
+            text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         text = re.sub(r"#define[^\n]*", "", text)
         names |= set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text))

@@ -8,7 +8,8 @@ import pytest
 
 from oracle import accounting as acc
 
-GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_accounting.json")))
+with open(os.path.join(os.path.dirname(__file__), "golden", "pages_accounting.json")) as _f:
+    GOLD = json.load(_f)
 
 
 def pct2(fr):

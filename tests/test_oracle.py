@@ -18,7 +18,8 @@ from oracle import attention as att
 from oracle import kvcache as kvc
 from oracle import online
 
-GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_accounting.json")))
+with open(os.path.join(os.path.dirname(__file__), "golden", "pages_accounting.json")) as _f:
+    GOLD = json.load(_f)
 
 
 def rand_case(seed, S, Hq, Hkv, d, B, lens, spare=1, q_scale=1.0, poison=True):

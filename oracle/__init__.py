@@ -41,7 +41,15 @@ blockmgr    the per-request / per-block bookkeeping and the copy-on-write
             (free counts of the shared-tail quiz, the lab's block counts, the
             24 GiB and 8 GiB pool figures, the 3-blocks / 4-requests case).
 
-No function here is "parity unpinned".
+Every function here is pinned by something other than itself (see the
+tests named in each module).  The sampled-row checkers
+``attention.paged_decode_rows`` and ``attention.paged_extend_rows`` are pinned
+by the plain-Python brute force on tiny poisoned cases, row by row, and by
+bitwise equality with the full ``paged_decode`` / ``paged_extend``;
+``accounting.tail_waste_bound`` by exhaustive enumeration (the bound holds for
+every length list and equals the largest total tail waste among lists with
+the same number of non-empty requests).  Planted indexing mistakes in each
+are caught.  No function here is "parity unpinned".
 """
 
 from . import accounting, attention, blockmgr, kvcache, online  # noqa: F401

@@ -131,3 +131,48 @@ def test_tail_waste_bound_and_edge_cases():
             assert 0 <= w <= B - 1
     with pytest.raises(ValueError):
         acc.blocks_for(-1, 16)
+
+
+def _bound_pins_pass(bound):
+    """The tail-waste bound of [Budgets] eq. (2) is N(B-1) over the N non-empty
+    requests.  Pinned by what the inequality must satisfy: it holds for every
+    length list, it is attained (the largest total tail waste over all lists
+    with the same number of empty and non-empty requests equals it, found here
+    by exhaustive enumeration), and empty requests add nothing."""
+    from itertools import product
+
+    for B in (1, 2, 3, 4):
+        for S in (1, 2, 3):
+            by_zeros = {}
+            for lens in product(range(0, 2 * B + 2), repeat=S):
+                w = acc.total_tail_waste(lens, B)
+                b = bound(list(lens), B)
+                if w > b:
+                    return False
+                z = sum(1 for n in lens if n == 0)
+                by_zeros.setdefault(z, []).append((w, b))
+            for z, pairs in by_zeros.items():
+                bs = {b for _, b in pairs}
+                if len(bs) != 1 or max(w for w, _ in pairs) != bs.pop():
+                    return False
+    # lengths all one past a block boundary attain it exactly; empty requests are not counted
+    for B in (16, 64):
+        lens = [1 + B * j for j in range(7)] + [0, 0, 0]
+        if not (acc.total_tail_waste(lens, B) == 7 * (B - 1) == bound(lens, B)):
+            return False
+    return bound([0, 0], 16) == 0
+
+
+def test_tail_waste_bound_is_attained_and_skips_empty_requests():
+    assert _bound_pins_pass(acc.tail_waste_bound)
+
+
+def test_tail_waste_bound_planted_mistakes_are_caught():
+    mutants = {
+        "counts_empty": lambda lens, B: len(lens) * (B - 1),
+        "N_times_B": lambda lens, B: sum(1 for n in lens if n > 0) * B,
+        "B_minus_one_total": lambda lens, B: (B - 1) if any(lens) else 0,
+        "ceil_of_sum": lambda lens, B: acc.tail_waste(sum(lens), B),
+    }
+    for kind, fn in mutants.items():
+        assert not _bound_pins_pass(fn), kind

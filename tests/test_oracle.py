@@ -422,3 +422,64 @@ def test_swap_round_trip_and_isolation():
     k2, v2 = kvc.swap_in(k, v, [0, 5], buf)
     assert np.array_equal(k2[:, 0], k[:, 4]) and np.array_equal(v2[:, 5], v[:, 1])
     assert np.array_equal(k2[:, 1:5], k[:, 1:5]) and np.array_equal(v2[:, 1:5], v[:, 1:5])
+
+
+# ---------------------------------------------------------------- sampled rows
+
+
+def _rows_case():
+    # five requests with distinct lengths (one empty, one of a single token),
+    # NaN-poisoned tails and spare blocks, asked for out of order
+    return rand_case(31, 5, 4, 2, 3, 4, [9, 0, 5, 1, 12], spare=2), [4, 0, 2, 1]
+
+
+def test_decode_rows_match_brute_force_and_full_oracle():
+    """paged_decode_rows is the reference for the sampled requests of large batches.
+
+    Each returned row equals the brute-force sum for that request, and is bit
+    for bit the full oracle's row for the same request.
+    """
+    (q, k, v, tab, n), rows = _rows_case()
+    got = att.paged_decode_rows(q, k, v, tab, n, 4, 0.7, rows)
+    assert sorted(got) == sorted(rows)
+    want = brute_attention(q, k, v, tab, n, 4, 0.7)
+    full = att.paged_decode(q, k, v, tab, n, 4, 0.7)
+    for s in rows:
+        assert np.all(np.isfinite(got[s]))
+        assert np.max(np.abs(got[s] - want[s])) <= 1e-14 * max(1.0, np.max(np.abs(want[s])))
+        assert np.array_equal(got[s], full[s])
+    assert np.array_equal(got[1], np.zeros_like(got[1]))  # length 0
+
+
+def _rows_pins_pass(rows_fn):
+    (q, k, v, tab, n), rows = _rows_case()
+    try:
+        got = rows_fn(q, k, v, tab, n, 4, 0.7, rows)
+    except (IndexError, ValueError):
+        return False
+    want = brute_attention(q, k, v, tab, n, 4, 0.7)
+    return sorted(got) == sorted(rows) and all(
+        np.all(np.isfinite(got[s])) and np.max(np.abs(got[s] - want[s])) <= 1e-13 for s in rows)
+
+
+def _rows_mutant(kind):
+    """Copies of the sampled-row wrapper with one plausible indexing slip each."""
+    def rows_fn(q, k, v, tab, lens, B, scale, rows):
+        res = {}
+        for i, s in enumerate(rows):
+            qs = q[i] if kind == "q_by_position" else q[s]
+            row = tab[(s + 1) % len(lens)] if kind == "table_of_next" else tab[s]
+            m = int(lens[rows[0]]) if kind == "length_of_first" else int(lens[s])
+            K_s = att.gather_sequence(k, row, m, B)
+            V_s = att.gather_sequence(v, row, m, B)
+            res[s] = att.dense_attention(qs, K_s, V_s, scale)
+        return res
+
+    return rows_fn
+
+
+def test_decode_rows_planted_mistakes_are_caught():
+    assert _rows_pins_pass(att.paged_decode_rows)
+    assert _rows_pins_pass(_rows_mutant("none"))
+    for kind in ("q_by_position", "table_of_next", "length_of_first"):
+        assert not _rows_pins_pass(_rows_mutant(kind)), kind

@@ -240,3 +240,60 @@ def test_extend_reference_passes_and_planted_mistakes_are_caught():
     assert _extend_pins_pass(_extend_mutant("none"))
     for kind in ("exclusive", "one_ahead", "reversed", "not_causal", "from_zero"):
         assert not _extend_pins_pass(_extend_mutant(kind)), kind
+
+
+# ---------------------------------------------------------------- sampled rows
+
+
+def _extend_rows_case():
+    # n < T for request 1, T = n for request 3; tails and spares poisoned
+    return rand_extend_case(41, 5, 3, 4, 2, 3, 4, [10, 2, 7, 3, 13], spare=2), [4, 1, 3, 0]
+
+
+def test_extend_rows_match_brute_force_and_full_oracle():
+    """paged_extend_rows is the reference for the sampled requests of large
+    several-token batches: each row equals the brute force, and bit for bit
+    the full oracle's row."""
+    (q, k, v, tab, n), rows = _extend_rows_case()
+    got = att.paged_extend_rows(q, k, v, tab, n, 4, 0.6, rows)
+    assert sorted(got) == sorted(rows)
+    want = brute_extend(q, k, v, tab, n, 4, 0.6)
+    full = att.paged_extend(q, k, v, tab, n, 4, 0.6)
+    for s in rows:
+        assert np.all(np.isfinite(got[s]))
+        assert np.max(np.abs(got[s] - want[s])) <= 1e-14 * max(1.0, np.max(np.abs(want[s])))
+        assert np.array_equal(got[s], full[s])
+    assert np.array_equal(got[1][0], np.zeros_like(got[1][0]))  # position -1 attends nothing
+
+
+def _extend_rows_pins_pass(rows_fn):
+    (q, k, v, tab, n), rows = _extend_rows_case()
+    try:
+        got = rows_fn(q, k, v, tab, n, 4, 0.6, rows)
+    except (IndexError, ValueError):
+        return False
+    want = brute_extend(q, k, v, tab, n, 4, 0.6)
+    return sorted(got) == sorted(rows) and all(
+        np.all(np.isfinite(got[s])) and np.max(np.abs(got[s] - want[s])) <= 1e-13 for s in rows)
+
+
+def _extend_rows_mutant(kind):
+    def rows_fn(q, k, v, tab, lens, B, scale, rows):
+        res = {}
+        for i, s in enumerate(rows):
+            qs = q[i] if kind == "q_by_position" else q[s]
+            row = tab[(s + 1) % len(lens)] if kind == "table_of_next" else tab[s]
+            m = int(lens[rows[0]]) if kind == "length_of_first" else int(lens[s])
+            K_s = att.gather_sequence(k, row, m, B)
+            V_s = att.gather_sequence(v, row, m, B)
+            res[s] = att.extend_attention(qs, K_s, V_s, scale)
+        return res
+
+    return rows_fn
+
+
+def test_extend_rows_planted_mistakes_are_caught():
+    assert _extend_rows_pins_pass(att.paged_extend_rows)
+    assert _extend_rows_pins_pass(_extend_rows_mutant("none"))
+    for kind in ("q_by_position", "table_of_next", "length_of_first"):
+        assert not _extend_rows_pins_pass(_extend_rows_mutant(kind)), kind

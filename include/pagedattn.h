@@ -91,7 +91,9 @@ typedef struct {
   int32_t num_blocks;         /* NB >= 1: blocks in each pool                  */
   pa_dtype dtype;             /* element type of q, pools, new K/V             */
   int32_t num_splits;         /* split-K parts: 0 = chosen by the library from
-                                 (S, Hkv, MB) alone, >= 1 forces that count     */
+                                 host-known sizes (S, Hq, Hkv, MB, B, dtype and
+                                 the query-token count), >= 1 asks for that
+                                 count (rounded as paged_attn_plan states)      */
   void* workspace;            /* device scratch for split-K partial states,
                                  256-byte aligned, caller-owned; may be NULL when
                                  paged_attn_plan reports 0 bytes                */
@@ -111,19 +113,46 @@ const char* pa_last_error(void);
 
 /*
  * Split-K plan for paged_attn_decode at block size B: the number of splits
- * the decode will use and the workspace it needs.  The workspace holds the
- * partial states that reach the merge: one per split with bf16; with float32
- * the splits run in groups of up to 4 that merge inside one workgroup, so it
- * holds one per group, and none for up to 4 splits.  0 bytes when nothing
- * reaches the merge.  Depends only on host-known sizes, so repeated calls
- * agree.  With dims->num_splits = 0 the plan takes enough splits to occupy
- * the GPU's compute units, but no more than the table holds whole runs of
- * 256 slots with bf16 (16 with float32), and at least one; the table is cut
- * into equal runs of whole max(16, B)-slot units, the last run taking the
- * rest.  A forced num_splits is capped at ceil(MB * B / max(16, B)).
+ * the decode will use and the workspace it needs.  A history cut into
+ * contiguous block ranges is attended range by range, and each range leaves
+ * an online-softmax state (m, l, o) that a merge combines exactly ([Budgets]
+ * eq. (4): the running max, the rescaled normaliser and the value
+ * accumulator rescaled by the same factor).  The workspace holds the
+ * partial states that reach the merge, float32 o [rows, P', d], then m and
+ * l [rows, P'] (rows = S * T * Hq): P' = P with bf16; with float32 the
+ * splits run in groups of up to 4 that merge inside one workgroup, so P' is
+ * the number of groups, and no workspace is needed for up to 4 splits.  0
+ * bytes when nothing reaches the merge.  Every call writes every partial
+ * state it later reads, so the workspace never needs clearing.
+ *
+ * The plan depends only on host-known values: S, Hq, Hkv, MB, B, dtype and
+ * the query-token count T (1 here), never on lengths or table contents, so
+ * repeated calls agree.  The table's MB * B slots are cut into units of
+ * max(16, B) slots (16-slot tiles, whole blocks).
+ *   - dims->num_splits = 0: enough splits to occupy the GPU's compute units
+ *     given the work items (S * Hkv, times the token groups of T), but no
+ *     split shorter than 256 slots with bf16 (16 with float32), and at least
+ *     one.
+ *   - dims->num_splits = P0 >= 1: P0 capped at the unit count.
+ * The requested count P0 then becomes P = ceil(units / ceil(units / P0)):
+ * each split takes ceil(units / P0) whole units, the last one the rest, and
+ * splits that would hold no unit are dropped.  So a forced count may come
+ * back smaller (MB * B = 160 slots at B = 16 is 10 units: 6 or 7 give 5).
+ * Callers size the workspace, and read partial states, by the num_splits
+ * returned here.
  */
 pa_status paged_attn_plan(const pa_dims* dims, int32_t B, int32_t* num_splits,
                           size_t* workspace_bytes);
+
+/*
+ * Workspace bytes paged_attn_decode needs for dims (dims->num_splits as
+ * given, 0 = the automatic plan) at block size B: the workspace_bytes
+ * paged_attn_plan reports for the same arguments, returned directly.  The
+ * workspace holds the mergeable (m, l, o) partial states of [Budgets]
+ * eq. (4), one per split and output row.  Returns 0 when the decode needs
+ * none, and SIZE_MAX when dims or B are rejected (pa_last_error() says why).
+ */
+size_t paged_attn_workspace_bytes(const pa_dims* dims, int32_t B);
 
 /*
  * One decode step of one layer: for every request s and query head h,
@@ -269,10 +298,16 @@ pa_status kv_swap_in(void* k_pool, void* v_pool, const int32_t* blocks, int32_t 
 
 /*
  * Debug helper, not on the decode path: materialise each request's history
- * contiguously through the same address computation the decode uses.
+ * contiguously through the same address computation the decode uses, the
+ * address function of [Slides] "把 token 6 变成真正的内存地址" (logical token t
+ * lives in slot t % B of the physical block the table names for logical
+ * block t / B):
  *   k_out[s, t, :, :] = k_pool[block_tables[s][t / B], t % B, :, :]  for t < seq_lens[s]
- * k_out/v_out are [S, MB*B, Hkv, d] of `dtype`; positions t >= seq_lens[s]
- * are not written.
+ * k_out/v_out are [S, MB*B, Hkv, d] of `dtype`, device memory; positions
+ * t >= seq_lens[s] are not written.  Lengths are clamped to [0, MB*B]; a table
+ * entry outside [0, NB) leaves that block's positions unwritten.  Bytes are
+ * copied exactly.  Errors: PA_ERR_INVALID_ARG for a NULL or misaligned
+ * pointer, PA_ERR_UNSUPPORTED for MB > 65535.
  */
 pa_status paged_kv_gather(const void* k_pool, const void* v_pool, const int32_t* block_tables,
                           const int32_t* seq_lens, int32_t B, void* k_out, void* v_out,

@@ -25,5 +25,6 @@ from ._lib import (  # noqa: F401
     paged_attn_extend,
     paged_attn_extend_plan,
     paged_attn_plan,
+    paged_attn_workspace_bytes,
     paged_kv_gather,
 )

@@ -66,6 +66,7 @@ def load():
         "pa_status_string": (ctypes.c_char_p, [I32]),
         "pa_last_error": (ctypes.c_char_p, []),
         "paged_attn_plan": (I32, [DP, I32, ctypes.POINTER(I32), ctypes.POINTER(SZ)]),
+        "paged_attn_workspace_bytes": (SZ, [DP, I32]),
         "paged_attn_decode": (I32, [P, P, P, P, P, I32, F32, P, P, DP]),
         "paged_attn_decode_append": (I32, [P, P, P, P, P, P, P, P, I32, F32, P, P, DP]),
         "paged_attn_extend_plan": (I32, [DP, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(SZ)]),
@@ -161,6 +162,16 @@ def paged_attn_plan(S, Hq, Hkv, D, MB, NB, dtype, B, num_splits=0):
     w = ctypes.c_size_t()
     _check("paged_attn_plan", lib.paged_attn_plan(ctypes.byref(d), B, ctypes.byref(p), ctypes.byref(w)))
     return p.value, w.value
+
+
+def paged_attn_workspace_bytes(S, Hq, Hkv, D, MB, NB, dtype, B, num_splits=0):
+    """Workspace bytes paged_attn_decode needs for this shape (0 = none)."""
+    lib = load()
+    d = make_dims(S, Hq, Hkv, D, MB, NB, dtype, num_splits)
+    n = lib.paged_attn_workspace_bytes(ctypes.byref(d), B)
+    if n == ctypes.c_size_t(-1).value:
+        raise PagedAttnError(f"paged_attn_workspace_bytes: {lib.pa_last_error().decode()}")
+    return n
 
 
 def paged_attn_extend_plan(S, Hq, Hkv, D, MB, NB, dtype, B, T, num_splits=0):

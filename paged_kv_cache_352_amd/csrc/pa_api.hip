@@ -249,6 +249,14 @@ pa_status paged_attn_plan(const pa_dims* dims, int32_t B, int32_t* num_splits, s
   return plan_common(dims, B, 1, num_splits, workspace_bytes);
 }
 
+size_t paged_attn_workspace_bytes(const pa_dims* dims, int32_t B) {
+  g_last_error.clear();
+  int32_t P = 0;
+  size_t bytes = 0;
+  if (plan_common(dims, B, 1, &P, &bytes) != PA_OK) return SIZE_MAX;
+  return bytes;
+}
+
 pa_status paged_attn_extend_plan(const pa_dims* dims, int32_t B, int32_t num_q_tokens, int32_t* num_splits,
                                  size_t* workspace_bytes) {
   g_last_error.clear();

@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol(lib):
     names = pa.declared_functions()
     assert {"paged_attn_decode", "kv_append", "kv_cow_copy", "paged_kv_gather", "paged_attn_plan",
             "paged_attn_extend", "paged_attn_extend_plan", "kv_append_tokens", "pa_bm_truncate",
-            "paged_attn_decode_append",
+            "paged_attn_decode_append", "paged_attn_workspace_bytes",
             "pa_bm_prepare_extend"} <= set(names)
     for name in names:
         assert hasattr(lib, name), name
@@ -253,3 +253,40 @@ def test_decode_append_rejects_before_launch(lib):
     e = dims(S=0)
     assert lib.paged_attn_decode_append(None, None, None, None, None, None, None, None, 16, ctypes.c_float(0.1),
                                         None, None, ctypes.byref(e)) == OK
+
+
+# The five decode workloads' shapes (S, Hq, Hkv, MB, NB, dtype) at B = 16.
+CONFIG_SHAPES = [
+    (5, 8, 2, 32, 64, torch.float32),        # 5 sequences of 37-511 tokens, fp32
+    (32, 32, 8, 256, 8192, torch.bfloat16),  # 32 x 4096 tokens
+    (256, 32, 8, 33, 12288, torch.bfloat16),  # 256 mixed lengths (one layer)
+    (64, 32, 8, 133, 1024, torch.bfloat16),  # prefix sharing
+    (168, 16, 4, 65, 10922, torch.bfloat16),  # 168 x 1025 tokens (one layer)
+]
+
+
+def test_workspace_bytes_agrees_with_plan_on_the_workload_shapes(lib):
+    size_max = ctypes.c_size_t(-1).value
+    for S, Hq, Hkv, MB, NB, dt in CONFIG_SHAPES:
+        for splits in (0, 1, 2, 3, 4, 7, 16, 64):
+            d = pa.make_dims(S, Hq, Hkv, 128, MB, NB, dt, splits)
+            P, want = pa.paged_attn_plan(S, Hq, Hkv, 128, MB, NB, dt, 16, num_splits=splits)
+            got = lib.paged_attn_workspace_bytes(ctypes.byref(d), 16)
+            assert got == want, (S, splits, got, want)
+            assert got == pa.paged_attn_workspace_bytes(S, Hq, Hkv, 128, MB, NB, dt, 16, num_splits=splits)
+            assert got == (S * Hq * merged_splits(P, dt) * 130 * 4 if merged_splits(P, dt) > 1 else 0)
+    # rejected arguments: SIZE_MAX and a reason, for the same cases paged_attn_plan refuses
+    for d in (dims(Hq=6, Hkv=4), dims(D=64), dims(splits=-2), dims(MB=0)):
+        assert lib.paged_attn_workspace_bytes(ctypes.byref(d), 16) == size_max
+        assert lib.pa_last_error().decode() != ""
+    assert lib.paged_attn_workspace_bytes(ctypes.byref(dims()), 12) == size_max
+    assert lib.paged_attn_workspace_bytes(None, 16) == size_max
+    with pytest.raises(pa.PagedAttnError):
+        pa.paged_attn_workspace_bytes(4, 6, 4, 128, 4, 16, torch.bfloat16, 16)
+    assert lib.paged_attn_workspace_bytes(ctypes.byref(dims()), 16) == 0 and lib.pa_last_error().decode() == ""
+
+
+def test_forced_split_counts_round_to_whole_units(lib):
+    # MB * B = 160 slots at B = 16 is 10 units of 16: 6 or 7 splits of ceil(10/P) units leave 5
+    for P0, want in [(1, 1), (2, 2), (3, 3), (4, 4), (5, 5), (6, 5), (7, 5), (9, 5), (10, 10), (40, 10)]:
+        assert pa.paged_attn_plan(3, 8, 2, 128, 10, 64, torch.bfloat16, 16, num_splits=P0)[0] == want, P0

@@ -135,6 +135,19 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _launch_stream(stream):
+    """The torch stream a call enqueues on (the current one when ``stream`` is None).
+
+    Tensors a call allocates for itself (its output, the split workspace, the
+    gather's zero-filled buffers) are created with this stream current, so the
+    caching allocator ties them to the stream the kernels run on: a workspace
+    dropped when the call returns is not handed to another stream's
+    allocation while the split and merge kernels still use it, and a fill
+    runs before the kernel that writes over it.
+    """
+    return stream if stream is not None else torch.cuda.current_stream()
+
+
 def _need_cuda(*ts):
     for t in ts:
         if not (t.is_cuda and t.is_contiguous()):
@@ -211,18 +224,21 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, B, scale, out=N
     if q.dim() != 3:
         raise PagedAttnError("paged_attn_decode takes q [S, Hq, d]")
     S, Hq, D, NB, Hkv, MB = _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, B, out)
-    if out is None:
-        out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
-    _need_cuda(q, k_pool, v_pool, block_tables, seq_lens, out)
+    _need_cuda(q, k_pool, v_pool, block_tables, seq_lens)
+    st = _launch_stream(stream)
     P, need = paged_attn_plan(S, Hq, Hkv, D, MB, NB, q.dtype, B, num_splits)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    with torch.cuda.stream(st):
+        if out is None:
+            out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
+        if need and workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _need_cuda(q, k_pool, v_pool, block_tables, seq_lens, out)
     if workspace is not None:
         _need_cuda(workspace)
     d = make_dims(S, Hq, Hkv, D, MB, NB, q.dtype, num_splits, workspace)
     _check("paged_attn_decode", lib.paged_attn_decode(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), B, ctypes.c_float(scale),
-        _ptr(out), _stream(stream), ctypes.byref(d)))
+        _ptr(out), _stream(st), ctypes.byref(d)))
     return out
 
 
@@ -239,18 +255,21 @@ def paged_attn_decode_append(q, k_pool, v_pool, k_new, v_new, block_tables, posi
         raise PagedAttnError("k_new/v_new must have the pool dtype")
     if positions.dtype != torch.int32 or tuple(positions.shape) != (S,):
         raise PagedAttnError("positions must be int32 [S]")
-    if out is None:
-        out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
-    _need_cuda(q, k_pool, v_pool, k_new, v_new, block_tables, positions, seq_lens, out)
+    _need_cuda(q, k_pool, v_pool, k_new, v_new, block_tables, positions, seq_lens)
+    st = _launch_stream(stream)
     P, need = paged_attn_plan(S, Hq, Hkv, D, MB, NB, q.dtype, B, num_splits)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    with torch.cuda.stream(st):
+        if out is None:
+            out = torch.empty((S, Hq, D), dtype=torch.float32, device=q.device)
+        if need and workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _need_cuda(out)
     if workspace is not None:
         _need_cuda(workspace)
     d = make_dims(S, Hq, Hkv, D, MB, NB, q.dtype, num_splits, workspace)
     _check("paged_attn_decode_append", lib.paged_attn_decode_append(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), _ptr(block_tables), _ptr(positions),
-        _ptr(seq_lens), B, ctypes.c_float(scale), _ptr(out), _stream(stream), ctypes.byref(d)))
+        _ptr(seq_lens), B, ctypes.c_float(scale), _ptr(out), _stream(st), ctypes.byref(d)))
     return out
 
 
@@ -265,18 +284,21 @@ def paged_attn_extend(q, k_pool, v_pool, block_tables, seq_lens, B, scale, out=N
         raise PagedAttnError("paged_attn_extend takes q [S, T, Hq, d]")
     S, Hq, D, NB, Hkv, MB = _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, B, out)
     T = q.shape[1]
-    if out is None:
-        out = torch.empty(tuple(q.shape), dtype=torch.float32, device=q.device)
-    _need_cuda(q, k_pool, v_pool, block_tables, seq_lens, out)
+    _need_cuda(q, k_pool, v_pool, block_tables, seq_lens)
+    st = _launch_stream(stream)
     P, need = paged_attn_extend_plan(S, Hq, Hkv, D, MB, NB, q.dtype, B, T, num_splits)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    with torch.cuda.stream(st):
+        if out is None:
+            out = torch.empty(tuple(q.shape), dtype=torch.float32, device=q.device)
+        if need and workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _need_cuda(q, k_pool, v_pool, block_tables, seq_lens, out)
     if workspace is not None:
         _need_cuda(workspace)
     d = make_dims(S, Hq, Hkv, D, MB, NB, q.dtype, num_splits, workspace, FLAG_BF16_WEIGHTS if bf16_weights else 0)
     _check("paged_attn_extend", lib.paged_attn_extend(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), T, B, ctypes.c_float(scale),
-        _ptr(out), _stream(stream), ctypes.byref(d)))
+        _ptr(out), _stream(st), ctypes.byref(d)))
     return out
 
 
@@ -384,17 +406,20 @@ def paged_kv_gather(k_pool, v_pool, block_tables, seq_lens, B, k_out=None, v_out
     if Bp != B or tuple(v_pool.shape) != tuple(k_pool.shape) or seq_lens.dtype != torch.int32 \
             or block_tables.dtype != torch.int32 or tuple(seq_lens.shape) != (S,):
         raise PagedAttnError("gather: shapes or dtypes disagree")
-    if k_out is None:
-        k_out = torch.zeros((S, MB * B, Hkv, D), dtype=k_pool.dtype, device=k_pool.device)
-    if v_out is None:
-        v_out = torch.zeros_like(k_out)
+    _need_cuda(k_pool, v_pool, block_tables, seq_lens)
+    st = _launch_stream(stream)
+    with torch.cuda.stream(st):
+        if k_out is None:
+            k_out = torch.zeros((S, MB * B, Hkv, D), dtype=k_pool.dtype, device=k_pool.device)
+        if v_out is None:
+            v_out = torch.zeros_like(k_out)
     for t in (k_out, v_out):
         if tuple(t.shape) != (S, MB * B, Hkv, D) or t.dtype != k_pool.dtype:
             raise PagedAttnError("gather outputs must be [S, MB*B, Hkv, d] of the pool dtype")
     _need_cuda(k_pool, v_pool, block_tables, seq_lens, k_out, v_out)
     d = make_dims(S, 1, Hkv, D, MB, NB, k_pool.dtype)
     _check("paged_kv_gather", lib.paged_kv_gather(_ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens),
-                                                  B, _ptr(k_out), _ptr(v_out), _stream(stream), ctypes.byref(d)))
+                                                  B, _ptr(k_out), _ptr(v_out), _stream(st), ctypes.byref(d)))
     return k_out, v_out
 
 
@@ -405,20 +430,26 @@ class DecodeLaunch:
     For tight loops (benchmarks, graph capture): ``launch()`` only re-issues the
     C call.  The tensors must stay alive and keep their shapes.  With
     ``stream=None`` each launch goes to the stream current at that moment
-    (so a launch inside a graph capture is captured).
+    (so a launch inside a graph capture is captured).  ``out`` and the
+    workspace, when allocated here, belong to ``stream`` (else to the stream
+    current at construction); keep this object alive until launches on any
+    other stream have finished.
     """
 
     def __init__(self, q, k_pool, v_pool, block_tables, seq_lens, B, scale, out=None, num_splits=0,
                  workspace=None, stream=None, bf16_weights=False):
         S, Hq, D, NB, Hkv, MB = _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, B, out)
-        self.out = out if out is not None else torch.empty(tuple(q.shape), dtype=torch.float32, device=q.device)
         extend = q.dim() == 4  # [S, T, Hq, d]: paged_attn_extend
         if extend:
             self.splits, need = paged_attn_extend_plan(S, Hq, Hkv, D, MB, NB, q.dtype, B, q.shape[1], num_splits)
         else:
             self.splits, need = paged_attn_plan(S, Hq, Hkv, D, MB, NB, q.dtype, B, num_splits)
-        if need and workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _need_cuda(q, k_pool, v_pool, block_tables, seq_lens)
+        with torch.cuda.stream(_launch_stream(stream)):
+            self.out = out if out is not None else torch.empty(tuple(q.shape), dtype=torch.float32,
+                                                               device=q.device)
+            if need and workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         self.workspace = workspace
         _need_cuda(q, k_pool, v_pool, block_tables, seq_lens, self.out)
         self._keep = (q, k_pool, v_pool, block_tables, seq_lens)

@@ -169,6 +169,35 @@ def test_deterministic_repeat():
     assert torch.equal(a.view(torch.int32), c.view(torch.int32))
 
 
+def test_split_decode_on_a_side_stream_keeps_its_workspace():
+    """A split decode enqueued on a stream other than the current one: the
+    binding's workspace goes back to the allocator when the call returns, while
+    the split and merge kernels may still be running.  Allocations and fills on
+    the current stream right after must not land in it: every output stays
+    bit-identical to the same decode on the current stream, and matches the
+    oracle on sampled requests."""
+    banner("side stream: 8-split decode of 32 x 4096 tokens, then fills on the current stream")
+    b = W.config2(device=DEV)
+    rows = [0, 13, 31]
+    want = HostLayer(b, 0).oracle(rows)
+    args = (b.q[0], b.k_pool[0], b.v_pool[0], b.block_tables, b.seq_lens, b.B, b.scale)
+    base = pa.paged_attn_decode(*args, num_splits=8)
+    torch.cuda.synchronize()
+    _, need = pa.paged_attn_plan(32, 32, 8, 128, b.block_tables.shape[1], b.k_pool.shape[1], torch.bfloat16, b.B,
+                                 num_splits=8)
+    assert need > 0
+    side = torch.cuda.Stream()
+    outs, junk = [], []
+    for _ in range(4):
+        outs.append(pa.paged_attn_decode(*args, num_splits=8, stream=side))
+        junk.append(torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV))  # NaN bytes, current stream
+    torch.cuda.synchronize()
+    for out in outs:
+        assert torch.equal(out.view(torch.int32), base.view(torch.int32))
+    got = host_f32(outs[-1])
+    assert_close(np.stack([got[s] for s in rows]), np.stack([want[s] for s in rows]), torch.bfloat16, "side stream")
+
+
 @pytest.mark.parametrize("splits", [1, 3])
 def test_graph_capture_replays_match_eager(splits):
     """The library only enqueues on the caller's stream, so a captured launch

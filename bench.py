@@ -64,8 +64,28 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(b, min_seconds):
-    """The float64 oracle on the host cores, over whole passes of the same batch."""
+def _blas_threads():
+    """Threads numpy's BLAS may use in this process (threadpoolctl), else the CPUs we may run on."""
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"]
+        if n:
+            return max(n)
+    except Exception:  # pragma: no cover - threadpoolctl absent
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(b, min_seconds, gpu_out=None):
+    """The float64 oracle on the host cores, request by request over the same batch.
+
+    Runs whole request passes (gather through the table, then dense attention)
+    for about ``min_seconds``, cycling over the batch's requests.  When
+    ``gpu_out`` (the GPU's output for the same step) is given, the rows the
+    oracle computed are also compared with it."""
+    import numpy as np
+
     from oracle import attention as att
 
     k = b.k_pool[0].float().cpu().numpy()
@@ -73,27 +93,38 @@ def cpu_baseline(b, min_seconds):
     q = b.q[0].float().cpu().numpy()
     tab = b.block_tables.cpu().numpy()
     lens = b.seq_lens.cpu().numpy()
-    rows = 0
+    passes = 0
+    ref = {}
     wall0, cpu0 = time.perf_counter(), time.process_time()
-    while True:
-        for s in range(b.S):
-            att.paged_decode_rows(q, k, v, tab, lens, b.B, b.scale, [s])
-            rows += 1
-            if time.perf_counter() - wall0 >= min_seconds and rows >= 1:
-                break
-        if time.perf_counter() - wall0 >= min_seconds:
-            break
+    while time.perf_counter() - wall0 < min_seconds:
+        s = passes % b.S
+        ref[s] = att.paged_decode_rows(q, k, v, tab, lens, b.B, b.scale, [s])[s]
+        passes += 1
     wall = time.perf_counter() - wall0
     cpu = time.process_time() - cpu0
-    kv_bytes = rows * int(lens[0]) * 2 * b.Hkv * b.D * 2
-    return {
+    kv_bytes = sum(int(lens[i % b.S]) for i in range(passes)) * 2 * b.Hkv * b.D * b.elem_bytes
+    res = {
         "value": kv_bytes / wall / 1e9,
         "unit": "GB/s",
-        "cores": max(1, round(cpu / wall)),
+        "cores": _blas_threads(),
         "kind": "oracle",
-        "sample": f"{rows} of the batch's 32 requests (float64 gather + dense attention), "
-                  f"{wall:.1f} s wall, {cpu:.1f} s CPU; host has {os.cpu_count()} CPUs",
+        "sample": f"{passes} request passes cycling over the {b.S}-request batch ({len(ref)} distinct requests; "
+                  f"float64 gather + dense attention), {wall:.1f} s wall, {cpu:.1f} s CPU",
+        "cpu_time_over_wall": round(cpu / wall, 2),
+        "host_cpus": os.cpu_count(),
+        "host_cpus_usable": len(os.sched_getaffinity(0)),
     }
+    if gpu_out is not None:
+        got = gpu_out.cpu().numpy()
+        rows = sorted(ref)
+        want = np.stack([ref[s] for s in rows])
+        err = float(np.max(np.abs(got[rows].astype(np.float64) - want)))
+        top = float(np.max(np.abs(want)))
+        res["max_abs_err_vs_oracle"] = err
+        res["max_err_over_max_out"] = err / top if top else 0.0
+        res["tolerance"] = "5e-3 * max|out| (bf16 K/V, fp32 accumulation)"
+        res["rows_compared"] = len(rows)
+    return res
 
 
 def calibrate_copy(torch, dev, n_bytes=1 << 30, reps=5):
@@ -485,6 +516,11 @@ def main():
             "algorithmic_bytes_per_launch": kv_bytes,
         },
     }
+    # The output of a step over the first pool copy (all copies hold the same
+    # K/V), for the comparison with the oracle rows the CPU baseline computes.
+    first.launch()
+    torch.cuda.synchronize()
+    host_out = out.cpu()
     del calls, first, pools
     torch.cuda.empty_cache()
     if not args.no_side_kernels:
@@ -496,7 +532,7 @@ def main():
         for k, v in st.items():
             log(f"suite: {k}: {json.dumps(v)}")
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(b, args.cpu_seconds, gpu_out=host_out)
     print(json.dumps(res), flush=True)
     return 0
 

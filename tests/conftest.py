@@ -30,3 +30,18 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """Write the GPU tests' per-case accuracy records when PA_ACCURACY_REPORT names a file."""
+    path = os.environ.get("PA_ACCURACY_REPORT")
+    if not path:
+        return
+    mod = sys.modules.get("tests.gpu_util")
+    recs = getattr(mod, "ACCURACY", []) if mod else []
+    if not recs:
+        return
+    import json
+
+    with open(path, "w") as f:
+        json.dump(recs, f, indent=1)

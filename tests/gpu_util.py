@@ -76,15 +76,69 @@ class HostLayer:
         return att.paged_decode_rows(self.q, k, v, self.tables, self.lens, self.B, self.scale, rows)
 
 
-def assert_close(got, want, dtype, what=""):
+class HostRows:
+    """Host copy of one layer's pre-step inputs for the listed requests only.
+
+    Holds just the blocks those requests' tables reference (renumbered), so
+    every layer of a large multi-layer batch can be checked on a handful of
+    requests without copying its pools.  Batches with copy-on-write pairs are
+    not supported (a copy may read blocks outside the listed requests)."""
+
+    def __init__(self, b, layer, rows):
+        assert not b.cow_src.numel()
+        self.rows = list(rows)
+        tab = b.block_tables.cpu().numpy()
+        lens = b.seq_lens.cpu().numpy()
+        pos = b.append_positions.cpu().numpy()
+        nblk = {s: -(-max(int(lens[s]), int(max(pos[:, s].max(initial=-1) + 1, 0))) // b.B) for s in self.rows}
+        used = sorted({int(tab[s, j]) for s in self.rows for j in range(nblk[s])})
+        remap = {blk: i for i, blk in enumerate(used)}
+        ids = torch.as_tensor(used, dtype=torch.long, device=b.k_pool.device)
+        self.k = host_f32(b.k_pool[layer].index_select(0, ids))
+        self.v = host_f32(b.v_pool[layer].index_select(0, ids))
+        sel = torch.as_tensor(self.rows, dtype=torch.long, device=b.q.device)
+        self.q = host_f32(b.q[layer].index_select(0, sel))
+        self.tables = np.zeros((len(self.rows), b.MB), dtype=np.int64)
+        for i, s in enumerate(self.rows):
+            self.tables[i, :nblk[s]] = [remap[int(tab[s, j])] for j in range(nblk[s])]
+        self.lens = lens[self.rows]
+        self.pos = pos[:, self.rows]
+        self.k_new = host_f32(b.k_new[:, layer].index_select(1, sel)) if b.rounds else None
+        self.v_new = host_f32(b.v_new[:, layer].index_select(1, sel)) if b.rounds else None
+        self.B, self.scale = b.B, b.scale
+
+    def oracle(self):
+        """[len(rows), Hq, d] float64, in the order the rows were listed."""
+        k, v = self.k, self.v
+        for r in range(self.pos.shape[0]):
+            k = kvc.append(k, self.k_new[r], self.tables, self.pos[r], self.B)
+            v = kvc.append(v, self.v_new[r], self.tables, self.pos[r], self.B)
+        return att.paged_decode(self.q, k, v, self.tables, self.lens, self.B, self.scale)
+
+
+# Largest error against the oracle per recorded case, written out at the end
+# of the session when PA_ACCURACY_REPORT names a file (tests/conftest.py).
+ACCURACY = []
+
+
+def assert_close(got, want, dtype, what="", record=None):
+    """Element-wise check against the oracle at the tolerance for ``dtype``.
+
+    ``record`` names the case in the accuracy report (largest absolute error,
+    largest |oracle|, their ratio and the tolerance)."""
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     assert got.shape == want.shape
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     err = float(np.max(np.abs(got - want))) if got.size else 0.0
+    ref = float(np.max(np.abs(want))) if want.size else 0.0
+    if record is not None:
+        ACCURACY.append({"case": record, "dtype": str(dtype).replace("torch.", ""), "elements": int(got.size),
+                         "max_abs_err": err, "max_abs_oracle": ref, "err_over_max_out": err / ref if ref else 0.0,
+                         "tolerance": (f"abs {FP32_ABS_TOL}" if dtype == torch.float32
+                                       else f"{BF16_REL_TOL} * max|oracle|")})
     if dtype == torch.float32:
         assert err <= FP32_ABS_TOL, f"{what}: max abs err {err:.3e} > {FP32_ABS_TOL}"
     else:
-        ref = float(np.max(np.abs(want))) if want.size else 0.0
         assert err <= BF16_REL_TOL * ref, f"{what}: max abs err {err:.3e} > {BF16_REL_TOL} * {ref:.3e}"
     return err

@@ -8,7 +8,7 @@ import torch
 
 import paged_kv_cache_352_amd as pa
 import workloads as W
-from tests.gpu_util import HostLayer, assert_close, banner, gpu_step, host_bits, host_f32
+from tests.gpu_util import HostLayer, HostRows, assert_close, banner, gpu_step, host_bits, host_f32
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -20,7 +20,7 @@ def test_config1_fp32_full():
     ref = HostLayer(b, 0).oracle()
     out = gpu_step(b)[0]
     torch.cuda.synchronize()
-    assert_close(host_f32(out), ref, torch.float32, "config1")
+    assert_close(host_f32(out), ref, torch.float32, "config1", record="fp32 5 requests (37..511 tokens), all rows")
 
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 5, 32])
@@ -39,25 +39,28 @@ def test_config2_bf16_full():
     host = HostLayer(b, 0)
     out = gpu_step(b)[0]
     torch.cuda.synchronize()
-    assert_close(host_f32(out), host.oracle(), torch.bfloat16, "config2")
+    assert_close(host_f32(out), host.oracle(), torch.bfloat16, "config2",
+                 record="bf16 32 x 4096 tokens (bench launch plan), all rows")
 
 
 def test_config3_bf16_32_layers():
+    """Layers 0 and 31 in full; every layer on the forced histories 0, 1, 16, 17
+    (attending 1, 2, 17, 18 tokens) and two drawn requests."""
     banner("config3 bf16 256 requests x 32 layers (append + decode)")
     b = W.config3(device=DEV)
     full_layers = (0, 31)
-    sampled_layers = tuple(range(1, 31, 6))
-    rows = [0, 1, 2, 3, 100, 255]  # the forced lengths 0, 1, 16, 17 and two drawn ones
-    hosts = {layer: HostLayer(b, layer) for layer in full_layers + sampled_layers}  # pre-step copies
+    rows = [0, 1, 2, 3, 100, 255]
+    hosts = {layer: HostLayer(b, layer) for layer in full_layers}  # pre-step copies
+    compact = {layer: HostRows(b, layer, rows) for layer in range(b.L)}
     outs = gpu_step(b)
     torch.cuda.synchronize()
     for layer in full_layers:
-        assert_close(host_f32(outs[layer]), hosts[layer].oracle(), torch.bfloat16, f"config3 layer {layer}")
-    for layer in sampled_layers:
-        ref = hosts[layer].oracle(rows)
-        got = host_f32(outs[layer])
-        assert_close(np.stack([got[s] for s in rows]), np.stack([ref[s] for s in rows]), torch.bfloat16,
-                     f"config3 layer {layer}")
+        assert_close(host_f32(outs[layer]), hosts[layer].oracle(), torch.bfloat16, f"config3 layer {layer}",
+                     record=f"bf16 256 mixed-length requests, layer {layer}, all rows")
+    for layer in range(b.L):
+        assert_close(host_f32(outs[layer])[rows], compact[layer].oracle(), torch.bfloat16,
+                     f"config3 layer {layer} rows {rows}",
+                     record=f"bf16 256 mixed-length requests, layer {layer}, rows {rows}")
 
 
 @pytest.mark.parametrize("t", [None, 1, 15])
@@ -67,23 +70,32 @@ def test_config4_cow_large_logits(t):
     host = HostLayer(b, 0)
     out = gpu_step(b)[0]
     torch.cuda.synchronize()
-    assert_close(host_f32(out), host.oracle(), torch.bfloat16, "config4")
+    assert_close(host_f32(out), host.oracle(), torch.bfloat16, "config4",
+                 record=f"bf16 prefix sharing, q x 20, tail fill t={b.info['t']}, all rows")
 
 
 @pytest.mark.parametrize("splits", [0, 4])
 def test_config5_bf16_24_layers(splits):
-    """168 x 1025 tokens, 24 layers.  Every plan splits the 65 blocks of a request
-    over several waves; splits=4 also splits them over workgroups (merge kernel)."""
+    """168 x 1025 tokens, 24 layers: layers 0 and 23 in full, every layer on six
+    requests.  Every plan splits the 65 blocks of a request over several waves;
+    splits=4 also splits them over workgroups (merge kernel)."""
     banner(f"config5 bf16 168x1025 x 24 layers (append + decode), splits={splits}")
     b = W.config5(device=DEV)
     full_layers = (0, 23)
+    rows = [0, 1, 57, 100, 166, 167]
     hosts = {layer: HostLayer(b, layer) for layer in full_layers}
+    compact = {layer: HostRows(b, layer, rows) for layer in range(b.L)}
     P, ws = pa.paged_attn_plan(b.S, b.Hq, b.Hkv, b.D, b.MB, b.NB, b.dtype, b.B, num_splits=splits)
     assert (P > 1 and ws > 0) if splits else P >= 1
     outs = gpu_step(b, num_splits=splits)
     torch.cuda.synchronize()
     for layer in full_layers:
-        assert_close(host_f32(outs[layer]), hosts[layer].oracle(), torch.bfloat16, f"config5 layer {layer}")
+        assert_close(host_f32(outs[layer]), hosts[layer].oracle(), torch.bfloat16, f"config5 layer {layer}",
+                     record=f"bf16 168 x 1025 tokens, splits={splits}, layer {layer}, all rows")
+    for layer in range(b.L):
+        assert_close(host_f32(outs[layer])[rows], compact[layer].oracle(), torch.bfloat16,
+                     f"config5 layer {layer} rows {rows}",
+                     record=f"bf16 168 x 1025 tokens, splits={splits}, layer {layer}, rows {rows}")
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])

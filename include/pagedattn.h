@@ -178,6 +178,35 @@ pa_status paged_attn_decode(const void* q, const void* k_pool, const void* v_poo
                             int32_t B, float scale, float* out, hipStream_t stream,
                             const pa_dims* dims);
 
+/* Bytes of the static device scratch paged_attn_decode_noalloc uses (16 MiB). */
+#define PA_NOALLOC_SCRATCH_BYTES (16 << 20)
+
+/*
+ * paged_attn_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and errors as paged_attn_decode, bit
+ * for bit, except that dims->workspace and dims->workspace_bytes are ignored:
+ * the split-K partial states go to a static device array inside the library,
+ * PA_NOALLOC_SCRATCH_BYTES long, of which each GPU the library runs on holds
+ * one copy until the process ends.  The caller still passes q, the pools, the
+ * tables, the lengths and out.  Nothing is allocated or freed, here or in the
+ * kernels; the first call on a device looks up that device's copy of the
+ * array (hipGetSymbolAddress) and keeps its address.
+ *   - A plan whose workspace (paged_attn_plan) exceeds the scratch returns
+ *     PA_ERR_WORKSPACE and enqueues nothing: ask for fewer splits, or use
+ *     paged_attn_decode with a workspace.
+ *   - `stream` must belong to the current device (PA_ERR_INVALID_ARG
+ *     otherwise).
+ *   - Every call on one GPU shares that GPU's copy, and the kernels write
+ *     every partial state before reading it, so nothing needs clearing
+ *     between calls; but calls that overlap on one GPU (two streams, or two
+ *     threads) race on it and may return wrong results.  Serialise them, for
+ *     example on one stream.
+ */
+pa_status paged_attn_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                    const int32_t* block_tables, const int32_t* seq_lens, int32_t B, float scale,
+                                    float* out, hipStream_t stream, const pa_dims* dims);
+
 /*
  * One decode step with the step's token appended in the same call:
  * kv_append(k_pool, v_pool, k_new, v_new, block_tables, positions, B) then

@@ -6,6 +6,7 @@ The compute runs in hand-written HIP kernels behind a C ABI
 
 from ._lib import (  # noqa: F401
     LIB_PATH,
+    NOALLOC_SCRATCH_BYTES,
     PA_BF16,
     PA_F32,
     BlockManager,
@@ -22,6 +23,7 @@ from ._lib import (  # noqa: F401
     make_dims,
     paged_attn_decode,
     paged_attn_decode_append,
+    paged_attn_decode_noalloc,
     paged_attn_extend,
     paged_attn_extend_plan,
     paged_attn_plan,

@@ -45,6 +45,7 @@ class PaDims(ctypes.Structure):
 
 
 ABI_VERSION = 3            # PA_ABI_VERSION of include/pagedattn.h that PaDims mirrors
+NOALLOC_SCRATCH_BYTES = 16 << 20  # PA_NOALLOC_SCRATCH_BYTES
 FLAG_BF16_WEIGHTS = 1      # PA_FLAG_BF16_WEIGHTS
 
 
@@ -68,6 +69,7 @@ def load():
         "paged_attn_plan": (I32, [DP, I32, ctypes.POINTER(I32), ctypes.POINTER(SZ)]),
         "paged_attn_workspace_bytes": (SZ, [DP, I32]),
         "paged_attn_decode": (I32, [P, P, P, P, P, I32, F32, P, P, DP]),
+        "paged_attn_decode_noalloc": (I32, [P, P, P, P, P, I32, F32, P, P, DP]),
         "paged_attn_decode_append": (I32, [P, P, P, P, P, P, P, P, I32, F32, P, P, DP]),
         "paged_attn_extend_plan": (I32, [DP, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(SZ)]),
         "paged_attn_extend": (I32, [P, P, P, P, P, I32, I32, F32, P, P, DP]),
@@ -239,6 +241,22 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, B, scale, out=N
     _check("paged_attn_decode", lib.paged_attn_decode(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), B, ctypes.c_float(scale),
         _ptr(out), _stream(st), ctypes.byref(d)))
+    return out
+
+
+def paged_attn_decode_noalloc(q, k_pool, v_pool, block_tables, seq_lens, B, scale, out, num_splits=0, stream=None):
+    """paged_attn_decode with the split workspace in the library's static device
+    scratch (PA_NOALLOC_SCRATCH_BYTES per GPU): nothing is allocated, so the
+    caller passes ``out``.  Calls that overlap on one GPU race on the scratch."""
+    lib = load()
+    if q.dim() != 3 or out is None:
+        raise PagedAttnError("paged_attn_decode_noalloc takes q [S, Hq, d] and a preallocated out")
+    S, Hq, D, NB, Hkv, MB = _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, B, out)
+    _need_cuda(q, k_pool, v_pool, block_tables, seq_lens, out)
+    d = make_dims(S, Hq, Hkv, D, MB, NB, q.dtype, num_splits)
+    _check("paged_attn_decode_noalloc", lib.paged_attn_decode_noalloc(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), B, ctypes.c_float(scale),
+        _ptr(out), _stream(stream), ctypes.byref(d)))
     return out
 
 

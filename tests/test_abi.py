@@ -290,3 +290,20 @@ def test_forced_split_counts_round_to_whole_units(lib):
     # MB * B = 160 slots at B = 16 is 10 units of 16: 6 or 7 splits of ceil(10/P) units leave 5
     for P0, want in [(1, 1), (2, 2), (3, 3), (4, 4), (5, 5), (6, 5), (7, 5), (9, 5), (10, 10), (40, 10)]:
         assert pa.paged_attn_plan(3, 8, 2, 128, 10, 64, torch.bfloat16, 16, num_splits=P0)[0] == want, P0
+
+
+@no_gpu
+def test_noalloc_decode_refuses_before_launch(lib):
+    def call(d):
+        return lib.paged_attn_decode_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, 16, ctypes.c_float(0.1), FAKE, None,
+                                             ctypes.byref(d) if d is not None else None)
+
+    assert call(None) == INVALID
+    assert call(dims(Hq=6, Hkv=4)) == INVALID
+    assert call(dims(D=64)) == UNSUPPORTED
+    # 64 requests x 32 heads in 19 splits need 20.2 MB of partial states: more than the static scratch
+    d = pa.make_dims(64, 32, 8, 128, 38, 4096, pa.PA_BF16, 32)
+    assert pa.paged_attn_plan(64, 32, 8, 128, 38, 4096, torch.bfloat16, 16, num_splits=32)[1] > pa.NOALLOC_SCRATCH_BYTES
+    assert call(d) == WORKSPACE
+    assert "static scratch" in lib.pa_last_error().decode()
+    assert call(dims(S=0)) == OK  # nothing to do, nothing launched

@@ -195,12 +195,19 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
 
   // Issue the 8 16-byte loads of the K and V rows of the wave's k-th tile:
   // row group i is slots 16*u + 4*i .. +3.  With B >= 16 the tile lies
-  // inside one block; with B < 16 each row group has its own block, and a
-  // group past the history reads the tile's first block instead (its rows
-  // are masked), so no table entry at or past ceil(n / B) addresses the
-  // pool.  A speculative load (issued before the length is known) clamps a
-  // block id outside the pool to block 0 without judging it: it is judged
-  // once the length says whether the tile is part of the history.
+  // inside one block; with B < 16 each row group has its own block.  Once
+  // the length is known, a row group wholly past the history is loaded
+  // through a descriptor of size 0: the hardware returns zeros for it and
+  // reads no memory (its rows are masked anyway), and no table entry at or
+  // past ceil(n / B) addresses the pool.  With `none` the whole tile is
+  // such a load: the prefetch slot past a wave's last tile keeps the same
+  // instruction count, so every wait still covers exactly the tile it
+  // needs, but fetches nothing (an earlier form re-loaded the last tile
+  // there, which with non-temporal loads went back to memory: 1.17x the
+  // algorithmic bytes on 256 requests of 2-513 tokens, 1.05x at 1025).  A
+  // speculative load (issued before the length is known) clamps a block id
+  // outside the pool to block 0 without judging it: it is judged once the
+  // length says whether the tile is part of the history.
   bool bad = false;
   auto pool_block = [&](int pb, bool judge) {
     if (pb < 0 || pb >= a.NB) {  // outside the pool: never dereferenced, result poisoned
@@ -210,26 +217,34 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
     return pb;
   };
   int n = 0;
-  auto load_tile = [&](int k, int kb, Tile& t, int tab, bool spec) {
+  auto load_tile = [&](int k, int kb, Tile& t, int tab, bool spec, bool none = false) {
     const int u = wave_tile(k);
     if constexpr (B >= kTile) {
-      const int pb = pool_block(__builtin_amdgcn_readlane(tab, k - kb), !spec);
-      const __amdgpu_buffer_rsrc_t kr = block_rsrc(kpool + (int64_t)pb * blk_bytes, blk_bytes);
-      const __amdgpu_buffer_rsrc_t vr = block_rsrc(vpool + (int64_t)pb * blk_bytes, blk_bytes);
+      const int pb = pool_block(__builtin_amdgcn_readlane(tab, k - kb), !spec && !none);
+      const char* kb_ptr = kpool + (int64_t)pb * blk_bytes;
+      const char* vb_ptr = vpool + (int64_t)pb * blk_bytes;
       const int row0 = (kTile * u) % B;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) t.k[i] = load_kv16<true>(kr, voff, (row0 + 4 * i) * row_bytes);
+      for (int i = 0; i < 4; ++i) {
+        const bool live = !none && (spec || kTile * u + 4 * i < n);
+        t.k[i] = load_kv16<true>(block_rsrc(kb_ptr, live ? blk_bytes : 0u), voff, (row0 + 4 * i) * row_bytes);
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) t.v[i] = load_kv16<true>(vr, voff, (row0 + 4 * i) * row_bytes);
+      for (int i = 0; i < 4; ++i) {
+        const bool live = !none && (spec || kTile * u + 4 * i < n);
+        t.v[i] = load_kv16<true>(block_rsrc(vb_ptr, live ? blk_bytes : 0u), voff, (row0 + 4 * i) * row_bytes);
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = kTile * u + 4 * i;
-        const bool live = spec || tok < n;
-        const int pb = pool_block(__builtin_amdgcn_readlane(tab, (k - kb) * E + (live ? (4 * i) / B : 0)), !spec);
+        const bool live = !none && (spec || tok < n);
+        const int pb = pool_block(__builtin_amdgcn_readlane(tab, (k - kb) * E + (live ? (4 * i) / B : 0)),
+                                  !spec && live);
         const int soff = live ? (tok % B) * row_bytes : 0;
-        t.k[i] = load_kv16<true>(block_rsrc(kpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
-        t.v[i] = load_kv16<true>(block_rsrc(vpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
+        const uint32_t size = live ? blk_bytes : 0u;
+        t.k[i] = load_kv16<true>(block_rsrc(kpool + (int64_t)pb * blk_bytes, size), voff, soff);
+        t.v[i] = load_kv16<true>(block_rsrc(vpool + (int64_t)pb * blk_bytes, size), voff, soff);
       }
     }
   };
@@ -343,11 +358,12 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
       load_tile(kb, kb, ring[0], tab, false);
     }
 #pragma unroll
-    for (int b = 1; b + 1 < kDepth; ++b) load_tile(min(kb + b, ke - 1), kb, ring[b], tab, false);
+    for (int b = 1; b + 1 < kDepth; ++b) load_tile(min(kb + b, ke - 1), kb, ring[b], tab, false, kb + b >= ke);
     for (int k = kb; k < ke; k += kDepth) {
 #pragma unroll
       for (int b = 0; b < kDepth; ++b) {
-        load_tile(min(k + b + kDepth - 1, ke - 1), kb, ring[(b + kDepth - 1) % kDepth], tab, false);
+        const int kn = k + b + kDepth - 1;  // the tile to prefetch; past the run: a load that fetches nothing
+        load_tile(min(kn, ke - 1), kb, ring[(b + kDepth - 1) % kDepth], tab, false, kn >= ke);
         __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the current tile's math
         process(wave_tile(k + b), ring[b]);
         if (k + b + 1 >= ke) break;

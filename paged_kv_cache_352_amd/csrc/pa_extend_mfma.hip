@@ -131,26 +131,30 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(Decode
     }
     return pb;
   };
-  // Rows past the history (only in the last tile, B < 16) read the history's
-  // last block instead and are zeroed or masked; no table entry at or past
-  // ceil(n / B) is read.  kStream: one workgroup covers all query tokens of
+  // Rows past the history (only in the last tile), and the loads of `none`
+  // (a pair's second tile past the range, the prefetch slot past a chunk's
+  // last pair), go through a descriptor of size 0: the hardware returns
+  // zeros and reads no memory, the instruction count (and so every wait)
+  // stays the same, and no table entry at or past ceil(n / B) addresses the
+  // pool.  Those rows are zeroed or masked.  kStream: one workgroup covers all query tokens of
   // its (request, KV head) (a.TG == 1), so each K/V byte is read once and the
   // loads carry the non-temporal hint; otherwise several workgroups read the
   // same history, and it is left to the caches (measured on the 512-token
   // chunk: 414 vs 440 us without and with the hint).
-  auto load_rows = [&](int u, uint4& k, uint4& v, int eb, int tab) {
+  auto load_rows = [&](int u, uint4& k, uint4& v, int eb, int tab, bool none) {
+    const int tok = kTile * u + 4 * w;
+    const bool live = !none && tok < n;
+    const uint32_t size = live ? blk_bytes : 0u;
     if constexpr (B >= kTile) {
-      const int pb = pool_block(__builtin_amdgcn_readlane(tab, (kTile * u) / B - eb));
+      const int pb = live ? pool_block(__builtin_amdgcn_readlane(tab, (kTile * u) / B - eb)) : 0;
       const int soff = ((kTile * u) % B + 4 * w) * row_bytes;
-      k = load_kv16<kStream>(block_rsrc(kpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
-      v = load_kv16<kStream>(block_rsrc(vpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
+      k = load_kv16<kStream>(block_rsrc(kpool + (int64_t)pb * blk_bytes, size), voff, soff);
+      v = load_kv16<kStream>(block_rsrc(vpool + (int64_t)pb * blk_bytes, size), voff, soff);
     } else {
-      const int tok = kTile * u + 4 * w;
-      const bool live = tok < n;
-      const int pb = pool_block(__builtin_amdgcn_readlane(tab, (live ? tok : n - 1) / B - eb));
+      const int pb = live ? pool_block(__builtin_amdgcn_readlane(tab, tok / B - eb)) : 0;
       const int soff = live ? (tok % B) * row_bytes : 0;
-      k = load_kv16<kStream>(block_rsrc(kpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
-      v = load_kv16<kStream>(block_rsrc(vpool + (int64_t)pb * blk_bytes, blk_bytes), voff, soff);
+      k = load_kv16<kStream>(block_rsrc(kpool + (int64_t)pb * blk_bytes, size), voff, soff);
+      v = load_kv16<kStream>(block_rsrc(vpool + (int64_t)pb * blk_bytes, size), voff, soff);
     }
   };
 
@@ -176,9 +180,11 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(Decode
   struct Rows {
     uint4 ka, va, kb, vb;
   };
-  auto load_pair = [&](int t, Rows& r, int eb, int tab, int te) {
-    load_rows(t, r.ka, r.va, eb, tab);
-    load_rows(min(t + 1, te - 1), r.kb, r.vb, eb, tab);  // past the range: a copy of tile t, masked below
+  // none: the prefetch slot past a chunk's last pair.  A second tile past the
+  // range (an odd tile count) fetches nothing and is masked below.
+  auto load_pair = [&](int t, Rows& r, int eb, int tab, int te, bool none) {
+    load_rows(t, r.ka, r.va, eb, tab, none);
+    load_rows(min(t + 1, te - 1), r.kb, r.vb, eb, tab, none || t + 1 >= te);
   };
 
   // Tiles t and t+1: write this lane's rows into buffer (t/2) & 1, wait for
@@ -229,12 +235,13 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(Decode
     const int tab = trow[min(eb + lane, nb - 1)];
     Rows ring[kDepth];
 #pragma unroll
-    for (int b = 0; b + 1 < kDepth; ++b) load_pair(min(tb + 2 * b, te - 1), ring[b], eb, tab, te);
+    for (int b = 0; b + 1 < kDepth; ++b) load_pair(min(tb + 2 * b, te - 1), ring[b], eb, tab, te, tb + 2 * b >= te);
     for (int t = tb; t < te; t += 2 * kDepth) {
 #pragma unroll
       for (int b = 0; b < kDepth; ++b) {
         constexpr int kNext = kDepth - 1;
-        load_pair(min(t + 2 * (b + kNext), te - 1), ring[(b + kNext) % kDepth], eb, tab, te);
+        const int tn = t + 2 * (b + kNext);  // the pair to prefetch; past the chunk: loads that fetch nothing
+        load_pair(min(tn, te - 1), ring[(b + kNext) % kDepth], eb, tab, te, tn >= te);
         __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the current pair's math
         process(t + 2 * b, ring[b], te);
         if (t + 2 * b + 2 >= te) break;

@@ -239,10 +239,17 @@ def suite(torch, pa, W, dev):
         us = graph_time_us(torch, launch_all, reps)
         return us / len(calls), calls[0].splits
 
-    def full_step_graph(b, fused=False):
+    def full_step_graph(b, fused=False, all_layers=False):
         def step():
             if b.cow_src.numel():
                 pa.kv_cow_copy(b.k_pool, b.v_pool, b.cow_src, b.cow_dst, b.cow_n, b.B)
+            if all_layers:  # the step's one append round, every layer in one launch, then the decodes
+                pa.kv_append_layers(b.k_pool, b.v_pool, b.k_new[0], b.v_new[0], b.block_tables,
+                                    b.append_positions[0], b.B)
+                for layer in range(b.L):
+                    pa.paged_attn_decode(b.q[layer], b.k_pool[layer], b.v_pool[layer], b.block_tables, b.seq_lens,
+                                         b.B, b.scale, out=outs[layer], workspace=ws)
+                return
             for layer in range(b.L):
                 if fused:  # the step's one append round inside the decode launch
                     pa.paged_attn_decode_append(b.q[layer], b.k_pool[layer], b.v_pool[layer], b.k_new[0, layer],
@@ -366,6 +373,9 @@ def suite(torch, pa, W, dev):
             if b.rounds == 1 and not b.cow_src.numel():
                 ent["full_step_fused_us"] = round(full_step_graph(b, fused=True), 2)
                 ent["full_step_fused_ops"] = f"one paged_attn_decode_append per layer, {b.L} layer(s)"
+                if b.L > 1:
+                    ent["full_step_append_layers_us"] = round(full_step_graph(b, all_layers=True), 2)
+                    ent["full_step_append_layers_ops"] = f"one kv_append_layers, then one decode per layer, {b.L} layers"
         if name.startswith("bf16 256 mixed"):
             ent["swap_500MiB"] = swap_time(torch, pa, b, dev)
         if name.startswith("bf16 prefix"):
@@ -374,6 +384,57 @@ def suite(torch, pa, W, dev):
         del b
         torch.cuda.empty_cache()
     return out
+
+
+PROFILE_WORKLOADS = {
+    "decode32x4096": "bf16 32 x 4096 tokens, one layer (the headline batch, 4 rotated pool copies)",
+    "mixed256": "bf16 256 mixed-length requests, 32 layers: one decode launch per layer, after the step's append",
+    "prefix64": "bf16 prefix sharing, 64 branches, one layer: one decode launch, after the COW and appends",
+    "long168": "bf16 168 x 1025 tokens, 24 layers: one decode launch per layer, after the step's append",
+    "chunk512": "bf16 prompt chunk, 8 x 4096 tokens, T = 512, one layer (paged_attn_extend)",
+}
+
+
+def profile_workload(torch, pa, W, dev, name, steps, warmup):
+    """Only one workload's attention launches, for rocprofv3: the step's
+    copies and appends run once, untimed, then ``warmup`` + ``steps`` rounds of
+    its decode (or extend) launches, one per layer per round, back to back.
+    Prints the algorithmic bytes of one launch and the launches made."""
+    if name == "decode32x4096":
+        b = W.config2(device=dev)
+        pools = [(b.k_pool[0], b.v_pool[0])] + [(b.k_pool[0].clone(), b.v_pool[0].clone()) for _ in range(3)]
+        calls = [pa.DecodeLaunch(b.q[0], k, v, b.block_tables, b.seq_lens, b.B, b.scale) for k, v in pools]
+        per_launch = b.valid_kv_bytes_per_layer()
+        rounds = [[c] for c in calls]
+    elif name == "chunk512":
+        b = W.prefill_chunk_batch(device=dev)
+        pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
+        calls = [pa.DecodeLaunch(b.q, b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B, b.scale)]
+        per_launch = b.valid_kv_bytes()
+        rounds = [calls]
+    else:
+        b = {"mixed256": W.config3, "prefix64": W.config4, "long168": W.config5}[name](device=dev)
+        if b.cow_src.numel():
+            pa.kv_cow_copy(b.k_pool, b.v_pool, b.cow_src, b.cow_dst, b.cow_n, b.B)
+        for r in range(b.rounds):
+            for layer in range(b.L):
+                pa.kv_append(b.k_pool[layer], b.v_pool[layer], b.k_new[r, layer], b.v_new[r, layer],
+                             b.block_tables, b.append_positions[r], b.B)
+        calls = [pa.DecodeLaunch(b.q[layer], b.k_pool[layer], b.v_pool[layer], b.block_tables, b.seq_lens, b.B,
+                                 b.scale) for layer in range(b.L)]
+        per_launch = b.valid_kv_bytes_per_layer()
+        rounds = [calls]
+    torch.cuda.synchronize()
+    n = 0
+    for i in range(warmup + steps):
+        for c in rounds[i % len(rounds)]:
+            c.launch()
+            n += 1
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_workload": name, "what": PROFILE_WORKLOADS[name],
+                      "algorithmic_kv_bytes_per_launch": int(per_launch), "launches": n,
+                      "splits": calls[0].splits}), flush=True)
+    return 0
 
 
 def main():
@@ -390,6 +451,8 @@ def main():
     ap.add_argument("--no-side-kernels", action="store_true", help="skip the kv_append / kv_cow_copy timings")
     ap.add_argument("--suite", metavar="PATH", default=None,
                     help="also time the other four workloads and write them as JSON to PATH")
+    ap.add_argument("--profile-workload", choices=sorted(PROFILE_WORKLOADS), default=None,
+                    help="only run one workload's attention launches (for rocprofv3), --warmup + --steps rounds")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB float32 negate-copy kernel (reads 1 GiB, writes 1 GiB) "
                          "a few times, to scale the HBM byte counters")
@@ -413,6 +476,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.calibrate_copy:
         return calibrate_copy(torch, dev)
+    if args.profile_workload:
+        return profile_workload(torch, pa, W, dev, args.profile_workload, args.steps, args.warmup)
     b = W.config2(device=dev)
     kv_bytes = b.valid_kv_bytes_per_layer()
     pools = [(b.k_pool[0], b.v_pool[0])]

@@ -275,6 +275,23 @@ pa_status kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v
                     hipStream_t stream, const pa_dims* dims);
 
 /*
+ * kv_append in every layer at once ([Slides] "写满一块，再拿下一块"; all layers
+ * share one block numbering, so the token's block and slot are the same in
+ * each): for every layer l < num_layers,
+ *   pool_l[block_tables[s][p / B], p % B, :, :] = new[l, s, :, :]   (p = positions[s])
+ * for K and V, one launch.  k_new/v_new are [num_layers, S, Hkv, d] of
+ * `dtype`; layer l's pool starts layer_stride_elems elements after layer
+ * l-1's (num_layers = 1 ignores the stride and is kv_append).  For when the
+ * new K/V of every layer are known together (restoring recomputed tokens, a
+ * step whose projections ran ahead); a model computing one layer after the
+ * other appends per layer, or with paged_attn_decode_append.  Positions,
+ * ownership and skipping as for kv_append.  Bytes are copied exactly.
+ */
+pa_status kv_append_layers(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                           const int32_t* block_tables, const int32_t* positions, int32_t B, int32_t num_layers,
+                           int64_t layer_stride_elems, hipStream_t stream, const pa_dims* dims);
+
+/*
  * kv_append for T = num_tokens consecutive tokens per request (draft tokens
  * or a prompt chunk, [Serving] §5): k_new/v_new are [S, T, Hkv, d] and
  * token i of request s goes to logical position positions[s] + i.  A

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     PoolExhausted,
     declared_functions,
     kv_append,
+    kv_append_layers,
     kv_append_tokens,
     kv_cow_copy,
     kv_swap_in,

@@ -75,6 +75,7 @@ def load():
         "paged_attn_extend": (I32, [P, P, P, P, P, I32, I32, F32, P, P, DP]),
         "kv_append": (I32, [P, P, P, P, P, P, I32, P, DP]),
         "kv_append_tokens": (I32, [P, P, P, P, P, P, I32, I32, P, DP]),
+        "kv_append_layers": (I32, [P, P, P, P, P, P, I32, I32, I64, P, DP]),
         "kv_cow_copy": (I32, [P, P, P, P, P, I32, I32, I32, I64, P, DP]),
         "paged_kv_gather": (I32, [P, P, P, P, I32, P, P, P, DP]),
         "kv_swap_out": (I32, [P, P, P, I32, P, I32, I32, I64, P, DP]),
@@ -359,6 +360,29 @@ def kv_append(k_pool, v_pool, k_new, v_new, block_tables, positions, B, stream=N
     d = make_dims(S, 1, Hkv, D, block_tables.shape[1], NB, k_pool.dtype)
     _check("kv_append", lib.kv_append(_ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), _ptr(block_tables),
                                       _ptr(positions), B, _stream(stream), ctypes.byref(d)))
+
+
+def kv_append_layers(k_pool, v_pool, k_new, v_new, block_tables, positions, B, stream=None):
+    """Write k_new/v_new [L, S, Hkv, d] at logical positions[s] in every layer of pools [L, NB, B, Hkv, d]."""
+    lib = load()
+    if k_pool.dim() != 5:
+        raise PagedAttnError("kv_append_layers takes pools [L, NB, B, Hkv, d]")
+    L, NB, Bp, Hkv, D = k_pool.shape
+    S = k_new.shape[1] if k_new.dim() == 4 else -1
+    if Bp != B or tuple(k_new.shape) != (L, S, Hkv, D) or tuple(v_new.shape) != (L, S, Hkv, D) \
+            or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise PagedAttnError("k_new/v_new must be [L, S, Hkv, d] matching the pools")
+    if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype or v_pool.dtype != k_pool.dtype:
+        raise PagedAttnError("dtype mismatch")
+    if positions.dtype != torch.int32 or block_tables.dtype != torch.int32 or tuple(positions.shape) != (S,):
+        raise PagedAttnError("positions and block_tables must be int32, positions [S]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise PagedAttnError("block_tables must be [S, MB]")
+    _need_cuda(k_pool, v_pool, k_new, v_new, block_tables, positions)
+    d = make_dims(S, 1, Hkv, D, block_tables.shape[1], NB, k_pool.dtype)
+    _check("kv_append_layers", lib.kv_append_layers(_ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
+                                                    _ptr(block_tables), _ptr(positions), B, L, NB * B * Hkv * D,
+                                                    _stream(stream), ctypes.byref(d)))
 
 
 def kv_cow_copy(k_pool, v_pool, src_blocks, dst_blocks, n_valid, B, stream=None):

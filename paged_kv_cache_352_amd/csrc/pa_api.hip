@@ -238,7 +238,7 @@ static pa_status attend(const void* q, const void* k_pool, const void* v_pool, c
     st = kv_common(dims, B, const_cast<void*>(k_pool), const_cast<void*>(v_pool), &ka);
     if (st != PA_OK) return st;
     st = launched(pa::launch_append(ka, static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new),
-                                    block_tables, positions, 1, stream));
+                                    block_tables, positions, 1, 1, 0, stream));
     if (st != PA_OK) return st;
   }
   return launched(pa::launch_decode(a, dims->dtype, B, a.Hq / a.Hkv, stream));
@@ -306,8 +306,11 @@ static pa_status kv_common(const pa_dims* dims, int32_t B, void* k_pool, void* v
 
 static pa_status append_common(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
                                const int32_t* block_tables, const int32_t* positions, int32_t T, int32_t B,
-                               hipStream_t stream, const pa_dims* dims) {
+                               hipStream_t stream, const pa_dims* dims, int32_t num_layers = 1,
+                               int64_t layer_stride_elems = 0) {
   if (T < 1) return fail(PA_ERR_INVALID_ARG, "num_tokens = %d < 1", T);
+  if (num_layers < 1 || num_layers > 65535)
+    return fail(PA_ERR_INVALID_ARG, "num_layers = %d outside [1, 65535]", num_layers);
   pa::KvArgs a{};
   if (dims && dims->num_seqs == 0) return check_dims(dims, B, false);
   pa_status st = kv_common(dims, B, k_pool, v_pool, &a);
@@ -315,14 +318,28 @@ static pa_status append_common(void* k_pool, void* v_pool, const void* k_new, co
   if (!k_new || !v_new || !block_tables || !positions) return fail(PA_ERR_INVALID_ARG, "a required pointer is NULL");
   if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(PA_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
   if ((int64_t)a.S * T > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "too many tokens");
+  const int64_t pool_elems = (int64_t)dims->num_blocks * B * dims->num_kv_heads * dims->head_dim;
+  if (num_layers > 1 && layer_stride_elems < pool_elems)
+    return fail(PA_ERR_INVALID_ARG, "layer_stride_elems %lld smaller than one layer's pool (%lld)",
+                (long long)layer_stride_elems, (long long)pool_elems);
+  const int64_t stride_bytes = num_layers > 1 ? layer_stride_elems * (int64_t)elem_size(dims->dtype) : 0;
+  if (stride_bytes % 16) return fail(PA_ERR_INVALID_ARG, "layer stride must be a multiple of 16 bytes");
   return launched(pa::launch_append(a, static_cast<const uint8_t*>(k_new), static_cast<const uint8_t*>(v_new),
-                                    block_tables, positions, T, stream));
+                                    block_tables, positions, T, num_layers, stride_bytes, stream));
 }
 
 pa_status kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new, const int32_t* block_tables,
                     const int32_t* positions, int32_t B, hipStream_t stream, const pa_dims* dims) {
   g_last_error.clear();
   return append_common(k_pool, v_pool, k_new, v_new, block_tables, positions, 1, B, stream, dims);
+}
+
+pa_status kv_append_layers(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                           const int32_t* block_tables, const int32_t* positions, int32_t B, int32_t num_layers,
+                           int64_t layer_stride_elems, hipStream_t stream, const pa_dims* dims) {
+  g_last_error.clear();
+  return append_common(k_pool, v_pool, k_new, v_new, block_tables, positions, 1, B, stream, dims, num_layers,
+                       layer_stride_elems);
 }
 
 pa_status kv_append_tokens(void* k_pool, void* v_pool, const void* k_new, const void* v_new,

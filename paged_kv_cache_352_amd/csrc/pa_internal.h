@@ -126,9 +126,12 @@ struct KvArgs {
   int row_bytes;  // Hkv * d * element size: one slot of one block
 };
 
-// T tokens per request: k_new/v_new [S, T, Hkv, d], token i at positions[s] + i.
+// T tokens per request in each of num_layers layers: k_new/v_new
+// [L, S, T, Hkv, d], token i at positions[s] + i; layer l's pools start
+// l * layer_stride_bytes after layer 0's.
 hipError_t launch_append(const KvArgs& a, const uint8_t* k_new, const uint8_t* v_new,
-                         const int32_t* tables, const int32_t* positions, int T, hipStream_t stream);
+                         const int32_t* tables, const int32_t* positions, int T, int num_layers,
+                         int64_t layer_stride_bytes, hipStream_t stream);
 
 hipError_t launch_cow(const KvArgs& a, const int32_t* src, const int32_t* dst, const int32_t* n_valid,
                       int num_pairs, int num_layers, int64_t layer_stride_bytes, hipStream_t stream);

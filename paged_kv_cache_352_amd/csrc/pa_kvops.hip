@@ -15,19 +15,30 @@ namespace {
 constexpr int kThreads = 256;
 
 __device__ inline void copy16(uint8_t* __restrict__ dst, const uint8_t* __restrict__ src, int64_t bytes) {
-  for (int64_t i = (int64_t)threadIdx.x * 16; i < bytes; i += kThreads * 16)
+  for (int64_t i = (int64_t)threadIdx.x * 16; i < bytes; i += (int64_t)blockDim.x * 16)
     *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(src + i);
 }
 
-// One workgroup per (request, new token, pool).  Token i of request s takes
-// logical index p = positions[s] + i and goes to slot p % B of block
-// table[p / B]; nothing else moves ([Slides] "写满一块，再拿下一块").  A
-// negative start skips the request; positions or blocks outside the pool are
-// skipped.
+// Threads of one append workgroup: one 16-byte vector per thread per slot
+// row (Hkv * d elements), in whole waves, at most kThreads: 128 for the
+// 2 KiB bf16 rows of 8 KV heads, which one pass then covers.
+int append_threads(int row_bytes) {
+  const int vecs = (row_bytes + 15) / 16;
+  const int waves = (vecs + 63) / 64;
+  return waves >= kThreads / 64 ? kThreads : 64 * waves;
+}
+
+// One workgroup per (request, new token, layer), K and V both.  Token i of
+// request s takes logical index p = positions[s] + i and goes to slot p % B
+// of block table[p / B] of the layer's pools; nothing else moves ([Slides]
+// "写满一块，再拿下一块").  A negative start skips the request; positions or
+// blocks outside the pool are skipped.  New rows are [L, S, T, Hkv, d]
+// (layer stride S*T rows), pools [L, NB, B, Hkv, d] (layer stride given).
 __global__ __launch_bounds__(kThreads) void append_kernel(KvArgs a, const uint8_t* __restrict__ k_new,
                                                           const uint8_t* __restrict__ v_new,
                                                           const int32_t* __restrict__ tables,
-                                                          const int32_t* __restrict__ positions, int T) {
+                                                          const int32_t* __restrict__ positions, int T,
+                                                          int64_t layer_stride_bytes) {
   const int s = blockIdx.x / T;
   const int i = blockIdx.x % T;
   const int start = positions[s];
@@ -36,10 +47,11 @@ __global__ __launch_bounds__(kThreads) void append_kernel(KvArgs a, const uint8_
   if (p >= (int64_t)a.MB * a.B) return;
   const int blk = tables[(int64_t)s * a.MB + p / a.B];
   if (blk < 0 || blk >= a.NB) return;
-  uint8_t* pool = blockIdx.y ? a.v_pool : a.k_pool;
-  const uint8_t* src = (blockIdx.y ? v_new : k_new) + (int64_t)blockIdx.x * a.row_bytes;
-  uint8_t* dst = pool + ((int64_t)blk * a.B + p % a.B) * a.row_bytes;
-  copy16(dst, src, a.row_bytes);
+  const int layer = blockIdx.y;
+  const int64_t src = ((int64_t)layer * gridDim.x + blockIdx.x) * a.row_bytes;
+  const int64_t dst = layer * layer_stride_bytes + ((int64_t)blk * a.B + p % a.B) * a.row_bytes;
+  copy16(a.k_pool + dst, k_new + src, a.row_bytes);
+  copy16(a.v_pool + dst, v_new + src, a.row_bytes);
 }
 
 // One workgroup per (pair, layer, pool): slots [0, n) of block src -> block dst
@@ -107,9 +119,10 @@ hipError_t launch_swap(const KvArgs& a, const int32_t* blocks, int nlist, uint8_
 }
 
 hipError_t launch_append(const KvArgs& a, const uint8_t* k_new, const uint8_t* v_new, const int32_t* tables,
-                         const int32_t* positions, int T, hipStream_t stream) {
-  hipLaunchKernelGGL(append_kernel, dim3(a.S * T, 2), dim3(kThreads), 0, stream, a, k_new, v_new, tables,
-                     positions, T);
+                         const int32_t* positions, int T, int num_layers, int64_t layer_stride_bytes,
+                         hipStream_t stream) {
+  hipLaunchKernelGGL(append_kernel, dim3(a.S * T, num_layers), dim3(append_threads(a.row_bytes)), 0, stream, a,
+                     k_new, v_new, tables, positions, T, layer_stride_bytes);
   return hipGetLastError();
 }
 

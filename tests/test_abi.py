@@ -174,6 +174,16 @@ def test_kv_ops_reject_before_launch(lib):
     assert lib.paged_kv_gather(FAKE, FAKE, None, FAKE, 16, FAKE, FAKE, None, ctypes.byref(d)) == INVALID
     # Hkv*d*2 bytes not a multiple of 16
     assert lib.kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None, ctypes.byref(dims(Hkv=1, D=4))) == UNSUPPORTED
+    # the all-layer append: layer count and stride checked like kv_cow_copy's
+    app = lambda layers, stride, d=d: lib.kv_append_layers(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, layers, stride,
+                                                           None, ctypes.byref(d))
+    assert app(0, 0) == INVALID
+    assert app(70000, 0) == INVALID
+    assert app(2, 10) == INVALID  # stride shorter than one layer's pool
+    assert app(2, 16 * 16 * 2 * 128 + 3) == INVALID  # stride not a multiple of 16 bytes
+    assert lib.kv_append_layers(FAKE, FAKE, None, FAKE, FAKE, FAKE, 16, 2, 16 * 16 * 2 * 128, None,
+                                ctypes.byref(d)) == INVALID
+    assert app(2, 0, d=dims(S=0)) == OK  # nothing to append, nothing launched
 
 
 def test_binding_refuses_host_tensors(lib):

@@ -235,20 +235,22 @@ def test_verify_32x4096_T4_sampled():
     out = host_f32(gpu_extend(b))
     rows = [0, 13, 31]
     ref = host.oracle(rows)
-    assert_close(np.stack([out[s] for s in rows]), np.stack([ref[s] for s in rows]), torch.bfloat16, "verify")
+    assert_close(np.stack([out[s] for s in rows]), np.stack([ref[s] for s in rows]), torch.bfloat16, "verify",
+                 record=f"bf16 verification 32 x 4096 tokens, T = 4, rows {rows}")
     assert np.all(np.isfinite(out))
 
 
 @pytest.mark.parametrize("bf16_weights", [False, True])
 def test_prefill_chunk_512_sampled(bf16_weights):
-    """A 512-token prompt chunk over 3584 tokens of history, 8 requests; one sampled request."""
-    banner(f"prefill chunk bf16 8x4096 T=512 bf16_weights={bf16_weights}, sampled row")
+    """A 512-token prompt chunk over 3584 tokens of history, 8 requests; three sampled requests."""
+    banner(f"prefill chunk bf16 8x4096 T=512 bf16_weights={bf16_weights}, sampled rows")
     b = W.prefill_chunk_batch(device=DEV)
     host = HostExtend(b)
     out = host_f32(gpu_extend(b, bf16_weights=bf16_weights))
-    rows = [5]
+    rows = [0, 5, 7]
     ref = host.oracle(rows)
-    assert_close(np.stack([out[s] for s in rows]), np.stack([ref[s] for s in rows]), torch.bfloat16, "chunk")
+    assert_close(np.stack([out[s] for s in rows]), np.stack([ref[s] for s in rows]), torch.bfloat16, "chunk",
+                 record=f"bf16 prompt chunk 8 x 4096 tokens, T = 512, bf16_weights={bf16_weights}, rows {rows}")
     assert np.all(np.isfinite(out))
 
 

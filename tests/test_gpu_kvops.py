@@ -30,6 +30,44 @@ def test_append_bit_exact(dtype):
     assert np.array_equal(host_bits(b.v_pool[0]), want_v)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_append_layers_bit_exact(dtype):
+    """One kv_append_layers launch writes the token in every layer, as one
+    kv_append per layer would; the other layers' bytes never move."""
+    banner(f"append all layers {dtype}")
+    b = W.custom([0, 1, 5, 16, 17, 31, 32, 33], Hq=8, Hkv=2, dtype=dtype, append=True, L=3, device=DEV, seed=4)
+    k0, v0 = host_bits(b.k_pool), host_bits(b.v_pool)
+    pa.kv_append_layers(b.k_pool, b.v_pool, b.k_new[0], b.v_new[0], b.block_tables, b.append_positions[0], b.B)
+    torch.cuda.synchronize()
+    tab, pos = b.block_tables.cpu().numpy(), b.append_positions[0].cpu().numpy()
+    kn, vn = host_bits(b.k_new[0]), host_bits(b.v_new[0])
+    gk, gv = host_bits(b.k_pool), host_bits(b.v_pool)
+    for layer in range(b.L):
+        assert np.array_equal(gk[layer], kvc.append(k0[layer], kn[layer], tab, pos, b.B)), layer
+        assert np.array_equal(gv[layer], kvc.append(v0[layer], vn[layer], tab, pos, b.B)), layer
+
+
+def test_append_layers_config3_matches_per_layer_appends():
+    """The 256-request batch's append in all 32 layers in one launch: every
+    pool byte equals that of 32 kv_append calls, and the step's decode over it
+    equals the oracle on a full layer."""
+    banner("append all 32 layers, 256 requests")
+    b = W.config3(device=DEV)
+    host = HostLayer(b, 17)
+    ref_k, ref_v = b.k_pool.clone(), b.v_pool.clone()
+    for layer in range(b.L):
+        pa.kv_append(ref_k[layer], ref_v[layer], b.k_new[0, layer], b.v_new[0, layer], b.block_tables,
+                     b.append_positions[0], b.B)
+    pa.kv_append_layers(b.k_pool, b.v_pool, b.k_new[0], b.v_new[0], b.block_tables, b.append_positions[0], b.B)
+    torch.cuda.synchronize()
+    assert torch.equal(b.k_pool.view(torch.int16), ref_k.view(torch.int16))
+    assert torch.equal(b.v_pool.view(torch.int16), ref_v.view(torch.int16))
+    del ref_k, ref_v
+    out = pa.paged_attn_decode(b.q[17], b.k_pool[17], b.v_pool[17], b.block_tables, b.seq_lens, b.B, b.scale)
+    torch.cuda.synchronize()
+    assert_close(host_f32(out), host.oracle(), torch.bfloat16, "config3 layer 17 after the all-layer append")
+
+
 def test_append_positions_outside_table_are_skipped():
     banner("append out-of-range positions")
     b = W.custom([5, 9], Hq=8, Hkv=2, dtype=torch.bfloat16, device=DEV, seed=2)

@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpagedattn.so")
-SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_decode_mfma.hip", "pa_extend_mfma.hip", "pa_kvops.hip",
+SOURCES = ["pa_api.hip", "pa_decode.hip", "pa_decode_mfma.hip", "pa_extend_mfma.hip", "pa_extend_wide.hip",
+           "pa_kvops.hip",
            "pa_noalloc.hip", "pa_blockmgr.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -15,9 +15,14 @@
 //
 // When the (token, head) pairs of a request's KV head outnumber the 16
 // columns of two column sets of one wave, the decode layout would stream
-// the history once per 32 columns.  Here a workgroup of 4 waves takes 4 or 8
-// column sets, one or two per wave (each K and V operand a wave reads from
-// LDS feeds all of its sets), and walks one split of the history tile by
+// the history once per 32 columns.  Here a workgroup of 4 waves takes 4
+// column sets, one per wave, which is how it runs: up to 4 sets of 16 columns
+// fit one workgroup (16 tokens of a 4-head group) and the history is read
+// once.  More tokens, two sets per wave, go to the 32-column kernel in
+// pa_extend_wide.hip, which takes the same columns per wave on the 32x32
+// tiles; the kSets = 2 form below stays as the reference of that layout (each
+// K and V operand a wave reads from LDS feeds all of its sets).  The
+// workgroup walks one split of the history tile by
 // tile: every tile's K and V are loaded once, each wave fetching one group
 // of 4 slot rows (16-byte lanes along a row, as in the decode kernel), and
 // written to a double-buffered LDS tile in the swizzled layout.  Tiles go
@@ -307,16 +312,11 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(Decode
 template <int G, int B, bool kOneRounding>
 void launch_gbr(const DecodeArgs& a, hipStream_t stream) {
   const int items = a.Hkv * a.S * a.P * a.TG;
-  // One column set per wave is chosen only while one workgroup holds all T tokens (a.TG == 1).
-  if (shared_tile_sets(PA_BF16, G, a.T) == 1)
-    hipLaunchKernelGGL((extend_shared_kernel<G, 1, B, kOneRounding, true>), dim3(items), dim3(kWave * kWaves), 0,
-                       stream, a);
-  else if (a.TG == 1)
-    hipLaunchKernelGGL((extend_shared_kernel<G, 2, B, kOneRounding, true>), dim3(items), dim3(kWave * kWaves), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL((extend_shared_kernel<G, 2, B, kOneRounding, false>), dim3(items), dim3(kWave * kWaves), 0,
-                       stream, a);
+  // One column set per wave is chosen only while one workgroup holds all T
+  // tokens (a.TG == 1); two sets per wave go to the 32-column kernel
+  // (pa_extend_wide.hip) instead.
+  hipLaunchKernelGGL((extend_shared_kernel<G, 1, B, kOneRounding, true>), dim3(items), dim3(kWave * kWaves), 0,
+                     stream, a);
 }
 
 template <int G, int B>
@@ -343,6 +343,10 @@ hipError_t launch_b(const DecodeArgs& a, int G, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_extend_shared(const DecodeArgs& a, int B, int G, hipStream_t stream) {
+  // Two 16-column sets per wave: the same columns as one 32-column set of the
+  // 32x32 kernel, which measured 6 % faster on a 512-token chunk (fewer
+  // vector instructions per score; see pa_extend_wide.hip).
+  if (shared_tile_sets(PA_BF16, G, a.T) == 2) return launch_extend_wide(a, B, G, stream);
   switch (B) {
     case 4: return launch_b<4>(a, G, stream);
     case 8: return launch_b<8>(a, G, stream);

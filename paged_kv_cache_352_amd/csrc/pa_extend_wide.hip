@@ -1,0 +1,432 @@
+// Several query tokens per request on the 32x32 matrix-core tiles: the
+// shared-tile kernel for query groups that give each wave 32 columns.
+//
+// [Slides]  = "PagedAttention：让 KV cache 按需生长"
+// [Budgets] = "内存预算约束下的语言模型服务：注意力、分页与调度"
+// [Serving] = "PagedAttention 与在线推理：KV 分页、共享及调度的联合分析"
+//
+// What is computed is the causal form of paged_attn_extend ([Serving] §5):
+// the T new tokens are the last T positions of the n-token history, token i
+// attends positions 0 .. n-T+i; each block is found through the table
+// ([Slides] "读 token 6，先查表，再找偏移"), slots past a column's limit are
+// masked ([Slides] quiz "逻辑顺序没错，为什么 attention 输出还是错？"), and the
+// history folds into the online-softmax state (m, l, o) of [Budgets] eq. (4).
+//
+// A workgroup of 4 waves walks one split of one (request, KV head) history,
+// 32 slots per step; each wave owns 32 columns, the (token, head) pairs of
+// 32/G query tokens of the G-head group.  Each step's 32 K and V slot rows
+// are loaded once (every wave fetches 8 rows: two 4-row groups of 16-byte
+// lanes), written to a double-buffered LDS tile, and after one barrier every
+// wave folds the whole step into its own columns.  The products are taken
+// transposed so that a lane owns one column throughout:
+//
+//   scores  S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = K (32 slots x 16
+//           dims, from LDS), B = Q^T (16 dims x 32 columns, in registers),
+//           8 MFMAs over d = 128.  Lane l gets column l%32 for the 16 slots
+//           8*(r/4) + 4*(l/32) + r%4, r = 0..15, so the column max is a max
+//           over its 16 values and one v_permlane32_swap with the lane 32
+//           away, which holds the other 16 slots.
+//   p.v     O^T += V^T P^T: A = V^T (32 dims x 16 slots), read from the
+//           row-major V tile by ds_read_b64_tr_b16, B = P^T (16 slots x 32
+//           columns).  B's K index 8*(l/32) + i of lane l stands for slot
+//           i < 4 ? 4*(l/32) + i : 8 + 4*(l/32) + i - 4 of the 16-slot half,
+//           which is exactly the order of the lane's own score registers
+//           8*kb .. 8*kb+7, so the weights feed p.v without leaving the lane;
+//           A reads the same slot order.  The accumulators hold o^T of the
+//           lane's own column (dims 32*mb + 8*(r/4) + 4*(l/32) + r%4), so a
+//           rescale needs the lane's own factor only.
+//
+// Weights as in the 16-column kernel: by default each p is a bf16 head plus a
+// bf16 remainder, both rounded to nearest (within 2^-18 of p), through two
+// MFMAs, and l is summed in fp32; with PA_FLAG_BF16_WEIGHTS each p is rounded
+// once to bf16 and l is summed on the matrix core from the same rounded
+// weights.  The running max is the lazy reference of the 16-column kernel
+// (moved only when a step's max exceeds it by more than kLazyMax, base 2).
+#include <hip/hip_runtime.h>
+
+#include "pa_mfma_common.h"
+
+namespace pa {
+namespace {
+
+using namespace mfma;
+
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+constexpr int kWaves = kSharedTileWaves;
+constexpr int kStep = 32;                        // slots per step
+constexpr int kStepBytes = kStep * kHeadDim * 2;  // one K or V step in LDS: 8 KiB
+
+// K step in LDS: slot t, 16-byte chunk k at 256*t + 16*(k ^ (t % 16)); the
+// q.k reads (32 lanes: 32 slots, one chunk each) then meet 16 different
+// chunks in every 16-lane group.  V step: the 32-byte pair of chunks k/2 at
+// 256*t + 32*((k/2) ^ (t % 8)) + 16*(k % 2); a transposing read covers 8
+// slots x 64 bytes, which then falls on every bank once per 32-byte half.
+__device__ inline int kw_pos(int k, int t) { return k ^ (t & 15); }
+
+template <int G, int B, bool kOneRounding, bool kStream>
+__global__ __launch_bounds__(kWave * kWaves, 2) void extend_wide_kernel(DecodeArgs a) {
+  static_assert(G >= 1 && G <= 16, "32 columns hold 32/G whole query tokens");
+  static_assert(B >= 4 && B <= 64 && (B & (B - 1)) == 0, "block size: a power of two from 4 to 64");
+  constexpr int TC = 32 / G;        // query tokens per wave
+  constexpr int TW = kWaves * TC;   // query tokens per workgroup
+  // [buffer][K, V][step bytes]
+  __shared__ __attribute__((aligned(16))) uint8_t steps[2][2][kStepBytes];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  // The wave index, in a scalar register (block offsets and table lanes
+  // derived from it must be scalar).
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int col = lane & 31;  // this lane's column
+  const int h = lane >> 5;    // which half of the column's slots it holds
+  const int n16 = lane & 15;
+  const int c4 = lane >> 4;
+
+  int item = xcd_remap(blockIdx.x, gridDim.x);
+  const int p = item % a.P;
+  item /= a.P;
+  const int tw = item % a.TG;
+  item /= a.TG;
+  const int s = item % a.S;
+  const int kvh = item / a.S;
+
+  const int n_raw = a.lens[s];
+  bool bad = n_raw < 0 || (int64_t)n_raw > (int64_t)a.MB * B;
+  const int n = bad ? 0 : n_raw;
+  const int nb = (n + B - 1) / B;
+  // Column col is query token tq, head kvh*G + col%G, and may see the first
+  // lim positions; the workgroup needs the tiles up to its last token's limit.
+  const int tq = tw * TW + w * TC + col / G;
+  const int lim = tq < a.T ? min(n, max(0, n - a.T + 1 + tq)) : n;
+  const int lim_hi = min(n, max(0, n - a.T + min(a.T, tw * TW + TW)));
+  const int nt = (lim_hi + kTile - 1) / kTile;  // 16-slot tiles
+  const int u0 = p * (a.tps / kTile);
+  const int u1 = min(nt, u0 + a.tps / kTile);
+
+  // q^T as the B operand of S^T = K q^T: lane l holds column col over dims
+  // 16*kk + 8*h .. +8.  A negative scale enters as q negated (exact in bf16)
+  // and the scale's magnitude, so scores are scaled by c >= 0.
+  const bool neg_scale = a.scale_log2 < 0.f;
+  const float c_log2 = neg_scale ? -a.scale_log2 : a.scale_log2;
+  const uint32_t qsign = neg_scale ? 0x80008000u : 0u;
+  bf16x8_t qv[8];
+  {
+    const bool live = tq < a.T;  // columns past T get q = 0 and are never stored
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         (((int64_t)s * a.T + min(tq, a.T - 1)) * a.Hq + (int64_t)kvh * G + col % G) * kHeadDim;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      uint4 v = *reinterpret_cast<const uint4*>(qp + 16 * kk + 8 * h);
+      v = make_uint4(v.x ^ qsign, v.y ^ qsign, v.z ^ qsign, v.w ^ qsign);
+      if (!live) v = make_uint4(0, 0, 0, 0);
+      qv[kk] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  // This wave loads slot rows 8w + 4i + c4 (i = 0, 1) of every step: lane l
+  // takes bytes 16*n16 .. +16 of KV head kvh.  A row group wholly past the
+  // history, past the split, or in a prefetch slot past the chunk (`none`)
+  // goes through a descriptor of size 0: zeros, no memory read, and no table
+  // entry at or past ceil(n / B) addresses the pool.
+  const int row_bytes = a.Hkv * kHeadDim * 2;
+  const uint32_t blk_bytes = (uint32_t)B * (uint32_t)row_bytes;
+  const uint32_t voff = (uint32_t)(c4 * row_bytes + (kvh * kHeadDim + 8 * n16) * 2);
+  const char* kpool = static_cast<const char*>(a.k_pool);
+  const char* vpool = static_cast<const char*>(a.v_pool);
+  const int32_t* trow = a.tables + (int64_t)s * a.MB;
+  auto pool_block = [&](int pb) {
+    if (pb < 0 || pb >= a.NB) {  // outside the pool: never dereferenced, result poisoned
+      bad = true;
+      pb = 0;
+    }
+    return pb;
+  };
+  struct Rows {
+    uint4 k[2], v[2];
+  };
+  // Step starting at tile t: slots 16t .. 16t+31; `te` ends the chunk (and
+  // the split): a second tile at or past it is not part of the step.
+  auto load_step = [&](int t, Rows& r, int eb, int tab, int te, bool none) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int tok = kTile * t + 8 * w + 4 * i;  // first slot of the row group
+      const bool live = !none && tok < n && (8 * w + 4 * i < kTile || t + 1 < te);
+      const int pb = live ? pool_block(__builtin_amdgcn_readlane(tab, tok / B - eb)) : 0;
+      const int soff = live ? (tok % B) * row_bytes : 0;
+      const uint32_t size = live ? blk_bytes : 0u;
+      r.k[i] = load_kv16<kStream>(block_rsrc(kpool + (int64_t)pb * blk_bytes, size), voff, soff);
+      r.v[i] = load_kv16<kStream>(block_rsrc(vpool + (int64_t)pb * blk_bytes, size), voff, soff);
+    }
+  };
+
+  float m = kNegInf;  // reference max (base 2) of this lane's column
+  float l = 0.f;      // two roundings: partial l over this lane's 16 slots of each step
+  f32x16_t lacc = {}; // one rounding: l of the column (every element), from the rounded weights
+  f32x16_t acc[4];    // o^T of the column: dims 32*mb + 8*(r/4) + 4*h + r%4
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x16_t{};
+
+  // LDS offsets this lane writes (rows 8w + 4i + c4, chunk n16) and reads.
+  int wk_off[2], wv_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * w + 4 * i + c4;
+    wk_off[i] = 256 * r + 16 * kw_pos(n16, r);
+    wv_off[i] = 256 * r + 16 * v_pos(n16, r);
+  }
+  // q.k A operand: slot col, chunk 2*kk + h.
+  const int rk_base = 256 * col;
+  // p.v A operand: lane (group g16 = lane/16, j = lane%16) reads slot
+  // 16*kb + 8*sec + 4*h + j/4, dims 32*mb + 16*(g16%2) + 4*(j%4) .. +3; the
+  // slot's position in its 8-row swizzle group, (4*h + j/4) % 8, does not
+  // depend on kb or sec, so one offset per mb serves all four reads.
+  int rv_off[4];
+  {
+    const int j = lane & 15;
+    const int rr = 4 * h + j / 4;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int pair = 2 * mb + ((lane >> 4) & 1);
+      rv_off[mb] = 256 * rr + 32 * (pair ^ (rr & 7)) + 8 * (j & 3);
+    }
+  }
+
+  auto process = [&](int t, const Rows& r, int te) {
+    const int buf = (t >> 1) & 1;
+    uint8_t* kb_ = &steps[buf][0][0];
+    uint8_t* vb_ = &steps[buf][1][0];
+    const int valid = n - kTile * t;  // slots of the step inside the history
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(kb_ + wk_off[i]) = r.k[i];
+    if (valid >= kStep) {  // the whole step lies inside the history (all but the last)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(vb_ + wv_off[i]) = r.v[i];
+    } else {
+      // V past the history may hold anything (NaN): zeroed, since a zero
+      // weight times NaN would still be NaN.
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = 8 * w + 4 * i + c4;
+        *reinterpret_cast<uint4*>(vb_ + wv_off[i]) = row < valid ? r.v[i] : make_uint4(0, 0, 0, 0);
+      }
+    }
+    __syncthreads();
+
+    // S^T = K q^T over d = 128.
+    f32x16_t sc = {};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const u32x4_t kv = *reinterpret_cast<const PA_LDS u32x4_t*>((const PA_LDS uint8_t*)kb_ + rk_base +
+                                                                  16 * kw_pos(2 * kk + h, col));
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv), qv[kk], sc, 0, 0, 0);
+    }
+
+    // Slots of this step the column may see: below its limit, and in the
+    // second tile only while that tile is part of the split.
+    int vq = lim - kTile * t;
+    if (t + 1 >= te) vq = min(vq, kTile);
+    // Below the diagonal every slot counts for every column: the scores go
+    // in unscaled and unmasked.
+    const bool mask = !__all(vq >= kStep);
+    float sv[16];
+    if (mask) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int slot = 8 * (rr >> 2) + 4 * h + (rr & 3);
+        sv[rr] = slot < vq ? sc[rr] : kNegInf;
+      }
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) sv[rr] = sc[rr];
+    }
+    // Column max: the lane's 16 slots, then the other 16 in the lane 32 away.
+    float bm = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+#pragma unroll
+    for (int rr = 3; rr < 15; rr += 2) bm = fmaxf(fmaxf(bm, sv[rr]), sv[rr + 1]);
+    bm = fmaxf(bm, sv[15]);
+    {
+      const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+      bm = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+    }
+    // The scale enters once: c * max s = max c*s for c >= 0 (rounding
+    // included), and each weight is 2^fma(s, c, -m).  c is kept at least
+    // FLT_MIN so that a masked -inf stays -inf (a zero scale then still gives
+    // equal weights: the scaled scores round to about 0).
+    const float c = fmaxf(c_log2, __FLT_MIN__);
+    bm *= c;
+    const bool move = bm > m + kLazyMax;
+    const float alpha = move ? fast_exp2(m - bm) : 1.f;
+    if (move) m = bm;
+    const float mref = m == kNegInf ? 0.f : m;  // a column with nothing valid yet keeps weights 0
+    float pw[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) pw[rr] = fast_exp2(fmaf(sv[rr], c, -mref));
+    if (__any(move)) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) acc[mb][rr] *= alpha;
+      if constexpr (kOneRounding) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) lacc[rr] *= alpha;
+      }
+    }
+
+    // P^T operands: weights 8*kb .. 8*kb+7 of this lane, in register order.
+    bf16x8_t phi[2], plo[2] = {};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (kOneRounding) {
+          hi[q] = pack_bf16_rn(pw[8 * kb + 2 * q], pw[8 * kb + 2 * q + 1]);
+        } else {
+          split_pair_rn(pw[8 * kb + 2 * q], pw[8 * kb + 2 * q + 1], hi[q], lo[q]);
+        }
+      }
+      phi[kb] = __builtin_bit_cast(bf16x8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+      if constexpr (!kOneRounding) plo[kb] = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+    }
+    if constexpr (kOneRounding) {
+      const bf16x8_t ones =
+          __builtin_bit_cast(bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, phi[kb], lacc, 0, 0, 0);
+    } else {
+      float sum = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sum += (pw[4 * q] + pw[4 * q + 1]) + (pw[4 * q + 2] + pw[4 * q + 3]);
+      l = fmaf(l, alpha, sum);
+    }
+
+    // O^T += V^T P^T.
+    const PA_LDS uint8_t* vrd = (const PA_LDS uint8_t*)vb_;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (PA_LDS s16x4_t*)(vrd + rv_off[mb] + 256 * (kTile * kb)));
+        const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (PA_LDS s16x4_t*)(vrd + rv_off[mb] + 256 * (kTile * kb + 8)));
+        const bf16x8_t va = __builtin_bit_cast(
+            bf16x8_t, make_uint4(__builtin_bit_cast(uint2, v0).x, __builtin_bit_cast(uint2, v0).y,
+                                 __builtin_bit_cast(uint2, v1).x, __builtin_bit_cast(uint2, v1).y));
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, phi[kb], acc[mb], 0, 0, 0);
+        if constexpr (!kOneRounding) acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, plo[kb], acc[mb], 0, 0, 0);
+      }
+    }
+  };
+
+  // Table entries 64 at a time into one register (one per lane): chunks of
+  // 64 tiles for B >= 16, 4*B tiles below.  Within a chunk the next step is
+  // requested before the current one is used.
+  constexpr int kChunkTiles = B >= kTile ? kWave : 4 * B;
+  static_assert(kChunkTiles % 2 == 0, "steps of two tiles stay inside one chunk");
+  constexpr int kDepth = 2;
+  for (int tb = u0; tb < u1; tb += kChunkTiles) {
+    const int te = min(u1, tb + kChunkTiles);
+    const int eb = (kTile * tb) / B;
+    const int tab = trow[min(eb + lane, nb - 1)];
+    Rows ring[kDepth];
+    load_step(tb, ring[0], eb, tab, te, false);
+    for (int t = tb; t < te; t += 2 * kDepth) {
+#pragma unroll
+      for (int b = 0; b < kDepth; ++b) {
+        const int tn = t + 2 * (b + 1);  // the step to prefetch; past the chunk: loads that fetch nothing
+        load_step(min(tn, te - 1), ring[(b + 1) % kDepth], eb, tab, te, tn >= te);
+        __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the current step's math
+        process(t + 2 * b, ring[b], te);
+        if (t + 2 * b + 2 >= te) break;
+      }
+    }
+  }
+
+  // The column's l: the two lanes holding its halves.
+  float lc;
+  if constexpr (kOneRounding) {
+    lc = lacc[0];
+  } else {
+    lc = l + __shfl_xor(l, 32, kWave);
+  }
+  bad = __syncthreads_or(bad);  // any wave that met an entry outside the pool
+
+  const float nan = __builtin_nanf("");
+  if (tq < a.T) {
+    const int64_t row = ((int64_t)s * a.T + tq) * a.Hq + kvh * G + col % G;
+    if (a.P == 1) {
+      const float inv = lc > 0.f ? 1.f / lc : 0.f;
+      float* dst = a.out + row * kHeadDim + 4 * h;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 o = bad ? make_float4(nan, nan, nan, nan)
+                               : make_float4(acc[mb][4 * q] * inv, acc[mb][4 * q + 1] * inv,
+                                             acc[mb][4 * q + 2] * inv, acc[mb][4 * q + 3] * inv);
+          *reinterpret_cast<float4*>(dst + 32 * mb + 8 * q) = o;
+        }
+    } else {
+      const int64_t slot = row * a.P + p;
+      float* dst = a.ws_o + slot * kHeadDim + 4 * h;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(dst + 32 * mb + 8 * q) =
+              make_float4(acc[mb][4 * q], acc[mb][4 * q + 1], acc[mb][4 * q + 2], acc[mb][4 * q + 3]);
+      if (h == 0) {
+        a.ws_m[slot] = bad ? 0.f : m;
+        a.ws_l[slot] = bad ? nan : lc;
+      }
+    }
+  }
+}
+
+template <int G, int B, bool kOneRounding>
+void launch_gbr(const DecodeArgs& a, hipStream_t stream) {
+  const int items = a.Hkv * a.S * a.P * a.TG;
+  if (a.TG == 1)
+    hipLaunchKernelGGL((extend_wide_kernel<G, B, kOneRounding, true>), dim3(items), dim3(kWave * kWaves), 0, stream,
+                       a);
+  else
+    hipLaunchKernelGGL((extend_wide_kernel<G, B, kOneRounding, false>), dim3(items), dim3(kWave * kWaves), 0, stream,
+                       a);
+}
+
+template <int G, int B>
+hipError_t launch_gb(const DecodeArgs& a, hipStream_t stream) {
+  if (a.bf16_weights)
+    launch_gbr<G, B, true>(a, stream);
+  else
+    launch_gbr<G, B, false>(a, stream);
+  return hipGetLastError();
+}
+
+template <int B>
+hipError_t launch_b(const DecodeArgs& a, int G, hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_gb<1, B>(a, stream);
+    case 2: return launch_gb<2, B>(a, stream);
+    case 4: return launch_gb<4, B>(a, stream);
+    case 8: return launch_gb<8, B>(a, stream);
+    case 16: return launch_gb<16, B>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_extend_wide(const DecodeArgs& a, int B, int G, hipStream_t stream) {
+  switch (B) {
+    case 4: return launch_b<4>(a, G, stream);
+    case 8: return launch_b<8>(a, G, stream);
+    case 16: return launch_b<16>(a, G, stream);
+    case 32: return launch_b<32>(a, G, stream);
+    case 64: return launch_b<64>(a, G, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

@@ -84,7 +84,8 @@ constexpr bool use_shared_tile(pa_dtype dtype, int G, int T) {
 // the history, else one.  Measured on 32 x 4096 tokens of 4-head groups:
 // 639 vs 675 us for a 512-token chunk; 148-155 vs 169-171 us for 17-28
 // tokens (some waves idle, one pass instead of two); but 184 vs 143 us for
-// 16 tokens, which one set per wave covers in one pass.
+// 16 tokens, which one set per wave covers in one pass.  Two sets per wave
+// run as one 32-column set of the 32x32 kernel (launch_extend_wide).
 constexpr int shared_tile_sets(pa_dtype dtype, int G, int T) {
   return T > kSharedTileWaves * tokens_per_wave(dtype, G) ? 2 : 1;
 }
@@ -118,6 +119,11 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int B, int G, bool causal, hi
 
 // bf16, several query tokens per wave group (pa_extend_mfma.hip); G and B as above.
 hipError_t launch_extend_shared(const DecodeArgs& a, int B, int G, hipStream_t stream);
+
+// bf16, 32 query columns per wave on the 32x32 matrix-core tiles
+// (pa_extend_wide.hip): the shared-tile step when each wave would take two
+// 16-column sets.  G and B as above.
+hipError_t launch_extend_wide(const DecodeArgs& a, int B, int G, hipStream_t stream);
 
 struct KvArgs {
   uint8_t* k_pool;

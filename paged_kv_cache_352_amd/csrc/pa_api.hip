@@ -87,9 +87,9 @@ pa_status check_dims(const pa_dims* d, int32_t B, bool need_attention_shape) {
 // Several query tokens multiply the work items by the token groups (TG), so
 // fewer splits reach the same wave count.  The shared-tile kernel (bf16, more
 // tokens than two 16-column sets hold) streams each tile once per workgroup of
-// kSharedTileWaves waves, all of which walk every tile of the split: about
-// two workgroups per CU (2048 waves), each split keeping at least 16 tiles
-// (more splits measured slower for 32 x 4096 tokens).
+// 4 waves (8 in the ping-pong form), all of which walk every tile of the
+// split: about 2048 waves, each split keeping at least 16 tiles (more splits
+// measured slower for 32 x 4096 tokens).
 int64_t token_groups(const pa_dims* d, int32_t T) {
   const int per = pa::tokens_per_item(d->dtype, d->num_q_heads / d->num_kv_heads, T);
   return ((int64_t)T + per - 1) / per;
@@ -104,7 +104,8 @@ void plan_splits(const pa_dims* d, int32_t B, int32_t T, int* P_out, int* tps_ou
     const int64_t items = (int64_t)d->num_seqs * d->num_kv_heads * token_groups(d, T);
     const bool mfma = d->dtype == PA_BF16;
     const bool shared = pa::use_shared_tile(d->dtype, d->num_q_heads / d->num_kv_heads, T);
-    const int64_t waves_per_item = shared ? pa::kSharedTileWaves : (mfma ? pa::kMfmaWaves : 1);
+    const int64_t waves_per_item =
+        shared ? pa::shared_tile_waves(d->dtype, d->num_q_heads / d->num_kv_heads, T) : (mfma ? pa::kMfmaWaves : 1);
     const int64_t target = (mfma && !shared) ? 1024 : 2048;
     const int64_t per = items * waves_per_item;
     P = (target + per - 1) / (per > 0 ? per : 1);

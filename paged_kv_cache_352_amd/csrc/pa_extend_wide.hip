@@ -42,7 +42,14 @@
 // once to bf16 and l is summed on the matrix core from the same rounded
 // weights.  The running max is the lazy reference of the 16-column kernel
 // (moved only when a step's max exceeds it by more than kLazyMax, base 2).
+//
+// Query groups wider than 128 columns run on the ping-pong form below: 8 such
+// waves per workgroup, two per SIMD, kept one phase apart so that the matrix
+// products of one overlap the softmax of the other.  Its per-column
+// arithmetic is the same, step for step, so both forms give the same bits.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "pa_mfma_common.h"
 
@@ -384,9 +391,396 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_wide_kernel(DecodeAr
   }
 }
 
+
+// The ping-pong form, for query groups of more than 128 columns: 8 waves of
+// 32 columns each (256 columns: the (token, head) pairs of 256/G query
+// tokens), all folding the same 32-slot steps.  The hardware places waves w
+// and w+4 of a workgroup on the same SIMD; waves 0-3 (group A) and 4-7 (group
+// B) run one phase apart, so that on every SIMD one wave issues matrix
+// products while the other runs vector work:
+//
+//   phase 2j:    A: M(j)      B: V(j-1)
+//   phase 2j+1:  A: V(j)      B: M(j)
+//
+// M(j) takes q.k of step j and p.v of step j-1; V(x) takes the softmax of
+// step x, the LDS write of this wave's rows of step j+1 and the request of
+// step j+4.  A workgroup barrier ends every phase.  Step k sits in LDS buffer
+// k % 3 from phase 2k-2 (written) to 2k+3 (its V read by B), so three
+// buffers (48 KiB) hold every step in use.  Both groups pass the same
+// barriers in their own copy of the loop.
+//
+// The scheduler could move vector work across a barrier into the other
+// phase (it did: the softmax sank into the next matrix phase); each barrier
+// is therefore fenced for the scheduler and the state live across it is
+// pinned with empty asm statements, so every instruction stays in its phase.
+template <int G, int B, bool kOneRounding, bool kStream>
+__global__ __launch_bounds__(kWave * kPingPongWaves, 1) void extend_pingpong_kernel(DecodeArgs a) {
+  static_assert(G >= 1 && G <= 16, "32 columns hold 32/G whole query tokens");
+  static_assert(B >= 4 && B <= 64 && (B & (B - 1)) == 0, "block size: a power of two from 4 to 64");
+  constexpr int TC = 32 / G;                // query tokens per wave
+  constexpr int TW = kPingPongWaves * TC;   // query tokens per workgroup
+  constexpr int kBufs = 3;
+  // [buffer][K, V][step bytes]
+  __shared__ __attribute__((aligned(16))) uint8_t steps[kBufs][2][kStepBytes];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const bool late = w >= kPingPongWaves / 2;  // group B
+  const int col = lane & 31;
+  const int h = lane >> 5;
+  const int n16 = lane & 15;
+  const int c4 = lane >> 4;
+
+  int item = xcd_remap(blockIdx.x, gridDim.x);
+  const int p = item % a.P;
+  item /= a.P;
+  const int tw = item % a.TG;
+  item /= a.TG;
+  const int s = item % a.S;
+  const int kvh = item / a.S;
+
+  const int n_raw = a.lens[s];
+  bool bad = n_raw < 0 || (int64_t)n_raw > (int64_t)a.MB * B;
+  const int n = bad ? 0 : n_raw;
+  const int tq = tw * TW + w * TC + col / G;
+  const int lim = tq < a.T ? min(n, max(0, n - a.T + 1 + tq)) : n;
+  const int lim_hi = min(n, max(0, n - a.T + min(a.T, tw * TW + TW)));
+  const int nt = (lim_hi + kTile - 1) / kTile;  // 16-slot tiles
+  const int u0 = p * (a.tps / kTile);
+  const int u1 = min(nt, u0 + a.tps / kTile);
+  const int nsteps = u1 > u0 ? (u1 - u0 + 1) / 2 : 0;  // step k: tiles u0+2k, u0+2k+1 (if < u1)
+  const int base_slot = kTile * u0;
+
+  const bool neg_scale = a.scale_log2 < 0.f;
+  const float c_log2 = neg_scale ? -a.scale_log2 : a.scale_log2;
+  const uint32_t qsign = neg_scale ? 0x80008000u : 0u;
+  bf16x8_t qv[8];
+  {
+    const bool live = tq < a.T;
+    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                         (((int64_t)s * a.T + min(tq, a.T - 1)) * a.Hq + (int64_t)kvh * G + col % G) * kHeadDim;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      uint4 v = *reinterpret_cast<const uint4*>(qp + 16 * kk + 8 * h);
+      v = make_uint4(v.x ^ qsign, v.y ^ qsign, v.z ^ qsign, v.w ^ qsign);
+      if (!live) v = make_uint4(0, 0, 0, 0);
+      qv[kk] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  // This wave loads slot rows 4w .. 4w+3 of every step (one 16-byte lane of
+  // K and of V each; a row group never straddles a block, B >= 4).  The
+  // block comes from the table through the constant address space, so it is
+  // a scalar load, requested at the start of the vector phase that uses it.
+  // A vector load of table entries kept across loop iterations made the
+  // compiler wait for every K/V load in flight before each LDS write.
+  const int row_bytes = a.Hkv * kHeadDim * 2;
+  const uint32_t blk_bytes = (uint32_t)B * (uint32_t)row_bytes;
+  const uint32_t voff = (uint32_t)(c4 * row_bytes + (kvh * kHeadDim + 8 * n16) * 2);
+  const char* kpool = static_cast<const char*>(a.k_pool);
+  const char* vpool = static_cast<const char*>(a.v_pool);
+  typedef const __attribute__((address_space(4))) int32_t ctab_t;
+  ctab_t* ctab = (ctab_t*)(a.tables + (int64_t)s * a.MB);  // read-only for the whole launch
+  // Whether this wave's row group of step k holds history: inside the split,
+  // inside the history, and (rows 16-31) in a second tile of the split.
+  auto rows_live = [&](int k) {
+    const int tok = base_slot + kStep * k + 4 * w;
+    return k < nsteps && tok < n && (4 * w < kTile || u0 + 2 * k + 1 < u1);
+  };
+  auto table_entry = [&](int k) { return rows_live(k) ? ctab[(base_slot + kStep * k + 4 * w) / B] : 0; };
+  struct Ld {
+    uint4 k, v;
+  };
+  // A dead row group, or an entry outside the pool (which poisons the
+  // output), loads through a descriptor of size 0: zeros, no memory read.
+  auto load_step = [&](int k, int e, Ld& r) {
+    const bool live = rows_live(k);
+    const bool in_pool = e >= 0 && e < a.NB;
+    if (live && !in_pool) bad = true;
+    const bool fetch = live && in_pool;
+    const int tok = base_slot + kStep * k + 4 * w;
+    const int soff = fetch ? (tok % B) * row_bytes : 0;
+    const char* kb = kpool + (fetch ? (int64_t)e * blk_bytes : 0);
+    const char* vb = vpool + (fetch ? (int64_t)e * blk_bytes : 0);
+    r.k = load_kv16<kStream>(block_rsrc(kb, fetch ? blk_bytes : 0u), voff, soff);
+    r.v = load_kv16<kStream>(block_rsrc(vb, fetch ? blk_bytes : 0u), voff, soff);
+  };
+
+  const int wrow = 4 * w + c4;
+  const int wk_off = 256 * wrow + 16 * kw_pos(n16, wrow);
+  const int wv_off = 256 * wrow + 16 * v_pos(n16, wrow);
+  // V rows past the history may hold anything (NaN): written as zeros, since
+  // a zero weight times NaN would still be NaN.
+  auto write_step = [&](int k, const Ld& r, uint8_t* kb_, uint8_t* vb_) {
+    const int valid = n - base_slot - kStep * k;
+    *reinterpret_cast<uint4*>(kb_ + wk_off) = r.k;
+    *reinterpret_cast<uint4*>(vb_ + wv_off) = wrow < valid ? r.v : make_uint4(0, 0, 0, 0);
+  };
+
+  float m = kNegInf;   // reference max (base 2) of this lane's column
+  float l = 0.f;       // two roundings: partial l over this lane's 16 slots of each step
+  f32x16_t lacc = {};  // one rounding: l of the column, from the rounded weights
+  f32x16_t acc[4];     // o^T of the column: dims 32*mb + 8*(r/4) + 4*h + r%4
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x16_t{};
+  f32x16_t sc = {};               // scores of the step between its M and V phases
+  bf16x8_t phi[2] = {}, plo[2] = {};  // weights between the V phase and the next M phase
+
+  const int rk_base = 256 * col;
+  int rv_off[4];
+  {
+    const int j = lane & 15;
+    const int rr = 4 * h + j / 4;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int pair = 2 * mb + ((lane >> 4) & 1);
+      rv_off[mb] = 256 * rr + 32 * (pair ^ (rr & 7)) + 8 * (j & 3);
+    }
+  }
+  const float c = fmaxf(c_log2, __FLT_MIN__);
+
+  // M(j): q.k of step j (K in kb_; all 8 reads issued first), then p.v of
+  // step j-1 (V in vb_).
+  auto mphase = [&](int j, const uint8_t* kb_, const uint8_t* vb_) {
+    if (j < nsteps) {
+      u32x4_t kr[8];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        kr[kk] = *reinterpret_cast<const PA_LDS u32x4_t*>((const PA_LDS uint8_t*)kb_ + rk_base +
+                                                          16 * kw_pos(2 * kk + h, col));
+      f32x16_t z = {};
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kr[kk]), qv[kk], z, 0, 0, 0);
+      sc = z;
+    }
+    if (j > 0 && j <= nsteps) {
+      if constexpr (kOneRounding) {
+        const bf16x8_t ones =
+            __builtin_bit_cast(bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, phi[kb], lacc, 0, 0, 0);
+      }
+      const PA_LDS uint8_t* vrd = (const PA_LDS uint8_t*)vb_;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (PA_LDS s16x4_t*)(vrd + rv_off[mb] + 256 * (kTile * kb)));
+          const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (PA_LDS s16x4_t*)(vrd + rv_off[mb] + 256 * (kTile * kb + 8)));
+          const bf16x8_t va = __builtin_bit_cast(
+              bf16x8_t, make_uint4(__builtin_bit_cast(uint2, v0).x, __builtin_bit_cast(uint2, v0).y,
+                                   __builtin_bit_cast(uint2, v1).x, __builtin_bit_cast(uint2, v1).y));
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, phi[kb], acc[mb], 0, 0, 0);
+          if constexpr (!kOneRounding)
+            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, plo[kb], acc[mb], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // Softmax of step x into the p.v operands (the same arithmetic as the
+  // 4-wave kernel, so the two give bitwise equal outputs).
+  auto softmax = [&](int x) {
+    int vq = lim - base_slot - kStep * x;
+    if (u0 + 2 * x + 1 >= u1) vq = min(vq, kTile);
+    const bool mask = !__all(vq >= kStep);
+    float sv[16];
+    if (mask) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int slot = 8 * (rr >> 2) + 4 * h + (rr & 3);
+        sv[rr] = slot < vq ? sc[rr] : kNegInf;
+      }
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) sv[rr] = sc[rr];
+    }
+    float bm = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+#pragma unroll
+    for (int rr = 3; rr < 15; rr += 2) bm = fmaxf(fmaxf(bm, sv[rr]), sv[rr + 1]);
+    bm = fmaxf(bm, sv[15]);
+    {
+      const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+      bm = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+    }
+    bm *= c;
+    const bool move = bm > m + kLazyMax;
+    const float alpha = move ? fast_exp2(m - bm) : 1.f;
+    if (move) m = bm;
+    const float mref = m == kNegInf ? 0.f : m;
+    float pw[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) pw[rr] = fast_exp2(fmaf(sv[rr], c, -mref));
+    if (__any(move)) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) acc[mb][rr] *= alpha;
+      if constexpr (kOneRounding) {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) lacc[rr] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (kOneRounding) {
+          hi[q] = pack_bf16_rn(pw[8 * kb + 2 * q], pw[8 * kb + 2 * q + 1]);
+        } else {
+          split_pair_rn(pw[8 * kb + 2 * q], pw[8 * kb + 2 * q + 1], hi[q], lo[q]);
+        }
+      }
+      phi[kb] = __builtin_bit_cast(bf16x8_t, make_uint4(hi[0], hi[1], hi[2], hi[3]));
+      if constexpr (!kOneRounding) plo[kb] = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+    }
+    if constexpr (!kOneRounding) {
+      float sum = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sum += (pw[4 * q] + pw[4 * q + 1]) + (pw[4 * q + 2] + pw[4 * q + 3]);
+      l = fmaf(l, alpha, sum);
+    }
+  };
+
+  // Phase boundaries.  After an M phase the scores are live, after a V phase
+  // the weights; the accumulators and the running state always.
+  auto pin_common = [&] {
+    if constexpr (!kOneRounding) asm volatile("" : "+v"(l));
+    if constexpr (kOneRounding) asm volatile("" : "+v"(lacc));
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) asm volatile("" : "+v"(acc[mb]));
+    asm volatile("" : "+v"(m));
+  };
+  auto pin_scores = [&] {
+    asm volatile("" : "+v"(sc));
+    pin_common();
+  };
+  auto pin_weights = [&] {
+    asm volatile("" : "+v"(phi[0]), "+v"(phi[1]));
+    if constexpr (!kOneRounding) asm volatile("" : "+v"(plo[0]), "+v"(plo[1]));
+    pin_common();
+  };
+  auto barrier_after_m = [&] {
+    pin_scores();
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    pin_scores();
+  };
+  auto barrier_after_v = [&] {
+    pin_weights();
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    pin_weights();
+  };
+
+  // Prologue: steps 0-2 requested, step 0 written, step 3 requested into the
+  // freed registers.  Step k's registers are ring[k % 3].
+  Ld ring[3];
+  load_step(0, table_entry(0), ring[0]);
+  load_step(1, table_entry(1), ring[1]);
+  load_step(2, table_entry(2), ring[2]);
+  if (nsteps > 0) write_step(0, ring[0], &steps[0][0][0], &steps[0][1][0]);
+  load_step(3, table_entry(3), ring[0]);
+  __syncthreads();
+
+  // Iterations j = 0 .. nsteps, three per trip so that buffer and register
+  // indices are compile-time; a trip runs all three (steps past the end do
+  // nothing), which keeps the compiler's count of loads in flight exact: an
+  // early exit from the unrolled trip made it wait for every load in flight.
+  auto run = [&](auto late_group) {
+    constexpr bool kLate = decltype(late_group)::value;
+    for (int j0 = 0; j0 <= nsteps; j0 += kBufs) {
+#pragma unroll
+      for (int b = 0; b < kBufs; ++b) {
+        const int j = j0 + b;
+        const uint8_t* kcur = &steps[b][0][0];
+        const uint8_t* vprev = &steps[(b + kBufs - 1) % kBufs][1][0];
+        uint8_t* knext = &steps[(b + 1) % kBufs][0][0];
+        uint8_t* vnext = &steps[(b + 1) % kBufs][1][0];
+        Ld& rn = ring[(b + 1) % kBufs];
+        auto vphase = [&](int x) {
+          const int e = table_entry(j + 4);  // scalar load, used at the end of the phase
+          if (x >= 0 && x < nsteps) softmax(x);
+          if (j + 1 < nsteps) write_step(j + 1, rn, knext, vnext);
+          load_step(j + 4, e, rn);
+        };
+        if constexpr (kLate) {
+          vphase(j - 1);
+          barrier_after_v();
+          mphase(j, kcur, vprev);
+          barrier_after_m();
+        } else {
+          mphase(j, kcur, vprev);
+          barrier_after_m();
+          vphase(j);
+          barrier_after_v();
+        }
+      }
+    }
+  };
+  if (late)
+    run(std::integral_constant<bool, true>{});
+  else
+    run(std::integral_constant<bool, false>{});
+
+  float lc;
+  if constexpr (kOneRounding) {
+    lc = lacc[0];
+  } else {
+    lc = l + __shfl_xor(l, 32, kWave);
+  }
+  bad = __syncthreads_or(bad);
+
+  const float nan = __builtin_nanf("");
+  if (tq < a.T) {
+    const int64_t row = ((int64_t)s * a.T + tq) * a.Hq + kvh * G + col % G;
+    if (a.P == 1) {
+      const float inv = lc > 0.f ? 1.f / lc : 0.f;
+      float* dst = a.out + row * kHeadDim + 4 * h;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 o = bad ? make_float4(nan, nan, nan, nan)
+                               : make_float4(acc[mb][4 * q] * inv, acc[mb][4 * q + 1] * inv,
+                                             acc[mb][4 * q + 2] * inv, acc[mb][4 * q + 3] * inv);
+          *reinterpret_cast<float4*>(dst + 32 * mb + 8 * q) = o;
+        }
+    } else {
+      const int64_t slot = row * a.P + p;
+      float* dst = a.ws_o + slot * kHeadDim + 4 * h;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(dst + 32 * mb + 8 * q) =
+              make_float4(acc[mb][4 * q], acc[mb][4 * q + 1], acc[mb][4 * q + 2], acc[mb][4 * q + 3]);
+      if (h == 0) {
+        a.ws_m[slot] = bad ? 0.f : m;
+        a.ws_l[slot] = bad ? nan : lc;
+      }
+    }
+  }
+}
+
 template <int G, int B, bool kOneRounding>
 void launch_gbr(const DecodeArgs& a, hipStream_t stream) {
   const int items = a.Hkv * a.S * a.P * a.TG;
+  if (use_pingpong(PA_BF16, G, a.T)) {
+    if (a.TG == 1)
+      hipLaunchKernelGGL((extend_pingpong_kernel<G, B, kOneRounding, true>), dim3(items),
+                         dim3(kWave * kPingPongWaves), 0, stream, a);
+    else
+      hipLaunchKernelGGL((extend_pingpong_kernel<G, B, kOneRounding, false>), dim3(items),
+                         dim3(kWave * kPingPongWaves), 0, stream, a);
+    return;
+  }
   if (a.TG == 1)
     hipLaunchKernelGGL((extend_wide_kernel<G, B, kOneRounding, true>), dim3(items), dim3(kWave * kWaves), 0, stream,
                        a);

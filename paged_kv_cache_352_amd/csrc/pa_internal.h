@@ -97,9 +97,30 @@ constexpr int decode_column_sets(pa_dtype dtype, int G, int T) {
   return dtype == PA_BF16 && T > tokens_per_wave(dtype, G) && !use_shared_tile(dtype, G, T) ? 2 : 1;
 }
 
+constexpr int kPingPongWaves = 8;  // waves of the ping-pong shared-tile kernel
+
+// bf16 query groups wider than one workgroup of four 32-column waves (more
+// than 128 (token, head) columns per KV head): the ping-pong kernel
+// (launch_extend_wide), whose 8 waves run two per SIMD in opposite phases,
+// one issuing its matrix products while the other runs its softmax.
+// Measured on the 512-token chunk of 4-head groups over 8 x 4096 tokens:
+// 375-382 vs 406-443 us (default weights), 298-300 vs 329-337 us (bf16
+// weights), outputs bitwise equal.  At 24 or 32 tokens of 4-head groups half
+// or more of its columns would be empty: 207-223 vs 136-147 us, so those stay
+// on the 4-wave kernel.
+constexpr bool use_pingpong(pa_dtype dtype, int G, int T) {
+  return use_shared_tile(dtype, G, T) && shared_tile_sets(dtype, G, T) == 2 && (int64_t)T * G > kSharedTileWaves * 32;
+}
+
+// Waves of one shared-tile work item.
+constexpr int shared_tile_waves(pa_dtype dtype, int G, int T) {
+  return use_pingpong(dtype, G, T) ? kPingPongWaves : kSharedTileWaves;
+}
+
 // Query tokens one work item covers (DecodeArgs::TG = ceil(T / this)).
 constexpr int tokens_per_item(pa_dtype dtype, int G, int T) {
   if (T <= 1) return 1;
+  if (use_pingpong(dtype, G, T)) return kPingPongWaves * (32 / G);
   if (use_shared_tile(dtype, G, T)) return kSharedTileWaves * shared_tile_sets(dtype, G, T) * tokens_per_wave(dtype, G);
   return decode_column_sets(dtype, G, T) * tokens_per_wave(dtype, G);
 }
@@ -122,7 +143,8 @@ hipError_t launch_extend_shared(const DecodeArgs& a, int B, int G, hipStream_t s
 
 // bf16, 32 query columns per wave on the 32x32 matrix-core tiles
 // (pa_extend_wide.hip): the shared-tile step when each wave would take two
-// 16-column sets.  G and B as above.
+// 16-column sets, on 4 waves, or on the 8-wave ping-pong kernel when
+// use_pingpong.  G and B as above.
 hipError_t launch_extend_wide(const DecodeArgs& a, int B, int G, hipStream_t stream);
 
 struct KvArgs {

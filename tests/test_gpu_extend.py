@@ -70,11 +70,14 @@ def test_bf16_one_item_per_group(T):
 
 
 @pytest.mark.parametrize("G,T", [(4, 7), (4, 16), (1, 17), (1, 40), (16, 3), (8, 5), (2, 9),
-                                 (4, 40), (16, 9), (2, 70), (8, 33), (4, 17), (4, 24), (2, 36), (1, 65)])
+                                 (4, 40), (16, 9), (2, 70), (8, 33), (4, 17), (4, 24), (2, 36), (1, 65),
+                                 (4, 33), (1, 150)])
 def test_bf16_several_items_per_group(G, T):
     """Separate items per column set up to two sets; the shared-tile kernel above,
     with one 16-column set per wave, or two once one set per wave would need a
-    second workgroup (then some waves may hold no live column)."""
+    second workgroup (then some waves may hold no live column); past 128 columns
+    the 8-wave ping-pong form (4 x 33: 132 columns, one live column past the
+    first four waves; 1 x 150: 32 tokens per wave)."""
     banner(f"extend bf16 G={G} T={T} ragged")
     b = W.extend_batch(RAGGED, T, Hq=2 * G, Hkv=2, seed=20 + G + T, device=DEV)
     check(b, torch.bfloat16, f"bf16 G={G} T={T}")
@@ -352,6 +355,28 @@ def test_speculative_loop_with_rollback():
         bm.check()
     # the first step copies the shared 5-token tail for all but the last branch
     assert copies >= 3
+
+
+@pytest.mark.parametrize("T", [4, 24, 40])
+def test_table_padding_past_the_history_may_hold_anything(T):
+    """Entries at or past ceil(n/B) never address the pools in the several-token
+    kernels either (decode-kernel causal form, 4-wave and ping-pong shared-tile
+    forms): ids outside the pool there change no output bit."""
+    banner(f"extend garbage table padding T={T}")
+    lens = [T, T + 1, T + 15, T + 16, T + 33, T + 300]
+    b = W.extend_batch(lens, T, Hq=8, Hkv=2, seed=120 + T, device=DEV)
+    pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
+    base = pa.paged_attn_extend(b.q, b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B, b.scale)
+    tab = b.block_tables.cpu().numpy()
+    garbage = np.array([-7, b.NB, b.NB + 12345, 2**31 - 1, -2**31], dtype=np.int64)
+    for s_, n in enumerate(lens):
+        need = -(-n // b.B)
+        tab[s_, need:] = garbage[(np.arange(tab.shape[1] - need) + s_) % len(garbage)]
+    t2 = torch.as_tensor(tab.astype(np.int32), device=DEV)
+    out = pa.paged_attn_extend(b.q, b.k_pool, b.v_pool, t2, b.seq_lens, b.B, b.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(out), host_bits(base))
+    assert np.all(np.isfinite(host_f32(out)))
 
 
 @pytest.mark.parametrize("T", [4, 40])

@@ -229,9 +229,9 @@ def suite(torch, pa, W, dev):
     """Decode (and full-step) timings of the other four workloads, one dict each."""
     out = {}
 
-    def decode_graph(b, layers, reps=1):
+    def decode_graph(b, layers, reps=1, order=None):
         calls = [pa.DecodeLaunch(b.q[layer], b.k_pool[layer], b.v_pool[layer], b.block_tables, b.seq_lens, b.B,
-                                 b.scale) for layer in layers]
+                                 b.scale, order=order) for layer in layers]
         def launch_all():
             for c in calls:
                 c.launch()
@@ -239,8 +239,9 @@ def suite(torch, pa, W, dev):
         us = graph_time_us(torch, launch_all, reps)
         return us / len(calls), calls[0].splits
 
-    def full_step_graph(b, fused=False, all_layers=False):
+    def full_step_graph(b, fused=False, all_layers=False, ordered=False):
         def step():
+            order = pa.paged_attn_order(b.seq_lens, out=order_buf) if ordered else None  # once per step
             if b.cow_src.numel():
                 pa.kv_cow_copy(b.k_pool, b.v_pool, b.cow_src, b.cow_dst, b.cow_n, b.B)
             if all_layers:  # the step's one append round, every layer in one launch, then the decodes
@@ -248,7 +249,7 @@ def suite(torch, pa, W, dev):
                                     b.append_positions[0], b.B)
                 for layer in range(b.L):
                     pa.paged_attn_decode(b.q[layer], b.k_pool[layer], b.v_pool[layer], b.block_tables, b.seq_lens,
-                                         b.B, b.scale, out=outs[layer], workspace=ws)
+                                         b.B, b.scale, out=outs[layer], workspace=ws, order=order)
                 return
             for layer in range(b.L):
                 if fused:  # the step's one append round inside the decode launch
@@ -260,8 +261,9 @@ def suite(torch, pa, W, dev):
                     pa.kv_append(b.k_pool[layer], b.v_pool[layer], b.k_new[r, layer], b.v_new[r, layer],
                                  b.block_tables, b.append_positions[r], b.B)
                 pa.paged_attn_decode(b.q[layer], b.k_pool[layer], b.v_pool[layer], b.block_tables, b.seq_lens,
-                                     b.B, b.scale, out=outs[layer], workspace=ws)
+                                     b.B, b.scale, out=outs[layer], workspace=ws, order=order)
         _, need = pa.paged_attn_plan(b.S, b.Hq, b.Hkv, b.D, b.MB, b.NB, b.dtype, b.B)
+        order_buf = torch.empty(b.S, dtype=torch.int32, device=dev)
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         outs = [torch.empty((b.S, b.Hq, b.D), dtype=torch.float32, device=dev) for _ in range(b.L)]
         return graph_time_us(torch, step, 1)
@@ -377,6 +379,14 @@ def suite(torch, pa, W, dev):
                     ent["full_step_append_layers_us"] = round(full_step_graph(b, all_layers=True), 2)
                     ent["full_step_append_layers_ops"] = f"one kv_append_layers, then one decode per layer, {b.L} layers"
         if name.startswith("bf16 256 mixed"):
+            # Work issued longest first (paged_attn_order once per step, passed to every layer's decode).
+            order = pa.paged_attn_order(b.seq_lens)
+            us_o, _ = decode_graph(b, layers, order=order)
+            ent["longest_first"] = dict(rate(kvb, us_o), tokens_per_s_per_layer=round(b.S / (us_o * 1e-6), 1),
+                                        full_step_append_layers_us=round(
+                                            full_step_graph(b, all_layers=True, ordered=True), 2),
+                                        ops="paged_attn_order once, one kv_append_layers, one decode per layer "
+                                            "with dims->order")
             ent["swap_500MiB"] = swap_time(torch, pa, b, dev)
         if name.startswith("bf16 prefix"):
             ent["note"] = "the shared prefix is cache-resident: logical bytes, no roofline claim"
@@ -389,6 +399,7 @@ def suite(torch, pa, W, dev):
 PROFILE_WORKLOADS = {
     "decode32x4096": "bf16 32 x 4096 tokens, one layer (the headline batch, 4 rotated pool copies)",
     "mixed256": "bf16 256 mixed-length requests, 32 layers: one decode launch per layer, after the step's append",
+    "mixed256o": "the same, the work issued longest first (paged_attn_order once, dims->order in every decode)",
     "prefix64": "bf16 prefix sharing, 64 branches, one layer: one decode launch, after the COW and appends",
     "long168": "bf16 168 x 1025 tokens, 24 layers: one decode launch per layer, after the step's append",
     "chunk512": "bf16 prompt chunk, 8 x 4096 tokens, T = 512, one layer (paged_attn_extend)",
@@ -415,15 +426,17 @@ def profile_workload(torch, pa, W, dev, name, steps, warmup):
         per_launch = b.valid_kv_bytes()
         rounds = [calls]
     else:
-        b = {"mixed256": W.config3, "prefix64": W.config4, "long168": W.config5}[name](device=dev)
+        b = {"mixed256": W.config3, "mixed256o": W.config3, "prefix64": W.config4, "long168": W.config5}[name](
+            device=dev)
         if b.cow_src.numel():
             pa.kv_cow_copy(b.k_pool, b.v_pool, b.cow_src, b.cow_dst, b.cow_n, b.B)
         for r in range(b.rounds):
             for layer in range(b.L):
                 pa.kv_append(b.k_pool[layer], b.v_pool[layer], b.k_new[r, layer], b.v_new[r, layer],
                              b.block_tables, b.append_positions[r], b.B)
+        order = pa.paged_attn_order(b.seq_lens) if name == "mixed256o" else None
         calls = [pa.DecodeLaunch(b.q[layer], b.k_pool[layer], b.v_pool[layer], b.block_tables, b.seq_lens, b.B,
-                                 b.scale) for layer in range(b.L)]
+                                 b.scale, order=order) for layer in range(b.L)]
         per_launch = b.valid_kv_bytes_per_layer()
         rounds = [calls]
     torch.cuda.synchronize()

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 
 /*
  * pa_dims.flags bits.
@@ -100,6 +100,19 @@ typedef struct {
   size_t workspace_bytes;
   int32_t flags;              /* PA_FLAG_* bits; 0 for the defaults; any other
                                  bit is PA_ERR_INVALID_ARG                     */
+  const int32_t* order;       /* optional, device [num_seqs]: the order in which
+                                 the bf16 matrix-core decode kernel (which also
+                                 runs paged_attn_extend steps of a few tokens)
+                                 issues the requests' work, in launches of more
+                                 than one round of resident work items
+                                 (paged_attn_order writes longest first);
+                                 NULL = request order.  A scheduling hint only:
+                                 every output bit is the same with or without
+                                 it.  Must be a permutation of 0..num_seqs-1;
+                                 an entry outside [0, num_seqs) stands for its
+                                 own position (never read out of bounds), a
+                                 repeated entry leaves another request's rows
+                                 unwritten.  Other kernels ignore it.          */
 } pa_dims;
 
 /* Library version of this header's ABI (PA_ABI_VERSION). */
@@ -153,6 +166,27 @@ pa_status paged_attn_plan(const pa_dims* dims, int32_t B, int32_t* num_splits,
  * none, and SIZE_MAX when dims or B are rejected (pa_last_error() says why).
  */
 size_t paged_attn_workspace_bytes(const pa_dims* dims, int32_t B);
+
+/*
+ * Longest-first order of a batch's requests, for dims->order: order[r] is
+ * the request with the r-th longest history (seq_lens descending, equal
+ * lengths by request index), a permutation of 0..S-1 written on stream.
+ * Requests of different lengths share one batch ([Slides] "调度决定谁上场，
+ * 分页决定住哪里"; the mixed-length batch of [Budgets] §5 draws lengths
+ * uniformly from 1 to 512).  A decode launch with more work items than fit
+ * on the GPU at once runs them in rounds as workgroups finish; issuing the
+ * longest first (the longest-processing-time rule) leaves short items to
+ * fill the end, so the last round is shorter.  Measured on 256 requests of
+ * 1-513 tokens, 32 layers: 49.6 -> 47.6 us per layer.  The lengths do not
+ * change between the layers of a step, so one call serves them all.
+ *
+ * seq_lens: device int32 [S], any values (compared as given); order: device
+ * int32 [S], caller-owned, overwritten.  One launch of ceil(S / 256)
+ * workgroups and S^2 comparisons.  S = 0 is a no-op; S < 0 or a NULL
+ * pointer with S > 0 is PA_ERR_INVALID_ARG; S > 65536 is PA_ERR_UNSUPPORTED
+ * (the comparisons grow as S^2: about 0.5 ms at that size).
+ */
+pa_status paged_attn_order(const int32_t* seq_lens, int32_t S, int32_t* order, hipStream_t stream);
 
 /*
  * One decode step of one layer: for every request s and query head h,

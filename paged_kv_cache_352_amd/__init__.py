@@ -27,6 +27,7 @@ from ._lib import (  # noqa: F401
     paged_attn_decode_noalloc,
     paged_attn_extend,
     paged_attn_extend_plan,
+    paged_attn_order,
     paged_attn_plan,
     paged_attn_workspace_bytes,
     paged_kv_gather,

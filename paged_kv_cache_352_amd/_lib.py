@@ -41,10 +41,11 @@ class PaDims(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("flags", ctypes.c_int32),
+        ("order", ctypes.c_void_p),
     ]
 
 
-ABI_VERSION = 3            # PA_ABI_VERSION of include/pagedattn.h that PaDims mirrors
+ABI_VERSION = 4            # PA_ABI_VERSION of include/pagedattn.h that PaDims mirrors
 NOALLOC_SCRATCH_BYTES = 16 << 20  # PA_NOALLOC_SCRATCH_BYTES
 FLAG_BF16_WEIGHTS = 1      # PA_FLAG_BF16_WEIGHTS
 
@@ -68,6 +69,7 @@ def load():
         "pa_last_error": (ctypes.c_char_p, []),
         "paged_attn_plan": (I32, [DP, I32, ctypes.POINTER(I32), ctypes.POINTER(SZ)]),
         "paged_attn_workspace_bytes": (SZ, [DP, I32]),
+        "paged_attn_order": (I32, [P, I32, P, P]),
         "paged_attn_decode": (I32, [P, P, P, P, P, I32, F32, P, P, DP]),
         "paged_attn_decode_noalloc": (I32, [P, P, P, P, P, I32, F32, P, P, DP]),
         "paged_attn_decode_append": (I32, [P, P, P, P, P, P, P, P, I32, F32, P, P, DP]),
@@ -157,9 +159,11 @@ def _need_cuda(*ts):
             raise PagedAttnError("tensors must be contiguous and on a HIP device")
 
 
-def make_dims(S, Hq, Hkv, D, MB, NB, dtype, num_splits=0, workspace=None, flags=0):
+def make_dims(S, Hq, Hkv, D, MB, NB, dtype, num_splits=0, workspace=None, flags=0, order=None):
     d = PaDims()
     d.flags = flags
+    if order is not None:
+        d.order = order.data_ptr()
     d.num_seqs, d.num_q_heads, d.num_kv_heads, d.head_dim = S, Hq, Hkv, D
     d.max_blocks_per_seq, d.num_blocks = MB, NB
     d.dtype = _DTYPES[dtype] if not isinstance(dtype, int) else dtype
@@ -201,6 +205,31 @@ def paged_attn_extend_plan(S, Hq, Hkv, D, MB, NB, dtype, B, T, num_splits=0):
     return p.value, w.value
 
 
+def _check_order(order, S):
+    """dims->order: None, or a device int32 [S] tensor (a permutation of 0..S-1)."""
+    if order is None:
+        return
+    if order.dtype != torch.int32 or tuple(order.shape) != (S,):
+        raise PagedAttnError("order must be int32 [S]")
+    _need_cuda(order)
+
+
+def paged_attn_order(seq_lens, out=None, stream=None):
+    """int32 [S] on the device: the requests longest first (ties by index), for ``order=``."""
+    lib = load()
+    if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1:
+        raise PagedAttnError("seq_lens must be int32 [S]")
+    _need_cuda(seq_lens)
+    S = seq_lens.shape[0]
+    st = _launch_stream(stream)
+    with torch.cuda.stream(st):
+        if out is None:
+            out = torch.empty(S, dtype=torch.int32, device=seq_lens.device)
+    _check_order(out, S)
+    _check("paged_attn_order", lib.paged_attn_order(_ptr(seq_lens), S, _ptr(out), _stream(st)))
+    return out
+
+
 def _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, B, out):
     if q.dim() not in (3, 4) or k_pool.dim() != 4 or block_tables.dim() != 2 or seq_lens.dim() != 1:
         raise PagedAttnError("expect q [S,Hq,d] (or [S,T,Hq,d]), pools [NB,B,Hkv,d], block_tables [S,MB], "
@@ -221,8 +250,11 @@ def _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, B, out):
 
 
 def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, B, scale, out=None, num_splits=0,
-                      workspace=None, stream=None):
-    """out[S, Hq, d] (float32) = one decode step over pools [NB, B, Hkv, d]."""
+                      workspace=None, stream=None, order=None):
+    """out[S, Hq, d] (float32) = one decode step over pools [NB, B, Hkv, d].
+
+    ``order`` (from paged_attn_order) only changes which request's work is
+    issued first; the output is the same bit for bit."""
     lib = load()
     if q.dim() != 3:
         raise PagedAttnError("paged_attn_decode takes q [S, Hq, d]")
@@ -238,14 +270,16 @@ def paged_attn_decode(q, k_pool, v_pool, block_tables, seq_lens, B, scale, out=N
     _need_cuda(q, k_pool, v_pool, block_tables, seq_lens, out)
     if workspace is not None:
         _need_cuda(workspace)
-    d = make_dims(S, Hq, Hkv, D, MB, NB, q.dtype, num_splits, workspace)
+    _check_order(order, S)
+    d = make_dims(S, Hq, Hkv, D, MB, NB, q.dtype, num_splits, workspace, order=order)
     _check("paged_attn_decode", lib.paged_attn_decode(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), B, ctypes.c_float(scale),
         _ptr(out), _stream(st), ctypes.byref(d)))
     return out
 
 
-def paged_attn_decode_noalloc(q, k_pool, v_pool, block_tables, seq_lens, B, scale, out, num_splits=0, stream=None):
+def paged_attn_decode_noalloc(q, k_pool, v_pool, block_tables, seq_lens, B, scale, out, num_splits=0, stream=None,
+                              order=None):
     """paged_attn_decode with the split workspace in the library's static device
     scratch (PA_NOALLOC_SCRATCH_BYTES per GPU): nothing is allocated, so the
     caller passes ``out``.  Calls that overlap on one GPU race on the scratch."""
@@ -254,7 +288,8 @@ def paged_attn_decode_noalloc(q, k_pool, v_pool, block_tables, seq_lens, B, scal
         raise PagedAttnError("paged_attn_decode_noalloc takes q [S, Hq, d] and a preallocated out")
     S, Hq, D, NB, Hkv, MB = _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, B, out)
     _need_cuda(q, k_pool, v_pool, block_tables, seq_lens, out)
-    d = make_dims(S, Hq, Hkv, D, MB, NB, q.dtype, num_splits)
+    _check_order(order, S)
+    d = make_dims(S, Hq, Hkv, D, MB, NB, q.dtype, num_splits, order=order)
     _check("paged_attn_decode_noalloc", lib.paged_attn_decode_noalloc(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(seq_lens), B, ctypes.c_float(scale),
         _ptr(out), _stream(stream), ctypes.byref(d)))
@@ -262,7 +297,7 @@ def paged_attn_decode_noalloc(q, k_pool, v_pool, block_tables, seq_lens, B, scal
 
 
 def paged_attn_decode_append(q, k_pool, v_pool, k_new, v_new, block_tables, positions, seq_lens, B, scale, out=None,
-                             num_splits=0, workspace=None, stream=None):
+                             num_splits=0, workspace=None, stream=None, order=None):
     """kv_append(k_new, v_new at positions) then paged_attn_decode, in one call (one kernel for bf16)."""
     lib = load()
     if q.dim() != 3:
@@ -285,7 +320,8 @@ def paged_attn_decode_append(q, k_pool, v_pool, k_new, v_new, block_tables, posi
     _need_cuda(out)
     if workspace is not None:
         _need_cuda(workspace)
-    d = make_dims(S, Hq, Hkv, D, MB, NB, q.dtype, num_splits, workspace)
+    _check_order(order, S)
+    d = make_dims(S, Hq, Hkv, D, MB, NB, q.dtype, num_splits, workspace, order=order)
     _check("paged_attn_decode_append", lib.paged_attn_decode_append(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new), _ptr(block_tables), _ptr(positions),
         _ptr(seq_lens), B, ctypes.c_float(scale), _ptr(out), _stream(st), ctypes.byref(d)))
@@ -479,7 +515,7 @@ class DecodeLaunch:
     """
 
     def __init__(self, q, k_pool, v_pool, block_tables, seq_lens, B, scale, out=None, num_splits=0,
-                 workspace=None, stream=None, bf16_weights=False):
+                 workspace=None, stream=None, bf16_weights=False, order=None):
         S, Hq, D, NB, Hkv, MB = _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, B, out)
         extend = q.dim() == 4  # [S, T, Hq, d]: paged_attn_extend
         if extend:
@@ -494,9 +530,10 @@ class DecodeLaunch:
                 workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         self.workspace = workspace
         _need_cuda(q, k_pool, v_pool, block_tables, seq_lens, self.out)
-        self._keep = (q, k_pool, v_pool, block_tables, seq_lens)
+        self._keep = (q, k_pool, v_pool, block_tables, seq_lens, order)
+        _check_order(order, S)
         self._dims = make_dims(S, Hq, Hkv, D, MB, NB, q.dtype, num_splits, workspace,
-                               FLAG_BF16_WEIGHTS if bf16_weights else 0)
+                               FLAG_BF16_WEIGHTS if bf16_weights else 0, order=order)
         lib = load()
         self._name = "paged_attn_extend" if extend else "paged_attn_decode"
         self._fn = getattr(lib, self._name)

@@ -214,6 +214,7 @@ static pa_status attend(const void* q, const void* k_pool, const void* v_pool, c
   a.T = T;
   a.TG = (int)TG;
   a.bf16_weights = (dims->flags & PA_FLAG_BF16_WEIGHTS) != 0;
+  a.order = dims->order;
   if (k_new) {
     if (!aligned(k_new, 16) || !aligned(v_new, 16)) return fail(PA_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
     if (dims->dtype == PA_BF16) {
@@ -256,6 +257,15 @@ size_t paged_attn_workspace_bytes(const pa_dims* dims, int32_t B) {
   size_t bytes = 0;
   if (plan_common(dims, B, 1, &P, &bytes) != PA_OK) return SIZE_MAX;
   return bytes;
+}
+
+pa_status paged_attn_order(const int32_t* seq_lens, int32_t S, int32_t* order, hipStream_t stream) {
+  g_last_error.clear();
+  if (S < 0) return fail(PA_ERR_INVALID_ARG, "S = %d < 0", S);
+  if (S == 0) return PA_OK;
+  if (!seq_lens || !order) return fail(PA_ERR_INVALID_ARG, "seq_lens and order are required");
+  if (S > (1 << 16)) return fail(PA_ERR_UNSUPPORTED, "more than 65536 requests to order");
+  return launched(pa::launch_order(seq_lens, S, order, stream));
 }
 
 pa_status paged_attn_extend_plan(const pa_dims* dims, int32_t B, int32_t num_q_tokens, int32_t* num_splits,

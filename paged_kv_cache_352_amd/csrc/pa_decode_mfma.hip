@@ -122,8 +122,17 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
     tg = item % a.TG;
     item /= a.TG;
   }
-  const int s = item % a.S;
-  const int kvh = item / a.S;
+  int s = item % a.S;
+  int kvh = item / a.S;
+  if (a.plain_order && a.order) {
+    // Requests in the caller's order (longest first from paged_attn_order),
+    // the KV heads of one request side by side.  An entry outside [0, S)
+    // stands for its own position.
+    const int r = item / a.Hkv;
+    kvh = item % a.Hkv;
+    const int so = a.order[r];
+    s = so >= 0 && so < a.S ? so : r;
+  }
 
   // Column n16 of set j is query token tq[j], head kvh*G + n16%G.
   int tq[NS];
@@ -459,6 +468,8 @@ hipError_t launch_gb(const DecodeArgs& args, hipStream_t stream) {
   // 92.0 vs 91.8 us).
   DecodeArgs a = args;
   a.plain_order = items > kResidentItems;
+  // dims->order acts only in launch order (more than one round): within one
+  // round every item is resident from the start.
   if constexpr (!kCausal) {
     if (a.k_new) {
       hipLaunchKernelGGL((decode_mfma_kernel<G, false, 1, kMfmaWaves, B, true>), dim3(items),

@@ -36,6 +36,7 @@ struct DecodeArgs {
   bool bf16_weights;  // PA_FLAG_BF16_WEIGHTS: the shared-tile kernel rounds p once to bf16
   bool plain_order;   // bf16 decode: work items in launch order, not grouped by XCD (set at launch)
   int W;              // float32: splits per workgroup, one wave each, merged in LDS (P counts the groups)
+  const int32_t* order;  // bf16 decode with plain_order: request issued r-th is order[r] (NULL: r)
 };
 
 // float32 decode: the P splits of one (request, KV head, token group) run in
@@ -160,6 +161,9 @@ struct KvArgs {
 hipError_t launch_append(const KvArgs& a, const uint8_t* k_new, const uint8_t* v_new,
                          const int32_t* tables, const int32_t* positions, int T, int num_layers,
                          int64_t layer_stride_bytes, hipStream_t stream);
+
+// order[r] = the request with the r-th longest length (ties by index).
+hipError_t launch_order(const int32_t* lens, int S, int32_t* order, hipStream_t stream);
 
 hipError_t launch_cow(const KvArgs& a, const int32_t* src, const int32_t* dst, const int32_t* n_valid,
                       int num_pairs, int num_layers, int64_t layer_stride_bytes, hipStream_t stream);

@@ -1,5 +1,6 @@
 // Data-movement kernels beside the decode: token append, copy-on-write of a
-// tail block's valid slots, and the debug gather.  All three move whole
+// tail block's valid slots, and the debug gather; and the longest-first
+// order of a batch's requests (paged_attn_order).  All three move whole
 // slots, and a slot of one block (all KV heads, all dims) is one contiguous
 // run of Hkv*d elements in the [NB, B, Hkv, d] pool, so each kernel is a
 // 16-byte-vector copy of contiguous runs.  Bytes are copied exactly.
@@ -109,7 +110,42 @@ __global__ __launch_bounds__(kThreads) void swap_kernel(KvArgs a, const int32_t*
     copy16(pool, slot, blk_bytes);
 }
 
+// One thread per request: its rank among all requests by (length
+// descending, index ascending), a strict total order, so the ranks are a
+// permutation; the lengths pass through LDS 256 at a time, read four at a
+// time (every lane the same address: a broadcast).
+__global__ __launch_bounds__(kThreads) void order_kernel(const int32_t* __restrict__ lens, int S,
+                                                         int32_t* __restrict__ order) {
+  __shared__ __attribute__((aligned(16))) int32_t tile[kThreads];
+  const int s = blockIdx.x * kThreads + threadIdx.x;
+  const int32_t mine = s < S ? lens[s] : 0;
+  int rank = 0;
+  auto before = [&](int32_t o, int idx) { return (int)((o > mine) | ((o == mine) & (idx < s))); };
+  for (int base = 0; base < S; base += kThreads) {
+    __syncthreads();
+    if (base + (int)threadIdx.x < S) tile[threadIdx.x] = lens[base + threadIdx.x];
+    __syncthreads();
+    const int cnt = min(kThreads, S - base);
+    if (cnt == kThreads) {
+#pragma unroll 8
+      for (int i = 0; i < kThreads; i += 4) {
+        const int4 o = *reinterpret_cast<const int4*>(&tile[i]);
+        rank += before(o.x, base + i) + before(o.y, base + i + 1) + before(o.z, base + i + 2) +
+                before(o.w, base + i + 3);
+      }
+    } else {
+      for (int i = 0; i < cnt; ++i) rank += before(tile[i], base + i);
+    }
+  }
+  if (s < S) order[rank] = s;
+}
+
 }  // namespace
+
+hipError_t launch_order(const int32_t* lens, int S, int32_t* order, hipStream_t stream) {
+  hipLaunchKernelGGL(order_kernel, dim3((S + kThreads - 1) / kThreads), dim3(kThreads), 0, stream, lens, S, order);
+  return hipGetLastError();
+}
 
 hipError_t launch_swap(const KvArgs& a, const int32_t* blocks, int nlist, uint8_t* buf, int num_layers,
                        int64_t layer_stride_bytes, bool to_buffer, hipStream_t stream) {

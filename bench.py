@@ -289,18 +289,21 @@ def suite(torch, pa, W, dev):
     # Several query tokens per request ([Serving] §5): a speculative-verification
     # step with T draft tokens over the headline histories (4 rotated pool
     # copies), and one 512-token prompt chunk.  GB/s counts the history once.
-    for T in (2, 4, 8, 16, 24):
+    # T = 16 and 24 (the shared-tile path) also with PA_FLAG_BF16_WEIGHTS.
+    for T, bf16_weights in ((2, False), (4, False), (8, False), (16, False), (16, True), (24, False), (24, True)):
         b = W.verify_batch(device=dev, T=T)
         pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
         pools = [(b.k_pool, b.v_pool)] + [(b.k_pool.clone(), b.v_pool.clone()) for _ in range(3)]
-        calls = [pa.DecodeLaunch(b.q, k, v, b.block_tables, b.seq_lens, b.B, b.scale) for k, v in pools]
+        calls = [pa.DecodeLaunch(b.q, k, v, b.block_tables, b.seq_lens, b.B, b.scale, bf16_weights=bf16_weights)
+                 for k, v in pools]
 
         def launch_all():
             for c in calls:
                 c.launch()
 
         us = graph_time_us(torch, launch_all, 10) / len(calls)
-        out[f"bf16 verification, 32 x 4096 tokens, T = {T} query tokens"] = dict(
+        tag = ", bf16 weights" if bf16_weights else ""
+        out[f"bf16 verification, 32 x 4096 tokens, T = {T} query tokens{tag}"] = dict(
             rate(b.valid_kv_bytes(), us), splits=calls[0].splits, layers=1,
             query_tokens_per_s_per_layer=round(b.S * T / (us * 1e-6), 1))
         del b, pools, calls

@@ -399,6 +399,91 @@ def suite(torch, pa, W, dev):
     return out
 
 
+def suite_markdown(S, command):
+    """The suite's JSON (``suite()``) as the markdown summary kept under profiles/:
+    ``command`` is the command line that produced the JSON."""
+    out = []
+    w = out.append
+    w("# Decode, several query tokens, block sizes, swap and full steps on the other workloads (MI355X, one GPU)\n")
+    w("Command (from the repository root):\n")
+    w(f"    {command}\n")
+    w("(`bench.py --suite-md PATH` writes this summary from the same JSON, with `--suite-json` when the")
+    w("suite has already run.)\n")
+    w("Timing: each workload's launches are captured in one HIP graph and replayed back to back; the time")
+    w("per launch includes the graph's inter-kernel gap.  Decode rows: per-layer decode time over all")
+    w("layers (each layer has its own K/V pools, so nothing is cache-resident across layers except where")
+    w("noted).  Full step: the whole decode step of all layers (copy-on-write where the workload has it,")
+    w("kv_append rounds, then paged_attn_decode per layer); fused: one paged_attn_decode_append per")
+    w("layer instead; all-layer append: one kv_append_layers launch for every layer, then the decodes.\n")
+    w("| Workload | Decode us / layer | Valid K+V bytes / layer | GB/s | of 8 TB/s | Splits | Full step us | Fused us | All-layer append us | Tokens/s per layer |")
+    w("|---|---|---|---|---|---|---|---|---|---|")
+    for k in ("fp32 5 requests (37..511 tokens), one layer", "bf16 256 mixed-length requests, 32 layers",
+              "bf16 prefix sharing, 64 branches (COW), one layer", "bf16 168 x 1025 tokens, 24 layers"):
+        e = S[k]
+        w(f"| {k} | {e['us']:.3f} | {e['bytes']:,} | {e['GB_s']:.1f} | {100*e['frac_hbm_peak']:.1f} % | {e['splits']} | "
+          f"{e.get('full_step_us', '')} | {e.get('full_step_fused_us', '')} | {e.get('full_step_append_layers_us', '')} | {e['tokens_per_s_per_layer']:.0f} |")
+    e = S["bf16 256 mixed-length requests, 32 layers"]
+    lf = e.get("longest_first")
+    if lf:
+        w(f"| bf16 256 mixed-length requests, 32 layers, issued longest first | {lf['us']:.3f} | {lf['bytes']:,} | {lf['GB_s']:.1f} | "
+          f"{100*lf['frac_hbm_peak']:.1f} % | {e['splits']} |  |  | {lf['full_step_append_layers_us']} | {lf['tokens_per_s_per_layer']:.0f} |")
+        w("\nLongest first: one paged_attn_order per step (its order serves all 32 layers), then each")
+        w("decode with dims->order; the full step there is paged_attn_order, one kv_append_layers and the")
+        w("32 decodes.  Outputs are bitwise those of request order (tests/test_gpu_order.py).")
+    w("\nThe prefix-sharing row reads the 128 shared prefix blocks 64 times, from cache after the first:")
+    w("its logical rate is not an HBM figure (decode_mfma_bf16_workload_traffic.md gives its DRAM bytes).")
+    w("The fp32 row is 2 MB of history: launch latency, not bandwidth.\n")
+    w("## Several query tokens per request (paged_attn_extend, bf16, one layer)\n")
+    w("Verification: 32 requests, 4096 positions each, the last T of them new (appended beforehand);")
+    w("4 pool copies rotated.  Prompt chunk: 8 requests, 3584 positions of history plus a 512-token chunk.")
+    w("GB/s counts the history once; TFLOP/s counts the causal q.k and p.v work (4 d flops per query")
+    w("token, head and visible position) against the 2.5 PFLOP/s dense bf16 peak.  Rows marked \"bf16 weights\"")
+    w("run with PA_FLAG_BF16_WEIGHTS (each softmax weight rounded once to bf16; see include/pagedattn.h).\n")
+    w("| Workload | us | GB/s | of 8 TB/s | TFLOP/s | of bf16 peak | Splits | Query tokens/s |")
+    w("|---|---|---|---|---|---|---|---|")
+    for k, e in S.items():
+        if k.startswith("bf16 verification") or k.startswith("bf16 prompt chunk"):
+            tf = e.get("TFLOP_s", ""); fr = e.get("frac_bf16_mfma_peak")
+            w(f"| {k} | {e['us']:.3f} | {e['GB_s']:.1f} | {100*e['frac_hbm_peak']:.1f} % | {tf} | {'' if fr is None else f'{100*fr:.1f} %'} | {e['splits']} | {e['query_tokens_per_s_per_layer']:.0f} |")
+    w("\n## Block size on the 32 x 4096 batch (same tokens; 4 pool copies rotated)\n")
+    w("| B | Decode us | GB/s | of 8 TB/s |")
+    w("|---|---|---|---|")
+    for B in (8, 16, 32, 64):
+        e = S[f"bf16 32 x 4096 tokens, block size {B}"]
+        w(f"| {B} | {e['us']:.3f} | {e['GB_s']:.1f} | {100*e['frac_hbm_peak']:.1f} % |")
+    w("\nThe pages' trade-off ([Slides] \"块越小，省下的是空位，多出来的是管理\"): smaller blocks waste fewer tail")
+    w("slots but need more table entries; for the read itself B = 16 to 64 are within 0.1 % here and B = 8 costs 3 %.\n")
+    sw = S["bf16 256 mixed-length requests, 32 layers"].get("swap_500MiB")
+    if sw:
+        w("## Block swap (500 MiB through pinned host memory)\n")
+        w("250 blocks x 32 layers x 64 KiB (K+V) = 524,288,000 B, the amount of the pages' recovery-cost")
+        w("example (4,000 tokens at 128 KiB per token), moved by kv_swap_out / kv_swap_in directly between the")
+        w("pools and pinned host memory:\n")
+        w("| Direction | ms | GiB/s |")
+        w("|---|---|---|")
+        w(f"| out (pool -> host) | {sw['out_ms']} | {sw['out_GiB_s']} |")
+        w(f"| in (host -> pool) | {sw['in_ms']} | {sw['in_GiB_s']} |\n")
+        w(f"Round trip {sw['out_ms'] + sw['in_ms']:.1f} ms; the pages' teaching estimate at 25 GiB/s is 19.5 ms one")
+        w("way and at least 39.1 ms for both.\n")
+    re = [(k, e) for k, e in S.items() if k.startswith("bf16 re-prefill")]
+    if re:
+        w("## Swap or recompute ([Slides] recovery-cost example)\n")
+        w("Recomputing instead of swapping means prefilling the 4,000 tokens again. The part of that which")
+        w("this library runs is the attention: the whole prompt again in 512-token chunks, chunk c attending")
+        w("the request's pages up to its own last token (paged_attn_extend, one request, bf16):\n")
+        w("| Workload | us per layer | Chunks | TFLOP/s | of bf16 peak | ms for 32 layers |")
+        w("|---|---|---|---|---|---|")
+        for k, e in re:
+            w(f"| {k} | {e['us_per_layer']} | {e['chunks']} | {e['TFLOP_s']} | {100*e['frac_bf16_mfma_peak']:.1f} % | {e['ms_for_32_layers']} |")
+        d = re[0][1]
+        w("\nThat is a lower bound on recomputation: the K/V projections and the rest of the model come on")
+        w("top, and one request leaves most of the GPU idle." + (f" Recovery by swapping costs the swap-in, {sw['in_ms']} ms here,"
+          f" after a {sw['out_ms']} ms swap-out at preemption time." if sw else ""))
+        w(f"Recovery by recomputing costs at least the {d['ms_for_32_layers']} ms above, and 200 ms at the pages'")
+        w("teaching rate of 20,000 tokens/s.")
+    return "\n".join(out) + "\n"
+
+
 PROFILE_WORKLOADS = {
     "decode32x4096": "bf16 32 x 4096 tokens, one layer (the headline batch, 4 rotated pool copies)",
     "mixed256": "bf16 256 mixed-length requests, 32 layers: one decode launch per layer, after the step's append",
@@ -469,6 +554,10 @@ def main():
     ap.add_argument("--no-side-kernels", action="store_true", help="skip the kv_append / kv_cow_copy timings")
     ap.add_argument("--suite", metavar="PATH", default=None,
                     help="also time the other four workloads and write them as JSON to PATH")
+    ap.add_argument("--suite-md", metavar="PATH", default=None,
+                    help="write the suite's markdown summary to PATH (with --suite, or alone with --suite-json)")
+    ap.add_argument("--suite-json", metavar="PATH", default=None,
+                    help="with --suite-md: format this suite JSON (written by --suite) instead of running anything")
     ap.add_argument("--profile-workload", choices=sorted(PROFILE_WORKLOADS), default=None,
                     help="only run one workload's attention launches (for rocprofv3), --warmup + --steps rounds")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -476,6 +565,13 @@ def main():
                          "a few times, to scale the HBM byte counters")
     args = ap.parse_args()
 
+    if args.suite_md and args.suite_json:  # formatting only: no GPU
+        with open(args.suite_json) as f:
+            S = json.load(f)
+        cmd = f"python3 bench.py --steps {args.steps} --no-cpu-baseline --no-side-kernels --suite {args.suite_json}"
+        with open(args.suite_md, "w") as f:
+            f.write(suite_markdown(S, cmd))
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); libpagedattn has no "
               "multi-GPU mode.", file=sys.stderr)
@@ -612,6 +708,9 @@ def main():
         st = suite(torch, pa, W, dev)
         with open(args.suite, "w") as f:
             json.dump(st, f, indent=1)
+        if args.suite_md:
+            with open(args.suite_md, "w") as f:
+                f.write(suite_markdown(st, " ".join(["python3", "bench.py"] + sys.argv[1:])))
         for k, v in st.items():
             log(f"suite: {k}: {json.dumps(v)}")
     if not args.no_cpu_baseline:

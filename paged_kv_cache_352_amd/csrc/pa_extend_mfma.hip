@@ -97,6 +97,9 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(Decode
   }
   const int lim_hi = min(n, max(0, n - a.T + min(a.T, tw * TW + TW)));
   const int nt = (lim_hi + kTile - 1) / kTile;
+  // A wave whose tokens all lie past T loads and writes its rows and passes
+  // every barrier, but skips the arithmetic (nothing of it is stored).
+  const bool idle = tw * TW + w * TS >= a.T;
   const int u0 = p * (a.tps / kTile);
   const int u1 = min(nt, u0 + a.tps / kTile);  // the same range for every wave
 
@@ -204,6 +207,7 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(Decode
     *reinterpret_cast<uint4*>(base + 3 * kVtBytes + wv_off) =
         r_own < n - tb_loaded * kTile ? r.vb : make_uint4(0, 0, 0, 0);
     __syncthreads();
+    if (idle) return;
     TileReads ra = rd0, rb = rd0;
     ra.k += buf * (4 * kVtBytes);
     ra.v += buf * (4 * kVtBytes);

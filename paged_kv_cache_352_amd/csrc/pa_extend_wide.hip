@@ -109,6 +109,11 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_wide_kernel(DecodeAr
   const int nt = (lim_hi + kTile - 1) / kTile;  // 16-slot tiles
   const int u0 = p * (a.tps / kTile);
   const int u1 = min(nt, u0 + a.tps / kTile);
+  // A wave whose tokens all lie past T (T not a multiple of the workgroup's
+  // tokens) still loads and writes its rows of every step and passes every
+  // barrier, but skips the arithmetic: nothing of it is stored, and its SIMD
+  // goes to the other workgroup's wave.
+  const bool idle = tw * TW + w * TC >= a.T;
 
   // q^T as the B operand of S^T = K q^T: lane l holds column col over dims
   // 16*kk + 8*h .. +8.  A negative scale enters as q negated (exact in bf16)
@@ -218,6 +223,7 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_wide_kernel(DecodeAr
       }
     }
     __syncthreads();
+    if (idle) return;
 
     // S^T = K q^T over d = 128.
     f32x16_t sc = {};
@@ -450,6 +456,10 @@ __global__ __launch_bounds__(kWave * kPingPongWaves, 1) void extend_pingpong_ker
   const int u1 = min(nt, u0 + a.tps / kTile);
   const int nsteps = u1 > u0 ? (u1 - u0 + 1) / 2 : 0;  // step k: tiles u0+2k, u0+2k+1 (if < u1)
   const int base_slot = kTile * u0;
+  // A wave whose tokens all lie past T loads, writes and passes every barrier
+  // but skips its matrix and vector work (nothing of it is stored); it runs a
+  // loop copy of its own, so the others' copies carry no test for it.
+  const bool idle = tw * TW + w * TC >= a.T;
 
   const bool neg_scale = a.scale_log2 < 0.f;
   const float c_log2 = neg_scale ? -a.scale_log2 : a.scale_log2;
@@ -693,8 +703,9 @@ __global__ __launch_bounds__(kWave * kPingPongWaves, 1) void extend_pingpong_ker
   // indices are compile-time; a trip runs all three (steps past the end do
   // nothing), which keeps the compiler's count of loads in flight exact: an
   // early exit from the unrolled trip made it wait for every load in flight.
-  auto run = [&](auto late_group) {
+  auto run = [&](auto late_group, auto idle_wave) {
     constexpr bool kLate = decltype(late_group)::value;
+    constexpr bool kIdle = decltype(idle_wave)::value;
     for (int j0 = 0; j0 <= nsteps; j0 += kBufs) {
 #pragma unroll
       for (int b = 0; b < kBufs; ++b) {
@@ -706,17 +717,18 @@ __global__ __launch_bounds__(kWave * kPingPongWaves, 1) void extend_pingpong_ker
         Ld& rn = ring[(b + 1) % kBufs];
         auto vphase = [&](int x) {
           const int e = table_entry(j + 4);  // scalar load, used at the end of the phase
-          if (x >= 0 && x < nsteps) softmax(x);
+          if constexpr (!kIdle)
+            if (x >= 0 && x < nsteps) softmax(x);
           if (j + 1 < nsteps) write_step(j + 1, rn, knext, vnext);
           load_step(j + 4, e, rn);
         };
         if constexpr (kLate) {
           vphase(j - 1);
           barrier_after_v();
-          mphase(j, kcur, vprev);
+          if constexpr (!kIdle) mphase(j, kcur, vprev);
           barrier_after_m();
         } else {
-          mphase(j, kcur, vprev);
+          if constexpr (!kIdle) mphase(j, kcur, vprev);
           barrier_after_m();
           vphase(j);
           barrier_after_v();
@@ -724,10 +736,19 @@ __global__ __launch_bounds__(kWave * kPingPongWaves, 1) void extend_pingpong_ker
       }
     }
   };
-  if (late)
-    run(std::integral_constant<bool, true>{});
-  else
-    run(std::integral_constant<bool, false>{});
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+  if (late) {
+    if (idle)
+      run(yes{}, yes{});
+    else
+      run(yes{}, no{});
+  } else {
+    if (idle)
+      run(no{}, yes{});
+    else
+      run(no{}, no{});
+  }
 
   float lc;
   if constexpr (kOneRounding) {

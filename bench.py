@@ -492,6 +492,8 @@ PROFILE_WORKLOADS = {
     "long168": "bf16 168 x 1025 tokens, 24 layers: one decode launch per layer, after the step's append",
     "chunk512": "bf16 prompt chunk, 8 x 4096 tokens, T = 512, one layer (paged_attn_extend)",
     "chunk512w": "bf16 prompt chunk, 8 x 4096 tokens, T = 512, one layer, PA_FLAG_BF16_WEIGHTS",
+    "verify16": "bf16 verification, 32 x 4096 tokens, T = 16 query tokens, one layer (paged_attn_extend)",
+    "verify24": "bf16 verification, 32 x 4096 tokens, T = 24 query tokens, one layer (paged_attn_extend)",
 }
 
 
@@ -506,6 +508,12 @@ def profile_workload(torch, pa, W, dev, name, steps, warmup):
         calls = [pa.DecodeLaunch(b.q[0], k, v, b.block_tables, b.seq_lens, b.B, b.scale) for k, v in pools]
         per_launch = b.valid_kv_bytes_per_layer()
         rounds = [[c] for c in calls]
+    elif name in ("verify16", "verify24"):
+        b = W.verify_batch(device=dev, T=int(name[-2:]))
+        pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
+        calls = [pa.DecodeLaunch(b.q, b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B, b.scale)]
+        per_launch = b.valid_kv_bytes()
+        rounds = [calls]
     elif name in ("chunk512", "chunk512w"):
         b = W.prefill_chunk_batch(device=dev)
         pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)

@@ -168,8 +168,8 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(Decode
 
   float m[kSets];
   float l[kSets];       // two roundings: partial l of column n16 over this lane's slots
-  f32x4_t lacc[kSets];  // one rounding: l of column 4*c4 + r, in the accumulator layout of o
-  f32x4_t acc[kSets][8];
+  f32x4_t lacc[kSets];  // one rounding: l of column n16 (in every element), in the layout of o^T
+  f32x4_t acc[kSets][8];  // o^T: column n16 at dims 16*jj + 4*c4 .. +3
 #pragma unroll
   for (int j = 0; j < kSets; ++j) {
     m[j] = kNegInf;
@@ -226,10 +226,7 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(Decode
 #pragma unroll
     for (int j = 0; j < kSets; ++j) full = full && vqb[j] >= kTile;
     const bool mask = !__all(full);
-    if constexpr (kOneRounding)
-      pair_update_sets_rn<kSets, true>(ra, rb, qv, acc, lacc, m, vqa, vqb, c_log2, n16, c4, mask);
-    else
-      pair_update_sets<kSets, true>(ra, rb, qv, acc, m, l, vqa, vqb, c_log2, n16, c4, mask);
+    pair_update_sets<kSets, true, kOneRounding>(ra, rb, qv, acc, lacc, m, l, vqa, vqb, c_log2, n16, c4, mask);
   };
 
   // Table entries are read 64 at a time into one register (one per lane), as
@@ -258,15 +255,16 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(Decode
     }
   }
 
-  // The full l of every column in the layout of o: lane (n16, c4) gets the
-  // l of columns 4*c4 .. 4*c4+3.
-  if constexpr (!kOneRounding) {
+  // The full l of column n16 in every lane of it (the accumulators hold o^T:
+  // lane (n16, c4) has column n16 at dims 16*jj + 4*c4 .. +3).
+  float lc[kSets];
 #pragma unroll
-    for (int j = 0; j < kSets; ++j) {
-      l[j] += __shfl_xor(l[j], 16, kWave);  // the four lanes of column n16
-      l[j] += __shfl_xor(l[j], 32, kWave);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) lacc[j][r] = __shfl(l[j], 4 * c4 + r, kWave);
+  for (int j = 0; j < kSets; ++j) {
+    if constexpr (kOneRounding) {
+      lc[j] = lacc[j][0];
+    } else {
+      lc[j] = l[j] + __shfl_xor(l[j], 16, kWave);  // the four lanes of column n16
+      lc[j] += __shfl_xor(lc[j], 32, kWave);
     }
   }
   bad = __syncthreads_or(bad);  // any wave that met an entry outside the pool
@@ -274,40 +272,24 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(Decode
   const float nan = __builtin_nanf("");
 #pragma unroll
   for (int j = 0; j < kSets; ++j) {
+    if (tq[j] >= a.T) continue;
+    const int64_t row = ((int64_t)s * a.T + tq[j]) * a.Hq + kvh * G + n16 % G;
     if (a.P == 1) {
+      const float inv = lc[j] > 0.f ? 1.f / lc[j] : 0.f;
+      float* dst = a.out + row * kHeadDim + 4 * c4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int col = 4 * c4 + r;
-        const float lc = lacc[j][r];
-        const int t_out = tw * TW + w * TS + j * TC + col / G;
-        if (t_out < a.T) {
-          const float inv = lc > 0.f ? 1.f / lc : 0.f;
-          float* dst = a.out + (((int64_t)s * a.T + t_out) * a.Hq + kvh * G + col % G) * kHeadDim + n16;
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) dst[16 * jj] = bad ? nan : acc[j][jj][r] * inv;
-        }
+      for (int jj = 0; jj < 8; ++jj) {
+        const f32x4_t o = acc[j][jj] * inv;
+        *reinterpret_cast<f32x4_t*>(dst + 16 * jj) = bad ? f32x4_t{nan, nan, nan, nan} : o;
       }
     } else {
+      const int64_t slot = row * a.P + p;
+      float* dst = a.ws_o + slot * kHeadDim + 4 * c4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int col = 4 * c4 + r;
-        const int t_out = tw * TW + w * TS + j * TC + col / G;
-        if (t_out < a.T) {
-          const int64_t slot = (((int64_t)s * a.T + t_out) * a.Hq + kvh * G + col % G) * a.P + p;
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj) a.ws_o[slot * kHeadDim + 16 * jj + n16] = acc[j][jj][r];
-        }
-      }
-      // Lane n16 holds column n16's m; its l sits in element n16 % 4 of the
-      // lanes with c4 = n16 / 4.
-      float lr[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) lr[r] = __shfl(lacc[j][r], 16 * (n16 >> 2), kWave);
-      const float lj = (n16 & 3) == 0 ? lr[0] : (n16 & 3) == 1 ? lr[1] : (n16 & 3) == 2 ? lr[2] : lr[3];
-      if (c4 == 0 && tq[j] < a.T) {
-        const int64_t slot = (((int64_t)s * a.T + tq[j]) * a.Hq + kvh * G + n16 % G) * a.P + p;
+      for (int jj = 0; jj < 8; ++jj) *reinterpret_cast<f32x4_t*>(dst + 16 * jj) = acc[j][jj];
+      if (c4 == 0) {
         a.ws_m[slot] = bad ? 0.f : m[j];
-        a.ws_l[slot] = bad ? nan : lj;
+        a.ws_l[slot] = bad ? nan : lc[j];
       }
     }
   }

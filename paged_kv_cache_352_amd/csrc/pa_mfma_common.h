@@ -144,10 +144,14 @@ constexpr float kLazyMax = 8.f;
 // where a masked score is -inf): the tile max is taken on them and scaled
 // once (c * max s = max c*s for c >= 0, rounding included), and each weight
 // is 2^(fma(s, c, -m)), so no score is multiplied on its own.
+//
+// softmax_weights updates the column's state and weights, sets move where
+// its reference moved and returns its alpha (1 where it stayed), leaving o
+// to the caller; softmax_core also rescales o in the layout of the 16x16
+// accumulators, where lane (n16, c4) holds columns 4*c4 .. +3.
 template <int R, bool kMayBeEmpty, bool kSumL = true, bool kRaw = false>
-__device__ __attribute__((always_inline)) inline void softmax_core(const float (&sv)[R], f32x4_t (&acc)[8],
-                                                                   float& m, float& l, int c4, float (&pw)[R],
-                                                                   f32x4_t* lacc = nullptr, float c = 1.f) {
+__device__ __attribute__((always_inline)) inline float softmax_weights(const float (&sv)[R], float& m, float& l,
+                                                                       float (&pw)[R], bool& move, float c = 1.f) {
   // Tile max over the column's slots.  v_permlane16_swap / 32_swap exchange
   // rows of 16 / 32 lanes in the vector ALU, so the max of each returned
   // pair is the max over the lane and its partner (lane ^ 16, then lane ^ 32)
@@ -164,7 +168,7 @@ __device__ __attribute__((always_inline)) inline void softmax_core(const float (
   if constexpr (kRaw) bm *= c;
   // A column that has seen nothing (m = -inf) moves to its first finite tile
   // max; one whose tile is all -inf (kMayBeEmpty) keeps its empty state.
-  const bool move = bm > m + kLazyMax;
+  move = bm > m + kLazyMax;
   const float alpha = move ? fast_exp2(m - bm) : 1.f;
   if (move) m = bm;
   float mref = m;
@@ -177,7 +181,15 @@ __device__ __attribute__((always_inline)) inline void softmax_core(const float (
     for (int r = 4; r < R; r += 4) sum += (pw[r] + pw[r + 1]) + (pw[r + 2] + pw[r + 3]);
     l = fmaf(l, alpha, sum);
   }
+  return alpha;
+}
 
+template <int R, bool kMayBeEmpty, bool kSumL = true, bool kRaw = false>
+__device__ __attribute__((always_inline)) inline void softmax_core(const float (&sv)[R], f32x4_t (&acc)[8],
+                                                                   float& m, float& l, int c4, float (&pw)[R],
+                                                                   float c = 1.f) {
+  bool move;
+  const float alpha = softmax_weights<R, kMayBeEmpty, kSumL, kRaw>(sv, m, l, pw, move, c);
   // Rescale o only where a column's reference moved.
   if (__any(move)) {
     float ar[4];
@@ -187,10 +199,6 @@ __device__ __attribute__((always_inline)) inline void softmax_core(const float (
     for (int jj = 0; jj < 8; ++jj)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[jj][r] *= ar[r];
-    if (lacc) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) (*lacc)[r] *= ar[r];
-    }
   }
 }
 
@@ -291,65 +299,89 @@ __device__ inline void split_pair_rn(float x0, float x1, uint32_t& hi, uint32_t&
 }
 
 // The step for two consecutive tiles a and b (32 slots) and NS sets of 16
-// columns.  q.k runs per tile as above; the softmax takes the lane's 8
-// scores (slots 4*c4 .. +3 of a, then of b); and p.v runs on
+// columns.  q.k runs per tile as above, and the softmax takes the lane's 8
+// scores (slots 4*c4 .. +3 of a, then of b).  p.v runs on
 // v_mfma_f32_16x16x32_bf16, which does twice the work of the 16-slot
 // instruction per issue: its K index 8*c4 + i stands for slot 4*c4 + i of
-// tile a (i < 4) or of tile b (i >= 4), so the A operand is the lane's 8
-// weights in that order and the B operand is the two transposing V reads
-// (tile a, then tile b) of the same lane side by side.  p is split into a
-// head and a remainder rounded to nearest (split_pair_rn), which keeps the
-// weights within 2^-18 of p instead of the 2^-16 of the truncating split.
-// mask = false (the same in every lane): the caller has checked that both
-// tiles lie wholly inside every column's limit; then no slot is masked, no
-// column is empty, and the scores go to softmax_core unscaled
-// (scale_log2 >= 0 required), which saves a multiply, a compare and a
-// select per score.  Only the softmax differs between the two forms; the
-// matrix-core steps around it are shared.
-template <int NS, bool kMayBeEmpty>
+// tile a (i < 4) or of tile b (i >= 4).  It forms o transposed, o^T += V^T
+// p^T: the A operand is the two transposing V reads (tile a, then tile b)
+// of the lane side by side (16 dims by the 32 slots) and the B operand the
+// lane's 8 weights in slot order (column n16).  Lane (n16, c4) so holds
+// column n16 at dims 16*jj + 4*c4 .. +3 (acc[j][jj]): the column whose
+// scores, max and alpha it already has, and a rescale is one multiply per
+// element with no exchange between lanes.
+//
+// In the default form the V reads are issued with the K reads, before the
+// softmax, whose latency hides theirs, and the rescale (rare under the lazy
+// reference) runs on a branch that carries its own copy of the p.v
+// products: with one copy after the join the compiler moved the 32
+// accumulators to other registers on the common path every step.  The
+// one-rounding form keeps one copy and late V reads, which hold it at three
+// workgroups per CU.
+//
+// Default weights: p is split into a head and a remainder rounded to
+// nearest (split_pair_rn), which keeps them within 2^-18 of p, and l is
+// summed in fp32 per lane.  mask = false (the same in every lane): the
+// caller has checked that both tiles lie wholly inside every column's
+// limit; then no slot is masked, no column is empty, and the scores go in
+// unscaled (scale_log2 >= 0 required), which saves a multiply, a compare
+// and a select per score.
+//
+// kOneRounding (PA_FLAG_BF16_WEIGHTS): p is rounded once to bf16 (to
+// nearest) and the softmax denominator is summed by the matrix core from the
+// same rounded weights: lacc[j] += ones * p~^T, one extra MFMA per pair,
+// holding the l of column n16 in every element.  o / l is then an exact
+// weighted mean of V with weights p~ / sum p~, each p~ within 2^-9 of p
+// relative, and rounding to nearest leaves no common sign to the errors, so
+// they partly cancel over the history; p.v and l take 9 MFMAs per set
+// instead of 16, with no split of p.  That form has one softmax path (the
+// mask applied by selects where needed; two took its kernel past 256
+// registers), with the scale kept at least FLT_MIN so that a masked -inf
+// stays -inf (a zero scale then still gives equal weights: the scaled
+// scores round to 0).
+template <int NS, bool kMayBeEmpty, bool kOneRounding>
 __device__ __attribute__((always_inline)) inline void pair_update_sets(const TileReads& ra, const TileReads& rb,
                                                                        const bf16x8_t (&qv)[NS][4],
-                                                                       f32x4_t (&acc)[NS][8], float (&m)[NS],
-                                                                       float (&l)[NS], const int (&vqa)[NS],
-                                                                       const int (&vqb)[NS], float scale_log2,
-                                                                       int n16, int c4, bool mask) {
+                                                                       f32x4_t (&acc)[NS][8], f32x4_t (&lacc)[NS],
+                                                                       float (&m)[NS], float (&l)[NS],
+                                                                       const int (&vqa)[NS], const int (&vqb)[NS],
+                                                                       float scale_log2, int n16, int c4, bool mask) {
+  wave_lds_order();  // both tiles' K and V are in LDS
   f32x4_t sa[NS], sb[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     sa[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     sb[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  // V^T operand jj: dims 16*jj .. +15 by the 32 slots.
+  constexpr bool kEarlyV = !kOneRounding;
+  auto read_vt = [&](int jj) {
+    const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(ra.v + 16 * ra.vchunk(jj)));
+    const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(rb.v + 16 * rb.vchunk(jj)));
+    return __builtin_bit_cast(bf16x8_t, make_uint4(__builtin_bit_cast(uint2, va).x, __builtin_bit_cast(uint2, va).y,
+                                                   __builtin_bit_cast(uint2, vb).x, __builtin_bit_cast(uint2, vb).y));
+  };
+  bf16x8_t vt[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const u32x4_t ka = *reinterpret_cast<const PA_LDS u32x4_t*>(ra.k + 16 * k_pos(4 * i + c4, n16));
     const u32x4_t kb = *reinterpret_cast<const PA_LDS u32x4_t*>(rb.k + 16 * k_pos(4 * i + c4, n16));
+    if constexpr (kEarlyV) {
+      vt[2 * i] = read_vt(2 * i);
+      vt[2 * i + 1] = read_vt(2 * i + 1);
+    }
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       sa[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qv[j][i], sa[j], 0, 0, 0);
       sb[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb), qv[j][i], sb[j], 0, 0, 0);
     }
   }
+
   bf16x8_t phi[NS], plo[NS];
-  auto weights = [&](int j, const float (&pw)[8]) {
-    uint32_t h[4], lo[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) split_pair_rn(pw[2 * q], pw[2 * q + 1], h[q], lo[q]);
-    phi[j] = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
-    plo[j] = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
-  };
-  if (mask) {
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      float sv[8], pw[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sv[r] = (4 * c4 + r < vqa[j]) ? sa[j][r] * scale_log2 : kNegInf;
-        sv[4 + r] = (4 * c4 + r < vqb[j]) ? sb[j][r] * scale_log2 : kNegInf;
-      }
-      softmax_core<8, kMayBeEmpty>(sv, acc[j], m[j], l[j], c4, pw);
-      weights(j, pw);
-    }
-  } else {
+  float alpha[NS];
+  bool move[NS];
+  if constexpr (kOneRounding) {
+    const float c = fmaxf(scale_log2, __FLT_MIN__);
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
       float sv[8], pw[8];
@@ -357,104 +389,88 @@ __device__ __attribute__((always_inline)) inline void pair_update_sets(const Til
       for (int r = 0; r < 4; ++r) {
         sv[r] = sa[j][r];
         sv[4 + r] = sb[j][r];
+        if (mask) {
+          sv[r] = (4 * c4 + r < vqa[j]) ? sv[r] : kNegInf;
+          sv[4 + r] = (4 * c4 + r < vqb[j]) ? sv[4 + r] : kNegInf;
+        }
       }
-      softmax_core<8, false, true, true>(sv, acc[j], m[j], l[j], c4, pw, nullptr, scale_log2);
-      weights(j, pw);
+      float unused = 0.f;
+      alpha[j] = softmax_weights<8, kMayBeEmpty, false, true>(sv, m[j], unused, pw, move[j], c);
+      phi[j] = __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16_rn(pw[0], pw[1]), pack_bf16_rn(pw[2], pw[3]),
+                                                       pack_bf16_rn(pw[4], pw[5]), pack_bf16_rn(pw[6], pw[7])));
     }
-  }
-
-  wave_lds_order();  // both tiles' V are in LDS
+  } else {
+    auto weights = [&](int j, const float (&pw)[8]) {
+      uint32_t h[4], lo[4];
 #pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    const int ca = ra.vchunk(jj);
-    const int cb = rb.vchunk(jj);
-    const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(ra.v + 16 * ca));
-    const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(rb.v + 16 * cb));
-    const bf16x8_t v8 = __builtin_bit_cast(
-        bf16x8_t, make_uint4(__builtin_bit_cast(uint2, va).x, __builtin_bit_cast(uint2, va).y,
-                             __builtin_bit_cast(uint2, vb).x, __builtin_bit_cast(uint2, vb).y));
+      for (int q = 0; q < 4; ++q) split_pair_rn(pw[2 * q], pw[2 * q + 1], h[q], lo[q]);
+      phi[j] = __builtin_bit_cast(bf16x8_t, make_uint4(h[0], h[1], h[2], h[3]));
+      plo[j] = __builtin_bit_cast(bf16x8_t, make_uint4(lo[0], lo[1], lo[2], lo[3]));
+    };
+    if (mask) {
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      acc[j][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi[j], v8, acc[j][jj], 0, 0, 0);
-      acc[j][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo[j], v8, acc[j][jj], 0, 0, 0);
-    }
-  }
-}
-
-// The pair step with p rounded once to bf16 (to nearest) and the softmax
-// denominator summed by the matrix core from the same rounded weights:
-// lacc[j][r] = the sum over slots of p~ of column 4*c4 + r, one extra
-// 16x16x32 MFMA per pair against a B operand of ones, in the accumulator
-// layout of o.  o / l is then an exact weighted mean of V with weights
-// p~ / sum p~, each p~ within 2^-9 of p relative, and rounding to nearest
-// leaves no common sign to the errors, so they partly cancel over the
-// history.  q.k, the mask and the reference max are as in pair_update_sets;
-// p.v and l take 9 MFMAs per set instead of 16, with no split of p.
-
-template <int NS, bool kMayBeEmpty>
-__device__ __attribute__((always_inline)) inline void pair_update_sets_rn(const TileReads& ra, const TileReads& rb,
-                                                                          const bf16x8_t (&qv)[NS][4],
-                                                                          f32x4_t (&acc)[NS][8], f32x4_t (&lacc)[NS],
-                                                                          float (&m)[NS], const int (&vqa)[NS],
-                                                                          const int (&vqb)[NS], float scale_log2,
-                                                                          int n16, int c4, bool mask) {
-  f32x4_t sa[NS], sb[NS];
+      for (int j = 0; j < NS; ++j) {
+        float sv[8], pw[8];
 #pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    sa[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    sb[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+        for (int r = 0; r < 4; ++r) {
+          sv[r] = (4 * c4 + r < vqa[j]) ? sa[j][r] * scale_log2 : kNegInf;
+          sv[4 + r] = (4 * c4 + r < vqb[j]) ? sb[j][r] * scale_log2 : kNegInf;
+        }
+        alpha[j] = softmax_weights<8, kMayBeEmpty>(sv, m[j], l[j], pw, move[j]);
+        weights(j, pw);
+      }
+    } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const u32x4_t ka = *reinterpret_cast<const PA_LDS u32x4_t*>(ra.k + 16 * k_pos(4 * i + c4, n16));
-    const u32x4_t kb = *reinterpret_cast<const PA_LDS u32x4_t*>(rb.k + 16 * k_pos(4 * i + c4, n16));
+      for (int j = 0; j < NS; ++j) {
+        float sv[8], pw[8];
 #pragma unroll
-    for (int j = 0; j < NS; ++j) {
-      sa[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka), qv[j][i], sa[j], 0, 0, 0);
-      sb[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb), qv[j][i], sb[j], 0, 0, 0);
-    }
-  }
-  // One softmax form here (the mask applied by selects where needed): two
-  // forms, as in pair_update_sets, took this kernel past 256 registers.  The
-  // scores go in unscaled (softmax_core's kRaw), with the scale kept at least
-  // FLT_MIN so that a masked -inf stays -inf (a zero scale then still gives
-  // equal weights: the scaled scores round to 0).
-  const float c = fmaxf(scale_log2, __FLT_MIN__);
-  bf16x8_t pr[NS];
-#pragma unroll
-  for (int j = 0; j < NS; ++j) {
-    float sv[8];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sv[r] = sa[j][r];
-      sv[4 + r] = sb[j][r];
-      if (mask) {
-        sv[r] = (4 * c4 + r < vqa[j]) ? sv[r] : kNegInf;
-        sv[4 + r] = (4 * c4 + r < vqb[j]) ? sv[4 + r] : kNegInf;
+        for (int r = 0; r < 4; ++r) {
+          sv[r] = sa[j][r];
+          sv[4 + r] = sb[j][r];
+        }
+        alpha[j] = softmax_weights<8, false, true, true>(sv, m[j], l[j], pw, move[j], scale_log2);
+        weights(j, pw);
       }
     }
-    float pw[8];
-    float unused = 0.f;
-    softmax_core<8, kMayBeEmpty, false, true>(sv, acc[j], m[j], unused, c4, pw, &lacc[j], c);
-    pr[j] = __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16_rn(pw[0], pw[1]), pack_bf16_rn(pw[2], pw[3]),
-                                                    pack_bf16_rn(pw[4], pw[5]), pack_bf16_rn(pw[6], pw[7])));
   }
-  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
-#pragma unroll
-  for (int j = 0; j < NS; ++j) lacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pr[j], ones, lacc[j], 0, 0, 0);
 
-  wave_lds_order();  // both tiles' V are in LDS
+  auto products = [&] {
+    if constexpr (kOneRounding) {
+      const bf16x8_t ones =
+          __builtin_bit_cast(bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
 #pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    const int ca = ra.vchunk(jj);
-    const int cb = rb.vchunk(jj);
-    const s16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(ra.v + 16 * ca));
-    const s16x4_t vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PA_LDS s16x4_t*)(rb.v + 16 * cb));
-    const bf16x8_t v8 = __builtin_bit_cast(
-        bf16x8_t, make_uint4(__builtin_bit_cast(uint2, va).x, __builtin_bit_cast(uint2, va).y,
-                             __builtin_bit_cast(uint2, vb).x, __builtin_bit_cast(uint2, vb).y));
+      for (int j = 0; j < NS; ++j) lacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, phi[j], lacc[j], 0, 0, 0);
+    }
 #pragma unroll
-    for (int j = 0; j < NS; ++j) acc[j][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pr[j], v8, acc[j][jj], 0, 0, 0);
+    for (int jj = 0; jj < 8; ++jj) {
+      if constexpr (!kEarlyV) vt[jj] = read_vt(jj);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        acc[j][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[jj], phi[j], acc[j][jj], 0, 0, 0);
+        if constexpr (!kOneRounding)
+          acc[j][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[jj], plo[j], acc[j][jj], 0, 0, 0);
+      }
+    }
+  };
+  bool moved = false;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) moved = moved || move[j];
+  auto rescale = [&] {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) acc[j][jj] *= alpha[j];
+      if constexpr (kOneRounding) lacc[j] *= alpha[j];
+    }
+  };
+  if constexpr (kOneRounding) {
+    if (__any(moved)) rescale();
+    products();
+  } else if (__any(moved)) {
+    rescale();
+    products();
+  } else {
+    products();
   }
 }
 

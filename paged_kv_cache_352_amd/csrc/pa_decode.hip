@@ -353,33 +353,63 @@ __global__ __launch_bounds__(kWave * W) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// Merge of the split states of one (request, query head):
+// Merge of the split states of one (request, query token, head) per half
+// wave:
 //   M = max_p m_p, L = sum_p 2^(m_p - M) l_p, O = sum_p 2^(m_p - M) o_p, out = O / L.
-// Empty splits carry m = -inf, l = 0 and drop out; all empty gives 0.
-__global__ __launch_bounds__(kWave) void decode_merge_kernel(DecodeArgs a) {
-  const int sh = blockIdx.x;  // (s * T + t) * Hq + h
-  const int lane = threadIdx.x;
-  const float* ms = a.ws_m + (int64_t)sh * a.P;
-  const float* ls = a.ws_l + (int64_t)sh * a.P;
-  float M = kNegInf;
-  for (int p = 0; p < a.P; ++p) M = fmaxf(M, ms[p]);
-  float* dst = a.out + (int64_t)sh * kHeadDim + lane * 2;
-  if (M == kNegInf) {
-    dst[0] = 0.f;
-    dst[1] = 0.f;
-    return;
-  }
-  float L = 0.f, o0 = 0.f, o1 = 0.f;
-  const float* os = a.ws_o + (int64_t)sh * a.P * kHeadDim + lane * 2;
-  for (int p = 0; p < a.P; ++p) {
-    const float w = fast_exp2(ms[p] - M);
-    L = fmaf(w, ls[p], L);
-    o0 = fmaf(w, os[p * kHeadDim], o0);
-    o1 = fmaf(w, os[p * kHeadDim + 1], o1);
+// Empty splits carry m = -inf, l = 0 and drop out; all empty gives 0.  Each
+// lane takes four consecutive dims (16-byte loads and stores), a workgroup
+// of four waves takes kMergeRows rows.  With kP > 0 (exactly kP splits)
+// every load of the row is issued before the first is used, so a row costs
+// one trip to memory instead of one per split; kP = 0 takes any count.  The
+// arithmetic is the same in both forms, in split order.
+constexpr int kMergeRows = 8;
+template <int kP>
+__global__ __launch_bounds__(kWave * 4) void decode_merge_kernel(DecodeArgs a) {
+  const int64_t rows = (int64_t)a.S * a.T * a.Hq;
+  const int64_t sh = (int64_t)blockIdx.x * kMergeRows + (threadIdx.x >> 5);  // (s * T + t) * Hq + h
+  if (sh >= rows) return;
+  const int lane = threadIdx.x & 31;
+  const int P = kP > 0 ? kP : a.P;
+  const float* ms = a.ws_m + sh * P;
+  const float* ls = a.ws_l + sh * P;
+  const float4* os = reinterpret_cast<const float4*>(a.ws_o + sh * P * kHeadDim) + lane;
+  float4* dst = reinterpret_cast<float4*>(a.out + sh * kHeadDim) + lane;
+  float M = kNegInf, L = 0.f;
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto fold = [&](float w, float lp, const float4& v) {
+    L = fmaf(w, lp, L);
+    o.x = fmaf(w, v.x, o.x);
+    o.y = fmaf(w, v.y, o.y);
+    o.z = fmaf(w, v.z, o.z);
+    o.w = fmaf(w, v.w, o.w);
+  };
+  if constexpr (kP > 0) {
+    float mv[kP], lv[kP];
+    float4 ov[kP];
+#pragma unroll
+    for (int p = 0; p < kP; ++p) {
+      mv[p] = ms[p];
+      lv[p] = ls[p];
+      ov[p] = os[p * (kHeadDim / 4)];
+    }
+#pragma unroll
+    for (int p = 0; p < kP; ++p) M = fmaxf(M, mv[p]);
+    if (M == kNegInf) {
+      *dst = make_float4(0.f, 0.f, 0.f, 0.f);
+      return;
+    }
+#pragma unroll
+    for (int p = 0; p < kP; ++p) fold(fast_exp2(mv[p] - M), lv[p], ov[p]);
+  } else {
+    for (int p = 0; p < P; ++p) M = fmaxf(M, ms[p]);
+    if (M == kNegInf) {
+      *dst = make_float4(0.f, 0.f, 0.f, 0.f);
+      return;
+    }
+    for (int p = 0; p < P; ++p) fold(fast_exp2(ms[p] - M), ls[p], os[p * (kHeadDim / 4)]);
   }
   const float inv = 1.f / L;
-  dst[0] = o0 * inv;
-  dst[1] = o1 * inv;
+  *dst = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
 }
 
 template <typename T, int G, bool kCausal, int B>
@@ -432,7 +462,14 @@ hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int B, int G, hipS
   else
     e = causal ? launch_valu<true>(a, B, G, stream) : launch_valu<false>(a, B, G, stream);
   if (e != hipSuccess || a.P == 1) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(a.S * a.T * a.Hq), dim3(kWave), 0, stream, a);
+  const int64_t rows = (int64_t)a.S * a.T * a.Hq;
+  const dim3 grid((unsigned)((rows + kMergeRows - 1) / kMergeRows)), block(kWave * 4);
+  switch (a.P) {
+    case 2: hipLaunchKernelGGL(decode_merge_kernel<2>, grid, block, 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(decode_merge_kernel<3>, grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(decode_merge_kernel<4>, grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL(decode_merge_kernel<0>, grid, block, 0, stream, a); break;
+  }
   return hipGetLastError();
 }
 

@@ -401,11 +401,13 @@ __global__ __launch_bounds__(kWave * 4) void decode_merge_kernel(DecodeArgs a) {
 #pragma unroll
     for (int p = 0; p < kP; ++p) fold(fast_exp2(mv[p] - M), lv[p], ov[p]);
   } else {
+#pragma unroll 8
     for (int p = 0; p < P; ++p) M = fmaxf(M, ms[p]);
     if (M == kNegInf) {
       *dst = make_float4(0.f, 0.f, 0.f, 0.f);
       return;
     }
+#pragma unroll 4
     for (int p = 0; p < P; ++p) fold(fast_exp2(ms[p] - M), ls[p], os[p * (kHeadDim / 4)]);
   }
   const float inv = 1.f / L;

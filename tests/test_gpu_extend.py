@@ -71,13 +71,16 @@ def test_bf16_one_item_per_group(T):
 
 @pytest.mark.parametrize("G,T", [(4, 7), (4, 16), (1, 17), (1, 40), (16, 3), (8, 5), (2, 9),
                                  (4, 40), (16, 9), (2, 70), (8, 33), (4, 17), (4, 24), (2, 36), (1, 65),
-                                 (4, 33), (1, 150)])
+                                 (4, 33), (1, 150), (4, 12), (4, 70)])
 def test_bf16_several_items_per_group(G, T):
     """Separate items per column set up to two sets; the shared-tile kernel above,
     with one 16-column set per wave, or two once one set per wave would need a
     second workgroup (then some waves may hold no live column); past 128 columns
     the 8-wave ping-pong form (4 x 33: 132 columns, one live column past the
-    first four waves; 1 x 150: 32 tokens per wave)."""
+    first four waves; 1 x 150: 32 tokens per wave).  Waves whose tokens all lie
+    past T skip their arithmetic: 4 x 12 (the 16-column kernel's last wave),
+    4 x 24 (the 32-column kernel's), 4 x 70 (the ping-pong kernel's second
+    workgroup, live in wave 0 only, idle waves in both phase groups)."""
     banner(f"extend bf16 G={G} T={T} ragged")
     b = W.extend_batch(RAGGED, T, Hq=2 * G, Hkv=2, seed=20 + G + T, device=DEV)
     check(b, torch.bfloat16, f"bf16 G={G} T={T}")

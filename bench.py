@@ -255,7 +255,7 @@ def suite(torch, pa, W, dev):
                 if fused:  # the step's one append round inside the decode launch
                     pa.paged_attn_decode_append(b.q[layer], b.k_pool[layer], b.v_pool[layer], b.k_new[0, layer],
                                                 b.v_new[0, layer], b.block_tables, b.append_positions[0],
-                                                b.seq_lens, b.B, b.scale, out=outs[layer], workspace=ws)
+                                                b.seq_lens, b.B, b.scale, out=outs[layer], workspace=ws, order=order)
                     continue
                 for r in range(b.rounds):
                     pa.kv_append(b.k_pool[layer], b.v_pool[layer], b.k_new[r, layer], b.v_new[r, layer],
@@ -386,9 +386,11 @@ def suite(torch, pa, W, dev):
             order = pa.paged_attn_order(b.seq_lens)
             us_o, _ = decode_graph(b, layers, order=order)
             ent["longest_first"] = dict(rate(kvb, us_o), tokens_per_s_per_layer=round(b.S / (us_o * 1e-6), 1),
+                                        full_step_fused_us=round(full_step_graph(b, fused=True, ordered=True), 2),
                                         full_step_append_layers_us=round(
                                             full_step_graph(b, all_layers=True, ordered=True), 2),
-                                        ops="paged_attn_order once, one kv_append_layers, one decode per layer "
+                                        ops="paged_attn_order once, then one paged_attn_decode_append per layer "
+                                            "(fused) or one kv_append_layers and one decode per layer, all "
                                             "with dims->order")
             ent["swap_500MiB"] = swap_time(torch, pa, b, dev)
         if name.startswith("bf16 prefix"):
@@ -426,10 +428,12 @@ def suite_markdown(S, command):
     lf = e.get("longest_first")
     if lf:
         w(f"| bf16 256 mixed-length requests, 32 layers, issued longest first | {lf['us']:.3f} | {lf['bytes']:,} | {lf['GB_s']:.1f} | "
-          f"{100*lf['frac_hbm_peak']:.1f} % | {e['splits']} |  |  | {lf['full_step_append_layers_us']} | {lf['tokens_per_s_per_layer']:.0f} |")
+          f"{100*lf['frac_hbm_peak']:.1f} % | {e['splits']} |  | {lf.get('full_step_fused_us', '')} | "
+          f"{lf['full_step_append_layers_us']} | {lf['tokens_per_s_per_layer']:.0f} |")
         w("\nLongest first: one paged_attn_order per step (its order serves all 32 layers), then each")
-        w("decode with dims->order; the full step there is paged_attn_order, one kv_append_layers and the")
-        w("32 decodes.  Outputs are bitwise those of request order (tests/test_gpu_order.py).")
+        w("decode with dims->order; the fused step there is paged_attn_order and one")
+        w("paged_attn_decode_append per layer, the all-layer one paged_attn_order, one kv_append_layers")
+        w("and the 32 decodes.  Outputs are bitwise those of request order (tests/test_gpu_order.py).")
     w("\nThe prefix-sharing row reads the 128 shared prefix blocks 64 times, from cache after the first:")
     w("its logical rate is not an HBM figure (decode_mfma_bf16_workload_traffic.md gives its DRAM bytes).")
     w("The fp32 row is 2 MB of history: launch latency, not bandwidth.\n")

@@ -333,15 +333,21 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
       const int r = 4 * i + c4;
       uint4 kk = cur.k[i];
       uint4 vv = cur.v[i];
-      if constexpr (kAppend) {
-        if (u * kTile + r == pos) {  // the token this step appends
-          kk = k_in;
-          vv = v_in;
-        }
-      }
       if (r >= valid) vv = make_uint4(0, 0, 0, 0);
       *reinterpret_cast<uint4*>(kt + 256 * r + 16 * k_pos(n16, r)) = kk;
       *reinterpret_cast<uint4*>(vt + 256 * r + 16 * v_pos(n16, r)) = vv;
+    }
+    if constexpr (kAppend) {
+      // The token this step appends: its row of the tile holding pos (the
+      // same test in every lane) is written over with the new K and V, by
+      // the 16 lanes that wrote that row; V stays zero past the length.
+      const int r = pos - u * kTile;
+      if (r >= 0 && r < kTile) {
+        if (c4 == (r & 3)) {
+          *reinterpret_cast<uint4*>(kt + 256 * r + 16 * k_pos(n16, r)) = k_in;
+          if (r < valid) *reinterpret_cast<uint4*>(vt + 256 * r + 16 * v_pos(n16, r)) = v_in;
+        }
+      }
     }
     wave_lds_order();
     // Mask past the length or, for several query tokens, past this column's

@@ -331,11 +331,17 @@ __global__ __launch_bounds__(kWave * W) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * i + c4;
-      uint4 kk = cur.k[i];
-      uint4 vv = cur.v[i];
-      if (r >= valid) vv = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(kt + 256 * r + 16 * k_pos(n16, r)) = kk;
-      *reinterpret_cast<uint4*>(vt + 256 * r + 16 * v_pos(n16, r)) = vv;
+      *reinterpret_cast<uint4*>(kt + 256 * r + 16 * k_pos(n16, r)) = cur.k[i];
+      *reinterpret_cast<uint4*>(vt + 256 * r + 16 * v_pos(n16, r)) = cur.v[i];
+    }
+    // V rows past the length are zeroed (their weights are 0, but 0 * NaN
+    // would not be): only in the history's last tile, the same in every lane.
+    if (valid < kTile) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + c4;
+        if (r >= valid) *reinterpret_cast<uint4*>(vt + 256 * r + 16 * v_pos(n16, r)) = make_uint4(0, 0, 0, 0);
+      }
     }
     if constexpr (kAppend) {
       // The token this step appends: its row of the tile holding pos (the

@@ -158,7 +158,9 @@ static pa_status plan_common(const pa_dims* dims, int32_t B, int32_t T, int32_t*
   int P, tps;
   plan_splits(dims, B, T, &P, &tps);
   *num_splits = P;
-  const int Pm = pa::merged_splits(dims->dtype, P);
+  const int Pm = pa::shared_tile_halves(dims->dtype, dims->num_q_heads / dims->num_kv_heads, T, P)
+                     ? 1
+                     : pa::merged_splits(dims->dtype, P);
   *workspace_bytes =
       (Pm > 1 && dims->num_seqs > 0)
           ? pa::decode_workspace_floats((int64_t)dims->num_seqs * T * dims->num_q_heads, Pm) * sizeof(float)
@@ -223,7 +225,7 @@ static pa_status attend(const void* q, const void* k_pool, const void* v_pool, c
       a.positions = positions;
     }
   }
-  if (a.P > 1) {
+  if (a.P > 1 && !pa::shared_tile_halves(dims->dtype, a.Hq / a.Hkv, T, a.P)) {
     const size_t need = pa::decode_workspace_floats(rows, a.P) * sizeof(float);
     if (!dims->workspace || dims->workspace_bytes < need)
       return fail(PA_ERR_WORKSPACE, "split-K needs %zu workspace bytes, got %zu", need,

@@ -457,9 +457,10 @@ hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int B, int G, hipS
   // bf16: q.k and p.v on the matrix cores; fp32: the vector-ALU kernel.
   const bool causal = a.T > 1;
   hipError_t e;
-  if (use_shared_tile(dtype, G, a.T))
+  if (use_shared_tile(dtype, G, a.T)) {
     e = launch_extend_shared(a, B, G, stream);
-  else if (dtype == PA_BF16)
+    if (shared_tile_halves(dtype, G, a.T, a.P)) return e;  // the two splits merged in the kernel
+  } else if (dtype == PA_BF16)
     e = launch_decode_mfma(a, B, G, causal, stream);
   else
     e = causal ? launch_valu<true>(a, B, G, stream) : launch_valu<false>(a, B, G, stream);

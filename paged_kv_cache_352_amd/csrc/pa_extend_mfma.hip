@@ -32,7 +32,8 @@
 // one barrier per pair suffices: a wave overwrites buffer b only after the
 // barrier of the next pair, which no wave passes before it has finished
 // reading b.  Each wave owns its columns, so no state is merged inside the
-// workgroup.
+// workgroup, except in the two-split form (kHalves below), whose two 4-wave
+// halves walk one split each and merge their states at the end.
 //
 // The weights p enter p.v in one of two forms.  By default each is a bf16
 // head plus a bf16 remainder, both rounded to nearest, through two MFMAs
@@ -57,26 +58,42 @@ constexpr int kDepth = 2;  // tile pairs in flight per wave (this lane's K and V
 // LDS feeds all of them.  kOneRounding: p rounded once to bf16 and l summed
 // on the matrix core from the rounded weights (PA_FLAG_BF16_WEIGHTS), else p
 // as a bf16 head plus remainder and l summed in fp32 by the vector ALU.
-template <int G, int kSets, int B, bool kOneRounding, bool kStream>
-__global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(DecodeArgs a) {
+// kHalves (two splits, one set per wave): one workgroup of 8 waves takes
+// both splits of its (request, KV head), waves 0-3 the first and 4-7 the
+// second, each half with its own LDS tiles; both pass the same barriers, and
+// at the end the second half hands its state to the first through LDS, which
+// merges the two as the merge kernel would (the same arithmetic, in split
+// order, so the output is bitwise that of two workgroups and the merge
+// kernel) and writes the output.  Against two workgroups of 4 waves on a CU
+// it saves the partial states' round trip through memory and the merge
+// kernel's launch.
+template <int G, int kSets, int B, bool kOneRounding, bool kStream, bool kHalves = false>
+__global__ __launch_bounds__(kWave * kWaves * (kHalves ? 2 : 1), kHalves ? 1 : 2) void extend_shared_kernel(DecodeArgs a) {
+  static_assert(!kHalves || (kSets == 1 && kStream), "halves: one set per wave, one workgroup per request");
   static_assert(G >= 1 && G <= 16, "the query group must fit the 16 columns of one MFMA tile");
   static_assert(B >= 4 && B <= 64 && (B & (B - 1)) == 0, "block size: a power of two from 4 to 64");
   constexpr int TC = G >= 16 ? 1 : 16 / G;  // query tokens per 16-column set
   constexpr int TS = kSets * TC;            // query tokens per wave
   constexpr int TW = kWaves * TS;           // query tokens per workgroup
-  // [buffer][tile a, tile b][K, V][tile bytes]
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[2][2][2][kVtBytes];
+  // [half][buffer][tile a, tile b][K, V][tile bytes]
+  __shared__ __attribute__((aligned(16))) uint8_t tiles_all[kHalves ? 2 : 1][2][2][2][kVtBytes];
 
   const int lane = threadIdx.x & (kWave - 1);
   // The wave index, in a scalar register: the compiler cannot see that it is
   // uniform, and block offsets and table lanes derived from it must be scalar.
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wt = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int grp = kHalves ? wt / kWaves : 0;  // kHalves: waves 0-3 take split 0, waves 4-7 split 1
+  const int w = kHalves ? wt % kWaves : wt;
+  auto& tiles = tiles_all[grp];
   const int n16 = lane & 15;
   const int c4 = lane >> 4;
 
   int item = xcd_remap(blockIdx.x, gridDim.x);
-  const int p = item % a.P;
-  item /= a.P;
+  int p = grp;
+  if constexpr (!kHalves) {
+    p = item % a.P;
+    item /= a.P;
+  }
   const int tw = item % a.TG;  // which TW query tokens of the request
   item /= a.TG;
   const int s = item % a.S;
@@ -207,7 +224,7 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(Decode
     *reinterpret_cast<uint4*>(base + 3 * kVtBytes + wv_off) =
         r_own < n - tb_loaded * kTile ? r.vb : make_uint4(0, 0, 0, 0);
     __syncthreads();
-    if (idle) return;
+    if (idle || t >= te) return;
     TileReads ra = rd0, rb = rd0;
     ra.k += buf * (4 * kVtBytes);
     ra.v += buf * (4 * kVtBytes);
@@ -235,22 +252,51 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(Decode
   // the next pair is requested before the current one is used.
   constexpr int kChunkTiles = B >= kTile ? kWave : 4 * B;
   static_assert(kChunkTiles % 2 == 0, "pairs of tiles stay inside one chunk");
-  for (int tb = u0; tb < u1; tb += kChunkTiles) {
-    const int te = min(u1, tb + kChunkTiles);
-    const int eb = (kTile * tb) / B;
-    const int tab = trow[min(eb + lane, nb - 1)];
-    Rows ring[kDepth];
+  if constexpr (kHalves) {
+    // Both halves pass the same barriers: chunks and pairs are counted on the
+    // first split's range (never shorter than the second's); a half past its
+    // own range loads nothing (size-0 descriptors) and skips the arithmetic.
+    const int c_u1 = min(nt, a.tps / kTile);
+    for (int cb = 0; cb < c_u1; cb += kChunkTiles) {
+      const int tb = u0 + cb;
+      const int te = min(u1, tb + kChunkTiles);  // te <= tb: nothing of this half's own
+      const int ce = min(c_u1, cb + kChunkTiles) - cb;
+      const int eb = (kTile * tb) / B;
+      const int tab = tb < te ? trow[min(eb + lane, nb - 1)] : 0;
+      Rows ring[kDepth];
 #pragma unroll
-    for (int b = 0; b + 1 < kDepth; ++b) load_pair(min(tb + 2 * b, te - 1), ring[b], eb, tab, te, tb + 2 * b >= te);
-    for (int t = tb; t < te; t += 2 * kDepth) {
+      for (int b = 0; b + 1 < kDepth; ++b)
+        load_pair(max(tb, min(tb + 2 * b, te - 1)), ring[b], eb, tab, te, tb + 2 * b >= te);
+      for (int t = 0; t < ce; t += 2 * kDepth) {
 #pragma unroll
-      for (int b = 0; b < kDepth; ++b) {
-        constexpr int kNext = kDepth - 1;
-        const int tn = t + 2 * (b + kNext);  // the pair to prefetch; past the chunk: loads that fetch nothing
-        load_pair(min(tn, te - 1), ring[(b + kNext) % kDepth], eb, tab, te, tn >= te);
-        __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the current pair's math
-        process(t + 2 * b, ring[b], te);
-        if (t + 2 * b + 2 >= te) break;
+        for (int b = 0; b < kDepth; ++b) {
+          constexpr int kNext = kDepth - 1;
+          const int tn = tb + t + 2 * (b + kNext);
+          load_pair(max(tb, min(tn, te - 1)), ring[(b + kNext) % kDepth], eb, tab, te, tn >= te);
+          __builtin_amdgcn_sched_barrier(0);
+          process(tb + t + 2 * b, ring[b], te);
+          if (t + 2 * b + 2 >= ce) break;
+        }
+      }
+    }
+  } else {
+    for (int tb = u0; tb < u1; tb += kChunkTiles) {
+      const int te = min(u1, tb + kChunkTiles);
+      const int eb = (kTile * tb) / B;
+      const int tab = trow[min(eb + lane, nb - 1)];
+      Rows ring[kDepth];
+#pragma unroll
+      for (int b = 0; b + 1 < kDepth; ++b) load_pair(min(tb + 2 * b, te - 1), ring[b], eb, tab, te, tb + 2 * b >= te);
+      for (int t = tb; t < te; t += 2 * kDepth) {
+#pragma unroll
+        for (int b = 0; b < kDepth; ++b) {
+          constexpr int kNext = kDepth - 1;
+          const int tn = t + 2 * (b + kNext);  // the pair to prefetch; past the chunk: loads that fetch nothing
+          load_pair(min(tn, te - 1), ring[(b + kNext) % kDepth], eb, tab, te, tn >= te);
+          __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the current pair's math
+          process(t + 2 * b, ring[b], te);
+          if (t + 2 * b + 2 >= te) break;
+        }
       }
     }
   }
@@ -270,6 +316,59 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_shared_kernel(Decode
   bad = __syncthreads_or(bad);  // any wave that met an entry outside the pool
 
   const float nan = __builtin_nanf("");
+  if constexpr (kHalves) {
+    // The second half's state goes to the first through LDS, lane for lane
+    // (both halves hold the same columns in the same lanes), into the tiles'
+    // space, free after the barrier above.  The first half merges the two
+    // as the merge kernel does (M, then 2^(m_p - M) weights folded in split
+    // order, o * (1 / L); an entry outside the pool gives NaN) and writes
+    // the output.
+    constexpr int kSlot = 2 + 32;  // m, l and o^T of one lane
+    static_assert(kWaves * kWave * kSlot * 4 <= (int)sizeof(tiles_all), "the handed-over states fit the tiles");
+    float* xs = reinterpret_cast<float*>(&tiles_all[0][0][0][0][0]);
+    const int slot = (w * kWave + lane) * kSlot;
+    if (grp == 1) {
+      xs[slot] = m[0];
+      xs[slot + 1] = lc[0];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xs[slot + 2 + 4 * jj + r] = acc[0][jj][r];
+    }
+    __syncthreads();
+    if (grp == 0 && tq[0] < a.T) {
+      const float mv[2] = {bad ? 0.f : m[0], bad ? 0.f : xs[slot]};
+      const float lv[2] = {bad ? nan : lc[0], bad ? nan : xs[slot + 1]};
+      float M = kNegInf;
+      M = fmaxf(M, mv[0]);
+      M = fmaxf(M, mv[1]);
+      const int64_t row = ((int64_t)s * a.T + tq[0]) * a.Hq + kvh * G + n16 % G;
+      float* dst = a.out + row * kHeadDim + 4 * c4;
+      if (M == kNegInf) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) *reinterpret_cast<f32x4_t*>(dst + 16 * jj) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      } else {
+        const float w0 = fast_exp2(mv[0] - M), w1 = fast_exp2(mv[1] - M);
+        float L = 0.f;
+        L = fmaf(w0, lv[0], L);
+        L = fmaf(w1, lv[1], L);
+        const float inv = 1.f / L;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          f32x4_t o;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float x = 0.f;
+            x = fmaf(w0, acc[0][jj][r], x);
+            x = fmaf(w1, xs[slot + 2 + 4 * jj + r], x);
+            o[r] = x * inv;
+          }
+          *reinterpret_cast<f32x4_t*>(dst + 16 * jj) = o;
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < kSets; ++j) {
     if (tq[j] >= a.T) continue;
@@ -301,6 +400,11 @@ void launch_gbr(const DecodeArgs& a, hipStream_t stream) {
   // One column set per wave is chosen only while one workgroup holds all T
   // tokens (a.TG == 1); two sets per wave go to the 32-column kernel
   // (pa_extend_wide.hip) instead.
+  if (shared_tile_halves(PA_BF16, G, a.T, a.P)) {
+    hipLaunchKernelGGL((extend_shared_kernel<G, 1, B, kOneRounding, true, true>), dim3(items / 2),
+                       dim3(2 * kWave * kWaves), 0, stream, a);
+    return;
+  }
   hipLaunchKernelGGL((extend_shared_kernel<G, 1, B, kOneRounding, true>), dim3(items), dim3(kWave * kWaves), 0,
                      stream, a);
 }

@@ -98,6 +98,14 @@ constexpr int decode_column_sets(pa_dtype dtype, int G, int T) {
   return dtype == PA_BF16 && T > tokens_per_wave(dtype, G) && !use_shared_tile(dtype, G, T) ? 2 : 1;
 }
 
+// A two-split plan of the one-set shared-tile kernel (one workgroup then
+// holds all T tokens of its (request, KV head)) runs as one workgroup of two
+// 4-wave halves, one per split, that merge their states in LDS at the end:
+// no partial state reaches the split workspace and no merge kernel runs.
+constexpr bool shared_tile_halves(pa_dtype dtype, int G, int T, int P) {
+  return use_shared_tile(dtype, G, T) && shared_tile_sets(dtype, G, T) == 1 && P == 2;
+}
+
 constexpr int kPingPongWaves = 8;  // waves of the ping-pong shared-tile kernel
 
 // bf16 query groups wider than one workgroup of four 32-column waves (more

@@ -207,6 +207,16 @@ def test_swap_rejects_bad_arguments(lib):
     assert lib.kv_swap_out(*args(n=0)) == OK  # nothing to do, nothing launched
 
 
+def shared_tile_halves(dt, G, T, P):
+    """Two splits of the one-set shared-tile kernel (bf16, more tokens than two
+    16-column sets hold, all of them in one 4-wave workgroup) run as one workgroup
+    of two halves that merge in LDS: no workspace."""
+    if dt != torch.bfloat16:
+        return False
+    per_wave = 1 if G >= 16 else 16 // G
+    return T > 2 * per_wave and T <= 4 * per_wave and P == 2
+
+
 def merged_splits(P, dt):
     """Partial states per output row that reach the split workspace: float32 runs
     groups of up to 4 splits (the next power of two) as the waves of one
@@ -224,9 +234,9 @@ def test_extend_plan_matches_decode_at_one_token_and_scales_workspace(lib):
                                (2, 8, 2, 4096, torch.float32)]:
         assert pa.paged_attn_extend_plan(S, Hq, Hkv, 128, MB, 10000, dt, 16, 1) == pa.paged_attn_plan(
             S, Hq, Hkv, 128, MB, 10000, dt, 16)
-        for T in (2, 4, 7, 33):
+        for T in (2, 4, 7, 16, 33):
             P, ws = pa.paged_attn_extend_plan(S, Hq, Hkv, 128, MB, 10000, dt, 16, T)
-            Pm = merged_splits(P, dt)
+            Pm = 1 if shared_tile_halves(dt, Hq // Hkv, T, P) else merged_splits(P, dt)
             assert P >= 1 and ws == (S * T * Hq * Pm * 130 * 4 if Pm > 1 else 0)
             # forced splits are honoured as in the one-token plan
             assert pa.paged_attn_extend_plan(S, Hq, Hkv, 128, MB, 10000, dt, 16, T, num_splits=2)[0] == min(2, MB)

@@ -405,3 +405,43 @@ def test_bad_lengths_and_out_of_pool_entries_poison_only_their_request(T):
         assert np.all(np.isnan(got[s_])), s_
     for s_ in (0, 4):
         assert_close(got[s_], ref[s_], torch.bfloat16, f"request {s_}")
+
+
+@pytest.mark.parametrize("T,B,bf16_weights", [(9, 16, False), (12, 16, True), (16, 16, False), (16, 4, False),
+                                              (16, 64, True)])
+def test_two_splits_as_one_workgroup_of_two_halves(T, B, bf16_weights):
+    """Two splits of the one-set shared-tile kernel run as one workgroup whose two
+    4-wave halves take a split each and merge in LDS: no workspace, no merge
+    kernel.  Requests shorter than a split leave the second half nothing of its
+    own (it still passes every barrier); lengths cross tile, block and split
+    boundaries."""
+    banner(f"extend two halves T={T} B={B} bf16_weights={bf16_weights}")
+    lens = [T, T + 5, 40, 300, 1000, 1031, 2049, 16 * 64 + 1]
+    b = W.extend_batch(lens, T, Hq=8, Hkv=2, B=B, seed=400 + T + B, device=DEV)
+    P, ws = pa.paged_attn_extend_plan(b.S, b.Hq, b.Hkv, b.D, b.MB, b.NB, b.dtype, b.B, T, num_splits=2)
+    assert (P, ws) == (2, 0)
+    check(b, torch.bfloat16, f"two halves T={T} B={B}", num_splits=2, bf16_weights=bf16_weights)
+
+
+def test_two_halves_poison_only_their_request():
+    """An out-of-pool entry in either split's range, a bad length: NaN for that
+    request only, through the halves' merge."""
+    banner("extend two halves bad inputs")
+    T = 16
+    lens = [1500, 1600, 1400, 1700, 1650]
+    b = W.extend_batch(lens, T, Hq=8, Hkv=2, seed=431, device=DEV)
+    host = HostExtend(b)
+    pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
+    ref = host.oracle()
+    tab = b.block_tables.clone()
+    tab[1, 3] = -9                 # in the first split
+    tab[2, 80] = b.NB + 5          # in the second split
+    ln = b.seq_lens.clone()
+    ln[3] = -1
+    out = pa.paged_attn_extend(b.q, b.k_pool, b.v_pool, tab, ln, b.B, b.scale, num_splits=2)
+    torch.cuda.synchronize()
+    got = host_f32(out)
+    for s_ in (1, 2, 3):
+        assert np.all(np.isnan(got[s_])), s_
+    for s_ in (0, 4):
+        assert_close(got[s_], ref[s_], torch.bfloat16, f"request {s_}")

@@ -71,27 +71,40 @@ constexpr int kStepBytes = kStep * kHeadDim * 2;  // one K or V step in LDS: 8 K
 // slots x 64 bytes, which then falls on every bank once per 32-byte half.
 __device__ inline int kw_pos(int k, int t) { return k ^ (t & 15); }
 
-template <int G, int B, bool kOneRounding, bool kStream>
-__global__ __launch_bounds__(kWave * kWaves, 2) void extend_wide_kernel(DecodeArgs a) {
+// kHalves (two splits): one workgroup of 8 waves takes both splits of its
+// (request, KV head), waves 0-3 the first and 4-7 the second, each half with
+// its own LDS steps and both passing the same barriers; at the end the second
+// half hands its state to the first, which merges the two as the merge
+// kernel would (bitwise the same result) and writes the output, so no
+// partial state goes through memory and no merge kernel runs.
+template <int G, int B, bool kOneRounding, bool kStream, bool kHalves = false>
+__global__ __launch_bounds__(kWave * kWaves * (kHalves ? 2 : 1), kHalves ? 1 : 2) void extend_wide_kernel(DecodeArgs a) {
+  static_assert(!kHalves || kStream, "halves: one workgroup per request");
   static_assert(G >= 1 && G <= 16, "32 columns hold 32/G whole query tokens");
   static_assert(B >= 4 && B <= 64 && (B & (B - 1)) == 0, "block size: a power of two from 4 to 64");
   constexpr int TC = 32 / G;        // query tokens per wave
   constexpr int TW = kWaves * TC;   // query tokens per workgroup
-  // [buffer][K, V][step bytes]
-  __shared__ __attribute__((aligned(16))) uint8_t steps[2][2][kStepBytes];
+  // [half][buffer][K, V][step bytes]
+  __shared__ __attribute__((aligned(16))) uint8_t steps_all[kHalves ? 2 : 1][2][2][kStepBytes];
 
   const int lane = threadIdx.x & (kWave - 1);
   // The wave index, in a scalar register (block offsets and table lanes
   // derived from it must be scalar).
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wt = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int grp = kHalves ? wt / kWaves : 0;  // kHalves: waves 0-3 take split 0, waves 4-7 split 1
+  const int w = kHalves ? wt % kWaves : wt;
+  auto& steps = steps_all[grp];
   const int col = lane & 31;  // this lane's column
   const int h = lane >> 5;    // which half of the column's slots it holds
   const int n16 = lane & 15;
   const int c4 = lane >> 4;
 
   int item = xcd_remap(blockIdx.x, gridDim.x);
-  const int p = item % a.P;
-  item /= a.P;
+  int p = grp;
+  if constexpr (!kHalves) {
+    p = item % a.P;
+    item /= a.P;
+  }
   const int tw = item % a.TG;
   item /= a.TG;
   const int s = item % a.S;
@@ -223,7 +236,7 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_wide_kernel(DecodeAr
       }
     }
     __syncthreads();
-    if (idle) return;
+    if (idle || t >= te) return;
 
     // S^T = K q^T over d = 128.
     f32x16_t sc = {};
@@ -338,20 +351,46 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_wide_kernel(DecodeAr
   constexpr int kChunkTiles = B >= kTile ? kWave : 4 * B;
   static_assert(kChunkTiles % 2 == 0, "steps of two tiles stay inside one chunk");
   constexpr int kDepth = 2;
-  for (int tb = u0; tb < u1; tb += kChunkTiles) {
-    const int te = min(u1, tb + kChunkTiles);
-    const int eb = (kTile * tb) / B;
-    const int tab = trow[min(eb + lane, nb - 1)];
-    Rows ring[kDepth];
-    load_step(tb, ring[0], eb, tab, te, false);
-    for (int t = tb; t < te; t += 2 * kDepth) {
+  if constexpr (kHalves) {
+    // Both halves pass the same barriers: chunks and steps are counted on the
+    // first split's range (never shorter than the second's); a half past its
+    // own range loads nothing (size-0 descriptors) and skips the arithmetic.
+    const int c_u1 = min(nt, a.tps / kTile);
+    for (int cb = 0; cb < c_u1; cb += kChunkTiles) {
+      const int tb = u0 + cb;
+      const int te = min(u1, tb + kChunkTiles);
+      const int ce = min(c_u1, cb + kChunkTiles) - cb;
+      const int eb = (kTile * tb) / B;
+      const int tab = tb < te ? trow[min(eb + lane, nb - 1)] : 0;
+      Rows ring[kDepth];
+      load_step(max(tb, min(tb, te - 1)), ring[0], eb, tab, te, tb >= te);
+      for (int t = 0; t < ce; t += 2 * kDepth) {
 #pragma unroll
-      for (int b = 0; b < kDepth; ++b) {
-        const int tn = t + 2 * (b + 1);  // the step to prefetch; past the chunk: loads that fetch nothing
-        load_step(min(tn, te - 1), ring[(b + 1) % kDepth], eb, tab, te, tn >= te);
-        __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the current step's math
-        process(t + 2 * b, ring[b], te);
-        if (t + 2 * b + 2 >= te) break;
+        for (int b = 0; b < kDepth; ++b) {
+          const int tn = tb + t + 2 * (b + 1);
+          load_step(max(tb, min(tn, te - 1)), ring[(b + 1) % kDepth], eb, tab, te, tn >= te);
+          __builtin_amdgcn_sched_barrier(0);
+          process(tb + t + 2 * b, ring[b], te);
+          if (t + 2 * b + 2 >= ce) break;
+        }
+      }
+    }
+  } else {
+    for (int tb = u0; tb < u1; tb += kChunkTiles) {
+      const int te = min(u1, tb + kChunkTiles);
+      const int eb = (kTile * tb) / B;
+      const int tab = trow[min(eb + lane, nb - 1)];
+      Rows ring[kDepth];
+      load_step(tb, ring[0], eb, tab, te, false);
+      for (int t = tb; t < te; t += 2 * kDepth) {
+#pragma unroll
+        for (int b = 0; b < kDepth; ++b) {
+          const int tn = t + 2 * (b + 1);  // the step to prefetch; past the chunk: loads that fetch nothing
+          load_step(min(tn, te - 1), ring[(b + 1) % kDepth], eb, tab, te, tn >= te);
+          __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the current step's math
+          process(t + 2 * b, ring[b], te);
+          if (t + 2 * b + 2 >= te) break;
+        }
       }
     }
   }
@@ -366,6 +405,70 @@ __global__ __launch_bounds__(kWave * kWaves, 2) void extend_wide_kernel(DecodeAr
   bad = __syncthreads_or(bad);  // any wave that met an entry outside the pool
 
   const float nan = __builtin_nanf("");
+  if constexpr (kHalves) {
+    // The second half's state goes to the first, lane for lane (both halves
+    // hold the same columns in the same lanes), through the steps' LDS (free
+    // after the barrier above), in two rounds of two accumulator blocks.  The
+    // first half merges as the merge kernel does (M, then 2^(m_p - M)
+    // weights folded in split order, o * (1 / L); an entry outside the pool
+    // gives NaN) and writes the output.
+    float* xs = reinterpret_cast<float*>(&steps_all[0][0][0][0]);
+    constexpr int kSlot = 2 + 32;
+    static_assert(kWaves * kWave * kSlot * 4 <= (int)sizeof(steps_all), "the handed-over states fit the steps");
+    const int slot = (w * kWave + lane) * kSlot;
+    float w0 = 0.f, w1 = 0.f, inv = 0.f;
+    bool empty = true;
+    const int64_t row = ((int64_t)s * a.T + tq) * a.Hq + kvh * G + col % G;
+    float* dst = a.out + row * kHeadDim + 4 * h;
+#pragma unroll
+    for (int round = 0; round < 2; ++round) {
+      if (round > 0) __syncthreads();  // the first round's values have been read
+      if (grp == 1) {
+        if (round == 0) {
+          xs[slot] = m;
+          xs[slot + 1] = lc;
+        }
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xs[slot + 2 + 16 * mb + r] = acc[2 * round + mb][r];
+      }
+      __syncthreads();
+      if (grp == 0 && tq < a.T) {
+        if (round == 0) {
+          const float m0 = bad ? 0.f : m, m1 = bad ? 0.f : xs[slot];
+          const float l0 = bad ? nan : lc, l1 = bad ? nan : xs[slot + 1];
+          float M = kNegInf;
+          M = fmaxf(M, m0);
+          M = fmaxf(M, m1);
+          empty = M == kNegInf;
+          if (!empty) {
+            w0 = fast_exp2(m0 - M);
+            w1 = fast_exp2(m1 - M);
+            float L = 0.f;
+            L = fmaf(w0, l0, L);
+            L = fmaf(w1, l1, L);
+            inv = 1.f / L;
+          }
+        }
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float x = 0.f;
+              x = fmaf(w0, acc[2 * round + mb][4 * q + e], x);
+              x = fmaf(w1, xs[slot + 2 + 16 * mb + 4 * q + e], x);
+              o[e] = empty ? 0.f : x * inv;
+            }
+            *reinterpret_cast<float4*>(dst + 32 * (2 * round + mb) + 8 * q) = make_float4(o[0], o[1], o[2], o[3]);
+          }
+      }
+    }
+    return;
+  }
   if (tq < a.T) {
     const int64_t row = ((int64_t)s * a.T + tq) * a.Hq + kvh * G + col % G;
     if (a.P == 1) {
@@ -800,6 +903,11 @@ void launch_gbr(const DecodeArgs& a, hipStream_t stream) {
     else
       hipLaunchKernelGGL((extend_pingpong_kernel<G, B, kOneRounding, false>), dim3(items),
                          dim3(kWave * kPingPongWaves), 0, stream, a);
+    return;
+  }
+  if (shared_tile_halves(PA_BF16, G, a.T, a.P)) {
+    hipLaunchKernelGGL((extend_wide_kernel<G, B, kOneRounding, true, true>), dim3(items / 2),
+                       dim3(2 * kWave * kWaves), 0, stream, a);
     return;
   }
   if (a.TG == 1)

@@ -98,14 +98,6 @@ constexpr int decode_column_sets(pa_dtype dtype, int G, int T) {
   return dtype == PA_BF16 && T > tokens_per_wave(dtype, G) && !use_shared_tile(dtype, G, T) ? 2 : 1;
 }
 
-// A two-split plan of the one-set shared-tile kernel (one workgroup then
-// holds all T tokens of its (request, KV head)) runs as one workgroup of two
-// 4-wave halves, one per split, that merge their states in LDS at the end:
-// no partial state reaches the split workspace and no merge kernel runs.
-constexpr bool shared_tile_halves(pa_dtype dtype, int G, int T, int P) {
-  return use_shared_tile(dtype, G, T) && shared_tile_sets(dtype, G, T) == 1 && P == 2;
-}
-
 constexpr int kPingPongWaves = 8;  // waves of the ping-pong shared-tile kernel
 
 // bf16 query groups wider than one workgroup of four 32-column waves (more
@@ -119,6 +111,15 @@ constexpr int kPingPongWaves = 8;  // waves of the ping-pong shared-tile kernel
 // on the 4-wave kernel.
 constexpr bool use_pingpong(pa_dtype dtype, int G, int T) {
   return use_shared_tile(dtype, G, T) && shared_tile_sets(dtype, G, T) == 2 && (int64_t)T * G > kSharedTileWaves * 32;
+}
+
+// A two-split plan of the 4-wave shared-tile kernels (one set per wave or
+// the 32-column form; one workgroup then holds all T tokens of its (request,
+// KV head)) runs as one workgroup of two 4-wave halves, one per split, that
+// merge their states in LDS at the end: no partial state reaches the split
+// workspace and no merge kernel runs.
+constexpr bool shared_tile_halves(pa_dtype dtype, int G, int T, int P) {
+  return use_shared_tile(dtype, G, T) && !use_pingpong(dtype, G, T) && P == 2;
 }
 
 // Waves of one shared-tile work item.

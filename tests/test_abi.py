@@ -208,13 +208,13 @@ def test_swap_rejects_bad_arguments(lib):
 
 
 def shared_tile_halves(dt, G, T, P):
-    """Two splits of the one-set shared-tile kernel (bf16, more tokens than two
-    16-column sets hold, all of them in one 4-wave workgroup) run as one workgroup
+    """Two splits of the 4-wave shared-tile kernels (bf16, more tokens than two
+    16-column sets hold, at most 128 (token, head) columns) run as one workgroup
     of two halves that merge in LDS: no workspace."""
     if dt != torch.bfloat16:
         return False
     per_wave = 1 if G >= 16 else 16 // G
-    return T > 2 * per_wave and T <= 4 * per_wave and P == 2
+    return T > 2 * per_wave and T * G <= 128 and P == 2
 
 
 def merged_splits(P, dt):

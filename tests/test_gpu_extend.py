@@ -407,29 +407,31 @@ def test_bad_lengths_and_out_of_pool_entries_poison_only_their_request(T):
         assert_close(got[s_], ref[s_], torch.bfloat16, f"request {s_}")
 
 
-@pytest.mark.parametrize("T,B,bf16_weights", [(9, 16, False), (12, 16, True), (16, 16, False), (16, 4, False),
-                                              (16, 64, True)])
-def test_two_splits_as_one_workgroup_of_two_halves(T, B, bf16_weights):
-    """Two splits of the one-set shared-tile kernel run as one workgroup whose two
-    4-wave halves take a split each and merge in LDS: no workspace, no merge
-    kernel.  Requests shorter than a split leave the second half nothing of its
-    own (it still passes every barrier); lengths cross tile, block and split
-    boundaries."""
-    banner(f"extend two halves T={T} B={B} bf16_weights={bf16_weights}")
-    lens = [T, T + 5, 40, 300, 1000, 1031, 2049, 16 * 64 + 1]
-    b = W.extend_batch(lens, T, Hq=8, Hkv=2, B=B, seed=400 + T + B, device=DEV)
+@pytest.mark.parametrize("G,T,B,bf16_weights", [(4, 9, 16, False), (4, 12, 16, True), (4, 16, 16, False),
+                                                (4, 16, 4, False), (4, 16, 64, True), (4, 24, 16, False),
+                                                (4, 32, 8, True), (2, 40, 32, False), (1, 100, 16, False)])
+def test_two_splits_as_one_workgroup_of_two_halves(G, T, B, bf16_weights):
+    """Two splits of the 4-wave shared-tile kernels (one 16-column set per wave
+    up to 16 tokens of a 4-head group, the 32-column kernel up to 128 columns)
+    run as one workgroup whose two 4-wave halves take a split each and merge in
+    LDS: no workspace, no merge kernel.  Requests shorter than a split leave the
+    second half nothing of its own (it still passes every barrier); lengths cross
+    tile, block and split boundaries; T = 24 leaves a whole wave idle."""
+    banner(f"extend two halves G={G} T={T} B={B} bf16_weights={bf16_weights}")
+    lens = [T, T + 5, 140, 300, 1000, 1031, 2049, 16 * 64 + 1]
+    b = W.extend_batch(lens, T, Hq=2 * G, Hkv=2, B=B, seed=400 + T + B, device=DEV)
     P, ws = pa.paged_attn_extend_plan(b.S, b.Hq, b.Hkv, b.D, b.MB, b.NB, b.dtype, b.B, T, num_splits=2)
     assert (P, ws) == (2, 0)
     check(b, torch.bfloat16, f"two halves T={T} B={B}", num_splits=2, bf16_weights=bf16_weights)
 
 
-def test_two_halves_poison_only_their_request():
+@pytest.mark.parametrize("T", [16, 24])
+def test_two_halves_poison_only_their_request(T):
     """An out-of-pool entry in either split's range, a bad length: NaN for that
-    request only, through the halves' merge."""
-    banner("extend two halves bad inputs")
-    T = 16
+    request only, through the halves' merge (16-column and 32-column kernels)."""
+    banner(f"extend two halves bad inputs T={T}")
     lens = [1500, 1600, 1400, 1700, 1650]
-    b = W.extend_batch(lens, T, Hq=8, Hkv=2, seed=431, device=DEV)
+    b = W.extend_batch(lens, T, Hq=8, Hkv=2, seed=431 + T, device=DEV)
     host = HostExtend(b)
     pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
     ref = host.oracle()

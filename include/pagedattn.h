@@ -91,9 +91,10 @@ typedef struct {
   int32_t num_blocks;         /* NB >= 1: blocks in each pool                  */
   pa_dtype dtype;             /* element type of q, pools, new K/V             */
   int32_t num_splits;         /* split-K parts: 0 = chosen by the library from
-                                 host-known sizes (S, Hq, Hkv, MB, B, dtype and
-                                 the query-token count), >= 1 asks for that
-                                 count (rounded as paged_attn_plan states)      */
+                                 host-known values (S, Hq, Hkv, MB, B, dtype,
+                                 the query-token count and flags), >= 1 asks
+                                 for that count (rounded as paged_attn_plan
+                                 states)                                       */
   void* workspace;            /* device scratch for split-K partial states,
                                  256-byte aligned, caller-owned; may be NULL when
                                  paged_attn_plan reports 0 bytes                */
@@ -138,9 +139,9 @@ const char* pa_last_error(void);
  * bytes when nothing reaches the merge.  Every call writes every partial
  * state it later reads, so the workspace never needs clearing.
  *
- * The plan depends only on host-known values: S, Hq, Hkv, MB, B, dtype and
- * the query-token count T (1 here), never on lengths or table contents, so
- * repeated calls agree.  The table's MB * B slots are cut into units of
+ * The plan depends only on host-known values: S, Hq, Hkv, MB, B, dtype,
+ * the query-token count T (1 here) and dims->flags, never on lengths or
+ * table contents, so repeated calls agree.  The table's MB * B slots are cut into units of
  * max(16, B) slots (16-slot tiles, whole blocks).
  *   - dims->num_splits = 0: enough splits to occupy the GPU's compute units
  *     given the work items (S * Hkv, times the token groups of T), but no
@@ -264,7 +265,13 @@ pa_status paged_attn_decode_append(const void* q, const void* k_pool, const void
 /*
  * Split-K plan for paged_attn_extend with num_q_tokens (T >= 1) query tokens
  * per request; T = 1 gives paged_attn_plan's answer.  The workspace holds
- * partial states for S*T*Hq rows.
+ * partial states for S*T*Hq rows.  With bf16, when every query token of a
+ * (request, KV head) fits one workgroup of the several-token kernels, a
+ * plan of 2 splits (and of 4 where the tokens fill at most 64 (token, head)
+ * columns per KV head, as 9-16 tokens of a 4-head group) runs them as the
+ * parts of one workgroup that merge inside it: no workspace (0 bytes).  The
+ * automatic plan there takes 4 splits where it would take 2, except with
+ * PA_FLAG_BF16_WEIGHTS.
  */
 pa_status paged_attn_extend_plan(const pa_dims* dims, int32_t B, int32_t num_q_tokens, int32_t* num_splits,
                                  size_t* workspace_bytes);

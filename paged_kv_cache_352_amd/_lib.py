@@ -194,10 +194,11 @@ def paged_attn_workspace_bytes(S, Hq, Hkv, D, MB, NB, dtype, B, num_splits=0):
     return n
 
 
-def paged_attn_extend_plan(S, Hq, Hkv, D, MB, NB, dtype, B, T, num_splits=0):
-    """(splits, workspace bytes) of paged_attn_extend with T query tokens per request."""
+def paged_attn_extend_plan(S, Hq, Hkv, D, MB, NB, dtype, B, T, num_splits=0, bf16_weights=False):
+    """(splits, workspace bytes) of paged_attn_extend with T query tokens per
+    request (the flags enter the plan: pass the call's ``bf16_weights``)."""
     lib = load()
-    d = make_dims(S, Hq, Hkv, D, MB, NB, dtype, num_splits)
+    d = make_dims(S, Hq, Hkv, D, MB, NB, dtype, num_splits, flags=FLAG_BF16_WEIGHTS if bf16_weights else 0)
     p = ctypes.c_int32()
     w = ctypes.c_size_t()
     _check("paged_attn_extend_plan",
@@ -341,7 +342,7 @@ def paged_attn_extend(q, k_pool, v_pool, block_tables, seq_lens, B, scale, out=N
     T = q.shape[1]
     _need_cuda(q, k_pool, v_pool, block_tables, seq_lens)
     st = _launch_stream(stream)
-    P, need = paged_attn_extend_plan(S, Hq, Hkv, D, MB, NB, q.dtype, B, T, num_splits)
+    P, need = paged_attn_extend_plan(S, Hq, Hkv, D, MB, NB, q.dtype, B, T, num_splits, bf16_weights)
     with torch.cuda.stream(st):
         if out is None:
             out = torch.empty(tuple(q.shape), dtype=torch.float32, device=q.device)
@@ -519,7 +520,8 @@ class DecodeLaunch:
         S, Hq, D, NB, Hkv, MB = _check_decode_shapes(q, k_pool, v_pool, block_tables, seq_lens, B, out)
         extend = q.dim() == 4  # [S, T, Hq, d]: paged_attn_extend
         if extend:
-            self.splits, need = paged_attn_extend_plan(S, Hq, Hkv, D, MB, NB, q.dtype, B, q.shape[1], num_splits)
+            self.splits, need = paged_attn_extend_plan(S, Hq, Hkv, D, MB, NB, q.dtype, B, q.shape[1], num_splits,
+                                                       bf16_weights)
         else:
             self.splits, need = paged_attn_plan(S, Hq, Hkv, D, MB, NB, q.dtype, B, num_splits)
         _need_cuda(q, k_pool, v_pool, block_tables, seq_lens)

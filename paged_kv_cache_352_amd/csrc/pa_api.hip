@@ -117,6 +117,14 @@ void plan_splits(const pa_dims* d, int32_t B, int32_t T, int* P_out, int* tps_ou
     const int64_t min_tokens = shared ? 256 : (mfma ? 64 * pa::kMfmaWaves : 16);
     const int64_t maxP = max_tokens / min_tokens > 1 ? max_tokens / min_tokens : 1;
     P = P < 1 ? 1 : (P > maxP ? maxP : P);
+    // 33-64 columns per KV head with the default weights: two splits become
+    // four, which run as the four parts of one workgroup on the 32-column
+    // kernel.  32 x 4096 tokens, 16 tokens of 4-head groups: 95.3 against
+    // 101.8-103.7 us for two halves of 16-column waves; 9-12 tokens alike;
+    // with PA_FLAG_BF16_WEIGHTS 2-4 % slower, so that form keeps two.
+    if (P == 2 && maxP >= 4 && shared && pa::shared_tile_sets(d->dtype, d->num_q_heads / d->num_kv_heads, T) == 1 &&
+        !(d->flags & PA_FLAG_BF16_WEIGHTS))
+      P = 4;
   }
   if (P > units) P = units;
   const int64_t upp = (units + P - 1) / P;  // units per split
@@ -158,7 +166,7 @@ static pa_status plan_common(const pa_dims* dims, int32_t B, int32_t T, int32_t*
   int P, tps;
   plan_splits(dims, B, T, &P, &tps);
   *num_splits = P;
-  const int Pm = pa::shared_tile_halves(dims->dtype, dims->num_q_heads / dims->num_kv_heads, T, P)
+  const int Pm = pa::shared_tile_parts(dims->dtype, dims->num_q_heads / dims->num_kv_heads, T, P) > 1
                      ? 1
                      : pa::merged_splits(dims->dtype, P);
   *workspace_bytes =
@@ -225,7 +233,7 @@ static pa_status attend(const void* q, const void* k_pool, const void* v_pool, c
       a.positions = positions;
     }
   }
-  if (a.P > 1 && !pa::shared_tile_halves(dims->dtype, a.Hq / a.Hkv, T, a.P)) {
+  if (a.P > 1 && pa::shared_tile_parts(dims->dtype, a.Hq / a.Hkv, T, a.P) == 1) {
     const size_t need = pa::decode_workspace_floats(rows, a.P) * sizeof(float);
     if (!dims->workspace || dims->workspace_bytes < need)
       return fail(PA_ERR_WORKSPACE, "split-K needs %zu workspace bytes, got %zu", need,

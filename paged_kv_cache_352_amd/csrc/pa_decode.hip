@@ -459,12 +459,13 @@ hipError_t launch_decode(const DecodeArgs& a, pa_dtype dtype, int B, int G, hipS
   hipError_t e;
   if (use_shared_tile(dtype, G, a.T)) {
     e = launch_extend_shared(a, B, G, stream);
-    if (shared_tile_halves(dtype, G, a.T, a.P)) return e;  // the two splits merged in the kernel
+    if (shared_tile_parts(dtype, G, a.T, a.P) > 1) return e;  // the splits merged in the kernel
   } else if (dtype == PA_BF16)
     e = launch_decode_mfma(a, B, G, causal, stream);
   else
     e = causal ? launch_valu<true>(a, B, G, stream) : launch_valu<false>(a, B, G, stream);
   if (e != hipSuccess || a.P == 1) return e;
+  if (!a.ws_o || !a.ws_m || !a.ws_l) return hipErrorInvalidValue;  // a merge reads the split workspace
   const int64_t rows = (int64_t)a.S * a.T * a.Hq;
   const dim3 grid((unsigned)((rows + kMergeRows - 1) / kMergeRows)), block(kWave * 4);
   switch (a.P) {

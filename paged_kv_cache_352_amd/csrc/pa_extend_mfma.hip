@@ -435,8 +435,11 @@ hipError_t launch_b(const DecodeArgs& a, int G, hipStream_t stream) {
 hipError_t launch_extend_shared(const DecodeArgs& a, int B, int G, hipStream_t stream) {
   // Two 16-column sets per wave: the same columns as one 32-column set of the
   // 32x32 kernel, which measured 6 % faster on a 512-token chunk (fewer
-  // vector instructions per score; see pa_extend_wide.hip).
-  if (shared_tile_sets(PA_BF16, G, a.T) == 2) return launch_extend_wide(a, B, G, stream);
+  // vector instructions per score; see pa_extend_wide.hip).  A four-split
+  // plan of one set per wave runs there too, as four parts of two 32-column
+  // waves in one workgroup.
+  if (shared_tile_sets(PA_BF16, G, a.T) == 2 || shared_tile_quarters(PA_BF16, G, a.T, a.P))
+    return launch_extend_wide(a, B, G, stream);
   switch (B) {
     case 4: return launch_b<4>(a, G, stream);
     case 8: return launch_b<8>(a, G, stream);

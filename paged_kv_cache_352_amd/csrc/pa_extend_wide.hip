@@ -16,8 +16,9 @@
 // 32 slots per step; each wave owns 32 columns, the (token, head) pairs of
 // 32/G query tokens of the G-head group.  Each step's 32 K and V slot rows
 // are loaded once (every wave fetches 8 rows: two 4-row groups of 16-byte
-// lanes), written to a double-buffered LDS tile, and after one barrier every
-// wave folds the whole step into its own columns.  The products are taken
+// lanes; 16 rows in the four-part form below), written to a double-buffered
+// LDS tile, and after one barrier every wave folds the whole step into its
+// own columns.  The products are taken
 // transposed so that a lane owns one column throughout:
 //
 //   scores  S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = K (32 slots x 16
@@ -71,28 +72,43 @@ constexpr int kStepBytes = kStep * kHeadDim * 2;  // one K or V step in LDS: 8 K
 // slots x 64 bytes, which then falls on every bank once per 32-byte half.
 __device__ inline int kw_pos(int k, int t) { return k ^ (t & 15); }
 
-// kHalves (two splits): one workgroup of 8 waves takes both splits of its
-// (request, KV head), waves 0-3 the first and 4-7 the second, each half with
-// its own LDS steps and both passing the same barriers; at the end the second
-// half hands its state to the first, which merges the two as the merge
-// kernel would (bitwise the same result) and writes the output, so no
-// partial state goes through memory and no merge kernel runs.
-template <int G, int B, bool kOneRounding, bool kStream, bool kHalves = false>
-__global__ __launch_bounds__(kWave * kWaves * (kHalves ? 2 : 1), kHalves ? 1 : 2) void extend_wide_kernel(DecodeArgs a) {
-  static_assert(!kHalves || kStream, "halves: one workgroup per request");
+// kParts = 2 or 4: one workgroup takes all splits of its (request, KV head),
+// one part of waves per split, each part with its own LDS steps and all
+// passing the same barriers; at the end the other parts hand their states to
+// the first, which merges them as the merge kernel would (M, then the
+// 2^(m_p - M) weights folded in split order) and writes the output, so no
+// partial state goes through memory and no merge kernel runs.  Two parts
+// (two splits) have 4 waves of 32 columns each, as the one-split form, and
+// give bitwise the result of two workgroups and the merge kernel.  Four
+// parts (four splits, up to 64 columns: 9-16 tokens of a 4-head group) have
+// 2 waves each, so every wave loads 16 rows of each step and the workgroup
+// holds 8 waves and four parts' double-buffered steps (128 KiB of LDS).
+// Measured on 32 x 4096 tokens with 16 tokens of 4-head groups against two
+// halves of four 16-column waves (pa_extend_mfma.hip): 95.3 against
+// 101.8-103.7 us, each wave's step on the 32x32 tiles doing a 16-column
+// wave's work twice over with fewer vector instructions per score, and half
+// as many steps and barriers.
+template <int G, int B, bool kOneRounding, bool kStream, int kParts = 1>
+__global__ __launch_bounds__(kWave * (kParts == 4 ? 2 : kWaves) * kParts, kParts > 1 ? 1 : 2) void extend_wide_kernel(
+    DecodeArgs a) {
+  constexpr bool kJoined = kParts > 1;  // the splits are parts of this workgroup
+  static_assert(kParts == 1 || kParts == 2 || kParts == 4, "one, two or four splits per workgroup");
+  static_assert(!kJoined || kStream, "parts: one workgroup per (request, KV head)");
+  constexpr int kCW = kParts == 4 ? 2 : kWaves;  // column waves per split
+  constexpr int kRG = 8 / kCW;                    // 4-row groups of a step each wave loads
   static_assert(G >= 1 && G <= 16, "32 columns hold 32/G whole query tokens");
   static_assert(B >= 4 && B <= 64 && (B & (B - 1)) == 0, "block size: a power of two from 4 to 64");
   constexpr int TC = 32 / G;        // query tokens per wave
-  constexpr int TW = kWaves * TC;   // query tokens per workgroup
-  // [half][buffer][K, V][step bytes]
-  __shared__ __attribute__((aligned(16))) uint8_t steps_all[kHalves ? 2 : 1][2][2][kStepBytes];
+  constexpr int TW = kCW * TC;      // query tokens per workgroup
+  // [part][buffer][K, V][step bytes]
+  __shared__ __attribute__((aligned(16))) uint8_t steps_all[kParts][2][2][kStepBytes];
 
   const int lane = threadIdx.x & (kWave - 1);
   // The wave index, in a scalar register (block offsets and table lanes
   // derived from it must be scalar).
   const int wt = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int grp = kHalves ? wt / kWaves : 0;  // kHalves: waves 0-3 take split 0, waves 4-7 split 1
-  const int w = kHalves ? wt % kWaves : wt;
+  const int grp = kJoined ? wt / kCW : 0;  // the part: the first kCW waves take split 0, and so on
+  const int w = kJoined ? wt % kCW : wt;
   auto& steps = steps_all[grp];
   const int col = lane & 31;  // this lane's column
   const int h = lane >> 5;    // which half of the column's slots it holds
@@ -101,7 +117,7 @@ __global__ __launch_bounds__(kWave * kWaves * (kHalves ? 2 : 1), kHalves ? 1 : 2
 
   int item = xcd_remap(blockIdx.x, gridDim.x);
   int p = grp;
-  if constexpr (!kHalves) {
+  if constexpr (!kJoined) {
     p = item % a.P;
     item /= a.P;
   }
@@ -167,15 +183,15 @@ __global__ __launch_bounds__(kWave * kWaves * (kHalves ? 2 : 1), kHalves ? 1 : 2
     return pb;
   };
   struct Rows {
-    uint4 k[2], v[2];
+    uint4 k[kRG], v[kRG];
   };
   // Step starting at tile t: slots 16t .. 16t+31; `te` ends the chunk (and
   // the split): a second tile at or past it is not part of the step.
   auto load_step = [&](int t, Rows& r, int eb, int tab, int te, bool none) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int tok = kTile * t + 8 * w + 4 * i;  // first slot of the row group
-      const bool live = !none && tok < n && (8 * w + 4 * i < kTile || t + 1 < te);
+    for (int i = 0; i < kRG; ++i) {
+      const int tok = kTile * t + 4 * kRG * w + 4 * i;  // first slot of the row group
+      const bool live = !none && tok < n && (4 * kRG * w + 4 * i < kTile || t + 1 < te);
       const int pb = live ? pool_block(__builtin_amdgcn_readlane(tab, tok / B - eb)) : 0;
       const int soff = live ? (tok % B) * row_bytes : 0;
       const uint32_t size = live ? blk_bytes : 0u;
@@ -192,10 +208,10 @@ __global__ __launch_bounds__(kWave * kWaves * (kHalves ? 2 : 1), kHalves ? 1 : 2
   for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x16_t{};
 
   // LDS offsets this lane writes (rows 8w + 4i + c4, chunk n16) and reads.
-  int wk_off[2], wv_off[2];
+  int wk_off[kRG], wv_off[kRG];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 8 * w + 4 * i + c4;
+  for (int i = 0; i < kRG; ++i) {
+    const int r = 4 * kRG * w + 4 * i + c4;
     wk_off[i] = 256 * r + 16 * kw_pos(n16, r);
     wv_off[i] = 256 * r + 16 * v_pos(n16, r);
   }
@@ -222,16 +238,16 @@ __global__ __launch_bounds__(kWave * kWaves * (kHalves ? 2 : 1), kHalves ? 1 : 2
     uint8_t* vb_ = &steps[buf][1][0];
     const int valid = n - kTile * t;  // slots of the step inside the history
 #pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(kb_ + wk_off[i]) = r.k[i];
+    for (int i = 0; i < kRG; ++i) *reinterpret_cast<uint4*>(kb_ + wk_off[i]) = r.k[i];
     if (valid >= kStep) {  // the whole step lies inside the history (all but the last)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(vb_ + wv_off[i]) = r.v[i];
+      for (int i = 0; i < kRG; ++i) *reinterpret_cast<uint4*>(vb_ + wv_off[i]) = r.v[i];
     } else {
       // V past the history may hold anything (NaN): zeroed, since a zero
       // weight times NaN would still be NaN.
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = 8 * w + 4 * i + c4;
+      for (int i = 0; i < kRG; ++i) {
+        const int row = 4 * kRG * w + 4 * i + c4;
         *reinterpret_cast<uint4*>(vb_ + wv_off[i]) = row < valid ? r.v[i] : make_uint4(0, 0, 0, 0);
       }
     }
@@ -351,9 +367,9 @@ __global__ __launch_bounds__(kWave * kWaves * (kHalves ? 2 : 1), kHalves ? 1 : 2
   constexpr int kChunkTiles = B >= kTile ? kWave : 4 * B;
   static_assert(kChunkTiles % 2 == 0, "steps of two tiles stay inside one chunk");
   constexpr int kDepth = 2;
-  if constexpr (kHalves) {
-    // Both halves pass the same barriers: chunks and steps are counted on the
-    // first split's range (never shorter than the second's); a half past its
+  if constexpr (kJoined) {
+    // All parts pass the same barriers: chunks and steps are counted on the
+    // first split's range (never shorter than the others'); a part past its
     // own range loads nothing (size-0 descriptors) and skips the arithmetic.
     const int c_u1 = min(nt, a.tps / kTile);
     for (int cb = 0; cb < c_u1; cb += kChunkTiles) {
@@ -405,7 +421,69 @@ __global__ __launch_bounds__(kWave * kWaves * (kHalves ? 2 : 1), kHalves ? 1 : 2
   bad = __syncthreads_or(bad);  // any wave that met an entry outside the pool
 
   const float nan = __builtin_nanf("");
-  if constexpr (kHalves) {
+  if constexpr (kParts == 4) {
+    // Parts 1-3 hand their states to part 0, lane for lane, through the
+    // steps' LDS in one round; part 0 merges the four as the merge kernel
+    // does (M, then 2^(m_p - M) weights folded in split order, o * (1 / L))
+    // and writes the output.
+    float* xs = reinterpret_cast<float*>(&steps_all[0][0][0][0]);
+    constexpr int kSlot = 2 + 64;
+    static_assert((kParts - 1) * kCW * kWave * kSlot * 4 <= (int)sizeof(steps_all), "the states fit the steps");
+    if (grp > 0) {
+      const int slot = (((grp - 1) * kCW + w) * kWave + lane) * kSlot;
+      xs[slot] = m;
+      xs[slot + 1] = lc;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xs[slot + 2 + 16 * mb + r] = acc[mb][r];
+    }
+    __syncthreads();
+    if (grp == 0 && tq < a.T) {
+      float mv[kParts], lv[kParts];
+      mv[0] = bad ? 0.f : m;
+      lv[0] = bad ? nan : lc;
+#pragma unroll
+      for (int q = 1; q < kParts; ++q) {
+        const int slot = (((q - 1) * kCW + w) * kWave + lane) * kSlot;
+        mv[q] = bad ? 0.f : xs[slot];
+        lv[q] = bad ? nan : xs[slot + 1];
+      }
+      float M = kNegInf;
+#pragma unroll
+      for (int q = 0; q < kParts; ++q) M = fmaxf(M, mv[q]);
+      const bool empty = M == kNegInf;
+      float wq[kParts];
+      float L = 0.f;
+#pragma unroll
+      for (int q = 0; q < kParts; ++q) {
+        wq[q] = empty ? 0.f : fast_exp2(mv[q] - M);
+        L = fmaf(wq[q], lv[q], L);
+      }
+      const float inv = 1.f / L;
+      const int64_t row = ((int64_t)s * a.T + tq) * a.Hq + kvh * G + col % G;
+      float* dst = a.out + row * kHeadDim + 4 * h;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float x = 0.f;
+            x = fmaf(wq[0], acc[mb][4 * q4 + e], x);
+#pragma unroll
+            for (int q = 1; q < kParts; ++q) {
+              const int slot = (((q - 1) * kCW + w) * kWave + lane) * kSlot;
+              x = fmaf(wq[q], xs[slot + 2 + 16 * mb + 4 * q4 + e], x);
+            }
+            o[e] = empty ? 0.f : x * inv;
+          }
+          *reinterpret_cast<float4*>(dst + 32 * mb + 8 * q4) = make_float4(o[0], o[1], o[2], o[3]);
+        }
+    }
+    return;
+  } else if constexpr (kJoined) {
     // The second half's state goes to the first, lane for lane (both halves
     // hold the same columns in the same lanes), through the steps' LDS (free
     // after the barrier above), in two rounds of two accumulator blocks.  The
@@ -905,8 +983,13 @@ void launch_gbr(const DecodeArgs& a, hipStream_t stream) {
                          dim3(kWave * kPingPongWaves), 0, stream, a);
     return;
   }
+  if (shared_tile_quarters(PA_BF16, G, a.T, a.P)) {
+    hipLaunchKernelGGL((extend_wide_kernel<G, B, kOneRounding, true, 4>), dim3(items / 4), dim3(4 * kWave * 2), 0,
+                       stream, a);
+    return;
+  }
   if (shared_tile_halves(PA_BF16, G, a.T, a.P)) {
-    hipLaunchKernelGGL((extend_wide_kernel<G, B, kOneRounding, true, true>), dim3(items / 2),
+    hipLaunchKernelGGL((extend_wide_kernel<G, B, kOneRounding, true, 2>), dim3(items / 2),
                        dim3(2 * kWave * kWaves), 0, stream, a);
     return;
   }

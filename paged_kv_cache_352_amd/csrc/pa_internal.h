@@ -122,6 +122,23 @@ constexpr bool shared_tile_halves(pa_dtype dtype, int G, int T, int P) {
   return use_shared_tile(dtype, G, T) && !use_pingpong(dtype, G, T) && P == 2;
 }
 
+// A four-split plan of the one-set-per-wave case (33-64 (token, head)
+// columns per KV head, e.g. 9-16 tokens of a 4-head group) runs on the
+// 32-column kernel as one workgroup of four parts of two 32-column waves,
+// one part per split, that merge their states in LDS at the end (no split
+// workspace, no merge kernel).
+constexpr bool shared_tile_quarters(pa_dtype dtype, int G, int T, int P) {
+  return use_shared_tile(dtype, G, T) && shared_tile_sets(dtype, G, T) == 1 && P == 4;
+}
+
+// Splits of one (request, KV head) that run as the parts of one workgroup
+// and merge inside it: 4 or 2, else 1 (each split a workgroup of its own,
+// merged afterwards by the merge kernel through the split workspace).  The
+// workspace size, its check and the merge launch all follow this.
+constexpr int shared_tile_parts(pa_dtype dtype, int G, int T, int P) {
+  return shared_tile_quarters(dtype, G, T, P) ? 4 : (shared_tile_halves(dtype, G, T, P) ? 2 : 1);
+}
+
 // Waves of one shared-tile work item.
 constexpr int shared_tile_waves(pa_dtype dtype, int G, int T) {
   return use_pingpong(dtype, G, T) ? kPingPongWaves : kSharedTileWaves;

@@ -217,6 +217,20 @@ def shared_tile_halves(dt, G, T, P):
     return T > 2 * per_wave and T * G <= 128 and P == 2
 
 
+def shared_tile_quarters(dt, G, T, P):
+    """Four splits of the one-set-per-wave case (bf16, more tokens than two
+    16-column sets hold, at most 64 (token, head) columns) run as one workgroup
+    of four parts of the 32-column kernel that merge in LDS: no workspace."""
+    if dt != torch.bfloat16:
+        return False
+    per_wave = 1 if G >= 16 else 16 // G
+    return T > 2 * per_wave and T <= 4 * per_wave and P == 4
+
+
+def shared_tile_parts(dt, G, T, P):
+    return 4 if shared_tile_quarters(dt, G, T, P) else (2 if shared_tile_halves(dt, G, T, P) else 1)
+
+
 def merged_splits(P, dt):
     """Partial states per output row that reach the split workspace: float32 runs
     groups of up to 4 splits (the next power of two) as the waves of one
@@ -235,13 +249,39 @@ def test_extend_plan_matches_decode_at_one_token_and_scales_workspace(lib):
         assert pa.paged_attn_extend_plan(S, Hq, Hkv, 128, MB, 10000, dt, 16, 1) == pa.paged_attn_plan(
             S, Hq, Hkv, 128, MB, 10000, dt, 16)
         for T in (2, 4, 7, 16, 33):
-            P, ws = pa.paged_attn_extend_plan(S, Hq, Hkv, 128, MB, 10000, dt, 16, T)
-            Pm = 1 if shared_tile_halves(dt, Hq // Hkv, T, P) else merged_splits(P, dt)
-            assert P >= 1 and ws == (S * T * Hq * Pm * 130 * 4 if Pm > 1 else 0)
+            for w in (False, True):
+                P, ws = pa.paged_attn_extend_plan(S, Hq, Hkv, 128, MB, 10000, dt, 16, T, bf16_weights=w)
+                Pm = 1 if shared_tile_parts(dt, Hq // Hkv, T, P) > 1 else merged_splits(P, dt)
+                assert P >= 1 and ws == (S * T * Hq * Pm * 130 * 4 if Pm > 1 else 0)
+            for P0 in (2, 3, 4, 5):
+                P, ws = pa.paged_attn_extend_plan(S, Hq, Hkv, 128, MB, 10000, dt, 16, T, num_splits=P0)
+                Pm = 1 if shared_tile_parts(dt, Hq // Hkv, T, P) > 1 else merged_splits(P, dt)
+                assert ws == (S * T * Hq * Pm * 130 * 4 if Pm > 1 else 0)
             # forced splits are honoured as in the one-token plan
             assert pa.paged_attn_extend_plan(S, Hq, Hkv, 128, MB, 10000, dt, 16, T, num_splits=2)[0] == min(2, MB)
     p, w = ctypes.c_int32(), ctypes.c_size_t()
     assert lib.paged_attn_extend_plan(ctypes.byref(dims()), 16, 0, ctypes.byref(p), ctypes.byref(w)) == INVALID
+
+
+def test_extend_plan_takes_four_parts_for_one_set_per_wave_with_default_weights(lib):
+    """32 requests of 4096 tokens, 4-head groups: the automatic plan for 9-16
+    query tokens (33-64 columns per KV head) takes 4 splits, run as the parts
+    of one workgroup (no workspace); with PA_FLAG_BF16_WEIGHTS it keeps 2
+    (two halves, no workspace); 8 and 17-32 tokens are unchanged; a history
+    too short for four 256-slot splits is not promoted."""
+    plan = lambda T, w=False, MB=256, S=32: pa.paged_attn_extend_plan(S, 32, 8, 128, MB, 40000, torch.bfloat16, 16,
+                                                                      T, bf16_weights=w)
+    for T in range(9, 17):
+        assert plan(T) == (4, 0)
+        assert plan(T, True) == (2, 0)
+    for T in (17, 24, 32):
+        assert plan(T) == plan(T, True) == (2, 0)
+    assert plan(8) == plan(8, True)
+    assert plan(12, MB=32) == plan(12, True, MB=32)  # 512 slots: at most 2 splits of 256
+    # G = 1, 2, 8 and 16 take the same rule on their own column counts
+    for Hq, T in ((8, 40), (16, 20), (64, 7), (128, 4)):
+        P, ws = pa.paged_attn_extend_plan(32, Hq, 8, 128, 256, 40000, torch.bfloat16, 16, T)
+        assert shared_tile_quarters(torch.bfloat16, Hq // 8, T, P) == (P == 4) and ws == 0, (Hq, T, P, ws)
 
 
 @no_gpu

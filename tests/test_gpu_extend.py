@@ -246,6 +246,25 @@ def test_verify_32x4096_T4_sampled():
     assert np.all(np.isfinite(out))
 
 
+@pytest.mark.parametrize("T,bf16_weights,parts", [(16, False, 4), (16, True, 2), (12, False, 4), (24, False, 2)])
+def test_verify_32x4096_shared_tile_sampled(T, bf16_weights, parts):
+    """The verification batch at full size with 12-24 draft tokens, in the
+    automatic plan the benchmark times: four parts of one workgroup on the
+    32-column kernel (default weights, up to 16 tokens of 4-head groups), two
+    halves otherwise; sampled requests against the oracle."""
+    banner(f"verify bf16 32x4096 T={T} bf16_weights={bf16_weights} ({parts} parts), sampled rows")
+    b = W.verify_batch(device=DEV, T=T)
+    assert pa.paged_attn_extend_plan(b.S, b.Hq, b.Hkv, b.D, b.MB, b.NB, b.dtype, b.B, T,
+                                     bf16_weights=bf16_weights) == (parts, 0)
+    host = HostExtend(b)
+    out = host_f32(gpu_extend(b, bf16_weights=bf16_weights))
+    rows = [0, 13, 31]
+    ref = host.oracle(rows)
+    assert_close(np.stack([out[s] for s in rows]), np.stack([ref[s] for s in rows]), torch.bfloat16, "verify",
+                 record=f"bf16 verification 32 x 4096 tokens, T = {T}, bf16_weights={bf16_weights}, rows {rows}")
+    assert np.all(np.isfinite(out))
+
+
 @pytest.mark.parametrize("bf16_weights", [False, True])
 def test_prefill_chunk_512_sampled(bf16_weights):
     """A 512-token prompt chunk over 3584 tokens of history, 8 requests; three sampled requests."""
@@ -444,6 +463,53 @@ def test_two_halves_poison_only_their_request(T):
     torch.cuda.synchronize()
     got = host_f32(out)
     for s_ in (1, 2, 3):
+        assert np.all(np.isnan(got[s_])), s_
+    for s_ in (0, 4):
+        assert_close(got[s_], ref[s_], torch.bfloat16, f"request {s_}")
+
+
+@pytest.mark.parametrize("G,T,B,bf16_weights", [(4, 9, 16, False), (4, 12, 16, True), (4, 16, 16, False),
+                                                (4, 16, 4, False), (4, 16, 64, True), (4, 13, 8, False),
+                                                (4, 16, 32, False), (2, 32, 32, False), (1, 64, 16, False),
+                                                (8, 8, 16, True), (16, 4, 16, False)])
+def test_four_splits_as_one_workgroup_of_four_parts(G, T, B, bf16_weights):
+    """Four splits of the one-set-per-wave case (at most 64 (token, head)
+    columns per KV head) run on the 32-column kernel as one workgroup of four
+    2-wave parts, one split each, every wave loading 16 rows of each step and
+    the parts merging in LDS: no workspace, no merge kernel.  Requests shorter
+    than a split leave later parts nothing of their own (they still pass every
+    barrier); lengths cross tile, block and split boundaries; T = 9 and 13 leave
+    the second wave of each part mostly padding columns."""
+    banner(f"extend four parts G={G} T={T} B={B} bf16_weights={bf16_weights}")
+    lens = [T, T + 5, 140, 300, 1000, 1031, 2049, 16 * 64 + 1]
+    b = W.extend_batch(lens, T, Hq=2 * G, Hkv=2, B=B, seed=500 + T + B, device=DEV)
+    P, ws = pa.paged_attn_extend_plan(b.S, b.Hq, b.Hkv, b.D, b.MB, b.NB, b.dtype, b.B, T, num_splits=4)
+    assert (P, ws) == (4, 0)
+    check(b, torch.bfloat16, f"four parts T={T} B={B}", num_splits=4, bf16_weights=bf16_weights)
+
+
+@pytest.mark.parametrize("T", [12, 16])
+def test_four_parts_poison_only_their_request(T):
+    """An out-of-pool entry in the first, third or last split's range, a bad
+    length: NaN for that request only, through the four parts' merge."""
+    banner(f"extend four parts bad inputs T={T}")
+    lens = [1500, 1600, 1400, 1700, 1650, 1690]
+    b = W.extend_batch(lens, T, Hq=8, Hkv=2, seed=531 + T, device=DEV)
+    host = HostExtend(b)
+    pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
+    ref = host.oracle()
+    P = 4
+    assert pa.paged_attn_extend_plan(b.S, b.Hq, b.Hkv, b.D, b.MB, b.NB, b.dtype, b.B, T, num_splits=P) == (4, 0)
+    tab = b.block_tables.clone()
+    tab[1, 3] = -9                 # in the first split
+    tab[2, 60] = b.NB + 5          # in the third split (blocks 54-80 of 107)
+    tab[5, 100] = -1               # in the last split
+    ln = b.seq_lens.clone()
+    ln[3] = -1
+    out = pa.paged_attn_extend(b.q, b.k_pool, b.v_pool, tab, ln, b.B, b.scale, num_splits=P)
+    torch.cuda.synchronize()
+    got = host_f32(out)
+    for s_ in (1, 2, 3, 5):
         assert np.all(np.isnan(got[s_])), s_
     for s_ in (0, 4):
         assert_close(got[s_], ref[s_], torch.bfloat16, f"request {s_}")

@@ -68,9 +68,16 @@ constexpr int kStepBytes = kStep * kHeadDim * 2;  // one K or V step in LDS: 8 K
 // K step in LDS: slot t, 16-byte chunk k at 256*t + 16*(k ^ (t % 16)); the
 // q.k reads (32 lanes: 32 slots, one chunk each) then meet 16 different
 // chunks in every 16-lane group.  V step: the 32-byte pair of chunks k/2 at
-// 256*t + 32*((k/2) ^ (t % 8)) + 16*(k % 2); a transposing read covers 8
-// slots x 64 bytes, which then falls on every bank once per 32-byte half.
+// 256*t + 32*((k/2) ^ g(t)) + 16*(k % 2), g(t) = 2*(t % 4) + (t / 4) % 2.  A
+// transposing read takes, in each half-wave, two neighbouring pairs (32
+// dims) of 4 slots t = 4i .. 4i+3, 8 bytes per lane: g gives those 4 slots
+// the even (or odd) values, so the two pairs land on all 8 32-byte bank
+// groups once.  (With g(t) = t % 8 they met only 4 of them, two ways each:
+// about 32 conflict cycles per 32-slot step and wave, though removing them
+// did not change the measured times.)
 __device__ inline int kw_pos(int k, int t) { return k ^ (t & 15); }
+__device__ inline int vw_perm(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+__device__ inline int vw_pos(int k, int t) { return (((k >> 1) ^ vw_perm(t)) << 1) | (k & 1); }
 
 // kParts = 2 or 4: one workgroup takes all splits of its (request, KV head),
 // one part of waves per split, each part with its own LDS steps and all
@@ -213,7 +220,7 @@ __global__ __launch_bounds__(kWave * (kParts == 4 ? 2 : kWaves) * kParts, kParts
   for (int i = 0; i < kRG; ++i) {
     const int r = 4 * kRG * w + 4 * i + c4;
     wk_off[i] = 256 * r + 16 * kw_pos(n16, r);
-    wv_off[i] = 256 * r + 16 * v_pos(n16, r);
+    wv_off[i] = 256 * r + 16 * vw_pos(n16, r);
   }
   // q.k A operand: slot col, chunk 2*kk + h.
   const int rk_base = 256 * col;
@@ -228,7 +235,7 @@ __global__ __launch_bounds__(kWave * (kParts == 4 ? 2 : kWaves) * kParts, kParts
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int pair = 2 * mb + ((lane >> 4) & 1);
-      rv_off[mb] = 256 * rr + 32 * (pair ^ (rr & 7)) + 8 * (j & 3);
+      rv_off[mb] = 256 * rr + 32 * (pair ^ vw_perm(rr)) + 8 * (j & 3);
     }
   }
 
@@ -699,7 +706,7 @@ __global__ __launch_bounds__(kWave * kPingPongWaves, 1) void extend_pingpong_ker
 
   const int wrow = 4 * w + c4;
   const int wk_off = 256 * wrow + 16 * kw_pos(n16, wrow);
-  const int wv_off = 256 * wrow + 16 * v_pos(n16, wrow);
+  const int wv_off = 256 * wrow + 16 * vw_pos(n16, wrow);
   // V rows past the history may hold anything (NaN): written as zeros, since
   // a zero weight times NaN would still be NaN.
   auto write_step = [&](int k, const Ld& r, uint8_t* kb_, uint8_t* vb_) {
@@ -725,7 +732,7 @@ __global__ __launch_bounds__(kWave * kPingPongWaves, 1) void extend_pingpong_ker
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int pair = 2 * mb + ((lane >> 4) & 1);
-      rv_off[mb] = 256 * rr + 32 * (pair ^ (rr & 7)) + 8 * (j & 3);
+      rv_off[mb] = 256 * rr + 32 * (pair ^ vw_perm(rr)) + 8 * (j & 3);
     }
   }
   const float c = fmaxf(c_log2, __FLT_MIN__);

@@ -270,7 +270,8 @@ pa_status paged_attn_decode_append(const void* q, const void* k_pool, const void
  * plan of 2 splits (and of 4 where the tokens fill at most 64 (token, head)
  * columns per KV head, as 9-16 tokens of a 4-head group) runs them as the
  * parts of one workgroup that merge inside it: no workspace (0 bytes).  The
- * automatic plan there takes 4 splits where it would take 2, except with
+ * automatic plan takes 4 splits where it would take 2 when the tokens fill
+ * 49-64 columns (13-16 tokens of a 4-head group), except with
  * PA_FLAG_BF16_WEIGHTS.
  */
 pa_status paged_attn_extend_plan(const pa_dims* dims, int32_t B, int32_t num_q_tokens, int32_t* num_splits,

@@ -117,12 +117,14 @@ void plan_splits(const pa_dims* d, int32_t B, int32_t T, int* P_out, int* tps_ou
     const int64_t min_tokens = shared ? 256 : (mfma ? 64 * pa::kMfmaWaves : 16);
     const int64_t maxP = max_tokens / min_tokens > 1 ? max_tokens / min_tokens : 1;
     P = P < 1 ? 1 : (P > maxP ? maxP : P);
-    // 33-64 columns per KV head with the default weights: two splits become
+    // 49-64 columns per KV head with the default weights: two splits become
     // four, which run as the four parts of one workgroup on the 32-column
-    // kernel.  32 x 4096 tokens, 16 tokens of 4-head groups: 95.3 against
-    // 101.8-103.7 us for two halves of 16-column waves; 9-12 tokens alike;
-    // with PA_FLAG_BF16_WEIGHTS 2-4 % slower, so that form keeps two.
-    if (P == 2 && maxP >= 4 && shared && pa::shared_tile_sets(d->dtype, d->num_q_heads / d->num_kv_heads, T) == 1 &&
+    // kernel (its second wave then more than half full).  32 x 4096 tokens:
+    // 94-97 against 101-106 us for two halves of 16-column waves at 64
+    // columns (G = 1, 2, 4, 8, 16); at 40-48 columns the halves were 1-3 %
+    // faster, and with PA_FLAG_BF16_WEIGHTS 2-4 % faster, so those keep two.
+    const int G = d->num_q_heads / d->num_kv_heads;
+    if (P == 2 && maxP >= 4 && shared && pa::shared_tile_sets(d->dtype, G, T) == 1 && (int64_t)T * G > 48 &&
         !(d->flags & PA_FLAG_BF16_WEIGHTS))
       P = 4;
   }

@@ -264,24 +264,26 @@ def test_extend_plan_matches_decode_at_one_token_and_scales_workspace(lib):
 
 
 def test_extend_plan_takes_four_parts_for_one_set_per_wave_with_default_weights(lib):
-    """32 requests of 4096 tokens, 4-head groups: the automatic plan for 9-16
-    query tokens (33-64 columns per KV head) takes 4 splits, run as the parts
-    of one workgroup (no workspace); with PA_FLAG_BF16_WEIGHTS it keeps 2
-    (two halves, no workspace); 8 and 17-32 tokens are unchanged; a history
-    too short for four 256-slot splits is not promoted."""
+    """32 requests of 4096 tokens, 4-head groups: the automatic plan for 13-16
+    query tokens (49-64 columns per KV head) takes 4 splits, run as the parts
+    of one workgroup (no workspace); with PA_FLAG_BF16_WEIGHTS, and for 9-12
+    tokens, it keeps 2 (two halves, no workspace); 8 and 17-32 tokens are
+    unchanged; a history too short for four 256-slot splits is not promoted."""
     plan = lambda T, w=False, MB=256, S=32: pa.paged_attn_extend_plan(S, 32, 8, 128, MB, 40000, torch.bfloat16, 16,
                                                                       T, bf16_weights=w)
-    for T in range(9, 17):
+    for T in range(13, 17):
         assert plan(T) == (4, 0)
         assert plan(T, True) == (2, 0)
+    for T in range(9, 13):  # the second 32-column wave at most half full: two halves
+        assert plan(T) == plan(T, True) == (2, 0)
     for T in (17, 24, 32):
         assert plan(T) == plan(T, True) == (2, 0)
     assert plan(8) == plan(8, True)
-    assert plan(12, MB=32) == plan(12, True, MB=32)  # 512 slots: at most 2 splits of 256
+    assert plan(16, MB=32) == plan(16, True, MB=32)  # 512 slots: at most 2 splits of 256
     # G = 1, 2, 8 and 16 take the same rule on their own column counts
-    for Hq, T in ((8, 40), (16, 20), (64, 7), (128, 4)):
-        P, ws = pa.paged_attn_extend_plan(32, Hq, 8, 128, 256, 40000, torch.bfloat16, 16, T)
-        assert shared_tile_quarters(torch.bfloat16, Hq // 8, T, P) == (P == 4) and ws == 0, (Hq, T, P, ws)
+    for Hq, T, P in ((8, 40, 2), (8, 49, 4), (16, 24, 2), (16, 25, 4), (64, 6, 2), (64, 7, 4), (128, 3, 2),
+                     (128, 4, 4)):
+        assert pa.paged_attn_extend_plan(32, Hq, 8, 128, 256, 40000, torch.bfloat16, 16, T) == (P, 0), (Hq, T)
 
 
 @no_gpu

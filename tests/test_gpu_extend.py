@@ -246,11 +246,12 @@ def test_verify_32x4096_T4_sampled():
     assert np.all(np.isfinite(out))
 
 
-@pytest.mark.parametrize("T,bf16_weights,parts", [(16, False, 4), (16, True, 2), (12, False, 4), (24, False, 2)])
+@pytest.mark.parametrize("T,bf16_weights,parts", [(16, False, 4), (16, True, 2), (13, False, 4), (12, False, 2),
+                                                  (24, False, 2)])
 def test_verify_32x4096_shared_tile_sampled(T, bf16_weights, parts):
     """The verification batch at full size with 12-24 draft tokens, in the
     automatic plan the benchmark times: four parts of one workgroup on the
-    32-column kernel (default weights, up to 16 tokens of 4-head groups), two
+    32-column kernel (default weights, 13-16 tokens of 4-head groups), two
     halves otherwise; sampled requests against the oracle."""
     banner(f"verify bf16 32x4096 T={T} bf16_weights={bf16_weights} ({parts} parts), sampled rows")
     b = W.verify_batch(device=DEV, T=T)

@@ -196,11 +196,12 @@ def test_physical_permutation_is_bitwise_invisible(dtype, T):
     assert np.array_equal(host_bits(out1), host_bits(out2))
 
 
-@pytest.mark.parametrize("T,splits", [(4, 0), (8, 3), (40, 0), (40, 2)])
+@pytest.mark.parametrize("T,splits", [(4, 0), (8, 3), (40, 0), (40, 2), (16, 2), (16, 4), (24, 2)])
 def test_graph_capture_replays_match_eager(T, splits):
     """A captured paged_attn_extend replays bit-identically, several times, with
     eager work between the replays (decode-kernel and shared-tile variants, with
-    and without the split merge)."""
+    and without the split merge, and the splits run as two halves or four parts
+    of one workgroup)."""
     banner(f"extend graph capture T={T} splits={splits}")
     b = W.extend_batch([9, 40, 300, 77, 130], T, Hq=8, Hkv=2, seed=95 + T, device=DEV)
     pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)

@@ -139,13 +139,16 @@ def calibrate_copy(torch, dev, n_bytes=1 << 30, reps=5):
     return 0
 
 
-def graph_time_us(torch, enqueue, launches, replays=5):
+def graph_time_us(torch, enqueue, launches, replays=5, settle_s=0.25):
     """Mean GPU time per launch, in microseconds, of ``launches`` calls of
     ``enqueue()`` captured in one HIP graph and replayed back to back.
 
     Used for kernels too short to time one by one from Python: the graph
     keeps the GPU fed, so the time is kernel time plus the graph's own
-    inter-kernel gap."""
+    inter-kernel gap.  Before the timed replays the graph is replayed for
+    ``settle_s`` seconds, untimed, so that the clocks have come up from the
+    idle of the workload's set-up (as the headline run's settle does): timed
+    straight after a set-up pause, a launch read up to 9 % slower."""
     enqueue()  # load the library and settle shapes outside the capture
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
@@ -154,6 +157,10 @@ def graph_time_us(torch, enqueue, launches, replays=5):
             enqueue()
     g.replay()
     torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < settle_s:
+        g.replay()
+        torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -412,7 +419,9 @@ def suite_markdown(S, command):
     w("(`bench.py --suite-md PATH` writes this summary from the same JSON, with `--suite-json` when the")
     w("suite has already run.)\n")
     w("Timing: each workload's launches are captured in one HIP graph and replayed back to back; the time")
-    w("per launch includes the graph's inter-kernel gap.  Decode rows: per-layer decode time over all")
+    w("per launch includes the graph's inter-kernel gap.  Each graph first replays untimed for 0.25 s so")
+    w("that the clocks have come up from the idle of the workload's set-up (suites taken before this")
+    w("settle read 2-9 % slower).  Decode rows: per-layer decode time over all")
     w("layers (each layer has its own K/V pools, so nothing is cache-resident across layers except where")
     w("noted).  Full step: the whole decode step of all layers (copy-on-write where the workload has it,")
     w("kv_append rounds, then paged_attn_decode per layer); fused: one paged_attn_decode_append per")

@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kWave * (kParts == 4 ? 2 : kWaves) * kParts, kParts
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x16_t{};
 
-  // LDS offsets this lane writes (rows 8w + 4i + c4, chunk n16) and reads.
+  // LDS offsets this lane writes (rows 4*kRG*w + 4i + c4, chunk n16) and reads.
   int wk_off[kRG], wv_off[kRG];
 #pragma unroll
   for (int i = 0; i < kRG; ++i) {

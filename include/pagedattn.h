@@ -267,12 +267,12 @@ pa_status paged_attn_decode_append(const void* q, const void* k_pool, const void
  * per request; T = 1 gives paged_attn_plan's answer.  The workspace holds
  * partial states for S*T*Hq rows.  With bf16, when every query token of a
  * (request, KV head) fits one workgroup of the several-token kernels, a
- * plan of 2 splits (and of 4 where the tokens fill at most 64 (token, head)
- * columns per KV head, as 9-16 tokens of a 4-head group) runs them as the
+ * plan of 2 splits (and of 4 where the tokens fill at most 96 (token, head)
+ * columns per KV head, as 9-24 tokens of a 4-head group) runs them as the
  * parts of one workgroup that merge inside it: no workspace (0 bytes).  The
  * automatic plan takes 4 splits where it would take 2 when the tokens fill
- * 49-64 columns (13-16 tokens of a 4-head group), except with
- * PA_FLAG_BF16_WEIGHTS.
+ * 49-64 columns (13-16 tokens of a 4-head group; not with
+ * PA_FLAG_BF16_WEIGHTS) or 65-96 columns (17-24 tokens).
  */
 pa_status paged_attn_extend_plan(const pa_dims* dims, int32_t B, int32_t num_q_tokens, int32_t* num_splits,
                                  size_t* workspace_bytes);

@@ -117,15 +117,20 @@ void plan_splits(const pa_dims* d, int32_t B, int32_t T, int* P_out, int* tps_ou
     const int64_t min_tokens = shared ? 256 : (mfma ? 64 * pa::kMfmaWaves : 16);
     const int64_t maxP = max_tokens / min_tokens > 1 ? max_tokens / min_tokens : 1;
     P = P < 1 ? 1 : (P > maxP ? maxP : P);
-    // 49-64 columns per KV head with the default weights: two splits become
-    // four, which run as the four parts of one workgroup on the 32-column
-    // kernel (its second wave then more than half full).  32 x 4096 tokens:
-    // 94-97 against 101-106 us for two halves of 16-column waves at 64
-    // columns (G = 1, 2, 4, 8, 16); at 40-48 columns the halves were 1-3 %
-    // faster, and with PA_FLAG_BF16_WEIGHTS 2-4 % faster, so those keep two.
+    // Two splits become four, which run as the four parts of one workgroup
+    // on the 32-column kernel, for 49-64 columns per KV head with the default
+    // weights (two waves per part, the second more than half full) and for
+    // 65-96 columns (three waves per part).  32 x 4096 tokens: at 64 columns
+    // 94-97 against 101-106 us for two halves of 16-column waves (G = 1, 2,
+    // 4, 8, 16), but at 40-48 columns the halves were 1-3 % faster, and with
+    // PA_FLAG_BF16_WEIGHTS 2-4 % faster; at 72-96 columns (T = 18-24, G = 4)
+    // 111.7-115.2 against 117.6-123.9 us for two halves of four 32-column
+    // waves, with bf16 weights 98.6-101.4 against 100.7-106.9 us.
     const int G = d->num_q_heads / d->num_kv_heads;
-    if (P == 2 && maxP >= 4 && shared && pa::shared_tile_sets(d->dtype, G, T) == 1 && (int64_t)T * G > 48 &&
-        !(d->flags & PA_FLAG_BF16_WEIGHTS))
+    const int sets = pa::shared_tile_sets(d->dtype, G, T);
+    if (P == 2 && maxP >= 4 && shared &&
+        ((sets == 1 && (int64_t)T * G > 48 && !(d->flags & PA_FLAG_BF16_WEIGHTS)) ||
+         (sets == 2 && (int64_t)T * G <= 96)))
       P = 4;
   }
   if (P > units) P = units;

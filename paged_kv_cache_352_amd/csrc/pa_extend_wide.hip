@@ -94,21 +94,33 @@ __device__ inline int vw_pos(int k, int t) { return (((k >> 1) ^ vw_perm(t)) << 
 // halves of four 16-column waves (pa_extend_mfma.hip): 95.3 against
 // 101.8-103.7 us, each wave's step on the 32x32 tiles doing a 16-column
 // wave's work twice over with fewer vector instructions per score, and half
-// as many steps and barriers.
-template <int G, int B, bool kOneRounding, bool kStream, int kParts = 1>
-__global__ __launch_bounds__(kWave * (kParts == 4 ? 2 : kWaves) * kParts, kParts > 1 ? 1 : 2) void extend_wide_kernel(
-    DecodeArgs a) {
+// as many steps and barriers.  kColsArg = 3 (four parts of three waves, up to
+// 96 columns: 17-24 tokens of a 4-head group) puts 12 waves, three per SIMD,
+// in the workgroup, held to 168 registers: q is read from LDS for every
+// product (24 KiB, written once by the first part) instead of 32 registers,
+// each wave loads 3 row groups of a step (the last wave 2), and the next
+// step is requested right after the current one is written to LDS, so one
+// set of row registers serves both.  The states are handed over in two
+// rounds.  Against two halves of four 32-column waves, the fourth of them
+// idle at 24 tokens, every SIMD then runs three waves over a quarter of the
+// history each instead of two over a half (or none): 32 x 4096 tokens,
+// T = 18-24, 111.7-115.2 against 117.6-123.9 us.
+template <int G, int B, bool kOneRounding, bool kStream, int kParts = 1, int kColsArg = 0>
+__global__ __launch_bounds__(kWave * (kColsArg ? kColsArg : (kParts == 4 ? 2 : kWaves)) * kParts,
+                             kParts > 1 ? 1 : 2) void extend_wide_kernel(DecodeArgs a) {
   constexpr bool kJoined = kParts > 1;  // the splits are parts of this workgroup
   static_assert(kParts == 1 || kParts == 2 || kParts == 4, "one, two or four splits per workgroup");
   static_assert(!kJoined || kStream, "parts: one workgroup per (request, KV head)");
-  constexpr int kCW = kParts == 4 ? 2 : kWaves;  // column waves per split
-  constexpr int kRG = 8 / kCW;                    // 4-row groups of a step each wave loads
+  constexpr int kCW = kColsArg ? kColsArg : (kParts == 4 ? 2 : kWaves);  // column waves per split
+  constexpr int kRG = (8 + kCW - 1) / kCW;  // 4-row groups of a step each wave loads (the last wave may load fewer)
+  constexpr bool kQLds = kCW == 3;           // q read from LDS each step (registers for 12 waves)
   static_assert(G >= 1 && G <= 16, "32 columns hold 32/G whole query tokens");
   static_assert(B >= 4 && B <= 64 && (B & (B - 1)) == 0, "block size: a power of two from 4 to 64");
   constexpr int TC = 32 / G;        // query tokens per wave
   constexpr int TW = kCW * TC;      // query tokens per workgroup
   // [part][buffer][K, V][step bytes]
   __shared__ __attribute__((aligned(16))) uint8_t steps_all[kParts][2][2][kStepBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t q_lds[kQLds ? kCW * 32 * 256 : 16];
 
   const int lane = threadIdx.x & (kWave - 1);
   // The wave index, in a scalar register (block offsets and table lanes
@@ -157,7 +169,8 @@ __global__ __launch_bounds__(kWave * (kParts == 4 ? 2 : kWaves) * kParts, kParts
   const bool neg_scale = a.scale_log2 < 0.f;
   const float c_log2 = neg_scale ? -a.scale_log2 : a.scale_log2;
   const uint32_t qsign = neg_scale ? 0x80008000u : 0u;
-  bf16x8_t qv[8];
+  bf16x8_t qv[kQLds ? 1 : 8];
+  const int q_base = 256 * (w * 32 + col);
   {
     const bool live = tq < a.T;  // columns past T get q = 0 and are never stored
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
@@ -167,12 +180,18 @@ __global__ __launch_bounds__(kWave * (kParts == 4 ? 2 : kWaves) * kParts, kParts
       uint4 v = *reinterpret_cast<const uint4*>(qp + 16 * kk + 8 * h);
       v = make_uint4(v.x ^ qsign, v.y ^ qsign, v.z ^ qsign, v.w ^ qsign);
       if (!live) v = make_uint4(0, 0, 0, 0);
-      qv[kk] = __builtin_bit_cast(bf16x8_t, v);
+      if constexpr (kQLds) {
+        if (grp == 0) *reinterpret_cast<uint4*>(q_lds + q_base + 16 * kw_pos(2 * kk + h, col)) = v;
+      } else {
+        qv[kk] = __builtin_bit_cast(bf16x8_t, v);
+      }
     }
+    if constexpr (kQLds) __syncthreads();
   }
 
-  // This wave loads slot rows 8w + 4i + c4 (i = 0, 1) of every step: lane l
-  // takes bytes 16*n16 .. +16 of KV head kvh.  A row group wholly past the
+  // This wave loads slot rows 4g + c4 of every step, row groups g = kRG*w + i
+  // below 8 (8w + 4i + c4 with four waves): lane l takes bytes 16*n16 .. +16
+  // of KV head kvh.  A row group wholly past the
   // history, past the split, or in a prefetch slot past the chunk (`none`)
   // goes through a descriptor of size 0: zeros, no memory read, and no table
   // entry at or past ceil(n / B) addresses the pool.
@@ -197,8 +216,9 @@ __global__ __launch_bounds__(kWave * (kParts == 4 ? 2 : kWaves) * kParts, kParts
   auto load_step = [&](int t, Rows& r, int eb, int tab, int te, bool none) {
 #pragma unroll
     for (int i = 0; i < kRG; ++i) {
-      const int tok = kTile * t + 4 * kRG * w + 4 * i;  // first slot of the row group
-      const bool live = !none && tok < n && (4 * kRG * w + 4 * i < kTile || t + 1 < te);
+      const int g = min(kRG * w + i, 7);  // the row group (past 7: none, the last wave's spare slot)
+      const int tok = kTile * t + 4 * g;  // first slot of the row group
+      const bool live = !none && kRG * w + i < 8 && tok < n && (4 * g < kTile || t + 1 < te);
       const int pb = live ? pool_block(__builtin_amdgcn_readlane(tab, tok / B - eb)) : 0;
       const int soff = live ? (tok % B) * row_bytes : 0;
       const uint32_t size = live ? blk_bytes : 0u;
@@ -214,11 +234,11 @@ __global__ __launch_bounds__(kWave * (kParts == 4 ? 2 : kWaves) * kParts, kParts
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x16_t{};
 
-  // LDS offsets this lane writes (rows 4*kRG*w + 4i + c4, chunk n16) and reads.
+  // LDS offsets this lane writes (rows 4g + c4, chunk n16) and reads.
   int wk_off[kRG], wv_off[kRG];
 #pragma unroll
   for (int i = 0; i < kRG; ++i) {
-    const int r = 4 * kRG * w + 4 * i + c4;
+    const int r = 4 * min(kRG * w + i, 7) + c4;
     wk_off[i] = 256 * r + 16 * kw_pos(n16, r);
     wv_off[i] = 256 * r + 16 * vw_pos(n16, r);
   }
@@ -239,25 +259,29 @@ __global__ __launch_bounds__(kWave * (kParts == 4 ? 2 : kWaves) * kParts, kParts
     }
   }
 
-  auto process = [&](int t, const Rows& r, int te) {
+  auto process = [&](int t, const Rows& r, int te, auto&& after_write) {
     const int buf = (t >> 1) & 1;
     uint8_t* kb_ = &steps[buf][0][0];
     uint8_t* vb_ = &steps[buf][1][0];
     const int valid = n - kTile * t;  // slots of the step inside the history
 #pragma unroll
-    for (int i = 0; i < kRG; ++i) *reinterpret_cast<uint4*>(kb_ + wk_off[i]) = r.k[i];
+    for (int i = 0; i < kRG; ++i)
+      if (kRG * w + i < 8) *reinterpret_cast<uint4*>(kb_ + wk_off[i]) = r.k[i];
     if (valid >= kStep) {  // the whole step lies inside the history (all but the last)
 #pragma unroll
-      for (int i = 0; i < kRG; ++i) *reinterpret_cast<uint4*>(vb_ + wv_off[i]) = r.v[i];
+      for (int i = 0; i < kRG; ++i)
+        if (kRG * w + i < 8) *reinterpret_cast<uint4*>(vb_ + wv_off[i]) = r.v[i];
     } else {
       // V past the history may hold anything (NaN): zeroed, since a zero
       // weight times NaN would still be NaN.
 #pragma unroll
       for (int i = 0; i < kRG; ++i) {
-        const int row = 4 * kRG * w + 4 * i + c4;
+        if (kRG * w + i >= 8) continue;
+        const int row = 4 * (kRG * w + i) + c4;
         *reinterpret_cast<uint4*>(vb_ + wv_off[i]) = row < valid ? r.v[i] : make_uint4(0, 0, 0, 0);
       }
     }
+    after_write();
     __syncthreads();
     if (idle || t >= te) return;
 
@@ -267,7 +291,13 @@ __global__ __launch_bounds__(kWave * (kParts == 4 ? 2 : kWaves) * kParts, kParts
     for (int kk = 0; kk < 8; ++kk) {
       const u32x4_t kv = *reinterpret_cast<const PA_LDS u32x4_t*>((const PA_LDS uint8_t*)kb_ + rk_base +
                                                                   16 * kw_pos(2 * kk + h, col));
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv), qv[kk], sc, 0, 0, 0);
+      bf16x8_t qk;
+      if constexpr (kQLds)
+        qk = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const PA_LDS u32x4_t*>(
+                                              (const PA_LDS uint8_t*)q_lds + q_base + 16 * kw_pos(2 * kk + h, col)));
+      else
+        qk = qv[kk];
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kv), qk, sc, 0, 0, 0);
     }
 
     // Slots of this step the column may see: below its limit, and in the
@@ -385,6 +415,17 @@ __global__ __launch_bounds__(kWave * (kParts == 4 ? 2 : kWaves) * kParts, kParts
       const int ce = min(c_u1, cb + kChunkTiles) - cb;
       const int eb = (kTile * tb) / B;
       const int tab = tb < te ? trow[min(eb + lane, nb - 1)] : 0;
+      if constexpr (kQLds) {
+        // One set of row registers: the next step is requested right after
+        // the current one is written to LDS, before the barrier.
+        Rows cur;
+        load_step(max(tb, min(tb, te - 1)), cur, eb, tab, te, tb >= te);
+        for (int t = 0; t < ce; t += 2) {
+          const int tn = tb + t + 2;
+          process(tb + t, cur, te, [&] { load_step(max(tb, min(tn, te - 1)), cur, eb, tab, te, tn >= te); });
+        }
+        continue;
+      }
       Rows ring[kDepth];
       load_step(max(tb, min(tb, te - 1)), ring[0], eb, tab, te, tb >= te);
       for (int t = 0; t < ce; t += 2 * kDepth) {
@@ -393,7 +434,7 @@ __global__ __launch_bounds__(kWave * (kParts == 4 ? 2 : kWaves) * kParts, kParts
           const int tn = tb + t + 2 * (b + 1);
           load_step(max(tb, min(tn, te - 1)), ring[(b + 1) % kDepth], eb, tab, te, tn >= te);
           __builtin_amdgcn_sched_barrier(0);
-          process(tb + t + 2 * b, ring[b], te);
+          process(tb + t + 2 * b, ring[b], te, [] {});
           if (t + 2 * b + 2 >= ce) break;
         }
       }
@@ -411,7 +452,7 @@ __global__ __launch_bounds__(kWave * (kParts == 4 ? 2 : kWaves) * kParts, kParts
           const int tn = t + 2 * (b + 1);  // the step to prefetch; past the chunk: loads that fetch nothing
           load_step(min(tn, te - 1), ring[(b + 1) % kDepth], eb, tab, te, tn >= te);
           __builtin_amdgcn_sched_barrier(0);  // issue the prefetch before the current step's math
-          process(t + 2 * b, ring[b], te);
+          process(t + 2 * b, ring[b], te, [] {});
           if (t + 2 * b + 2 >= te) break;
         }
       }
@@ -430,64 +471,78 @@ __global__ __launch_bounds__(kWave * (kParts == 4 ? 2 : kWaves) * kParts, kParts
   const float nan = __builtin_nanf("");
   if constexpr (kParts == 4) {
     // Parts 1-3 hand their states to part 0, lane for lane, through the
-    // steps' LDS in one round; part 0 merges the four as the merge kernel
-    // does (M, then 2^(m_p - M) weights folded in split order, o * (1 / L))
-    // and writes the output.
+    // steps' LDS (in two rounds of two accumulator blocks when one does not
+    // fit); part 0 merges the four as the merge kernel does (M, then
+    // 2^(m_p - M) weights folded in split order, o * (1 / L)) and writes the
+    // output.
     float* xs = reinterpret_cast<float*>(&steps_all[0][0][0][0]);
-    constexpr int kSlot = 2 + 64;
+    constexpr bool kOneRound = (kParts - 1) * kCW * kWave * (2 + 64) * 4 <= (int)sizeof(steps_all);
+    constexpr int kRounds = kOneRound ? 1 : 2;
+    constexpr int kMB = 4 / kRounds;  // accumulator blocks per round
+    constexpr int kSlot = 2 + 16 * kMB;
     static_assert((kParts - 1) * kCW * kWave * kSlot * 4 <= (int)sizeof(steps_all), "the states fit the steps");
-    if (grp > 0) {
-      const int slot = (((grp - 1) * kCW + w) * kWave + lane) * kSlot;
-      xs[slot] = m;
-      xs[slot + 1] = lc;
+    float wq[kParts];
+    float inv = 0.f;
+    bool empty = true;
+    const int64_t row = ((int64_t)s * a.T + tq) * a.Hq + kvh * G + col % G;
+    float* dst = a.out + row * kHeadDim + 4 * h;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) xs[slot + 2 + 16 * mb + r] = acc[mb][r];
-    }
-    __syncthreads();
-    if (grp == 0 && tq < a.T) {
-      float mv[kParts], lv[kParts];
-      mv[0] = bad ? 0.f : m;
-      lv[0] = bad ? nan : lc;
-#pragma unroll
-      for (int q = 1; q < kParts; ++q) {
-        const int slot = (((q - 1) * kCW + w) * kWave + lane) * kSlot;
-        mv[q] = bad ? 0.f : xs[slot];
-        lv[q] = bad ? nan : xs[slot + 1];
-      }
-      float M = kNegInf;
-#pragma unroll
-      for (int q = 0; q < kParts; ++q) M = fmaxf(M, mv[q]);
-      const bool empty = M == kNegInf;
-      float wq[kParts];
-      float L = 0.f;
-#pragma unroll
-      for (int q = 0; q < kParts; ++q) {
-        wq[q] = empty ? 0.f : fast_exp2(mv[q] - M);
-        L = fmaf(wq[q], lv[q], L);
-      }
-      const float inv = 1.f / L;
-      const int64_t row = ((int64_t)s * a.T + tq) * a.Hq + kvh * G + col % G;
-      float* dst = a.out + row * kHeadDim + 4 * h;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          float o[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float x = 0.f;
-            x = fmaf(wq[0], acc[mb][4 * q4 + e], x);
-#pragma unroll
-            for (int q = 1; q < kParts; ++q) {
-              const int slot = (((q - 1) * kCW + w) * kWave + lane) * kSlot;
-              x = fmaf(wq[q], xs[slot + 2 + 16 * mb + 4 * q4 + e], x);
-            }
-            o[e] = empty ? 0.f : x * inv;
-          }
-          *reinterpret_cast<float4*>(dst + 32 * mb + 8 * q4) = make_float4(o[0], o[1], o[2], o[3]);
+    for (int round = 0; round < kRounds; ++round) {
+      if (round > 0) __syncthreads();  // the previous round's values have been read
+      if (grp > 0) {
+        const int slot = (((grp - 1) * kCW + w) * kWave + lane) * kSlot;
+        if (round == 0) {
+          xs[slot] = m;
+          xs[slot + 1] = lc;
         }
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xs[slot + 2 + 16 * mb + r] = acc[kMB * round + mb][r];
+      }
+      __syncthreads();
+      if (grp == 0 && tq < a.T) {
+        if (round == 0) {
+          float mv[kParts], lv[kParts];
+          mv[0] = bad ? 0.f : m;
+          lv[0] = bad ? nan : lc;
+#pragma unroll
+          for (int q = 1; q < kParts; ++q) {
+            const int slot = (((q - 1) * kCW + w) * kWave + lane) * kSlot;
+            mv[q] = bad ? 0.f : xs[slot];
+            lv[q] = bad ? nan : xs[slot + 1];
+          }
+          float M = kNegInf;
+#pragma unroll
+          for (int q = 0; q < kParts; ++q) M = fmaxf(M, mv[q]);
+          empty = M == kNegInf;
+          float L = 0.f;
+#pragma unroll
+          for (int q = 0; q < kParts; ++q) {
+            wq[q] = empty ? 0.f : fast_exp2(mv[q] - M);
+            L = fmaf(wq[q], lv[q], L);
+          }
+          inv = 1.f / L;
+        }
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float x = 0.f;
+              x = fmaf(wq[0], acc[kMB * round + mb][4 * q4 + e], x);
+#pragma unroll
+              for (int q = 1; q < kParts; ++q) {
+                const int slot = (((q - 1) * kCW + w) * kWave + lane) * kSlot;
+                x = fmaf(wq[q], xs[slot + 2 + 16 * mb + 4 * q4 + e], x);
+              }
+              o[e] = empty ? 0.f : x * inv;
+            }
+            *reinterpret_cast<float4*>(dst + 32 * (kMB * round + mb) + 8 * q4) = make_float4(o[0], o[1], o[2], o[3]);
+          }
+      }
     }
     return;
   } else if constexpr (kJoined) {
@@ -991,8 +1046,12 @@ void launch_gbr(const DecodeArgs& a, hipStream_t stream) {
     return;
   }
   if (shared_tile_quarters(PA_BF16, G, a.T, a.P)) {
-    hipLaunchKernelGGL((extend_wide_kernel<G, B, kOneRounding, true, 4>), dim3(items / 4), dim3(4 * kWave * 2), 0,
-                       stream, a);
+    if (shared_tile_sets(PA_BF16, G, a.T) == 2)
+      hipLaunchKernelGGL((extend_wide_kernel<G, B, kOneRounding, true, 4, 3>), dim3(items / 4), dim3(4 * kWave * 3),
+                         0, stream, a);
+    else
+      hipLaunchKernelGGL((extend_wide_kernel<G, B, kOneRounding, true, 4>), dim3(items / 4), dim3(4 * kWave * 2), 0,
+                         stream, a);
     return;
   }
   if (shared_tile_halves(PA_BF16, G, a.T, a.P)) {

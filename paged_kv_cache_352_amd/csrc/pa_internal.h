@@ -122,13 +122,15 @@ constexpr bool shared_tile_halves(pa_dtype dtype, int G, int T, int P) {
   return use_shared_tile(dtype, G, T) && !use_pingpong(dtype, G, T) && P == 2;
 }
 
-// A four-split plan of the one-set-per-wave case (33-64 (token, head)
-// columns per KV head, e.g. 9-16 tokens of a 4-head group) runs on the
-// 32-column kernel as one workgroup of four parts of two 32-column waves,
-// one part per split, that merge their states in LDS at the end (no split
-// workspace, no merge kernel).
+// A four-split plan of up to 96 (token, head) columns per KV head runs on
+// the 32-column kernel as one workgroup of four parts, one part per split,
+// that merge their states in LDS at the end (no split workspace, no merge
+// kernel): two 32-column waves per part for the one-set-per-wave case
+// (33-64 columns, e.g. 9-16 tokens of a 4-head group), three for 65-96
+// columns (17-24 tokens of a 4-head group).
 constexpr bool shared_tile_quarters(pa_dtype dtype, int G, int T, int P) {
-  return use_shared_tile(dtype, G, T) && shared_tile_sets(dtype, G, T) == 1 && P == 4;
+  return use_shared_tile(dtype, G, T) && (shared_tile_sets(dtype, G, T) == 1 || (int64_t)T * G <= 96) &&
+         !use_pingpong(dtype, G, T) && P == 4;
 }
 
 // Splits of one (request, KV head) that run as the parts of one workgroup

@@ -218,13 +218,14 @@ def shared_tile_halves(dt, G, T, P):
 
 
 def shared_tile_quarters(dt, G, T, P):
-    """Four splits of the one-set-per-wave case (bf16, more tokens than two
-    16-column sets hold, at most 64 (token, head) columns) run as one workgroup
-    of four parts of the 32-column kernel that merge in LDS: no workspace."""
+    """Four splits of the shared-tile case (bf16, more tokens than two 16-column
+    sets hold) with at most 64 (token, head) columns, or at most 96 once they
+    need two sets per wave, run as one workgroup of four parts of the 32-column
+    kernel that merge in LDS: no workspace."""
     if dt != torch.bfloat16:
         return False
     per_wave = 1 if G >= 16 else 16 // G
-    return T > 2 * per_wave and T <= 4 * per_wave and P == 4
+    return T > 2 * per_wave and (T <= 4 * per_wave or T * G <= 96) and P == 4
 
 
 def shared_tile_parts(dt, G, T, P):
@@ -267,8 +268,10 @@ def test_extend_plan_takes_four_parts_for_one_set_per_wave_with_default_weights(
     """32 requests of 4096 tokens, 4-head groups: the automatic plan for 13-16
     query tokens (49-64 columns per KV head) takes 4 splits, run as the parts
     of one workgroup (no workspace); with PA_FLAG_BF16_WEIGHTS, and for 9-12
-    tokens, it keeps 2 (two halves, no workspace); 8 and 17-32 tokens are
-    unchanged; a history too short for four 256-slot splits is not promoted."""
+    tokens, it keeps 2 (two halves, no workspace); 17-24 tokens (65-96
+    columns) take 4 with either weights (three waves per part); 8 and 25-32
+    tokens are unchanged; a history too short for four 256-slot splits is not
+    promoted."""
     plan = lambda T, w=False, MB=256, S=32: pa.paged_attn_extend_plan(S, 32, 8, 128, MB, 40000, torch.bfloat16, 16,
                                                                       T, bf16_weights=w)
     for T in range(13, 17):
@@ -276,13 +279,16 @@ def test_extend_plan_takes_four_parts_for_one_set_per_wave_with_default_weights(
         assert plan(T, True) == (2, 0)
     for T in range(9, 13):  # the second 32-column wave at most half full: two halves
         assert plan(T) == plan(T, True) == (2, 0)
-    for T in (17, 24, 32):
+    for T in range(17, 25):
+        assert plan(T) == plan(T, True) == (4, 0)
+    for T in (25, 32):
         assert plan(T) == plan(T, True) == (2, 0)
     assert plan(8) == plan(8, True)
     assert plan(16, MB=32) == plan(16, True, MB=32)  # 512 slots: at most 2 splits of 256
     # G = 1, 2, 8 and 16 take the same rule on their own column counts
     for Hq, T, P in ((8, 40, 2), (8, 49, 4), (16, 24, 2), (16, 25, 4), (64, 6, 2), (64, 7, 4), (128, 3, 2),
-                     (128, 4, 4)):
+                     (128, 4, 4), (8, 96, 4), (8, 97, 2), (16, 48, 4), (16, 49, 2), (64, 12, 4), (64, 13, 2),
+                     (128, 6, 4), (128, 7, 2)):
         assert pa.paged_attn_extend_plan(32, Hq, 8, 128, 256, 40000, torch.bfloat16, 16, T) == (P, 0), (Hq, T)
 
 

@@ -196,7 +196,7 @@ def test_physical_permutation_is_bitwise_invisible(dtype, T):
     assert np.array_equal(host_bits(out1), host_bits(out2))
 
 
-@pytest.mark.parametrize("T,splits", [(4, 0), (8, 3), (40, 0), (40, 2), (16, 2), (16, 4), (24, 2)])
+@pytest.mark.parametrize("T,splits", [(4, 0), (8, 3), (40, 0), (40, 2), (16, 2), (16, 4), (24, 2), (24, 4)])
 def test_graph_capture_replays_match_eager(T, splits):
     """A captured paged_attn_extend replays bit-identically, several times, with
     eager work between the replays (decode-kernel and shared-tile variants, with
@@ -248,12 +248,13 @@ def test_verify_32x4096_T4_sampled():
 
 
 @pytest.mark.parametrize("T,bf16_weights,parts", [(16, False, 4), (16, True, 2), (13, False, 4), (12, False, 2),
-                                                  (24, False, 2)])
+                                                  (24, False, 4), (24, True, 4), (20, False, 4)])
 def test_verify_32x4096_shared_tile_sampled(T, bf16_weights, parts):
     """The verification batch at full size with 12-24 draft tokens, in the
     automatic plan the benchmark times: four parts of one workgroup on the
-    32-column kernel (default weights, 13-16 tokens of 4-head groups), two
-    halves otherwise; sampled requests against the oracle."""
+    32-column kernel (two waves each for 13-16 tokens of 4-head groups with
+    the default weights, three each for 17-24 tokens), two halves otherwise;
+    sampled requests against the oracle."""
     banner(f"verify bf16 32x4096 T={T} bf16_weights={bf16_weights} ({parts} parts), sampled rows")
     b = W.verify_batch(device=DEV, T=T)
     assert pa.paged_attn_extend_plan(b.S, b.Hq, b.Hkv, b.D, b.MB, b.NB, b.dtype, b.B, T,
@@ -473,15 +474,21 @@ def test_two_halves_poison_only_their_request(T):
 @pytest.mark.parametrize("G,T,B,bf16_weights", [(4, 9, 16, False), (4, 12, 16, True), (4, 16, 16, False),
                                                 (4, 16, 4, False), (4, 16, 64, True), (4, 13, 8, False),
                                                 (4, 16, 32, False), (2, 32, 32, False), (1, 64, 16, False),
-                                                (8, 8, 16, True), (16, 4, 16, False)])
+                                                (8, 8, 16, True), (16, 4, 16, False),
+                                                (4, 17, 16, False), (4, 20, 16, True), (4, 24, 16, False),
+                                                (4, 24, 4, False), (4, 24, 64, True), (4, 21, 8, False),
+                                                (4, 24, 32, True), (1, 96, 16, False), (2, 40, 32, False),
+                                                (8, 12, 16, True), (16, 6, 16, False)])
 def test_four_splits_as_one_workgroup_of_four_parts(G, T, B, bf16_weights):
-    """Four splits of the one-set-per-wave case (at most 64 (token, head)
-    columns per KV head) run on the 32-column kernel as one workgroup of four
-    2-wave parts, one split each, every wave loading 16 rows of each step and
-    the parts merging in LDS: no workspace, no merge kernel.  Requests shorter
-    than a split leave later parts nothing of their own (they still pass every
-    barrier); lengths cross tile, block and split boundaries; T = 9 and 13 leave
-    the second wave of each part mostly padding columns."""
+    """Four splits of up to 64 (token, head) columns per KV head run on the
+    32-column kernel as one workgroup of four 2-wave parts, one split each,
+    every wave loading 16 rows of each step; 65-96 columns as four 3-wave parts
+    (12 waves, q read from LDS, 3 row groups per wave and 2 for the last, the
+    states handed over in two rounds).  The parts merge in LDS: no workspace,
+    no merge kernel.  Requests shorter than a split leave later parts nothing
+    of their own (they still pass every barrier); lengths cross tile, block and
+    split boundaries; T = 9, 13 and 17 leave the last wave of each part mostly
+    padding columns."""
     banner(f"extend four parts G={G} T={T} B={B} bf16_weights={bf16_weights}")
     lens = [T, T + 5, 140, 300, 1000, 1031, 2049, 16 * 64 + 1]
     b = W.extend_batch(lens, T, Hq=2 * G, Hkv=2, B=B, seed=500 + T + B, device=DEV)
@@ -490,7 +497,7 @@ def test_four_splits_as_one_workgroup_of_four_parts(G, T, B, bf16_weights):
     check(b, torch.bfloat16, f"four parts T={T} B={B}", num_splits=4, bf16_weights=bf16_weights)
 
 
-@pytest.mark.parametrize("T", [12, 16])
+@pytest.mark.parametrize("T", [12, 16, 24])
 def test_four_parts_poison_only_their_request(T):
     """An out-of-pool entry in the first, third or last split's range, a bad
     length: NaN for that request only, through the four parts' merge."""

@@ -111,17 +111,18 @@ def test_bf16_weights_flag(G, T, splits, B):
     assert not torch.equal(fast, exact)
 
 
-@pytest.mark.parametrize("T,bf16_weights", [(4, False), (40, False), (40, True), (300, False)])
-def test_negative_scale(T, bf16_weights):
+@pytest.mark.parametrize("T,bf16_weights,splits", [(4, False, 0), (40, False, 0), (40, True, 0), (300, False, 0),
+                                                   (16, False, 4), (24, True, 4)])
+def test_negative_scale(T, bf16_weights, splits):
     """A negative scale (legal, if unusual) reverses the order of the logits, and a
     zero scale weighs every visible position the same: the decode-kernel form (T = 4)
-    and the shared-tile kernel, which feeds q negated and the scale's magnitude to its
-    unmasked steps, both match the oracle."""
+    and the shared-tile kernel (also as four parts of one workgroup), which feeds q
+    negated and the scale's magnitude to its unmasked steps, both match the oracle."""
     for factor in (-3.0, 0.0):  # a zero scale: every visible position weighs the same
-        banner(f"extend bf16 scale x {factor} T={T} bf16_weights={bf16_weights}")
+        banner(f"extend bf16 scale x {factor} T={T} bf16_weights={bf16_weights} splits={splits}")
         b = W.extend_batch([T + 1, T + 60, T + 700], T, Hq=8, Hkv=2, seed=250 + T, device=DEV)
         b.scale = abs(b.scale) * factor
-        check(b, torch.bfloat16, f"scale x {factor} T={T}", bf16_weights=bf16_weights)
+        check(b, torch.bfloat16, f"scale x {factor} T={T}", num_splits=splits, bf16_weights=bf16_weights)
 
 
 @pytest.mark.parametrize("dtype,G,T", [(torch.bfloat16, 4, 1), (torch.bfloat16, 4, 5), (torch.bfloat16, 4, 8),
@@ -303,14 +304,16 @@ def test_chunked_prefill_matches_one_pass(dtype):
     assert_close(host_f32(torch.cat(outs, dim=1)), ref, dtype, "chunked prefill")
 
 
-@pytest.mark.parametrize("T,bf16_weights", [(5, False), (40, False), (40, True)])
-def test_rising_logits(T, bf16_weights):
+@pytest.mark.parametrize("T,bf16_weights,splits", [(5, False, 0), (40, False, 0), (40, True, 0), (16, False, 4),
+                                                   (16, True, 2), (24, False, 4), (24, True, 4)])
+def test_rising_logits(T, bf16_weights, splits):
     """Logits climbing along the history in stairs of 10 (14.4 in base 2, beyond the
     reference-move threshold of the matrix-core kernels), for the decode kernel's causal
-    form (T = 5) and the shared-tile kernel (T = 40)."""
+    form (T = 5), the shared-tile kernel (T = 40), and its splits run as two halves or
+    four parts of one workgroup, each part with its own reference max until the merge."""
     from tests.test_gpu_decode import _ramp_keys
 
-    banner(f"extend bf16 rising logits T={T}")
+    banner(f"extend bf16 rising logits T={T} bf16_weights={bf16_weights} splits={splits}")
     b = W.extend_batch([100, 600, 1500], T, Hq=8, Hkv=2, seed=71 + T, device=DEV)
     pa.kv_append_tokens(b.k_pool, b.v_pool, b.k_new, b.v_new, b.block_tables, b.positions, b.B)
     lens = b.seq_lens.cpu().numpy()
@@ -319,7 +322,7 @@ def test_rising_logits(T, bf16_weights):
         b.k_new[s, :, g] = r[int(lens[s]) - T:]
     host = HostExtend(b)
     out = pa.paged_attn_extend(b.q, b.k_pool, b.v_pool, b.block_tables, b.seq_lens, b.B, b.scale,
-                               bf16_weights=bf16_weights)
+                               bf16_weights=bf16_weights, num_splits=splits)
     torch.cuda.synchronize()
     assert_close(host_f32(out), host.oracle(), torch.bfloat16, f"rising logits T={T}")
 
